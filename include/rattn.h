@@ -1,0 +1,160 @@
+/*
+ * rattn.h -- fused residual attention over a shared base KV cache (AMD Instinct
+ * MI355X, gfx950).  C ABI.
+ *
+ * The method (ForkKV Guide, "The Copy-on-Write Paradigm" and "Fused
+ * ResidualAttention"; LRAgent, "Schemi di Condivisione" and
+ * "Flash-LoRA-Attention"): N LoRA agents share one base KV cache of a common
+ * prefix (K_base, V_base: the bCache), and agent a keeps only rank-r residual
+ * caches Lk_a, Lv_a (the rCache / "LR cache", the down-projected activations
+ * X A) and the up-projections Bk_a, Bv_a, so that
+ *     K_a = K_base + Lk_a Bk_a,      V_a = V_base + Lv_a Bv_a.
+ * The library computes softmax(q K_a^T * scale) V_a for every agent without
+ * materialising K_a or V_a, using
+ *     q K_a^T = q K_base^T + (q Bk_a^T) Lk_a^T     (ForkKV Guide, "Mathematical
+ *                                                   Formulation of ResidualAttention")
+ *     P V_a   = P V_base + (P Lv_a) Bv_a            (LRAgent, Flash-LoRA-Attention).
+ * The LoRA scale alpha/r is folded into Bk and Bv by the caller.
+ *
+ * Notation.  N agents; H_q query heads and H_kv KV heads (H_q % H_kv == 0);
+ * query head h reads KV head floor(h / (H_q/H_kv)) (consecutive query heads share
+ * a KV head); head dimension d; rank r; shared prefix length L; S private tokens
+ * per agent; q_len query tokens per agent.
+ *
+ * Conventions for every entry point.
+ *   - All tensor pointers are DEVICE pointers, owned by the caller, row-major,
+ *     contiguous, and 16-byte aligned.  The library never allocates, frees or
+ *     synchronises; work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns before it finishes.
+ *   - Every argument is validated on the host before any HIP call.  A negative
+ *     rattn_status is returned and nothing is launched when validation fails.
+ *     A failed launch returns RATTN_E_HIP.  Faults during execution surface at
+ *     the caller's next synchronisation.
+ *   - Block-table entries must lie in [0, n_phys_pages); this is not checked on
+ *     the device (an out-of-range entry is undefined behaviour).  Duplicate
+ *     entries (aliased pages) are allowed.
+ *   - The library keeps no global mutable state and is reentrant, except that
+ *     rattn_last_hip_error() reports the calling thread's last HIP failure.
+ */
+#ifndef RATTN_H
+#define RATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RATTN_VERSION 1
+
+typedef enum rattn_status {
+    RATTN_OK = 0,
+    RATTN_E_NULL = -1,        /* a required pointer is NULL (or a forbidden one is not) */
+    RATTN_E_SHAPE = -2,       /* inconsistent or out-of-range sizes */
+    RATTN_E_UNSUPPORTED = -3, /* valid, but outside what the kernels implement */
+    RATTN_E_WORKSPACE = -4,   /* workspace NULL or smaller than rattn_workspace_bytes */
+    RATTN_E_ALIGN = -5,       /* a pointer is not 16-byte aligned */
+    RATTN_E_HIP = -6          /* a HIP runtime call or kernel launch failed */
+} rattn_status;
+
+typedef enum rattn_dtype {
+    RATTN_F32 = 0, /* IEEE binary32 */
+    RATTN_BF16 = 1 /* bfloat16 */
+} rattn_dtype;
+
+typedef enum rattn_op {
+    RATTN_OP_DECODE = 0,
+    RATTN_OP_PREFILL = 1
+} rattn_op;
+
+/* Shape of one call (one layer). */
+typedef struct rattn_desc {
+    int32_t n_agents;     /* N >= 1 */
+    int32_t n_q_heads;    /* H_q >= 1, a multiple of n_kv_heads */
+    int32_t n_kv_heads;   /* H_kv >= 1 */
+    int32_t head_dim;     /* d: 64 or 128 */
+    int32_t rank;         /* r: 0 (no residual), 8, 16, 32, 64 or 128 */
+    int32_t q_len;        /* query tokens per agent (decode: >= 1; prefill: == priv_len) */
+    int64_t prefix_len;   /* L >= 0: shared base tokens */
+    int64_t priv_len;     /* S >= 0: private tokens per agent; L + S >= 1 */
+    int32_t page_size;    /* 0: contiguous base cache; else a multiple of 16 (paged pool) */
+    int32_t shared_lr;    /* 0: per-agent Lk/Lv; 1: one Lk/Lv for all agents (BaseLRShared) */
+    int64_t n_phys_pages; /* pages in the pool (paged only) */
+    int32_t dtype;        /* rattn_dtype of q, caches and up-projections */
+    float sm_scale;       /* softmax scale; <= 0 means 1/sqrt(head_dim) */
+} rattn_desc;
+
+/* Tensors of one call.  Shapes use the descriptor's names. */
+typedef struct rattn_args {
+    const void *q;             /* [N, q_len, H_q, d] */
+    const void *k_base;        /* contiguous: [H_kv, L, d]; paged: pool [n_phys_pages, H_kv, page_size, d] */
+    const void *v_base;        /* same layout as k_base */
+    const int32_t *block_table;/* paged: [ceil(L / page_size)] physical page of each logical page; else NULL */
+    const void *lk;            /* [N, L, r], or [1, L, r] when shared_lr (NULL iff r == 0 or L == 0) */
+    const void *lv;            /* same layout as lk */
+    const void *bk;            /* [N, r, H_kv * d]; head k uses columns [k d, (k+1) d) (NULL iff r == 0) */
+    const void *bv;            /* same layout as bk */
+    const void *k_priv;        /* [N, H_kv, S, d] private keys, no residual (NULL iff S == 0) */
+    const void *v_priv;        /* [N, H_kv, S, d] */
+    float *out;                /* [N, q_len, H_q, d] fp32 */
+    float *lse;                /* [N, q_len, H_q] fp32 natural-log sum of exp of the scores, or NULL */
+} rattn_args;
+
+/* Bytes of device workspace that rattn_decode (op = RATTN_OP_DECODE) or
+ * rattn_prefill_chunk (op = RATTN_OP_PREFILL) needs for this descriptor.
+ * Returns a rattn_status; *bytes is written on success. */
+int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes);
+
+/*
+ * Decode: every one of the q_len query tokens of agent a attends the L prefix
+ * tokens (base + agent a's residual) and all S private tokens of agent a.
+ * Split-K over the context with an online softmax per split (partials in the
+ * workspace), then one merge that also applies Bv once per query row
+ * (LRAgent, Flash-LoRA-Attention: B is applied once per query block).
+ * `workspace` must hold rattn_workspace_bytes(desc, RATTN_OP_DECODE) bytes; its
+ * contents on entry do not matter and are garbage on exit.
+ */
+int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace, size_t workspace_bytes,
+                 void *stream);
+
+/*
+ * Chunked prefill: agent a appends a chunk of C = priv_len = q_len new tokens
+ * whose keys/values are k_priv/v_priv[a]; chunk query t attends the L prefix
+ * tokens and chunk tokens 0..t (causal).  Same residual algebra as decode.
+ */
+int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/*
+ * Copies the logical base cache of a paged pool into dst [H_kv, L, d] (same
+ * dtype): dst[k][j] = pool[block_table[j / page_size]][k][j % page_size].
+ * Byte-exact.  Uses desc->n_kv_heads, head_dim, prefix_len, page_size,
+ * n_phys_pages, dtype.
+ */
+int rattn_gather_base(const rattn_desc *desc, const void *pool, const int32_t *block_table, void *dst,
+                      void *stream);
+
+/* Work decomposition chosen for a decode call (host-only introspection; no HIP call). */
+typedef struct rattn_plan_info {
+    int32_t n_prefix_splits;  /* context splits of the prefix */
+    int64_t prefix_split_len; /* tokens per prefix split */
+    int32_t n_priv_splits;    /* splits of each agent's private tokens */
+    int64_t priv_split_len;
+    int32_t row_blocks;       /* 16-row MFMA blocks per KV head over the prefix */
+    int32_t agents_per_block; /* agents whose query rows share one block */
+    int32_t resid_cols;       /* residual columns per block, padded (0 if r == 0) */
+    int32_t work_items;       /* workgroups of the split kernel */
+} rattn_plan_info;
+
+int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info);
+
+const char *rattn_status_str(int status);
+int rattn_version(void);
+/* hipError_t of the calling thread's last RATTN_E_HIP, or 0. */
+int rattn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RATTN_H */

@@ -1,0 +1,265 @@
+"""Python binding of librattn: fused residual attention over a shared base KV cache
+on AMD Instinct MI355X (gfx950).
+
+Thin marshalling over the C ABI declared in ``include/rattn.h`` (same names):
+shapes are read from the torch tensors, pointers and the current HIP stream are
+passed through ctypes, and the workspace is a torch allocation.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.  If the
+library has not been built, importing succeeds but every call raises.
+
+Tensor layouts (row-major, contiguous, on the GPU):
+  q        [N, q_len, H_q, d]
+  k_base   [H_kv, L, d], or a paged pool [n_phys, H_kv, page, d] with block_table [ceil(L/page)] int32
+  lk, lv   [N, L, r] (or [1, L, r] with shared_lr)
+  bk, bv   [N, r, H_kv*d]
+  k_priv   [N, H_kv, S, d]
+  out      [N, q_len, H_q, d] fp32,  lse [N, q_len, H_q] fp32
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "librattn.so")
+
+RATTN_F32, RATTN_BF16 = 0, 1
+RATTN_OP_DECODE, RATTN_OP_PREFILL = 0, 1
+STATUS = {0: "RATTN_OK", -1: "RATTN_E_NULL", -2: "RATTN_E_SHAPE", -3: "RATTN_E_UNSUPPORTED",
+          -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP"}
+EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
+           "rattn_decode_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error")
+
+
+class RattnError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = f"{what}: {STATUS.get(status, status)}"
+        if status == -6 and _lib is not None:
+            msg += f" (hipError {_lib.rattn_last_hip_error()})"
+        super().__init__(msg)
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [
+        ("n_agents", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("rank", ctypes.c_int32), ("q_len", ctypes.c_int32),
+        ("prefix_len", ctypes.c_int64), ("priv_len", ctypes.c_int64),
+        ("page_size", ctypes.c_int32), ("shared_lr", ctypes.c_int32),
+        ("n_phys_pages", ctypes.c_int64), ("dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+    ]
+
+
+class Args(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out",
+                 "lse")]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("n_prefix_splits", ctypes.c_int32), ("prefix_split_len", ctypes.c_int64),
+                ("n_priv_splits", ctypes.c_int32), ("priv_split_len", ctypes.c_int64),
+                ("row_blocks", ctypes.c_int32), ("agents_per_block", ctypes.c_int32),
+                ("resid_cols", ctypes.c_int32), ("work_items", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded librattn (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"librattn is not built ({LIB_PATH} missing): run "
+                               "`python -m shared_base_residual_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I = ctypes.c_void_p, ctypes.c_int
+        L.rattn_workspace_bytes.argtypes = [ctypes.POINTER(Desc), I, ctypes.POINTER(ctypes.c_size_t)]
+        L.rattn_decode.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P, ctypes.c_size_t, P]
+        L.rattn_prefill_chunk.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P, ctypes.c_size_t, P]
+        L.rattn_gather_base.argtypes = [ctypes.POINTER(Desc), P, P, P, P]
+        L.rattn_decode_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PlanInfo)]
+        L.rattn_status_str.argtypes = [I]
+        L.rattn_status_str.restype = ctypes.c_char_p
+        for f in ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
+                  "rattn_decode_plan", "rattn_version", "rattn_last_hip_error"):
+            getattr(L, f).restype = I
+        _lib = L
+    return _lib
+
+
+def make_desc(*, n_agents, n_q_heads, n_kv_heads, head_dim, rank, q_len, prefix_len, priv_len=0, page_size=0,
+              shared_lr=False, n_phys_pages=0, dtype=RATTN_BF16, sm_scale=0.0) -> Desc:
+    return Desc(n_agents, n_q_heads, n_kv_heads, head_dim, rank, q_len, prefix_len, priv_len, page_size,
+                int(bool(shared_lr)), n_phys_pages, dtype, sm_scale)
+
+
+def workspace_bytes(desc: Desc, op: int = RATTN_OP_DECODE) -> int:
+    n = ctypes.c_size_t(0)
+    st = lib().rattn_workspace_bytes(ctypes.byref(desc), op, ctypes.byref(n))
+    if st:
+        raise RattnError(st, "rattn_workspace_bytes")
+    return n.value
+
+
+def decode_plan(desc: Desc) -> dict:
+    info = PlanInfo()
+    st = lib().rattn_decode_plan(ctypes.byref(desc), ctypes.byref(info))
+    if st:
+        raise RattnError(st, "rattn_decode_plan")
+    return {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def describe(q, k_base, lk=None, bk=None, *, block_table=None, k_priv=None, prefix_len=None, shared_lr=None,
+             sm_scale=0.0, op=RATTN_OP_DECODE) -> Desc:
+    """Descriptor read off the tensors' shapes."""
+    import torch
+
+    if q.dim() != 4:
+        raise ValueError("q must be [N, q_len, H_q, d]")
+    N, QL, HQ, D = q.shape
+    paged = block_table is not None
+    if k_base is not None:
+        if paged:
+            n_phys, HK, ps = k_base.shape[0], k_base.shape[1], k_base.shape[2]
+        else:
+            HK, ps, n_phys = k_base.shape[0], 0, 0
+    else:
+        HK = k_priv.shape[1]
+        ps, n_phys = 0, 0
+    if prefix_len is None:
+        if lk is not None:
+            prefix_len = lk.shape[1]
+        elif k_base is not None and not paged:
+            prefix_len = k_base.shape[1]
+        else:
+            raise ValueError("prefix_len must be given for a paged base cache without a low-rank cache")
+    r = bk.shape[1] if bk is not None else 0
+    if shared_lr is None:
+        shared_lr = lk is not None and lk.shape[0] == 1 and N > 1
+    S = k_priv.shape[2] if k_priv is not None else 0
+    if q.dtype == torch.bfloat16:
+        dt = RATTN_BF16
+    elif q.dtype == torch.float32:
+        dt = RATTN_F32
+    else:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    return make_desc(n_agents=N, n_q_heads=HQ, n_kv_heads=HK, head_dim=D, rank=r, q_len=QL,
+                     prefix_len=prefix_len, priv_len=S, page_size=ps, shared_lr=shared_lr,
+                     n_phys_pages=n_phys, dtype=dt, sm_scale=sm_scale)
+
+
+def _check_tensors(desc: Desc, tensors: dict):
+    """Marshalling checks the C ABI cannot make on raw pointers: device, dtype,
+    contiguity and shapes."""
+    import torch
+
+    dt = torch.bfloat16 if desc.dtype == RATTN_BF16 else torch.float32
+    N, QL, HQ, HK, D, r = desc.n_agents, desc.q_len, desc.n_q_heads, desc.n_kv_heads, desc.head_dim, desc.rank
+    L, S = desc.prefix_len, desc.priv_len
+    nlr = 1 if desc.shared_lr else N
+    want = {"q": (N, QL, HQ, D), "lk": (nlr, L, r), "lv": (nlr, L, r), "bk": (N, r, HK * D),
+            "bv": (N, r, HK * D), "k_priv": (N, HK, S, D), "v_priv": (N, HK, S, D),
+            "out": (N, QL, HQ, D), "lse": (N, QL, HQ)}
+    if desc.page_size:
+        want["k_base"] = want["v_base"] = (desc.n_phys_pages, HK, desc.page_size, D)
+        want["block_table"] = ((L + desc.page_size - 1) // desc.page_size,)
+    else:
+        want["k_base"] = want["v_base"] = (HK, L, D)
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        exp_dt = torch.float32 if name in ("out", "lse") else (torch.int32 if name == "block_table" else dt)
+        if t.dtype != exp_dt:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {exp_dt}")
+        if name in want and tuple(t.shape) != want[name]:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want[name]}")
+
+
+def _run(fn_name, op, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_priv, shared_lr, out, lse,
+         workspace, sm_scale, prefix_len, stream, desc):
+    import torch
+
+    if desc is None:
+        desc = describe(q, k_base, lk, bk, block_table=block_table, k_priv=k_priv, prefix_len=prefix_len,
+                        shared_lr=shared_lr, sm_scale=sm_scale, op=op)
+    if out is None:
+        out = torch.empty(tuple(q.shape), device=q.device, dtype=torch.float32)
+    tensors = dict(q=q, k_base=k_base, v_base=v_base, block_table=block_table, lk=lk, lv=lv, bk=bk, bv=bv,
+                   k_priv=k_priv, v_priv=v_priv, out=out, lse=lse)
+    _check_tensors(desc, tensors)
+    nbytes = workspace_bytes(desc, op)
+    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    args = Args(*[_ptr(tensors[n]) for n in
+                  ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out",
+                   "lse")])
+    st = getattr(lib(), fn_name)(ctypes.byref(desc), ctypes.byref(args), ctypes.c_void_p(workspace.data_ptr()),
+                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
+    if st:
+        raise RattnError(st, fn_name)
+    return out
+
+
+def decode(q, k_base, v_base, lk=None, lv=None, bk=None, bv=None, *, block_table=None, k_priv=None,
+           v_priv=None, shared_lr=None, out=None, lse=None, workspace=None, sm_scale=0.0, prefix_len=None,
+           stream=None, desc: Optional[Desc] = None):
+    """rattn_decode: every query token of agent a attends the shared prefix (base +
+    agent a's low-rank residual) and all of agent a's private tokens.  Returns out."""
+    return _run("rattn_decode", RATTN_OP_DECODE, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_priv,
+                shared_lr, out, lse, workspace, sm_scale, prefix_len, stream, desc)
+
+
+def prefill_chunk(q, k_base, v_base, lk=None, lv=None, bk=None, bv=None, *, block_table=None, k_priv=None,
+                  v_priv=None, shared_lr=None, out=None, lse=None, workspace=None, sm_scale=0.0,
+                  prefix_len=None, stream=None, desc: Optional[Desc] = None):
+    """rattn_prefill_chunk: chunk query t of agent a attends the prefix and chunk
+    tokens 0..t (k_priv/v_priv hold the chunk's own keys and values)."""
+    return _run("rattn_prefill_chunk", RATTN_OP_PREFILL, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv,
+                v_priv, shared_lr, out, lse, workspace, sm_scale, prefix_len, stream, desc)
+
+
+def gather_base(pool, block_table, prefix_len: int, *, out=None, stream=None):
+    """rattn_gather_base: logical base cache [H_kv, L, d] from a paged pool."""
+    import torch
+
+    n_phys, HK, ps, D = pool.shape
+    dt = RATTN_BF16 if pool.dtype == torch.bfloat16 else RATTN_F32
+    desc = make_desc(n_agents=1, n_q_heads=HK, n_kv_heads=HK, head_dim=D, rank=0, q_len=1,
+                     prefix_len=prefix_len, page_size=ps, n_phys_pages=n_phys, dtype=dt)
+    if out is None:
+        out = torch.empty((HK, prefix_len, D), device=pool.device, dtype=pool.dtype)
+    _check_tensors(desc, dict(k_base=pool, block_table=block_table))
+    st = lib().rattn_gather_base(ctypes.byref(desc), ctypes.c_void_p(pool.data_ptr()),
+                                 ctypes.c_void_p(block_table.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                 _stream(stream))
+    if st:
+        raise RattnError(st, "rattn_gather_base")
+    return out
+
+
+def attend(inputs: dict, *, mode: str = "decode", shared_lr=None, prefix_len=None, out=None, lse=None,
+           workspace=None, stream=None):
+    """Runs decode or prefill on a dict of device tensors named as in the layouts above."""
+    fn = decode if mode == "decode" else prefill_chunk
+    return fn(inputs["q"], inputs["k_base"], inputs["v_base"], inputs.get("lk"), inputs.get("lv"),
+              inputs.get("bk"), inputs.get("bv"), block_table=inputs.get("block_table"),
+              k_priv=inputs.get("k_priv"), v_priv=inputs.get("v_priv"), shared_lr=shared_lr,
+              prefix_len=prefix_len, out=out, lse=lse, workspace=workspace, stream=stream)

@@ -1,0 +1,336 @@
+// api.cpp -- C ABI of librattn: host-side validation, work decomposition and
+// dispatch.  Every check runs before the first HIP call, so argument errors
+// return a status without touching the device.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/rattn.h"
+#include "internal.h"
+
+namespace rattn {
+hipError_t launch_decode(int bf16_in, const DecodeParams &dp, const CombineParams &cp, const UParams &up, int D,
+                         int cpad, size_t lds, hipStream_t st);
+hipError_t launch_gather(const void *pool, const int32_t *table, void *dst, int64_t L, int HK, int ps,
+                         int row_bytes, hipStream_t st);
+}  // namespace rattn
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+constexpr int kMaxSlots = 1024;     // splits per query row the merge handles in LDS
+constexpr int kTargetItems = 512;   // split-kernel workgroups aimed for (2 per CU)
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t roundup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int pow2ceil(int x) {
+    int v = 1;
+    while (v < x) v <<= 1;
+    return v;
+}
+
+size_t esize(int dtype) { return dtype == RATTN_BF16 ? 2 : 4; }
+
+int check_desc(const rattn_desc *d, int op) {
+    if (!d) return RATTN_E_NULL;
+    if (d->n_agents < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->rank < 0 ||
+        d->q_len < 1 || d->prefix_len < 0 || d->priv_len < 0 || d->page_size < 0 || d->n_phys_pages < 0)
+        return RATTN_E_SHAPE;
+    if (d->n_q_heads % d->n_kv_heads) return RATTN_E_SHAPE;
+    if (d->prefix_len + d->priv_len < 1) return RATTN_E_SHAPE;
+    if (d->dtype != RATTN_F32 && d->dtype != RATTN_BF16) return RATTN_E_UNSUPPORTED;
+    if (d->shared_lr != 0 && d->shared_lr != 1) return RATTN_E_SHAPE;
+    if (d->head_dim != 64 && d->head_dim != 128) return RATTN_E_UNSUPPORTED;
+    const int r = d->rank;
+    if (!(r == 0 || r == 8 || r == 16 || r == 32 || r == 64 || r == 128)) return RATTN_E_UNSUPPORTED;
+    if (d->page_size > 0) {
+        if (d->page_size % 16) return RATTN_E_UNSUPPORTED;
+        if (d->prefix_len > 0 && d->n_phys_pages < 1) return RATTN_E_SHAPE;
+    }
+    if (op == RATTN_OP_PREFILL && d->q_len != d->priv_len) return RATTN_E_SHAPE;
+    if (op != RATTN_OP_DECODE && op != RATTN_OP_PREFILL) return RATTN_E_SHAPE;
+    // Index arithmetic inside the kernels uses 32-bit row and item counts.
+    const int64_t rows = (int64_t)d->n_agents * d->q_len * d->n_q_heads;
+    if (rows > (1ll << 28) || d->prefix_len > (1ll << 31) || d->priv_len > (1ll << 31))
+        return RATTN_E_UNSUPPORTED;
+    return RATTN_OK;
+}
+
+struct Plan {
+    rattn::DecodeParams dp;
+    int cpad;
+    size_t lds;
+    size_t off_u, off_ml, off_o, off_w, total;
+};
+
+int make_plan(const rattn_desc *d, int op, Plan *pl) {
+    rattn::DecodeParams &p = pl->dp;
+    p = rattn::DecodeParams{};
+    const int N = d->n_agents, HK = d->n_kv_heads, g = d->n_q_heads / d->n_kv_heads, r = d->rank;
+    const int D = d->head_dim;
+    const int64_t L = d->prefix_len, S = d->priv_len;
+    const int rpa = d->q_len * g;
+    const bool resid = r > 0 && L > 0;
+    p.L = L;
+    p.S = S;
+    p.N = N;
+    p.QL = d->q_len;
+    p.HQ = d->n_q_heads;
+    p.HK = HK;
+    p.g = g;
+    p.r = r;
+    p.rpa = rpa;
+    p.ps = d->page_size;
+    p.shared_lr = d->shared_lr;
+    p.causal = op == RATTN_OP_PREFILL;
+    const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
+    p.c = scale * 1.44269504088896340736f;
+
+    // Row blocks over the prefix.
+    if (rpa <= 16) {
+        int apb = 16 / rpa;
+        if (resid && !d->shared_lr) {
+            const int by_cols = rattn::kMaxResidCols / r;
+            if (by_cols < apb) apb = by_cols;
+        }
+        if (apb > N) apb = N;
+        if (apb < 1) apb = 1;
+        p.apb = apb;
+        p.bpa = 1;
+        p.n_blocks = (int)cdiv(N, apb);
+        p.pb = 1;
+    } else {
+        p.apb = 1;
+        p.bpa = (int)cdiv(rpa, 16);
+        p.n_blocks = N * p.bpa;
+        p.pb = p.bpa;
+    }
+    p.n_rg = (int)cdiv(p.n_blocks, 4);
+    p.n_prg = (int)cdiv(p.pb, 4);
+    int cols = 0;
+    if (resid) cols = d->shared_lr ? r : (rpa <= 16 ? p.apb * r : r);
+    pl->cpad = resid ? (pow2ceil(cols) < 32 ? 32 : pow2ceil(cols)) : 0;
+    if (pl->cpad > rattn::kMaxResidCols) return RATTN_E_UNSUPPORTED;
+
+    // Context splits.
+    if (L > 0) {
+        const int64_t base = (int64_t)HK * p.n_rg;
+        int64_t n = cdiv(kTargetItems, base);
+        const int64_t nmax = cdiv(L, rattn::kSplitQuantum);
+        if (n > nmax) n = nmax;
+        if (n < 1) n = 1;
+        // n splits of a 128-multiple length; trailing splits may be empty, which
+        // keeps the split count (and the workspace) non-decreasing in L.
+        p.tok_ps = roundup(cdiv(L, n), rattn::kSplitQuantum);
+        p.n_ps = (int)n;
+    }
+    if (S > 0) {
+        const int64_t base = (int64_t)N * HK * p.n_prg;
+        int64_t n = cdiv(kTargetItems, base);
+        const int64_t nmax = cdiv(S, rattn::kSplitQuantum);
+        if (n > nmax) n = nmax;
+        if (n < 1) n = 1;
+        p.tok_pv = roundup(cdiv(S, n), rattn::kSplitQuantum);
+        p.n_pv = (int)n;
+    }
+    p.n_slots = p.n_ps + p.n_pv;
+    if (p.n_slots > kMaxSlots) return RATTN_E_UNSUPPORTED;
+    const int64_t n_pre = (int64_t)p.n_ps * p.n_rg * HK;
+    const int64_t n_all = n_pre + (int64_t)N * p.n_prg * p.n_pv * HK;
+    if (n_all > (1ll << 30)) return RATTN_E_UNSUPPORTED;
+    p.n_prefix_items = (int)n_pre;
+    p.n_items = (int)n_all;
+    p.per_xcd = (int)cdiv(n_all, 8);
+
+    // Merge area of the split kernel: needed when some row group has fewer than
+    // four row blocks (several waves then share one block).
+    const bool share_pre = L > 0 && (p.n_blocks % 4 != 0);
+    const bool share_pv = S > 0 && (p.pb % 4 != 0);
+    const int cpl = pl->cpad > 0 ? pl->cpad / 16 : 1;
+    const int per_lane = 4 * (D / 16) + 4 * cpl;
+    pl->lds = (share_pre || share_pv) ? (size_t)3 * (64 * per_lane + 32) * sizeof(float) : 0;
+
+    // Workspace: U, then (max, sum), O and W partials.
+    const int64_t rows_kv = (int64_t)HK * N * rpa;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    pl->off_u = take(resid ? (size_t)N * d->q_len * d->n_q_heads * r * sizeof(float) : 0);
+    pl->off_ml = take((size_t)rows_kv * p.n_slots * 2 * sizeof(float));
+    pl->off_o = take((size_t)rows_kv * p.n_slots * D * sizeof(float));
+    pl->off_w = take(resid ? (size_t)rows_kv * p.n_slots * r * sizeof(float) : 0);
+    pl->total = off;
+    return RATTN_OK;
+}
+
+int check_args(const rattn_desc *d, const rattn_args *a) {
+    if (!a) return RATTN_E_NULL;
+    const bool paged = d->page_size > 0;
+    const bool pre = d->prefix_len > 0;
+    const bool resid = d->rank > 0 && pre;
+    if (!a->q || !a->out) return RATTN_E_NULL;
+    if (pre && (!a->k_base || !a->v_base)) return RATTN_E_NULL;
+    if (paged && pre && !a->block_table) return RATTN_E_NULL;
+    if (!paged && a->block_table) return RATTN_E_NULL;
+    if (resid && (!a->lk || !a->lv || !a->bk || !a->bv)) return RATTN_E_NULL;
+    if (d->priv_len > 0 && (!a->k_priv || !a->v_priv)) return RATTN_E_NULL;
+    const void *ptrs[] = {a->q, a->k_base, a->v_base, a->lk, a->lv, a->bk, a->bv, a->k_priv, a->v_priv, a->out};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return RATTN_E_ALIGN;
+    if (a->lse && !aligned(a->lse, 4)) return RATTN_E_ALIGN;
+    if (a->block_table && !aligned(a->block_table, 4)) return RATTN_E_ALIGN;
+    return RATTN_OK;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return RATTN_OK;
+    g_last_hip = (int)e;
+    return RATTN_E_HIP;
+}
+
+int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_bytes, void *stream, int op) {
+    int st = check_desc(d, op);
+    if (st) return st;
+    st = check_args(d, a);
+    if (st) return st;
+    Plan pl;
+    st = make_plan(d, op, &pl);
+    if (st) return st;
+    if (pl.total > 0 && !ws) return RATTN_E_WORKSPACE;
+    if (ws_bytes < pl.total) return RATTN_E_WORKSPACE;
+    if (ws && !aligned(ws, 256)) return RATTN_E_ALIGN;
+
+    char *w = static_cast<char *>(ws);
+    rattn::DecodeParams &p = pl.dp;
+    p.q = a->q;
+    p.kb = a->k_base;
+    p.vb = a->v_base;
+    p.table = a->block_table;
+    p.lk = a->lk;
+    p.lv = a->lv;
+    p.kp = a->k_priv;
+    p.vp = a->v_priv;
+    p.u = reinterpret_cast<const float *>(w + pl.off_u);
+    p.p_ml = reinterpret_cast<float *>(w + pl.off_ml);
+    p.p_o = reinterpret_cast<float *>(w + pl.off_o);
+    p.p_w = reinterpret_cast<float *>(w + pl.off_w);
+
+    rattn::CombineParams cp{};
+    cp.p_ml = p.p_ml;
+    cp.p_o = p.p_o;
+    cp.p_w = p.p_w;
+    cp.bv = a->bv;
+    cp.out = a->out;
+    cp.lse = a->lse;
+    cp.N = p.N;
+    cp.QL = p.QL;
+    cp.HQ = p.HQ;
+    cp.HK = p.HK;
+    cp.g = p.g;
+    cp.r = (d->rank > 0 && d->prefix_len > 0) ? d->rank : 0;
+    cp.rpa = p.rpa;
+    cp.n_slots = p.n_slots;
+    cp.n_ps = p.n_ps;
+    cp.S = p.S;
+
+    rattn::UParams up{};
+    up.q = a->q;
+    up.bk = a->bk;
+    up.u = reinterpret_cast<float *>(w + pl.off_u);
+    up.N = p.N;
+    up.QL = p.QL;
+    up.HQ = p.HQ;
+    up.HK = p.HK;
+    up.g = p.g;
+    up.r = p.r;
+    up.c = p.c;
+
+    return hip_status(rattn::launch_decode(d->dtype == RATTN_BF16, p, cp, up, d->head_dim, pl.cpad, pl.lds,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int rattn_version(void) { return RATTN_VERSION; }
+
+int rattn_last_hip_error(void) { return g_last_hip; }
+
+const char *rattn_status_str(int s) {
+    switch (s) {
+        case RATTN_OK: return "ok";
+        case RATTN_E_NULL: return "null or forbidden pointer";
+        case RATTN_E_SHAPE: return "inconsistent shape";
+        case RATTN_E_UNSUPPORTED: return "unsupported configuration";
+        case RATTN_E_WORKSPACE: return "workspace missing or too small";
+        case RATTN_E_ALIGN: return "misaligned pointer";
+        case RATTN_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes) {
+    if (!bytes) return RATTN_E_NULL;
+    int st = check_desc(desc, op);
+    if (st) return st;
+    Plan pl;
+    st = make_plan(desc, op, &pl);
+    if (st) return st;
+    *bytes = pl.total;
+    return RATTN_OK;
+}
+
+int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info) {
+    if (!info) return RATTN_E_NULL;
+    int st = check_desc(desc, RATTN_OP_DECODE);
+    if (st) return st;
+    Plan pl;
+    st = make_plan(desc, RATTN_OP_DECODE, &pl);
+    if (st) return st;
+    info->n_prefix_splits = pl.dp.n_ps;
+    info->prefix_split_len = pl.dp.tok_ps;
+    info->n_priv_splits = pl.dp.n_pv;
+    info->priv_split_len = pl.dp.tok_pv;
+    info->row_blocks = pl.dp.n_blocks;
+    info->agents_per_block = pl.dp.apb;
+    info->resid_cols = pl.cpad;
+    info->work_items = pl.dp.n_items;
+    return RATTN_OK;
+}
+
+int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace, size_t workspace_bytes,
+                 void *stream) {
+    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_DECODE);
+}
+
+int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_PREFILL);
+}
+
+int rattn_gather_base(const rattn_desc *d, const void *pool, const int32_t *block_table, void *dst,
+                      void *stream) {
+    if (!d) return RATTN_E_NULL;
+    if (d->n_kv_heads < 1 || d->head_dim < 1 || d->prefix_len < 0 || d->page_size < 0 || d->n_phys_pages < 0)
+        return RATTN_E_SHAPE;
+    if (d->dtype != RATTN_F32 && d->dtype != RATTN_BF16) return RATTN_E_UNSUPPORTED;
+    if (d->page_size == 0 || d->page_size % 16) return RATTN_E_UNSUPPORTED;
+    if ((d->head_dim * esize(d->dtype)) % 16) return RATTN_E_UNSUPPORTED;
+    if (d->prefix_len == 0) return RATTN_OK;
+    if (d->n_phys_pages < 1) return RATTN_E_SHAPE;
+    if (!pool || !block_table || !dst) return RATTN_E_NULL;
+    if (!aligned(pool, 16) || !aligned(dst, 16) || !aligned(block_table, 4)) return RATTN_E_ALIGN;
+    return hip_status(rattn::launch_gather(pool, block_table, dst, d->prefix_len, d->n_kv_heads, d->page_size,
+                                           (int)(d->head_dim * esize(d->dtype)), static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

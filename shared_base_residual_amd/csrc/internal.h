@@ -1,0 +1,93 @@
+// internal.h -- work decomposition shared by the host dispatcher and the HIP
+// kernels of librattn.  Not installed; the public interface is include/rattn.h.
+#pragma once
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define RATTN_HD __host__ __device__ inline
+#else
+#define RATTN_HD inline
+#endif
+
+namespace rattn {
+
+// Largest padded residual width (agents sharing a row block times r) a decode
+// row block may carry; bounds the split kernel's registers.
+constexpr int kMaxResidCols = 128;
+// Context tokens per split are a multiple of this (4 waves x 32-token chunks),
+// which also keeps every 16-token MFMA tile inside one 16-aligned page.
+constexpr int kSplitQuantum = 128;
+
+// Query rows of one KV head are ordered (agent, query token, head-in-group):
+// row = agent * rpa + t * g + hh, rpa = q_len * g rows per agent.  The rows are
+// cut into MFMA row blocks of at most 16 rows.  When an agent has <= 16 rows, a
+// block holds `apb` whole agents; otherwise an agent spans `bpa` blocks.
+struct RowBlock {
+    int a0;  // first agent
+    int na;  // agents in the block
+    int f;   // first row within the agent (rpa > 16 only)
+    int nr;  // valid rows (<= 16)
+};
+
+RATTN_HD RowBlock prefix_block(int b, int n_agents, int rpa, int apb, int bpa) {
+    RowBlock rb;
+    if (rpa <= 16) {
+        rb.a0 = b * apb;
+        rb.na = n_agents - rb.a0 < apb ? n_agents - rb.a0 : apb;
+        rb.f = 0;
+        rb.nr = rb.na * rpa;
+    } else {
+        rb.a0 = b / bpa;
+        rb.na = 1;
+        rb.f = 16 * (b % bpa);
+        rb.nr = rpa - rb.f < 16 ? rpa - rb.f : 16;
+    }
+    return rb;
+}
+
+// Agent and row-within-agent of row m (< nr) of a block.
+RATTN_HD void block_row(const RowBlock &rb, int m, int rpa, int *agent, int *ria) {
+    if (rpa <= 16) {
+        *agent = rb.a0 + m / rpa;
+        *ria = m % rpa;
+    } else {
+        *agent = rb.a0;
+        *ria = rb.f + m;
+    }
+}
+
+struct DecodeParams {
+    const void *q, *kb, *vb;
+    const int32_t *table;
+    const void *lk, *lv, *kp, *vp;
+    const float *u;   // [N*q_len*H_q, r] fp32, already multiplied by scale*log2(e)
+    float *p_ml;      // [H_kv, N*rpa, n_slots, 2]  running max (log2 units), sum of weights
+    float *p_o;       // [H_kv, N*rpa, n_slots, d]  unnormalised P V_base (+ private P V)
+    float *p_w;       // [H_kv, N*rpa, n_slots, r]  unnormalised P Lv
+    int64_t L, S;
+    int N, QL, HQ, HK, g, r, rpa, apb, bpa, ps, shared_lr;
+    int causal;       // private token j is visible to query token t only if j <= t
+    float c;          // softmax scale * log2(e)
+    int n_blocks, n_rg, n_ps;
+    int64_t tok_ps;
+    int pb, n_prg, n_pv;
+    int64_t tok_pv;
+    int n_slots, n_prefix_items, n_items, per_xcd;
+};
+
+struct CombineParams {
+    const float *p_ml, *p_o, *p_w;
+    const void *bv;
+    float *out, *lse;
+    int N, QL, HQ, HK, g, r, rpa, n_slots, n_ps;
+    int64_t S;
+};
+
+struct UParams {
+    const void *q, *bk;
+    float *u;
+    int N, QL, HQ, HK, g, r;
+    float c;
+};
+
+}  // namespace rattn

@@ -1,0 +1,216 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Inputs come from ``synth`` (seeded); expected values only from ``oracle``.
+Bars (tests/parity.py): max-abs 2e-2, mean-abs 2e-3, relative RMS 1e-2 (bf16) or
+1e-4 (fp32), and for the full workloads an error below 5 % of what the residual
+terms contribute.  Indexing results (page gather, shuffled vs identity table) are
+compared bit for bit.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def rattn():
+    import shared_base_residual_amd as R
+
+    R.lib()  # raises if the HIP library is missing
+    return R
+
+
+def run_gpu(case, x, lse=True):
+    R = rattn()
+    t = synth.to_torch(x, DEV)
+    lse_t = torch.empty(t["q"].shape[:3], device=DEV, dtype=torch.float32) if lse else None
+    out = R.attend(t, mode=case.mode, shared_lr=case.shared_lr, prefix_len=case.prefix_len, lse=lse_t)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), (lse_t.cpu().numpy().astype(np.float64) if lse else None)
+
+
+def ref(case, x, **kw):
+    return oracle.attend(case, x, **kw)
+
+
+def compare(case, x, *, with_b0=False, what="", row_mask=None):
+    say(f"[gpu] {what}: {case}")
+    got, got_lse = run_gpu(case, x)
+    exp, exp_lse = ref(case, x, row_mask=row_mask)
+    b0 = None
+    if with_b0:
+        b0, _ = ref(case, dict(x, bk=np.zeros_like(x["bk"]), bv=np.zeros_like(x["bv"])), row_mask=row_mask)
+    s = parity.check(got, exp, case.dtype, b0, what)
+    m = ~np.isnan(exp_lse)
+    assert np.abs(got_lse[m] - exp_lse[m]).max() <= 2e-3 * max(1.0, np.abs(exp_lse[m]).max()), what
+    say(f"[gpu] {what}: ok {s}")
+    return got, s
+
+
+# ------------------------------------------------------------- workloads --
+
+@pytest.mark.parametrize("variant", ["base", "stress"])
+def test_tiny_decode_fp32(variant):
+    c = synth.CONFIGS[0]
+    kw = synth.STRESS if variant == "stress" else {}
+    seed = 0 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0)
+    compare(c, synth.make_inputs(c, seed, **kw), with_b0=True, what=f"tiny decode fp32 {variant}")
+
+
+@pytest.mark.parametrize("variant", ["base", "stress"])
+def test_llama8b_decode(variant):
+    c = synth.CONFIGS[1]
+    kw = synth.STRESS if variant == "stress" else {}
+    seed = 1 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0)
+    compare(c, synth.make_inputs(c, seed, **kw), with_b0=(variant == "base"), what=f"8B decode {variant}")
+
+
+@pytest.mark.parametrize("variant", ["base", "stress"])
+def test_paged_cow_decode(variant):
+    c = synth.CONFIGS[2]
+    kw = synth.STRESS if variant == "stress" else {}
+    seed = 2 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0)
+    x = synth.make_inputs(c, seed, **kw)
+    got, _ = compare(c, x, with_b0=(variant == "base"), what=f"paged decode {variant}")
+    assert np.all(np.isfinite(got)), "NaN-poisoned unused pages reached the output"
+
+
+def _sample_rows(case, n, seed):
+    rng = np.random.default_rng(seed)
+    m = np.zeros((case.n_agents, case.q_len, case.n_q_heads), bool)
+    idx = rng.choice(m.size, size=min(n, m.size), replace=False)
+    m.reshape(-1)[idx] = True
+    # always include the first and last chunk positions of some agent
+    m[0, 0, 0] = m[-1, -1, -1] = True
+    return m
+
+
+def test_shared_lr_chunked_prefill_sampled():
+    c = synth.CONFIGS[3]
+    x = synth.make_inputs(c, 3)
+    mask = _sample_rows(c, 48, 0)
+    compare(c, x, with_b0=True, row_mask=mask, what="BaseLRShared prefill (sampled rows)")
+
+
+def test_full_depth_decode_sampled_layers():
+    """All 80 layers run back to back on one stream (as timed); sampled layers and
+    rows are checked against the oracle."""
+    R = rattn()
+    c = synth.CONFIGS[4]
+    say(f"[gpu] 70B full-depth decode: generating {c.layers} layers on the device")
+    layers = [synth.make_inputs_torch(c, 4, l, DEV) for l in range(c.layers)]
+    outs = [torch.empty(layers[0]["q"].shape, device=DEV, dtype=torch.float32) for _ in range(c.layers)]
+    desc = R.describe(layers[0]["q"], layers[0]["k_base"], layers[0]["lk"], layers[0]["bk"])
+    ws = torch.empty(R.workspace_bytes(desc), device=DEV, dtype=torch.uint8)
+    for l in range(c.layers):
+        R.attend(layers[l], out=outs[l], workspace=ws)
+    torch.cuda.synchronize()
+    say("[gpu] 70B full-depth decode: ran all layers")
+    errs = []
+    for l in (0, 41, 79):
+        x = {k: synth.torch_to_numpy(v) for k, v in layers[l].items()}
+        mask = _sample_rows(c, 24, l)
+        exp, _ = oracle.attend(c, x, row_mask=mask)
+        b0, _ = oracle.attend(c, dict(x, bk=np.zeros_like(x["bk"]), bv=np.zeros_like(x["bv"])), row_mask=mask)
+        got = outs[l].cpu().numpy().astype(np.float64)
+        errs.append(parity.check(got, exp, "bf16", b0, f"layer {l}"))
+        say(f"[gpu] layer {l}: {errs[-1]}")
+    del layers
+
+
+# ------------------------------------------------------------ edge cases --
+
+EDGE = [
+    synth.Case(3, 8, 2, 128, 16, 1000, name="ragged prefix"),
+    synth.Case(2, 8, 2, 128, 16, 1, name="single prefix token"),
+    synth.Case(2, 8, 2, 128, 16, 0, priv_len=37, name="private only"),
+    synth.Case(2, 8, 2, 128, 16, 333, priv_len=45, name="ragged prefix and private"),
+    synth.Case(5, 8, 8, 64, 8, 700, priv_len=3, name="d=64 MHA r=8"),
+    synth.Case(4, 8, 2, 128, 0, 500, priv_len=20, name="rank 0"),
+    synth.Case(3, 8, 2, 128, 128, 300, name="rank 128"),
+    synth.Case(6, 16, 2, 128, 32, 777, shared_lr=True, name="shared low-rank decode"),
+    synth.Case(2, 64, 2, 128, 16, 400, priv_len=10, name="g=32 (rows beyond one block)"),
+    synth.Case(3, 8, 2, 128, 16, 290, q_len=3, priv_len=7, name="multi-token decode"),
+    synth.Case(2, 8, 2, 128, 64, 600, priv_len=50, page_size=32, n_phys_pages=40, name="paged 32"),
+    synth.Case(9, 8, 2, 128, 16, 2100, page_size=16, n_phys_pages=200, name="paged ragged"),
+    synth.Case(2, 8, 2, 64, 16, 500, priv_len=40, q_len=40, mode="prefill", name="prefill per-agent LR"),
+    synth.Case(3, 8, 2, 128, 32, 260, priv_len=33, q_len=33, mode="prefill", shared_lr=True,
+               name="prefill shared ragged"),
+    synth.Case(2, 4, 2, 64, 8, 300, priv_len=20, q_len=20, mode="prefill", dtype="f32", name="prefill fp32"),
+    synth.Case(17, 4, 1, 128, 8, 129, name="17 agents g=4"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: c.name)
+def test_edge_cases(case):
+    x = synth.make_inputs(case, 31, b_sigma=0.3, q_scale=2.0)
+    compare(case, x, what=case.name)
+
+
+def test_run_twice_bitwise():
+    c = synth.CONFIGS[1].replace(prefix_len=8192)
+    x = synth.make_inputs(c, 5)
+    a, la = run_gpu(c, x)
+    b, lb = run_gpu(c, x)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+# -------------------------------------------------------------- indexing --
+
+def test_gather_base_bit_exact():
+    R = rattn()
+    c = synth.CONFIGS[2]
+    x = synth.make_inputs(c, 2)
+    say("[gpu] gather_base on the paged workload")
+    t = synth.to_torch(x, DEV)
+    g = R.gather_base(t["k_base"], t["block_table"], c.prefix_len)
+    torch.cuda.synchronize()
+    got = synth.torch_to_numpy(g)
+    exp = oracle.gather_base(c, x["k_base"], x["block_table"])
+    assert got.dtype == exp.dtype and np.array_equal(got, exp)
+    # ragged prefix, larger page
+    c2 = synth.Case(1, 4, 4, 64, 0, 1000, page_size=32, n_phys_pages=50, dtype="f32")
+    x2 = synth.make_inputs(c2, 3)
+    t2 = synth.to_torch(x2, DEV)
+    g2 = R.gather_base(t2["v_base"], t2["block_table"], c2.prefix_len)
+    torch.cuda.synchronize()
+    assert np.array_equal(g2.cpu().numpy().view(np.uint32),
+                          oracle.gather_base(c2, x2["v_base"], x2["block_table"]).view(np.uint32))
+
+
+def test_shuffled_table_bitwise_equals_identity():
+    """Output depends only on logical token order: a shuffled pool with its table and
+    the identity pool give bit-identical results; unused NaN pages change nothing."""
+    c = synth.CONFIGS[2].replace(prefix_len=2048, n_phys_pages=300, priv_len=100)
+    x = synth.make_inputs(c, 9)
+    say("[gpu] shuffled vs identity page table")
+    a, la = run_gpu(c, x)
+    ident = dict(x)
+    n = c.n_table
+    for key in ("k_base", "v_base"):
+        pool = np.full_like(x[key], synth.BF16_NAN)
+        pool[:n] = x[key][x["block_table"]]
+        ident[key] = pool
+    ident["block_table"] = np.arange(n, dtype=np.int32)
+    b, lb = run_gpu(c, ident)
+    assert np.all(np.isfinite(a))
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+    # duplicate (aliased) table entries are legal and read the same page twice
+    alias = dict(x)
+    alias["block_table"] = x["block_table"].copy()
+    alias["block_table"][1] = alias["block_table"][0]
+    got, _ = run_gpu(c, alias)
+    exp, _ = oracle.attend(c, alias)
+    parity.check(got, exp, "bf16", what="aliased pages")
