@@ -1,0 +1,267 @@
+"""Benchmark of fused residual attention over a shared base KV cache on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu]
+
+One step = one rattn_decode call (split kernel, then combine) over one
+layer of the Llama-3-8B-shaped decode workload: 4 agents on a 32768-token shared
+prefix, H_q=32, H_kv=8, d=128, per-agent rank-16 residual caches, bf16 inputs,
+fp32 accumulation.  Inputs are seeded synthetic data already resident in HBM.
+Several replicas of the input set are rotated so that each step reads its
+143 MB from HBM, not from the 256 MB Infinity Cache left warm by the previous
+step.
+
+Prints one JSON line.  `value` is agent x context-token pairs per second (Gtok/s).
+`roofline` is for the split kernel: its algorithmic bytes per launch (inputs it
+must read once: base K/V, low-rank caches, private tokens, queries) divided by
+its average duration, measured with HIP events recorded on the launch stream
+around that kernel in every timed step.  `cpu_baseline` times the fp64 oracle
+on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "agent x ctx-token attention throughput (Gtok/s) + achieved HBM GB/s, 1 GPU"
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "shared_base_residual_amd", "csrc", f)
+                  for f in ("decode.hip", "device.h", "internal.h")]
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Hip:
+    """Minimal HIP runtime access for events on an explicit stream."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def record(self, e, stream):
+        assert self.h.hipEventRecord(e, stream) == 0
+
+    def elapsed_ms(self, a, b):
+        t = ctypes.c_float()
+        assert self.h.hipEventSynchronize(b) == 0
+        assert self.h.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
+        return t.value
+
+
+def algorithmic_bytes(c):
+    """Bytes every input is read once plus the fp32 output written once."""
+    es = 2 if c.dtype == "bf16" else 4
+    base = 2 * c.n_kv_heads * c.prefix_len * c.head_dim * es
+    resid = 2 * c.n_lr * c.prefix_len * c.rank * es
+    bmat = 2 * c.n_agents * c.rank * c.n_kv_heads * c.head_dim * es
+    q = c.n_agents * c.q_len * c.n_q_heads * c.head_dim * es
+    priv = 2 * c.n_agents * c.n_kv_heads * c.priv_len * c.head_dim * es
+    table = 4 * c.n_table
+    out = 4 * c.n_agents * c.q_len * c.n_q_heads * c.head_dim
+    split = base + resid + priv + q + table
+    return dict(base=base, resid=resid, bmat=bmat, q=q, priv=priv, table=table, out=out,
+                call=base + resid + bmat + q + priv + table + out, split=split)
+
+
+def pairs_per_call(c):
+    if c.mode == "prefill":
+        return c.n_agents * c.q_len * (c.prefix_len + (c.q_len + 1) / 2.0)
+    return c.n_agents * c.q_len * (c.prefix_len + c.priv_len)
+
+
+def cpu_baseline(case, seed, budget_s=12.0):
+    """The fp64 oracle, as it stands, on the host cores, over a bounded sample of
+    the workload: the whole call for the decode workloads that finish in seconds,
+    one agent's rows otherwise; repeated until about `budget_s` seconds of work
+    have been timed.  The rate is scaled by the fraction of rows computed."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    threads = oracle.default_threads()
+    x = synth.make_inputs(case.replace(layers=1), seed)
+    mask, frac, what = None, 1.0, "whole call"
+    if case.mode == "prefill" or case.prefix_len * case.n_agents > 2 ** 18:
+        mask = np.zeros((case.n_agents, case.q_len, case.n_q_heads), bool)
+        mask[0] = True
+        frac, what = 1.0 / case.n_agents, "agent 0's rows of one call"
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.attend(case, x, n_threads=threads, row_mask=mask)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 20:
+            break
+    t = statistics.median(times)
+    return {"value": round(pairs_per_call(case) * frac / t / 1e9, 6), "unit": "Gtok/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{what} ({case.name}, one layer), {len(times)} runs, median {t:.3f} s, fp64, "
+                      f"{threads} threads"}
+
+
+def traffic_from_counters(kernel_key, launches_per_step=1):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("source_hash") != source_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--replicas", type=int, default=0, help="input sets rotated (0: auto)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU "
+              "path: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import shared_base_residual_amd as R
+    import synth
+
+    R.lib()
+    case = synth.CONFIGS[args.config]
+    seed = args.config if args.seed is None else args.seed
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    ab = algorithmic_bytes(case)
+    layers = case.layers
+    op = R.RATTN_OP_PREFILL if case.mode == "prefill" else R.RATTN_OP_DECODE
+
+    # ---- inputs resident in HBM
+    if layers > 1 or args.config == 4:
+        sets = [synth.make_inputs_torch(case, seed, l, dev) for l in range(layers)]
+        n_sets = layers
+    else:
+        x = synth.make_inputs(case, seed)
+        base = synth.to_torch(x, dev)
+        per_set = ab["call"]
+        reps = args.replicas or max(1, min(8, -(-1024 * 2 ** 20 // per_set)))
+        sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(reps - 1)]
+        n_sets = reps
+    desc = R.describe(sets[0]["q"], sets[0]["k_base"], sets[0]["lk"], sets[0]["bk"],
+                      block_table=sets[0]["block_table"], k_priv=sets[0]["k_priv"], prefix_len=case.prefix_len,
+                      shared_lr=case.shared_lr)
+    wsb = R.workspace_bytes(desc, op)
+    ws = torch.empty(max(wsb, 1), device=dev, dtype=torch.uint8)
+    outs = [torch.empty(tuple(s["q"].shape), device=dev, dtype=torch.float32) for s in sets]
+    argv = []
+    for s, o in zip(sets, outs):
+        t = dict(s, out=o, lse=None)
+        R._check_tensors(desc, t)
+        argv.append(R.Args(*[None if t[n] is None else t[n].data_ptr() for n, _ in R.Args._fields_]))
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    lib = R.lib()
+    wsp, wss = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel())
+    dref = ctypes.byref(desc)
+    arefs = [ctypes.byref(a) for a in argv]
+    fn = lib.rattn_attention_stages
+
+    def launch(i, stages):
+        st = fn(dref, op, arefs[i], wsp, wss, sp, stages)
+        if st:
+            raise R.RattnError(st, "rattn_attention_stages")
+
+    # one step = all layers' calls (one call when layers == 1)
+    hip = Hip()
+    K, W = args.steps, args.warmup
+    ev = [[hip.event() for _ in range(3)] for _ in range(K)]
+
+    def step(k, timed):
+        for l in range(layers):
+            i = (k * layers + l) % n_sets
+            if timed:
+                e = ev[k]
+                if l == 0:
+                    hip.record(e[0], sp)
+                launch(i, R.STAGE_SPLIT)
+                if l == 0:
+                    hip.record(e[1], sp)
+                launch(i, R.STAGE_COMBINE)
+                if l == layers - 1:
+                    hip.record(e[2], sp)
+            else:
+                launch(i, R.STAGE_ALL)
+
+    for k in range(W):
+        step(k, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(k, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    split_ms = [hip.elapsed_ms(ev[k][0], ev[k][1]) for k in range(K)]
+    step_ms_ev = [hip.elapsed_ms(ev[k][0], ev[k][2]) for k in range(K)]
+    ms_step = wall * 1e3 / K
+    pairs = pairs_per_call(case) * layers
+    value = pairs / (ms_step / 1e3) / 1e9
+    split_avg = statistics.mean(split_ms)
+    achieved = ab["split"] / (split_avg / 1e3) / 1e9
+    traffic = traffic_from_counters(f"decode_split_cfg{args.config}")
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+            "kernel": "decode_split_kernel", "bytes_per_launch": ab["split"],
+            "avg_launch_us": round(split_avg * 1e3, 2), "median_launch_us": round(statistics.median(split_ms) * 1e3, 2)}
+    res = {
+        "metric": METRIC, "value": round(value, 4), "unit": "Gtok/s", "n_gpus": 1, "steps": K, "warmup": W,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.dtype, "data": "synthetic (seeded N(0,1) caches and queries, N(0,0.05^2) up-projections)",
+        "config": {"workload": case.name, "n_agents": case.n_agents, "n_q_heads": case.n_q_heads,
+                   "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim, "prefix_len": case.prefix_len,
+                   "priv_len": case.priv_len, "q_len": case.q_len, "rank": case.rank, "page_size": case.page_size,
+                   "shared_lr": case.shared_lr, "layers": layers, "mode": case.mode, "input_sets_rotated": n_sets},
+        "hbm_gbps_call": round(ab["call"] * layers / (ms_step / 1e3) / 1e9, 1),
+        "gpu_ms_per_step_events": round(statistics.mean(step_ms_ev), 5),
+        "roofline": roof,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(case, seed)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

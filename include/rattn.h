@@ -135,6 +135,24 @@ int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *wo
 int rattn_gather_base(const rattn_desc *desc, const void *pool, const int32_t *block_table, void *dst,
                       void *stream);
 
+/*
+ * Runs selected stages of rattn_decode (op = RATTN_OP_DECODE) or
+ * rattn_prefill_chunk (op = RATTN_OP_PREFILL) in their fixed order:
+ *   RATTN_STAGE_SPLIT    per-split partial attention (including U = q Bk^T)
+ *                        into the workspace;
+ *   RATTN_STAGE_COMBINE  merge of the splits, Bv applied, out and lse written.
+ * The combine reads what the split stage wrote into the same workspace (by this
+ * call or by an earlier call on the same stream with the same descriptor and
+ * tensors).  stages == RATTN_STAGE_ALL is exactly rattn_decode / _prefill_chunk.
+ * Lets a caller place events between the launches.  Same validation and errors
+ * as the full calls; bits outside RATTN_STAGE_ALL return RATTN_E_SHAPE.
+ */
+#define RATTN_STAGE_SPLIT 1u
+#define RATTN_STAGE_COMBINE 2u
+#define RATTN_STAGE_ALL 3u
+int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,
+                           size_t workspace_bytes, void *stream, unsigned stages);
+
 /* Work decomposition chosen for a decode call (host-only introspection; no HIP call). */
 typedef struct rattn_plan_info {
     int32_t n_prefix_splits;  /* context splits of the prefix */

@@ -10,8 +10,8 @@
 #include "internal.h"
 
 namespace rattn {
-hipError_t launch_decode(int bf16_in, const DecodeParams &dp, const CombineParams &cp, const UParams &up, int D,
-                         int cpad, size_t lds, hipStream_t st);
+hipError_t launch_decode(int bf16_in, const DecodeParams &dp, const CombineParams &cp, int D, int cpad, size_t lds,
+                         unsigned stages, hipStream_t st);
 hipError_t launch_gather(const void *pool, const int32_t *table, void *dst, int64_t L, int HK, int ps,
                          int row_bytes, hipStream_t st);
 }  // namespace rattn
@@ -56,7 +56,7 @@ int check_desc(const rattn_desc *d, int op) {
     if (op != RATTN_OP_DECODE && op != RATTN_OP_PREFILL) return RATTN_E_SHAPE;
     // Index arithmetic inside the kernels uses 32-bit row and item counts.
     const int64_t rows = (int64_t)d->n_agents * d->q_len * d->n_q_heads;
-    if (rows > (1ll << 28) || d->prefix_len > (1ll << 31) || d->priv_len > (1ll << 31))
+    if (rows > (1ll << 28) || d->prefix_len > (1ll << 30) || d->priv_len > (1ll << 30))
         return RATTN_E_UNSUPPORTED;
     return RATTN_OK;
 }
@@ -65,7 +65,7 @@ struct Plan {
     rattn::DecodeParams dp;
     int cpad;
     size_t lds;
-    size_t off_u, off_ml, off_o, off_w, total;
+    size_t off_ml, off_o, off_w, total;
 };
 
 int make_plan(const rattn_desc *d, int op, Plan *pl) {
@@ -84,6 +84,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     p.HK = HK;
     p.g = g;
     p.r = r;
+    p.lr_shift = 0;
+    while (r > 0 && (1 << p.lr_shift) < r) ++p.lr_shift;
     p.rpa = rpa;
     p.ps = d->page_size;
     p.shared_lr = d->shared_lr;
@@ -95,7 +97,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     if (rpa <= 16) {
         int apb = 16 / rpa;
         if (resid && !d->shared_lr) {
-            const int by_cols = rattn::kMaxResidCols / r;
+            const int cap = d->dtype == RATTN_BF16 ? rattn::kMaxResidCols : rattn::kMaxResidColsF32;
+            const int by_cols = cap / r;
             if (by_cols < apb) apb = by_cols;
         }
         if (apb > N) apb = N;
@@ -115,7 +118,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     int cols = 0;
     if (resid) cols = d->shared_lr ? r : (rpa <= 16 ? p.apb * r : r);
     pl->cpad = resid ? (pow2ceil(cols) < 32 ? 32 : pow2ceil(cols)) : 0;
-    if (pl->cpad > rattn::kMaxResidCols) return RATTN_E_UNSUPPORTED;
+    if (pl->cpad > rattn::kMaxResidColsHard) return RATTN_E_UNSUPPORTED;
 
     // Context splits.
     if (L > 0) {
@@ -126,7 +129,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         if (n < 1) n = 1;
         // n splits of a 128-multiple length; trailing splits may be empty, which
         // keeps the split count (and the workspace) non-decreasing in L.
-        p.tok_ps = roundup(cdiv(L, n), rattn::kSplitQuantum);
+        p.tok_ps = (int)roundup(cdiv(L, n), rattn::kSplitQuantum);
         p.n_ps = (int)n;
     }
     if (S > 0) {
@@ -135,7 +138,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         const int64_t nmax = cdiv(S, rattn::kSplitQuantum);
         if (n > nmax) n = nmax;
         if (n < 1) n = 1;
-        p.tok_pv = roundup(cdiv(S, n), rattn::kSplitQuantum);
+        p.tok_pv = (int)roundup(cdiv(S, n), rattn::kSplitQuantum);
         p.n_pv = (int)n;
     }
     p.n_slots = p.n_ps + p.n_pv;
@@ -155,7 +158,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     const int per_lane = 4 * (D / 16) + 4 * cpl;
     pl->lds = (share_pre || share_pv) ? (size_t)3 * (64 * per_lane + 32) * sizeof(float) : 0;
 
-    // Workspace: U, then (max, sum), O and W partials.
+    // Workspace: (max, sum), O and W partials.
     const int64_t rows_kv = (int64_t)HK * N * rpa;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -163,7 +166,6 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         off += (bytes + 255) & ~(size_t)255;
         return o;
     };
-    pl->off_u = take(resid ? (size_t)N * d->q_len * d->n_q_heads * r * sizeof(float) : 0);
     pl->off_ml = take((size_t)rows_kv * p.n_slots * 2 * sizeof(float));
     pl->off_o = take((size_t)rows_kv * p.n_slots * D * sizeof(float));
     pl->off_w = take(resid ? (size_t)rows_kv * p.n_slots * r * sizeof(float) : 0);
@@ -196,7 +198,9 @@ int hip_status(hipError_t e) {
     return RATTN_E_HIP;
 }
 
-int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_bytes, void *stream, int op) {
+int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_bytes, void *stream, int op,
+                  unsigned stages) {
+    if (stages & ~(unsigned)RATTN_STAGE_ALL) return RATTN_E_SHAPE;
     int st = check_desc(d, op);
     if (st) return st;
     st = check_args(d, a);
@@ -218,7 +222,7 @@ int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_
     p.lv = a->lv;
     p.kp = a->k_priv;
     p.vp = a->v_priv;
-    p.u = reinterpret_cast<const float *>(w + pl.off_u);
+    p.bk = a->bk;
     p.p_ml = reinterpret_cast<float *>(w + pl.off_ml);
     p.p_o = reinterpret_cast<float *>(w + pl.off_o);
     p.p_w = reinterpret_cast<float *>(w + pl.off_w);
@@ -241,19 +245,7 @@ int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_
     cp.n_ps = p.n_ps;
     cp.S = p.S;
 
-    rattn::UParams up{};
-    up.q = a->q;
-    up.bk = a->bk;
-    up.u = reinterpret_cast<float *>(w + pl.off_u);
-    up.N = p.N;
-    up.QL = p.QL;
-    up.HQ = p.HQ;
-    up.HK = p.HK;
-    up.g = p.g;
-    up.r = p.r;
-    up.c = p.c;
-
-    return hip_status(rattn::launch_decode(d->dtype == RATTN_BF16, p, cp, up, d->head_dim, pl.cpad, pl.lds,
+    return hip_status(rattn::launch_decode(d->dtype == RATTN_BF16, p, cp, d->head_dim, pl.cpad, pl.lds, stages,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -309,12 +301,17 @@ int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info) {
 
 int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace, size_t workspace_bytes,
                  void *stream) {
-    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_DECODE);
+    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_DECODE, RATTN_STAGE_ALL);
 }
 
 int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *workspace,
                         size_t workspace_bytes, void *stream) {
-    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_PREFILL);
+    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_PREFILL, RATTN_STAGE_ALL);
+}
+
+int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,
+                           size_t workspace_bytes, void *stream, unsigned stages) {
+    return run_attention(desc, args, workspace, workspace_bytes, stream, op, stages);
 }
 
 int rattn_gather_base(const rattn_desc *d, const void *pool, const int32_t *block_table, void *dst,

@@ -4,50 +4,182 @@
 // (ForkKV Guide, "Fused ResidualAttention"; LRAgent, "Flash-LoRA-Attention"):
 //   score  s = scale * (q . K_base[j] + (q Bk_a^T) . Lk_a[j])
 //   output o = sum_j p_j V_base[j] + (sum_j p_j Lv_a[j]) Bv_a
-// Three launches on the caller's stream:
-//   1. u_prologue   U = scale*log2(e) * q Bk_a^(k)^T, fp32, one row per query row;
-//   2. decode_split per (KV head, row group, context split): streams the base
-//      K/V tiles once for all agents' query rows (one MFMA contraction over the
-//      rows of every agent), adds the rank-r score correction with a second MFMA
-//      over the agents' Lk rows, runs an online softmax in the log2 domain, and
-//      accumulates P V_base and P Lv; private tokens are extra work items with
-//      per-agent keys and no residual.  Partials (max, sum, O, W) go to the
-//      workspace;
-//   3. combine per query row: log-sum-exp merge of the splits (wave shuffles),
-//      then o = (sum w O + (sum w W) Bv_a^(k)) / sum w l: Bv is applied once per
-//      row, not per token.
+// Two launches on the caller's stream:
+//   1. decode_split, one workgroup per (KV head, row group, context split):
+//      computes U = scale*log2(e) * q Bk_a^T for its query rows with MFMA,
+//      then streams the base K/V tiles once for all agents' query rows (one
+//      MFMA contraction over the rows of every agent), adds the rank-r score
+//      correction with a second MFMA over the agents' Lk rows, runs an online
+//      softmax in the log2 domain and accumulates P V_base and P Lv.  Private
+//      tokens are extra work items with per-agent keys and no residual.
+//      Partials (max, sum, O, W) go to the workspace;
+//   2. combine, one wavefront per query row: log-sum-exp merge of the splits
+//      with wavefront shuffles, then o = (sum w O + (sum w W) Bv_a^(k)) / sum w l:
+//      Bv is applied once per row, not per token.
 //
 // Layout inside decode_split (S^T formulation): the MFMA A operand is the key
 // tile (rows = 16 tokens), the B operand the query rows (columns = 16 query
 // rows), so the scores arrive with one query row per lane column and the
 // softmax statistics of a row live in the lanes that own it.  The value product
 // is O^T = V^T P^T, so P feeds the B operand straight from the score registers.
-// Every lane reads 16 contiguous bytes per key row and 16*(d/16)/8 contiguous
-// bytes per value row; the value tile needs no transpose through LDS.
+// Every lane reads 16 contiguous bytes per key row and d/16 contiguous elements
+// per value row; the value tile needs no transpose through LDS.
+//
+// Loads never branch: token indices beyond the split are clamped to its last
+// token (finite data) and those scores are masked to -inf, so their weights are
+// exactly zero.  Chunks are software-pipelined two deep.
 #include "device.h"
 #include "internal.h"
 
 namespace rattn {
 
-// ---------------------------------------------------------------- prologue --
+template <typename T, int D, int CPAD>
+struct Chunk {
+    static constexpr int KS = D / 32;
+    static constexpr int VPL = D / 16;
+    static constexpr int CS = CPAD > 0 ? CPAD / 32 : 1;
+    static constexpr int CPL = CPAD > 0 ? CPAD / 16 : 1;
+    typename Ops<T>::frag k[2][KS];
+    Row<T, VPL> v[8];
+    typename Ops<T>::frag lk[2][CS];
+    Row<T, CPL> lv[8];
+};
 
-template <typename T>
-__global__ __launch_bounds__(256) void u_prologue_kernel(UParams p, int D) {
-    const int blk = blockIdx.x;  // (a, t, k)
-    const int k = blk % p.HK;
-    const int at = blk / p.HK;   // a * QL + t
-    const int a = at / p.QL;
-    const T *q = static_cast<const T *>(p.q);
-    const T *bk = static_cast<const T *>(p.bk);
-    const int64_t ldb = (int64_t)p.HK * D;
-    for (int idx = threadIdx.x; idx < p.g * p.r; idx += blockDim.x) {
-        const int hh = idx / p.r, j = idx % p.r;
-        const int h = k * p.g + hh;
-        const T *qr = q + ((int64_t)at * p.HQ + h) * D;
-        const T *br = bk + ((int64_t)a * p.r + j) * ldb + (int64_t)k * D;
-        float acc = 0.0f;
-        for (int dd = 0; dd < D; ++dd) acc += (float)qr[dd] * (float)br[dd];
-        p.u[((int64_t)at * p.HQ + h) * p.r + j] = acc * p.c;
+// Per-lane, loop-invariant state of one work item's token stream.
+template <typename T, int D, int CPAD>
+struct Stream {
+    const T *kb, *vb;       // contiguous segment base, or paged pool
+    const int32_t *table;   // NULL: contiguous
+    int64_t page_stride;    // elements per physical page (all heads)
+    int64_t head_off;       // elements to this head inside a page
+    int ps;
+    int tlast;              // last valid token of the item
+    int tlast16;            // its 16-aligned tile start
+    const T *lk[Chunk<T, D, CPAD>::CS];  // this lane's low-rank column pointers (token 0)
+    const T *lv;
+    int r;
+    bool resid;
+
+    // First row of the 16-token tile starting at t16 (clamped into the item).
+    __device__ inline int tile_row0(int t16) const { return t16 < tlast16 ? t16 : tlast16; }
+    __device__ inline const T *tile_ptr(const T *base, int t16c) const {
+        if (table) {
+            const int64_t pg = table[t16c / ps];
+            return base + pg * page_stride + head_off + (int64_t)(t16c % ps) * D;
+        }
+        return base + (int64_t)t16c * D;
+    }
+};
+
+template <typename T, int D, int CPAD>
+__device__ inline void load_chunk(Chunk<T, D, CPAD> &ch, const Stream<T, D, CPAD> &st, int tc, int n16,
+                                  int j4) {
+    using O = Ops<T>;
+    constexpr int KS = Chunk<T, D, CPAD>::KS, VPL = Chunk<T, D, CPAD>::VPL, CS = Chunk<T, D, CPAD>::CS,
+                  CPL = Chunk<T, D, CPAD>::CPL;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        const int t16 = tc + 16 * c;
+        const int t16c = st.tile_row0(t16);
+        const T *kt = st.tile_ptr(st.kb, t16c);
+        const T *vt = st.tile_ptr(st.vb, t16c);
+        int tk = t16 + n16;
+        tk = tk < st.tlast ? tk : st.tlast;
+        const T *krow = kt + (tk - t16c) * D + 8 * j4;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) ch.k[c][s] = O::load8(krow + 32 * s);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int tv = t16 + 4 * j4 + i;
+            tv = tv < st.tlast ? tv : st.tlast;
+            ch.v[4 * c + i] = load_row<T, VPL>(vt + (tv - t16c) * D + VPL * n16);
+        }
+        if (CPAD > 0 && st.resid) {
+#pragma unroll
+            for (int s = 0; s < CS; ++s) ch.lk[c][s] = O::load8(st.lk[s] + (int64_t)tk * st.r);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                int tv = t16 + 4 * j4 + i;
+                tv = tv < st.tlast ? tv : st.tlast;
+                ch.lv[4 * c + i] = load_row<T, CPL>(st.lv + (int64_t)tv * st.r);
+            }
+        }
+    }
+}
+
+template <typename T, int D, int CPAD>
+struct Acc {
+    f32x4 o[D / 16];
+    f32x4 w[CPAD > 0 ? CPAD / 16 : 1];
+    float m, l;
+};
+
+// One 32-token chunk: scores, online softmax, value and low-rank value products.
+template <typename T, int D, int CPAD>
+__device__ inline void compute_chunk(Acc<T, D, CPAD> &acc, const Chunk<T, D, CPAD> &ch,
+                                     const typename Ops<T>::frag *qB, const typename Ops<T>::frag *uH,
+                                     const typename Ops<T>::frag *uL, float cl2, bool resid, int tc,
+                                     int t1, bool causal, int tq, int j4) {
+    using O = Ops<T>;
+    using frag = typename O::frag;
+    constexpr int KS = Chunk<T, D, CPAD>::KS, VPL = Chunk<T, D, CPAD>::VPL, CS = CPAD / 32,
+                  CPL = CPAD / 16;
+    f32x4 sc[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; ++s) a = O::mma(ch.k[c][s], qB[s], a);
+        a *= cl2;
+        if (CPAD > 0 && resid) {
+#pragma unroll
+            for (int s = 0; s < CS; ++s) {
+                a = O::mma(ch.lk[c][s], uH[s], a);
+                if constexpr (O::kSplitU) a = O::mma(ch.lk[c][s], uL[s], a);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = tc + 16 * c + 4 * j4 + i;
+            if (t >= t1 || (causal && t > tq)) a[i] = -__builtin_inff();
+        }
+        sc[c] = a;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(acc.m, mx);
+    const float alpha = fexp2(acc.m - m_new);
+    acc.m = m_new;
+    frag pB;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float e = fexp2(sc[i >> 2][i & 3] - m_new);
+        psum += e;
+        O::set(pB, i, e);
+    }
+    acc.l = acc.l * alpha + psum;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) acc.o[i] *= alpha;
+#pragma unroll
+    for (int jj = 0; jj < VPL; ++jj) {
+        frag vA;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) O::set_raw(vA, i, ch.v[i].e[jj]);
+        acc.o[jj] = O::mma(vA, pB, acc.o[jj]);
+    }
+    if (CPAD > 0 && resid) {
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) acc.w[i] *= alpha;
+#pragma unroll
+        for (int jj = 0; jj < CPL; ++jj) {
+            frag wA;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) O::set_raw(wA, i, ch.lv[i].e[jj]);
+            acc.w[jj] = O::mma(wA, pB, acc.w[jj]);
+        }
     }
 }
 
@@ -57,17 +189,16 @@ template <typename T, int D, int CPAD>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     using O = Ops<T>;
     using frag = typename O::frag;
-    constexpr int KS = D / 32;     // contraction steps over the head dimension
-    constexpr int VPL = D / 16;    // value columns per lane per token = O^T tiles
-    constexpr int CS = CPAD / 32;  // contraction steps over residual columns
-    constexpr int CPL = CPAD / 16; // residual columns per lane per token = W^T tiles
-    constexpr int CPLx = CPL > 0 ? CPL : 1;
+    constexpr int KS = D / 32;
+    constexpr int VPL = D / 16;
+    constexpr int CS = CPAD / 32;
     constexpr int CSx = CS > 0 ? CS : 1;
+    constexpr int CPLx = CPAD > 0 ? CPAD / 16 : 1;
 
     extern __shared__ float smem[];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
     const int n16 = lane & 15;
     const int j4 = lane >> 4;
 
@@ -79,7 +210,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     if (li >= p.n_items) return;
 
     int k, slot, nblk, blk0, agent_p = 0;
-    int64_t t0, t1;
+    int t0, t1;
     bool prefix;
     if (li < p.n_prefix_items) {
         k = li % p.HK;
@@ -88,8 +219,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         const int s = rest / p.n_rg;
         blk0 = rg * 4;
         nblk = p.n_blocks - blk0 < 4 ? p.n_blocks - blk0 : 4;
-        t0 = (int64_t)s * p.tok_ps;
-        t1 = t0 + p.tok_ps < p.L ? t0 + p.tok_ps : p.L;
+        t0 = s * p.tok_ps;
+        t1 = t0 + p.tok_ps < p.L ? t0 + p.tok_ps : (int)p.L;
         slot = s;
         prefix = true;
     } else {
@@ -102,18 +233,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         agent_p = rest / p.n_prg;
         blk0 = prg * 4;
         nblk = p.pb - blk0 < 4 ? p.pb - blk0 : 4;
-        t0 = (int64_t)s * p.tok_pv;
-        t1 = t0 + p.tok_pv < p.S ? t0 + p.tok_pv : p.S;
+        t0 = s * p.tok_pv;
+        t1 = t0 + p.tok_pv < p.S ? t0 + p.tok_pv : (int)p.S;
         slot = p.n_ps + s;
         prefix = false;
     }
     const bool resid = prefix && (CPAD > 0) && p.r > 0;
     const bool causal = !prefix && p.causal;
-    const bool paged = prefix && p.ps > 0;
     const int TG = 4 / nblk;  // waves sharing one row block (token groups)
     const int rbi = wave / TG;
     const int tg = wave % TG;
-    const bool active = rbi < nblk;
+    const bool active = rbi < nblk && t0 < t1;
 
     // Row block of this wave.
     RowBlock blk;
@@ -122,25 +252,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     } else {
         blk.a0 = agent_p;
         blk.na = 1;
-        blk.f = 16 * (blk0 + rbi);
+        blk.f = p.rpa <= 16 ? 0 : 16 * (blk0 + rbi);
         blk.nr = p.rpa - blk.f < 16 ? p.rpa - blk.f : 16;
-        if (p.rpa <= 16) blk.f = 0;
     }
     // Query row owned by this lane's column.
-    const bool vm = active && n16 < blk.nr;
+    const bool vm = rbi < nblk && n16 < blk.nr;
     int agent_m = 0, ria = 0;
     if (vm) block_row(blk, n16, p.rpa, &agent_m, &ria);
     const int tq = ria / p.g, hh = ria % p.g;
     const int64_t qrow = ((int64_t)agent_m * p.QL + tq) * p.HQ + (int64_t)k * p.g + hh;
     const int64_t grow = (int64_t)agent_m * p.rpa + ria;
+    const float cl2 = p.c;
 
     const T *qp = static_cast<const T *>(p.q);
-    const T *kb = static_cast<const T *>(prefix ? p.kb : p.kp);
-    const T *vb = static_cast<const T *>(prefix ? p.vb : p.vp);
-    const T *lk = static_cast<const T *>(p.lk);
-    const T *lv = static_cast<const T *>(p.lv);
-    // Offset of the (contiguous) segment this item streams.
-    const int64_t seg = prefix ? (int64_t)k * p.L * D : ((int64_t)agent_p * p.HK + k) * p.S * D;
     const int cvalid = resid ? (p.shared_lr ? p.r : blk.na * p.r) : 0;
 
     // Query rows as the B operand of S^T = K Q^T.
@@ -148,161 +272,146 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) qB[s] = vm ? O::load8(qp + qrow * D + 32 * s + 8 * j4) : O::zero();
 
-    // U (block-diagonal over the agents of the block) as the B operand of the
-    // rank-r score correction; bf16 carries it as hi + lo halves.
+    // U = scale*log2(e) * q Bk^T as the B operand of the rank-r score correction,
+    // block-diagonal over the agents of the block (bf16 carries hi + lo halves).
+    // Computed as U^T = Bk Q^T with MFMA; A-operand row rho of output tile 2s+h
+    // is residual column 32s + 8(rho/4) + 4h + rho%4, so that each lane's
+    // results land in its own B-operand slots.
     frag uH[CSx], uL[CSx];
 #pragma unroll
     for (int s = 0; s < CSx; ++s) {
         uH[s] = O::zero();
         uL[s] = O::zero();
+    }
+    if (CPAD > 0 && resid && active) {
+        const T *bk = static_cast<const T *>(p.bk);
+        const int64_t ldb = (int64_t)p.HK * D;
+        const int rmask = p.r - 1;
+        const int na_loop = p.shared_lr ? blk.na : 1;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = 32 * s + 8 * j4 + i;
-            float v = 0.0f;
-            if (resid && vm && c < cvalid) {
-                if (p.shared_lr)
-                    v = p.u[qrow * p.r + c];
-                else if (blk.a0 + c / p.r == agent_m)
-                    v = p.u[qrow * p.r + (c % p.r)];
+        for (int s = 0; s < CSx; ++s) {
+            float uv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) uv[i] = 0.0f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int crow = 32 * s + 8 * (n16 >> 2) + 4 * h + (n16 & 3);  // A-operand row
+                for (int ai = 0; ai < na_loop; ++ai) {
+                    int arow, colr;
+                    if (p.shared_lr) {
+                        arow = blk.a0 + ai;
+                        colr = crow < p.r ? crow : 0;
+                    } else {
+                        const bool okc = crow < cvalid;
+                        arow = blk.a0 + (okc ? (crow >> p.lr_shift) : 0);
+                        colr = okc ? (crow & rmask) : 0;
+                    }
+                    const T *brow = bk + ((int64_t)arow * p.r + colr) * ldb + (int64_t)k * D + 8 * j4;
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2) a = O::mma(O::load8(brow + 32 * s2), qB[s2], a);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = 32 * s + 8 * j4 + 4 * h + i;  // column this lane received
+                        bool keep = vm && c < cvalid;
+                        if (p.shared_lr)
+                            keep = keep && agent_m == blk.a0 + ai;
+                        else
+                            keep = keep && blk.a0 + (c >> p.lr_shift) == agent_m;
+                        if (keep) uv[4 * h + i] += a[i] * cl2;
+                    }
+                }
             }
-            O::set(uH[s], i, v);
-            if constexpr (O::kSplitU) {
-                const float hi = (float)(bf16)v;
-                O::set(uL[s], i, v - hi);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                O::set(uH[s], i, uv[i]);
+                if constexpr (O::kSplitU) {
+                    const float hi = (float)(bf16)uv[i];
+                    O::set(uL[s], i, uv[i] - hi);
+                }
             }
         }
     }
 
-    f32x4 accO[VPL];
-    f32x4 accW[CPLx];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) accO[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < CPLx; ++i) accW[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -1.0e30f, l_run = 0.0f;
-
-    // Pointer to token t16 (16-aligned) of the streamed segment; tokens
-    // t16..t16+15 are contiguous rows of d elements.
-    auto tile = [&](const T *base, int64_t t16) -> const T * {
-        if (paged) {
-            const int64_t pg = p.table[t16 / p.ps];
-            return base + ((pg * p.HK + k) * p.ps + (t16 % p.ps)) * D;
+    // Token stream of this item.
+    Stream<T, D, CPAD> st;
+    st.r = p.r;
+    st.resid = resid;
+    st.tlast = t1 - 1;
+    st.tlast16 = st.tlast & ~15;
+    if (prefix) {
+        st.kb = static_cast<const T *>(p.kb);
+        st.vb = static_cast<const T *>(p.vb);
+        if (p.ps > 0) {
+            st.table = p.table;
+            st.ps = p.ps;
+            st.page_stride = (int64_t)p.HK * p.ps * D;
+            st.head_off = (int64_t)k * p.ps * D;
+        } else {
+            st.table = nullptr;
+            st.ps = 16;
+            st.page_stride = 0;
+            st.head_off = 0;
+            st.kb += (int64_t)k * p.L * D;
+            st.vb += (int64_t)k * p.L * D;
         }
-        return base + seg + t16 * D;
-    };
+    } else {
+        const int64_t seg = ((int64_t)agent_p * p.HK + k) * p.S * D;
+        st.kb = static_cast<const T *>(p.kp) + seg;
+        st.vb = static_cast<const T *>(p.vp) + seg;
+        st.table = nullptr;
+        st.ps = 16;
+        st.page_stride = 0;
+        st.head_off = 0;
+    }
+    {
+        const T *lk = static_cast<const T *>(p.lk);
+        const T *lv = static_cast<const T *>(p.lv);
+#pragma unroll
+        for (int s = 0; s < CSx; ++s) {
+            const int cc = 32 * s + 8 * j4;
+            int lr = 0, col = 0;
+            if (resid && cc < cvalid) {
+                lr = p.shared_lr ? 0 : blk.a0 + (cc >> p.lr_shift);
+                col = cc & (p.r - 1);
+            } else if (resid) {
+                lr = p.shared_lr ? 0 : blk.a0;  // padding column: any finite data (U is zero there)
+            }
+            st.lk[s] = lk + (int64_t)lr * p.L * p.r + col;
+        }
+        const int cl = CPLx * n16;
+        int lr = 0, col = 0;
+        if (resid && cl < cvalid) {
+            lr = p.shared_lr ? 0 : blk.a0 + (cl >> p.lr_shift);
+            col = cl & (p.r - 1);
+        } else if (resid) {
+            lr = p.shared_lr ? 0 : blk.a0;
+        }
+        st.lv = lv + (int64_t)lr * p.L * p.r + col;
+    }
+
+    Acc<T, D, CPAD> acc;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) acc.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < CPLx; ++i) acc.w[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc.m = -1.0e30f;
+    acc.l = 0.0f;
 
     if (active) {
-        for (int64_t tc = t0 + 32 * tg; tc < t1; tc += 32 * TG) {
-            // ---- loads of this 32-token chunk
-            frag kA[2][KS];
-            frag lkA[2][CSx];
-            Row<T, VPL> vR[8];
-            Row<T, CPLx> lvR[8];
-            const T *kt[2], *vt[2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int64_t t16 = tc + 16 * c;
-                kt[c] = t16 < t1 ? tile(kb, t16) : kb;
-                vt[c] = t16 < t1 ? tile(vb, t16) : vb;
-            }
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const int64_t t = tc + 16 * c + n16;
-                const bool ok = t < t1;
-#pragma unroll
-                for (int s = 0; s < KS; ++s)
-                    kA[c][s] = ok ? O::load8(kt[c] + n16 * D + 32 * s + 8 * j4) : O::zero();
-#pragma unroll
-                for (int s = 0; s < CSx; ++s) {
-                    const int cc = 32 * s + 8 * j4;
-                    lkA[c][s] = O::zero();
-                    if (resid && ok && cc < cvalid) {
-                        const int64_t lr = p.shared_lr ? 0 : blk.a0 + cc / p.r;
-                        lkA[c][s] = O::load8(lk + (lr * p.L + t) * p.r + (cc % p.r));
-                    }
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int tl = 16 * (i >> 2) + 4 * j4 + (i & 3);
-                const int64_t t = tc + tl;
-                const bool ok = t < t1;
-                vR[i] = ok ? load_row<T, VPL>(vt[i >> 2] + (4 * j4 + (i & 3)) * D + VPL * n16)
-                           : zero_row<T, VPL>();
-                lvR[i] = zero_row<T, CPLx>();
-                const int cl = CPLx * n16;
-                if (resid && ok && cl < cvalid) {
-                    const int64_t lr = p.shared_lr ? 0 : blk.a0 + cl / p.r;
-                    lvR[i] = load_row<T, CPLx>(lv + (lr * p.L + t) * p.r + (cl % p.r));
-                }
-            }
-
-            // ---- scores S^T (rows = tokens, columns = query rows), log2 domain
-            f32x4 sc[2];
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < KS; ++s) acc = O::mma(kA[c][s], qB[s], acc);
-                acc *= p.c;
-                if (resid) {
-#pragma unroll
-                    for (int s = 0; s < CS; ++s) {
-                        acc = O::mma(lkA[c][s], uH[s], acc);
-                        if constexpr (O::kSplitU) acc = O::mma(lkA[c][s], uL[s], acc);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t t = tc + 16 * c + 4 * j4 + i;
-                    if (t >= t1 || (causal && t > tq)) acc[i] = -__builtin_inff();
-                }
-                sc[c] = acc;
-            }
-
-            // ---- online softmax for this lane's query row
-            float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                             fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = fexp2(m_run - m_new);
-            m_run = m_new;
-            frag pB;
-            float psum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float e = fexp2(sc[i >> 2][i & 3] - m_new);
-                psum += e;
-                O::set(pB, i, e);
-            }
-            l_run = l_run * alpha + psum;
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) accO[i] *= alpha;
-            if (resid) {
-#pragma unroll
-                for (int i = 0; i < CPLx; ++i) accW[i] *= alpha;
-            }
-
-            // ---- O^T += V^T P^T and W^T += Lv^T P^T
-#pragma unroll
-            for (int jj = 0; jj < VPL; ++jj) {
-                frag vA;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) O::set_raw(vA, i, vR[i].e[jj]);
-                accO[jj] = O::mma(vA, pB, accO[jj]);
-            }
-            if (resid) {
-#pragma unroll
-                for (int jj = 0; jj < CPL; ++jj) {
-                    frag wA;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) O::set_raw(wA, i, lvR[i].e[jj]);
-                    accW[jj] = O::mma(wA, pB, accW[jj]);
-                }
-            }
+        const int step = 32 * TG;
+        int tc = t0 + 32 * tg;
+        Chunk<T, D, CPAD> ca, cb;
+        load_chunk(ca, st, tc, n16, j4);
+        for (; tc < t1; tc += 2 * step) {
+            load_chunk(cb, st, tc + step, n16, j4);
+            compute_chunk(acc, ca, qB, uH, uL, cl2, resid, tc, t1, causal, tq, j4);
+            if (tc + step >= t1) break;
+            load_chunk(ca, st, tc + 2 * step, n16, j4);
+            compute_chunk(acc, cb, qB, uH, uL, cl2, resid, tc + step, t1, causal, tq, j4);
         }
     }
+    float m_run = acc.m, l_run = acc.l;
     // Sum of weights over the four lanes that share this query row.
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
@@ -311,19 +420,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     constexpr int PER_LANE = 4 * VPL + 4 * CPLx;
     // Waves 1..3 publish their state (wave 0 always has tg == 0): three slots.
     if (TG > 1) {
-        float *st = smem + (size_t)(wave - 1) * (64 * PER_LANE + 32);
+        float *sm = smem + (size_t)(wave - 1) * (64 * PER_LANE + 32);
         if (tg > 0) {
 #pragma unroll
             for (int jj = 0; jj < VPL; ++jj)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) st[(4 * jj + i) * 64 + lane] = accO[jj][i];
+                for (int i = 0; i < 4; ++i) sm[(4 * jj + i) * 64 + lane] = acc.o[jj][i];
 #pragma unroll
             for (int jj = 0; jj < CPLx; ++jj)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) st[(4 * VPL + 4 * jj + i) * 64 + lane] = accW[jj][i];
+                for (int i = 0; i < 4; ++i) sm[(4 * VPL + 4 * jj + i) * 64 + lane] = acc.w[jj][i];
             if (j4 == 0) {
-                st[64 * PER_LANE + n16] = m_run;
-                st[64 * PER_LANE + 16 + n16] = l_run;
+                sm[64 * PER_LANE + n16] = m_run;
+                sm[64 * PER_LANE + 16 + n16] = l_run;
             }
         }
         __syncthreads();
@@ -334,9 +443,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
             const float s0 = fexp2(m_run - mt);
             l_run *= s0;
 #pragma unroll
-            for (int jj = 0; jj < VPL; ++jj) accO[jj] *= s0;
+            for (int jj = 0; jj < VPL; ++jj) acc.o[jj] *= s0;
 #pragma unroll
-            for (int jj = 0; jj < CPLx; ++jj) accW[jj] *= s0;
+            for (int jj = 0; jj < CPLx; ++jj) acc.w[jj] *= s0;
             for (int w = 1; w < TG; ++w) {
                 const float *sw = smem + (size_t)(wave + w - 1) * (64 * PER_LANE + 32);
                 const float sf = fexp2(sw[64 * PER_LANE + n16] - mt);
@@ -344,11 +453,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
                 for (int jj = 0; jj < VPL; ++jj)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) accO[jj][i] += sf * sw[(4 * jj + i) * 64 + lane];
+                    for (int i = 0; i < 4; ++i) acc.o[jj][i] += sf * sw[(4 * jj + i) * 64 + lane];
 #pragma unroll
                 for (int jj = 0; jj < CPLx; ++jj)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) accW[jj][i] += sf * sw[(4 * VPL + 4 * jj + i) * 64 + lane];
+                    for (int i = 0; i < 4; ++i) acc.w[jj][i] += sf * sw[(4 * VPL + 4 * jj + i) * 64 + lane];
             }
             m_run = mt;
         }
@@ -361,7 +470,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int jj = 0; jj < VPL; ++jj) ov[VPL * i + jj] = accO[jj][i];
+            for (int jj = 0; jj < VPL; ++jj) ov[VPL * i + jj] = acc.o[jj][i];
         float *po = p.p_o + rec * D + 4 * VPL * j4;
 #pragma unroll
         for (int c = 0; c < VPL; ++c)
@@ -371,9 +480,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int jj = 0; jj < CPL; ++jj) {
+                for (int jj = 0; jj < CPLx; ++jj) {
                     const int c = CPLx * (4 * j4 + i) + jj;
-                    if (c < cvalid && (p.shared_lr || c / p.r == arel)) p.p_w[rec * p.r + (c % p.r)] = accW[jj][i];
+                    if (c < cvalid && (p.shared_lr || (c >> p.lr_shift) == arel))
+                        p.p_w[rec * p.r + (c & (p.r - 1))] = acc.w[jj][i];
                 }
         }
         if (j4 == 0) {
@@ -385,12 +495,15 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 
 // ----------------------------------------------------------------- combine --
 
+// One wavefront per query row.  Loads every split's (max, sum) at once, merges
+// them with wavefront shuffles, then sums the weighted O and W partials and
+// applies Bv once.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-    __shared__ float s_w[1024];
-    __shared__ float s_o[256];
-    __shared__ float s_wr[256];
-    __shared__ float s_ml[2];
+__global__ __launch_bounds__(64) void combine_kernel(CombineParams p) {
+    constexpr int MAXS = 1024;
+    constexpr int DPL = D / 64;  // output columns per lane
+    __shared__ float s_w[MAXS];
+    __shared__ float s_wr[128];
     const int R = blockIdx.x;  // (a * QL + t) * HQ + h
     const int h = R % p.HQ;
     const int at = R / p.HQ;
@@ -398,102 +511,124 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
     const int k = h / p.g, hh = h % p.g;
     const int64_t grow = (int64_t)a * p.rpa + (int64_t)t * p.g + hh;
     const int64_t rec0 = ((int64_t)k * p.N * p.rpa + grow) * p.n_slots;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int lane = threadIdx.x;
     const int ns = p.n_slots;
 
-    // Wave 0: maximum over the splits and the merged weight sum (wave shuffles).
-    if (tid < 64) {
-        float mx = -3.0e38f;
-        for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, p.p_ml[(rec0 + s) * 2]);
-        mx = wave_max(mx);
-        float l = 0.0f;
-        for (int s = lane; s < ns; s += 64) {
-            const float w = fexp2(p.p_ml[(rec0 + s) * 2] - mx);
-            if (s < 1024) s_w[s] = w;
-            l += w * p.p_ml[(rec0 + s) * 2 + 1];
+    float mv[MAXS / 64], lv[MAXS / 64];
+    float mx = -3.0e38f;
+#pragma unroll
+    for (int u = 0; u < MAXS / 64; ++u) {
+        const int s = lane + 64 * u;
+        mv[u] = -3.0e38f;
+        lv[u] = 0.0f;
+        if (s < ns) {
+            const float2 ml = *reinterpret_cast<const float2 *>(p.p_ml + (rec0 + s) * 2);
+            mv[u] = ml.x;
+            lv[u] = ml.y;
         }
-        l = wave_sum(l);
-        if (lane == 0) {
-            s_ml[0] = mx;
-            s_ml[1] = l;
-        }
+        mx = fmaxf(mx, mv[u]);
     }
+    mx = wave_max(mx);
+    float lsum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < MAXS / 64; ++u) {
+        const int s = lane + 64 * u;
+        const float w = fexp2(mv[u] - mx);
+        if (s < ns) s_w[s] = w;
+        lsum += w * lv[u];
+    }
+    lsum = wave_sum(lsum);
     __syncthreads();
-    const float mx = s_ml[0], lsum = s_ml[1];
-    constexpr int NG = 256 / D;  // slot groups
-    const int sg = tid / D, dd = tid % D;
-    float acc = 0.0f;
-    for (int s = sg; s < ns; s += NG) {
-        const float w = s < 1024 ? s_w[s] : fexp2(p.p_ml[(rec0 + s) * 2] - mx);
-        acc += w * p.p_o[(rec0 + s) * D + dd];
+
+    float o[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
+    const float *po = p.p_o + rec0 * D + DPL * lane;
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+        float v[8][DPL];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) v[u][e] = po[(int64_t)(s + u) * D + e];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) o[e] += s_w[s + u] * v[u][e];
     }
-    s_o[tid] = acc;
-    // Residual value columns, prefix splits only.
+    for (; s < ns; ++s)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] += s_w[s] * po[(int64_t)s * D + e];
+
     if (p.r > 0) {
-        const int gr = 256 / p.r;  // r divides 256
-        const int sgw = tid / p.r, jw = tid % p.r;
-        float aw = 0.0f;
-        if (sgw < gr)
-            for (int s = sgw; s < p.n_ps; s += gr) {
-                const float w = s < 1024 ? s_w[s] : fexp2(p.p_ml[(rec0 + s) * 2] - mx);
-                aw += w * p.p_w[(rec0 + s) * p.r + jw];
+        // W = sum over prefix splits of w_s W_s (lane j, and j + 64 when r = 128)
+        for (int j = lane; j < p.r; j += 64) {
+            float wj = 0.0f;
+            const float *pw = p.p_w + rec0 * p.r + j;
+            int s2 = 0;
+            for (; s2 + 8 <= p.n_ps; s2 += 8) {
+                float v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) v[u] = pw[(int64_t)(s2 + u) * p.r];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) wj += s_w[s2 + u] * v[u];
             }
-        s_wr[tid] = aw;
-    }
-    __syncthreads();
-    if (tid < D) {
-        float o = 0.0f;
-        for (int g2 = 0; g2 < NG; ++g2) o += s_o[g2 * D + tid];
-        if (p.r > 0) {
-            const int gr = 256 / p.r;
-            const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * p.r * p.HK * D + (int64_t)k * D + tid;
-            for (int j = 0; j < p.r; ++j) {
-                float wj = 0.0f;
-                for (int g2 = 0; g2 < gr; ++g2) wj += s_wr[g2 * p.r + j];
-                o += wj * (float)bv[(int64_t)j * p.HK * D];
-            }
+            for (; s2 < p.n_ps; ++s2) wj += s_w[s2] * pw[(int64_t)s2 * p.r];
+            s_wr[j] = wj;
         }
-        p.out[(int64_t)R * D + tid] = o / lsum;
+        __syncthreads();
+        const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * p.r * p.HK * D + (int64_t)k * D + DPL * lane;
+        for (int j = 0; j < p.r; ++j) {
+            const float wj = s_wr[j];
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) o[e] += wj * (float)bv[(int64_t)j * p.HK * D + e];
+        }
     }
-    if (tid == 0 && p.lse) p.lse[R] = (mx + __builtin_log2f(lsum)) * 0.69314718055994530942f;
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) p.out[(int64_t)R * D + DPL * lane + e] = o[e] * inv;
+    if (lane == 0 && p.lse) p.lse[R] = (mx + __builtin_log2f(lsum)) * 0.69314718055994530942f;
 }
 
 // ---------------------------------------------------------------- launchers --
 
 template <typename T>
-static hipError_t launch_decode_t(const DecodeParams &dp, const CombineParams &cp, const UParams &up, int D,
-                                  int cpad, size_t lds, hipStream_t st) {
-    if (dp.r > 0 && dp.L > 0) {
-        hipLaunchKernelGGL(u_prologue_kernel<T>, dim3(dp.N * dp.QL * dp.HK), dim3(256), 0, st, up, D);
-    }
+static hipError_t launch_decode_t(const DecodeParams &dp, const CombineParams &cp, int D, int cpad, size_t lds,
+                                  unsigned stages, hipStream_t st) {
     const dim3 grid(8 * dp.per_xcd);
 #define RATTN_SPLIT(DD, CP) \
     hipLaunchKernelGGL((decode_split_kernel<T, DD, CP>), grid, dim3(256), lds, st, dp)
-    if (D == 128) {
-        switch (cpad) {
-            case 0: RATTN_SPLIT(128, 0); break;
-            case 32: RATTN_SPLIT(128, 32); break;
-            case 64: RATTN_SPLIT(128, 64); break;
-            default: RATTN_SPLIT(128, 128); break;
+    if (stages & 1u) {
+        if (D == 128) {
+            switch (cpad) {
+                case 0: RATTN_SPLIT(128, 0); break;
+                case 32: RATTN_SPLIT(128, 32); break;
+                case 64: RATTN_SPLIT(128, 64); break;
+                default: RATTN_SPLIT(128, 128); break;
+            }
+        } else {
+            switch (cpad) {
+                case 0: RATTN_SPLIT(64, 0); break;
+                case 32: RATTN_SPLIT(64, 32); break;
+                case 64: RATTN_SPLIT(64, 64); break;
+                default: RATTN_SPLIT(64, 128); break;
+            }
         }
-        hipLaunchKernelGGL((combine_kernel<T, 128>), dim3(dp.N * dp.QL * dp.HQ), dim3(256), 0, st, cp);
-    } else {
-        switch (cpad) {
-            case 0: RATTN_SPLIT(64, 0); break;
-            case 32: RATTN_SPLIT(64, 32); break;
-            case 64: RATTN_SPLIT(64, 64); break;
-            default: RATTN_SPLIT(64, 128); break;
-        }
-        hipLaunchKernelGGL((combine_kernel<T, 64>), dim3(dp.N * dp.QL * dp.HQ), dim3(256), 0, st, cp);
     }
 #undef RATTN_SPLIT
+    if (stages & 2u) {
+        if (D == 128)
+            hipLaunchKernelGGL((combine_kernel<T, 128>), dim3(dp.N * dp.QL * dp.HQ), dim3(64), 0, st, cp);
+        else
+            hipLaunchKernelGGL((combine_kernel<T, 64>), dim3(dp.N * dp.QL * dp.HQ), dim3(64), 0, st, cp);
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_decode(int bf16_in, const DecodeParams &dp, const CombineParams &cp, const UParams &up, int D,
-                         int cpad, size_t lds, hipStream_t st) {
-    if (bf16_in) return launch_decode_t<bf16>(dp, cp, up, D, cpad, lds, st);
-    return launch_decode_t<float>(dp, cp, up, D, cpad, lds, st);
+hipError_t launch_decode(int bf16_in, const DecodeParams &dp, const CombineParams &cp, int D, int cpad, size_t lds,
+                         unsigned stages, hipStream_t st) {
+    if (bf16_in) return launch_decode_t<bf16>(dp, cp, D, cpad, lds, stages, st);
+    return launch_decode_t<float>(dp, cp, D, cpad, lds, stages, st);
 }
 
 }  // namespace rattn

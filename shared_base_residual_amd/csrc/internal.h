@@ -12,8 +12,11 @@
 namespace rattn {
 
 // Largest padded residual width (agents sharing a row block times r) a decode
-// row block may carry; bounds the split kernel's registers.
-constexpr int kMaxResidCols = 128;
+// row block is given when r allows; bounds the split kernel's registers
+// (bf16 / fp32 inputs).  r = 128 still runs, with 128 columns.
+constexpr int kMaxResidCols = 64;
+constexpr int kMaxResidColsF32 = 32;
+constexpr int kMaxResidColsHard = 128;
 // Context tokens per split are a multiple of this (4 waves x 32-token chunks),
 // which also keeps every 16-token MFMA tile inside one 16-aligned page.
 constexpr int kSplitQuantum = 128;
@@ -59,19 +62,18 @@ RATTN_HD void block_row(const RowBlock &rb, int m, int rpa, int *agent, int *ria
 struct DecodeParams {
     const void *q, *kb, *vb;
     const int32_t *table;
-    const void *lk, *lv, *kp, *vp;
-    const float *u;   // [N*q_len*H_q, r] fp32, already multiplied by scale*log2(e)
+    const void *lk, *lv, *bk, *kp, *vp;
     float *p_ml;      // [H_kv, N*rpa, n_slots, 2]  running max (log2 units), sum of weights
     float *p_o;       // [H_kv, N*rpa, n_slots, d]  unnormalised P V_base (+ private P V)
     float *p_w;       // [H_kv, N*rpa, n_slots, r]  unnormalised P Lv
-    int64_t L, S;
-    int N, QL, HQ, HK, g, r, rpa, apb, bpa, ps, shared_lr;
+    int64_t L, S;     // < 2^31 (validated on the host)
+    int N, QL, HQ, HK, g, r, lr_shift, rpa, apb, bpa, ps, shared_lr;
     int causal;       // private token j is visible to query token t only if j <= t
     float c;          // softmax scale * log2(e)
     int n_blocks, n_rg, n_ps;
-    int64_t tok_ps;
+    int tok_ps;
     int pb, n_prg, n_pv;
-    int64_t tok_pv;
+    int tok_pv;
     int n_slots, n_prefix_items, n_items, per_xcd;
 };
 
@@ -81,13 +83,6 @@ struct CombineParams {
     float *out, *lse;
     int N, QL, HQ, HK, g, r, rpa, n_slots, n_ps;
     int64_t S;
-};
-
-struct UParams {
-    const void *q, *bk;
-    float *u;
-    int N, QL, HQ, HK, g, r;
-    float c;
 };
 
 }  // namespace rattn
