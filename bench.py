@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu]
 
-One step = one rattn_decode call (split kernel, then combine) over one
+One step = one rattn_decode call (a single kernel launch) over one
 layer of the Llama-3-8B-shaped decode workload: 4 agents on a 32768-token shared
 prefix, H_q=32, H_kv=8, d=128, per-agent rank-16 residual caches, bf16 inputs,
 fp32 accumulation.  Inputs are seeded synthetic data already resident in HBM.
@@ -11,10 +11,10 @@ Several replicas of the input set are rotated so that each step reads its
 step.
 
 Prints one JSON line.  `value` is agent x context-token pairs per second (Gtok/s).
-`roofline` is for the split kernel: its algorithmic bytes per launch (inputs it
-must read once: base K/V, low-rank caches, private tokens, queries) divided by
-its average duration, measured with HIP events recorded on the launch stream
-around that kernel in every timed step.  `cpu_baseline` times the fp64 oracle
+`roofline` is for that kernel: its algorithmic bytes per launch (every input
+read once and the fp32 output written once) divided by its average duration,
+measured with HIP events recorded on the launch stream around the launch in
+every timed step.  `cpu_baseline` times the fp64 oracle
 on the host cores.
 """
 from __future__ import annotations
@@ -184,7 +184,7 @@ def main():
                       block_table=sets[0]["block_table"], k_priv=sets[0]["k_priv"], prefix_len=case.prefix_len,
                       shared_lr=case.shared_lr)
     wsb = R.workspace_bytes(desc, op)
-    ws = torch.empty(max(wsb, 1), device=dev, dtype=torch.uint8)
+    ws = torch.zeros(max(wsb, 256), device=dev, dtype=torch.uint8)  # zero-filled once (rattn.h)
     outs = [torch.empty(tuple(s["q"].shape), device=dev, dtype=torch.float32) for s in sets]
     argv = []
     for s, o in zip(sets, outs):
@@ -197,14 +197,15 @@ def main():
     wsp, wss = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel())
     dref = ctypes.byref(desc)
     arefs = [ctypes.byref(a) for a in argv]
-    fn = lib.rattn_attention_stages
+    fn = lib.rattn_prefill_chunk if case.mode == "prefill" else lib.rattn_decode
 
-    def launch(i, stages):
-        st = fn(dref, op, arefs[i], wsp, wss, sp, stages)
+    def launch(i):
+        st = fn(dref, arefs[i], wsp, wss, sp)
         if st:
-            raise R.RattnError(st, "rattn_attention_stages")
+            raise R.RattnError(st, fn.__name__)
 
-    # one step = all layers' calls (one call when layers == 1)
+    # One step = all layers' calls (one call when layers == 1).  HIP events on the
+    # launch stream bracket every call of layer 0, which is one kernel launch.
     hip = Hip()
     K, W = args.steps, args.warmup
     ev = [[hip.event() for _ in range(3)] for _ in range(K)]
@@ -212,18 +213,13 @@ def main():
     def step(k, timed):
         for l in range(layers):
             i = (k * layers + l) % n_sets
-            if timed:
-                e = ev[k]
-                if l == 0:
-                    hip.record(e[0], sp)
-                launch(i, R.STAGE_SPLIT)
-                if l == 0:
-                    hip.record(e[1], sp)
-                launch(i, R.STAGE_COMBINE)
-                if l == layers - 1:
-                    hip.record(e[2], sp)
-            else:
-                launch(i, R.STAGE_ALL)
+            if timed and l == 0:
+                hip.record(ev[k][0], sp)
+            launch(i)
+            if timed and l == 0:
+                hip.record(ev[k][1], sp)
+        if timed:
+            hip.record(ev[k][2], sp)
 
     for k in range(W):
         step(k, False)
@@ -234,18 +230,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    split_ms = [hip.elapsed_ms(ev[k][0], ev[k][1]) for k in range(K)]
+    kern_ms = [hip.elapsed_ms(ev[k][0], ev[k][1]) for k in range(K)]
     step_ms_ev = [hip.elapsed_ms(ev[k][0], ev[k][2]) for k in range(K)]
     ms_step = wall * 1e3 / K
     pairs = pairs_per_call(case) * layers
     value = pairs / (ms_step / 1e3) / 1e9
-    split_avg = statistics.mean(split_ms)
-    achieved = ab["split"] / (split_avg / 1e3) / 1e9
-    traffic = traffic_from_counters(f"decode_split_cfg{args.config}")
+    kern_avg = statistics.mean(kern_ms)
+    achieved = ab["call"] / (kern_avg / 1e3) / 1e9
+    traffic = traffic_from_counters(f"decode_cfg{args.config}")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-            "kernel": "decode_split_kernel", "bytes_per_launch": ab["split"],
-            "avg_launch_us": round(split_avg * 1e3, 2), "median_launch_us": round(statistics.median(split_ms) * 1e3, 2)}
+            "kernel": "decode_split_kernel", "bytes_per_launch": ab["call"],
+            "avg_launch_us": round(kern_avg * 1e3, 2), "median_launch_us": round(statistics.median(kern_ms) * 1e3, 2)}
     res = {
         "metric": METRIC, "value": round(value, 4), "unit": "Gtok/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

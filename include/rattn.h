@@ -109,11 +109,21 @@ int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes);
 /*
  * Decode: every one of the q_len query tokens of agent a attends the L prefix
  * tokens (base + agent a's residual) and all S private tokens of agent a.
- * Split-K over the context with an online softmax per split (partials in the
- * workspace), then one merge that also applies Bv once per query row
- * (LRAgent, Flash-LoRA-Attention: B is applied once per query block).
- * `workspace` must hold rattn_workspace_bytes(desc, RATTN_OP_DECODE) bytes; its
- * contents on entry do not matter and are garbage on exit.
+ * One kernel launch: split-K over the context with an online softmax per split
+ * (partials in the workspace); the last split to finish for an agent merges
+ * that agent's rows and applies Bv once per query row (LRAgent,
+ * Flash-LoRA-Attention: B is applied once per query block).
+ *
+ * Workspace: at least rattn_workspace_bytes(desc, RATTN_OP_DECODE) bytes of
+ * device memory, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE (for
+ * example with a fill kernel once after allocation).  Its first 64 KiB hold
+ * completion counters, one per (KV head, agent), so H_kv * N <= 16384
+ * (RATTN_E_UNSUPPORTED otherwise).  No call writes anything else there, and
+ * every call that completes leaves them zero again, so one workspace serves
+ * any sequence of calls of any shapes whose size fits.  Calls that share a
+ * workspace must not overlap in time (use one stream, or one workspace per
+ * stream).  A call that does not complete (a fault) leaves the counters
+ * undefined: zero the workspace again before reusing it.
  */
 int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace, size_t workspace_bytes,
                  void *stream);
@@ -121,7 +131,8 @@ int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace
 /*
  * Chunked prefill: agent a appends a chunk of C = priv_len = q_len new tokens
  * whose keys/values are k_priv/v_priv[a]; chunk query t attends the L prefix
- * tokens and chunk tokens 0..t (causal).  Same residual algebra as decode.
+ * tokens and chunk tokens 0..t (causal).  Same residual algebra and the same
+ * workspace rules as rattn_decode (op = RATTN_OP_PREFILL for its size).
  */
 int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *workspace,
                         size_t workspace_bytes, void *stream);
@@ -134,24 +145,6 @@ int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *wo
  */
 int rattn_gather_base(const rattn_desc *desc, const void *pool, const int32_t *block_table, void *dst,
                       void *stream);
-
-/*
- * Runs selected stages of rattn_decode (op = RATTN_OP_DECODE) or
- * rattn_prefill_chunk (op = RATTN_OP_PREFILL) in their fixed order:
- *   RATTN_STAGE_SPLIT    per-split partial attention (including U = q Bk^T)
- *                        into the workspace;
- *   RATTN_STAGE_COMBINE  merge of the splits, Bv applied, out and lse written.
- * The combine reads what the split stage wrote into the same workspace (by this
- * call or by an earlier call on the same stream with the same descriptor and
- * tensors).  stages == RATTN_STAGE_ALL is exactly rattn_decode / _prefill_chunk.
- * Lets a caller place events between the launches.  Same validation and errors
- * as the full calls; bits outside RATTN_STAGE_ALL return RATTN_E_SHAPE.
- */
-#define RATTN_STAGE_SPLIT 1u
-#define RATTN_STAGE_COMBINE 2u
-#define RATTN_STAGE_ALL 3u
-int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,
-                           size_t workspace_bytes, void *stream, unsigned stages);
 
 /* Work decomposition chosen for a decode call (host-only introspection; no HIP call). */
 typedef struct rattn_plan_info {

@@ -29,9 +29,7 @@ RATTN_OP_DECODE, RATTN_OP_PREFILL = 0, 1
 STATUS = {0: "RATTN_OK", -1: "RATTN_E_NULL", -2: "RATTN_E_SHAPE", -3: "RATTN_E_UNSUPPORTED",
           -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP"}
 EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
-           "rattn_decode_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error",
-           "rattn_attention_stages")
-STAGE_SPLIT, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
+           "rattn_decode_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error")
 
 
 class RattnError(RuntimeError):
@@ -83,12 +81,10 @@ def lib():
         L.rattn_prefill_chunk.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P, ctypes.c_size_t, P]
         L.rattn_gather_base.argtypes = [ctypes.POINTER(Desc), P, P, P, P]
         L.rattn_decode_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PlanInfo)]
-        L.rattn_attention_stages.argtypes = [ctypes.POINTER(Desc), I, ctypes.POINTER(Args), P, ctypes.c_size_t, P,
-                                             ctypes.c_uint]
         L.rattn_status_str.argtypes = [I]
         L.rattn_status_str.restype = ctypes.c_char_p
         for f in ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
-                  "rattn_decode_plan", "rattn_version", "rattn_last_hip_error", "rattn_attention_stages"):
+                  "rattn_decode_plan", "rattn_version", "rattn_last_hip_error"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -197,8 +193,24 @@ def _check_tensors(desc: Desc, tensors: dict):
             raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want[name]}")
 
 
+_workspaces = {}
+
+
+def workspace_for(nbytes: int, device):
+    """A zero-filled workspace of at least ``nbytes`` (cached per device and
+    stream).  The library leaves it zero-filled after every call."""
+    import torch
+
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), device=device, dtype=torch.uint8)
+        _workspaces[key] = ws
+    return ws
+
+
 def _run(fn_name, op, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_priv, shared_lr, out, lse,
-         workspace, sm_scale, prefix_len, stream, desc, stages=None):
+         workspace, sm_scale, prefix_len, stream, desc):
     import torch
 
     if desc is None:
@@ -210,19 +222,17 @@ def _run(fn_name, op, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_
                    k_priv=k_priv, v_priv=v_priv, out=out, lse=lse)
     _check_tensors(desc, tensors)
     nbytes = workspace_bytes(desc, op)
-    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
-        workspace = torch.empty(max(nbytes, 1), device=q.device, dtype=torch.uint8)
+    if workspace is None:
+        workspace = workspace_for(nbytes, q.device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise RattnError(-4, f"{fn_name}: workspace has {workspace.numel() * workspace.element_size()} bytes, "
+                             f"needs {nbytes}")
     args = Args(*[_ptr(tensors[n]) for n in
                   ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out",
                    "lse")])
     wsp = ctypes.c_void_p(workspace.data_ptr())
     wsb = ctypes.c_size_t(workspace.numel() * workspace.element_size())
-    if stages is None:
-        st = getattr(lib(), fn_name)(ctypes.byref(desc), ctypes.byref(args), wsp, wsb, _stream(stream))
-    else:
-        st = lib().rattn_attention_stages(ctypes.byref(desc), op, ctypes.byref(args), wsp, wsb, _stream(stream),
-                                          stages)
-        fn_name = f"rattn_attention_stages({stages})"
+    st = getattr(lib(), fn_name)(ctypes.byref(desc), ctypes.byref(args), wsp, wsb, _stream(stream))
     if st:
         raise RattnError(st, fn_name)
     return out
@@ -266,9 +276,9 @@ def gather_base(pool, block_table, prefix_len: int, *, out=None, stream=None):
 
 
 def attend(inputs: dict, *, mode: str = "decode", shared_lr=None, prefix_len=None, out=None, lse=None,
-           workspace=None, stream=None, stages=None, desc=None):
+           workspace=None, stream=None, desc=None):
     """Runs decode or prefill on a dict of device tensors named as in the layouts above.
-    ``stages`` (a mask of STAGE_*) runs only those stages through rattn_attention_stages."""
+    A given ``workspace`` must be zero-filled before its first use (see rattn.h)."""
     if mode == "decode":
         fn_name, op = "rattn_decode", RATTN_OP_DECODE
     else:
@@ -276,4 +286,4 @@ def attend(inputs: dict, *, mode: str = "decode", shared_lr=None, prefix_len=Non
     g = inputs.get
     return _run(fn_name, op, inputs["q"], g("k_base"), g("v_base"), g("lk"), g("lv"), g("bk"), g("bv"),
                 g("block_table"), g("k_priv"), g("v_priv"), shared_lr, out, lse, workspace, 0.0, prefix_len, stream,
-                desc, stages)
+                desc)

@@ -10,8 +10,7 @@
 #include "internal.h"
 
 namespace rattn {
-hipError_t launch_decode(int bf16_in, const DecodeParams &dp, const CombineParams &cp, int D, int cpad, size_t lds,
-                         unsigned stages, hipStream_t st);
+hipError_t launch_decode(int bf16_in, const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st);
 hipError_t launch_gather(const void *pool, const int32_t *table, void *dst, int64_t L, int HK, int ps,
                          int row_bytes, hipStream_t st);
 }  // namespace rattn
@@ -20,8 +19,7 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
-constexpr int kMaxSlots = 1024;     // splits per query row the merge handles in LDS
-constexpr int kTargetItems = 512;   // split-kernel workgroups aimed for (2 per CU)
+constexpr int kTargetItems = 256;   // split-kernel workgroups aimed for (one per CU)
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t roundup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -65,7 +63,7 @@ struct Plan {
     rattn::DecodeParams dp;
     int cpad;
     size_t lds;
-    size_t off_ml, off_o, off_w, total;
+    size_t off_cnt, off_ml, off_o, off_w, total;
 };
 
 int make_plan(const rattn_desc *d, int op, Plan *pl) {
@@ -142,7 +140,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         p.n_pv = (int)n;
     }
     p.n_slots = p.n_ps + p.n_pv;
-    if (p.n_slots > kMaxSlots) return RATTN_E_UNSUPPORTED;
+    if (p.n_slots > rattn::kMaxSlots) return RATTN_E_UNSUPPORTED;
     const int64_t n_pre = (int64_t)p.n_ps * p.n_rg * HK;
     const int64_t n_all = n_pre + (int64_t)N * p.n_prg * p.n_pv * HK;
     if (n_all > (1ll << 30)) return RATTN_E_UNSUPPORTED;
@@ -156,9 +154,12 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     const bool share_pv = S > 0 && (p.pb % 4 != 0);
     const int cpl = pl->cpad > 0 ? pl->cpad / 16 : 1;
     const int per_lane = 4 * (D / 16) + 4 * cpl;
-    pl->lds = (share_pre || share_pv) ? (size_t)3 * (64 * per_lane + 32) * sizeof(float) : 0;
+    const size_t lds_merge = (share_pre || share_pv) ? (size_t)3 * (64 * per_lane + 32) * sizeof(float) : 0;
+    const size_t lds_final = (size_t)4 * (rattn::kMaxSlots + 128) * sizeof(float);
+    pl->lds = lds_merge > lds_final ? lds_merge : lds_final;
 
-    // Workspace: (max, sum), O and W partials.
+    // Workspace: a fixed-size header of completion counters (zero between calls,
+    // never written by any call's partials), then the (max, sum), O and W partials.
     const int64_t rows_kv = (int64_t)HK * N * rpa;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -166,6 +167,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         off += (bytes + 255) & ~(size_t)255;
         return o;
     };
+    if ((int64_t)HK * N * (int64_t)sizeof(unsigned) > rattn::kCounterHeaderBytes) return RATTN_E_UNSUPPORTED;
+    pl->off_cnt = take((size_t)rattn::kCounterHeaderBytes);
     pl->off_ml = take((size_t)rows_kv * p.n_slots * 2 * sizeof(float));
     pl->off_o = take((size_t)rows_kv * p.n_slots * D * sizeof(float));
     pl->off_w = take(resid ? (size_t)rows_kv * p.n_slots * r * sizeof(float) : 0);
@@ -198,9 +201,7 @@ int hip_status(hipError_t e) {
     return RATTN_E_HIP;
 }
 
-int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_bytes, void *stream, int op,
-                  unsigned stages) {
-    if (stages & ~(unsigned)RATTN_STAGE_ALL) return RATTN_E_SHAPE;
+int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_bytes, void *stream, int op) {
     int st = check_desc(d, op);
     if (st) return st;
     st = check_args(d, a);
@@ -208,9 +209,9 @@ int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_
     Plan pl;
     st = make_plan(d, op, &pl);
     if (st) return st;
-    if (pl.total > 0 && !ws) return RATTN_E_WORKSPACE;
+    if (!ws) return RATTN_E_WORKSPACE;
     if (ws_bytes < pl.total) return RATTN_E_WORKSPACE;
-    if (ws && !aligned(ws, 256)) return RATTN_E_ALIGN;
+    if (!aligned(ws, 256)) return RATTN_E_ALIGN;
 
     char *w = static_cast<char *>(ws);
     rattn::DecodeParams &p = pl.dp;
@@ -220,32 +221,18 @@ int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_
     p.table = a->block_table;
     p.lk = a->lk;
     p.lv = a->lv;
+    p.bk = a->bk;
+    p.bv = a->bv;
     p.kp = a->k_priv;
     p.vp = a->v_priv;
-    p.bk = a->bk;
+    p.out = a->out;
+    p.lse = a->lse;
+    p.cnt = reinterpret_cast<unsigned *>(w + pl.off_cnt);
     p.p_ml = reinterpret_cast<float *>(w + pl.off_ml);
     p.p_o = reinterpret_cast<float *>(w + pl.off_o);
     p.p_w = reinterpret_cast<float *>(w + pl.off_w);
-
-    rattn::CombineParams cp{};
-    cp.p_ml = p.p_ml;
-    cp.p_o = p.p_o;
-    cp.p_w = p.p_w;
-    cp.bv = a->bv;
-    cp.out = a->out;
-    cp.lse = a->lse;
-    cp.N = p.N;
-    cp.QL = p.QL;
-    cp.HQ = p.HQ;
-    cp.HK = p.HK;
-    cp.g = p.g;
-    cp.r = (d->rank > 0 && d->prefix_len > 0) ? d->rank : 0;
-    cp.rpa = p.rpa;
-    cp.n_slots = p.n_slots;
-    cp.n_ps = p.n_ps;
-    cp.S = p.S;
-
-    return hip_status(rattn::launch_decode(d->dtype == RATTN_BF16, p, cp, d->head_dim, pl.cpad, pl.lds, stages,
+    if (!(d->rank > 0 && d->prefix_len > 0)) p.r = 0;  // no residual without a prefix
+    return hip_status(rattn::launch_decode(d->dtype == RATTN_BF16, p, d->head_dim, pl.cpad, pl.lds,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -301,17 +288,12 @@ int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info) {
 
 int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace, size_t workspace_bytes,
                  void *stream) {
-    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_DECODE, RATTN_STAGE_ALL);
+    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_DECODE);
 }
 
 int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *workspace,
                         size_t workspace_bytes, void *stream) {
-    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_PREFILL, RATTN_STAGE_ALL);
-}
-
-int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,
-                           size_t workspace_bytes, void *stream, unsigned stages) {
-    return run_attention(desc, args, workspace, workspace_bytes, stream, op, stages);
+    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_PREFILL);
 }
 
 int rattn_gather_base(const rattn_desc *d, const void *pool, const int32_t *block_table, void *dst,

@@ -1,23 +1,23 @@
-// decode.hip -- decode kernels of librattn (gfx950).
+// decode.hip -- decode kernel of librattn (gfx950).
 //
 // Fused residual attention for N agents that share one base KV cache
 // (ForkKV Guide, "Fused ResidualAttention"; LRAgent, "Flash-LoRA-Attention"):
 //   score  s = scale * (q . K_base[j] + (q Bk_a^T) . Lk_a[j])
 //   output o = sum_j p_j V_base[j] + (sum_j p_j Lv_a[j]) Bv_a
-// Two launches on the caller's stream:
-//   1. decode_split, one workgroup per (KV head, row group, context split):
-//      computes U = scale*log2(e) * q Bk_a^T for its query rows with MFMA,
-//      then streams the base K/V tiles once for all agents' query rows (one
-//      MFMA contraction over the rows of every agent), adds the rank-r score
-//      correction with a second MFMA over the agents' Lk rows, runs an online
-//      softmax in the log2 domain and accumulates P V_base and P Lv.  Private
-//      tokens are extra work items with per-agent keys and no residual.
-//      Partials (max, sum, O, W) go to the workspace;
-//   2. combine, one wavefront per query row: log-sum-exp merge of the splits
-//      with wavefront shuffles, then o = (sum w O + (sum w W) Bv_a^(k)) / sum w l:
-//      Bv is applied once per row, not per token.
+// One launch.  Each workgroup takes one (KV head, row group, context split):
+//   * it computes U = scale*log2(e) * q Bk_a^T for its query rows with MFMA;
+//   * it streams the base K/V tiles once for all agents' query rows (one MFMA
+//     contraction over the rows of every agent), adds the rank-r score
+//     correction with a second MFMA over the agents' Lk rows, runs an online
+//     softmax in the log2 domain and accumulates P V_base and P Lv.  Private
+//     tokens are extra work items with per-agent keys and no residual;
+//   * it writes its partial state (max, sum, O, W) to the workspace and takes a
+//     ticket on a per-(KV head, agent) counter; the workgroup that completes an
+//     agent merges that agent's rows: a log-sum-exp merge over the splits with
+//     wavefront shuffles, then o = (sum w O + (sum w W) Bv_a^(k)) / sum w l, so
+//     Bv is applied once per row, not per token.  It resets the counter to zero.
 //
-// Layout inside decode_split (S^T formulation): the MFMA A operand is the key
+// Layout of the streaming loop (S^T formulation): the MFMA A operand is the key
 // tile (rows = 16 tokens), the B operand the query rows (columns = 16 query
 // rows), so the scores arrive with one query row per lane column and the
 // softmax statistics of a row live in the lanes that own it.  The value product
@@ -183,6 +183,102 @@ __device__ inline void compute_chunk(Acc<T, D, CPAD> &acc, const Chunk<T, D, CPA
     }
 }
 
+// ------------------------------------------------------------------- merge --
+
+// Expected completion tickets of (KV head, agent a): one per prefix item whose
+// row group holds some of a's rows, one per private item of a.
+__device__ inline unsigned expected_tickets(const DecodeParams &p, int a) {
+    unsigned e = 0;
+    if (p.n_ps > 0) {
+        int nrg = 1;
+        if (p.rpa > 16) nrg = (a * p.bpa + p.bpa - 1) / 4 - (a * p.bpa) / 4 + 1;
+        e += (unsigned)(p.n_ps * nrg);
+    }
+    if (p.n_pv > 0) e += (unsigned)(p.n_pv * p.n_prg);
+    return e;
+}
+
+// One wavefront merges the splits of one query row and writes out/lse.
+// wbuf: n_slots floats of LDS for the weights, wr: r floats for the merged W.
+template <typename T, int D>
+__device__ inline void merge_row(const DecodeParams &p, int k, int a, int ria, float *wbuf, float *wr, int lane) {
+    constexpr int DPL = D / 64;
+    const int t = ria / p.g, hh = ria % p.g;
+    const int64_t R = ((int64_t)a * p.QL + t) * p.HQ + (int64_t)k * p.g + hh;
+    const int64_t rec0 = ((int64_t)k * p.N * p.rpa + (int64_t)a * p.rpa + ria) * p.n_slots;
+    const int ns = p.n_slots, r = p.r;
+
+    float mx = -3.0e38f;
+    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, p.p_ml[(rec0 + s) * 2]);
+    mx = wave_max(mx);
+    float lsum = 0.0f;
+    for (int s = lane; s < ns; s += 64) {
+        const float2 ml = *reinterpret_cast<const float2 *>(p.p_ml + (rec0 + s) * 2);
+        const float w = fexp2(ml.x - mx);
+        wbuf[s] = w;
+        lsum += w * ml.y;
+    }
+    lsum = wave_sum(lsum);
+    __builtin_amdgcn_wave_barrier();
+
+    float o[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
+    const float *po = p.p_o + rec0 * D + DPL * lane;
+    for (int s0 = 0; s0 < ns; s0 += 16) {
+        float v[16][DPL], wv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int s = s0 + u;
+            const int sc = s < ns ? s : ns - 1;
+            wv[u] = s < ns ? wbuf[sc] : 0.0f;
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) v[u][e] = po[(int64_t)sc * D + e];
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) o[e] += wv[u] * v[u][e];
+    }
+    if (r > 0 && p.n_ps > 0) {
+        for (int j = lane; j < r; j += 64) {
+            float wj = 0.0f;
+            const float *pw = p.p_w + rec0 * r + j;
+            for (int s0 = 0; s0 < p.n_ps; s0 += 16) {
+                float v[16], wv[16];
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const int s = s0 + u;
+                    const int sc = s < p.n_ps ? s : p.n_ps - 1;
+                    wv[u] = s < p.n_ps ? wbuf[sc] : 0.0f;
+                    v[u] = pw[(int64_t)sc * r];
+                }
+#pragma unroll
+                for (int u = 0; u < 16; ++u) wj += wv[u] * v[u];
+            }
+            wr[j] = wj;
+        }
+        __builtin_amdgcn_wave_barrier();
+        const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * r * p.HK * D + (int64_t)k * D + DPL * lane;
+        for (int j0 = 0; j0 < r; j0 += 8) {
+            float bvv[8][DPL];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) bvv[u][e] = (float)bv[(int64_t)(j0 + u) * p.HK * D + e];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int e = 0; e < DPL; ++e) o[e] += wr[j0 + u] * bvv[u][e];
+        }
+    }
+    const float inv = 1.0f / lsum;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) p.out[R * D + DPL * lane + e] = o[e] * inv;
+    if (lane == 0 && p.lse) p.lse[R] = (mx + __builtin_log2f(lsum)) * 0.69314718055994530942f;
+    __builtin_amdgcn_wave_barrier();
+}
+
 // ------------------------------------------------------------ split kernel --
 
 template <typename T, int D, int CPAD>
@@ -272,6 +368,69 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) qB[s] = vm ? O::load8(qp + qrow * D + 32 * s + 8 * j4) : O::zero();
 
+    // Token stream of this item.
+    Stream<T, D, CPAD> st;
+    st.r = p.r;
+    st.resid = resid;
+    st.tlast = t1 - 1;
+    st.tlast16 = st.tlast & ~15;
+    if (prefix) {
+        st.kb = static_cast<const T *>(p.kb);
+        st.vb = static_cast<const T *>(p.vb);
+        if (p.ps > 0) {
+            st.table = p.table;
+            st.ps = p.ps;
+            st.page_stride = (int64_t)p.HK * p.ps * D;
+            st.head_off = (int64_t)k * p.ps * D;
+        } else {
+            st.table = nullptr;
+            st.ps = 16;
+            st.page_stride = 0;
+            st.head_off = 0;
+            st.kb += (int64_t)k * p.L * D;
+            st.vb += (int64_t)k * p.L * D;
+        }
+    } else {
+        const int64_t seg = ((int64_t)agent_p * p.HK + k) * p.S * D;
+        st.kb = static_cast<const T *>(p.kp) + seg;
+        st.vb = static_cast<const T *>(p.vp) + seg;
+        st.table = nullptr;
+        st.ps = 16;
+        st.page_stride = 0;
+        st.head_off = 0;
+    }
+    {
+        const T *lk = static_cast<const T *>(p.lk);
+        const T *lv = static_cast<const T *>(p.lv);
+#pragma unroll
+        for (int s = 0; s < CSx; ++s) {
+            const int cc = 32 * s + 8 * j4;
+            int lr = 0, col = 0;
+            if (resid && cc < cvalid) {
+                lr = p.shared_lr ? 0 : blk.a0 + (cc >> p.lr_shift);
+                col = cc & (p.r - 1);
+            } else if (resid) {
+                lr = p.shared_lr ? 0 : blk.a0;  // padding column: any finite data (U is zero there)
+            }
+            st.lk[s] = lk + (int64_t)lr * p.L * p.r + col;
+        }
+        const int cl = CPLx * n16;
+        int lr = 0, col = 0;
+        if (resid && cl < cvalid) {
+            lr = p.shared_lr ? 0 : blk.a0 + (cl >> p.lr_shift);
+            col = cl & (p.r - 1);
+        } else if (resid) {
+            lr = p.shared_lr ? 0 : blk.a0;
+        }
+        st.lv = lv + (int64_t)lr * p.L * p.r + col;
+    }
+
+    // First chunk's loads go out before U is computed.
+    Chunk<T, D, CPAD> ca, cb;
+    const int step = 32 * TG;
+    int tc = t0 + 32 * tg;
+    if (active) load_chunk(ca, st, tc, n16, j4);
+
     // U = scale*log2(e) * q Bk^T as the B operand of the rank-r score correction,
     // block-diagonal over the agents of the block (bf16 carries hi + lo halves).
     // Computed as U^T = Bk Q^T with MFMA; A-operand row rho of output tile 2s+h
@@ -333,63 +492,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         }
     }
 
-    // Token stream of this item.
-    Stream<T, D, CPAD> st;
-    st.r = p.r;
-    st.resid = resid;
-    st.tlast = t1 - 1;
-    st.tlast16 = st.tlast & ~15;
-    if (prefix) {
-        st.kb = static_cast<const T *>(p.kb);
-        st.vb = static_cast<const T *>(p.vb);
-        if (p.ps > 0) {
-            st.table = p.table;
-            st.ps = p.ps;
-            st.page_stride = (int64_t)p.HK * p.ps * D;
-            st.head_off = (int64_t)k * p.ps * D;
-        } else {
-            st.table = nullptr;
-            st.ps = 16;
-            st.page_stride = 0;
-            st.head_off = 0;
-            st.kb += (int64_t)k * p.L * D;
-            st.vb += (int64_t)k * p.L * D;
-        }
-    } else {
-        const int64_t seg = ((int64_t)agent_p * p.HK + k) * p.S * D;
-        st.kb = static_cast<const T *>(p.kp) + seg;
-        st.vb = static_cast<const T *>(p.vp) + seg;
-        st.table = nullptr;
-        st.ps = 16;
-        st.page_stride = 0;
-        st.head_off = 0;
-    }
-    {
-        const T *lk = static_cast<const T *>(p.lk);
-        const T *lv = static_cast<const T *>(p.lv);
-#pragma unroll
-        for (int s = 0; s < CSx; ++s) {
-            const int cc = 32 * s + 8 * j4;
-            int lr = 0, col = 0;
-            if (resid && cc < cvalid) {
-                lr = p.shared_lr ? 0 : blk.a0 + (cc >> p.lr_shift);
-                col = cc & (p.r - 1);
-            } else if (resid) {
-                lr = p.shared_lr ? 0 : blk.a0;  // padding column: any finite data (U is zero there)
-            }
-            st.lk[s] = lk + (int64_t)lr * p.L * p.r + col;
-        }
-        const int cl = CPLx * n16;
-        int lr = 0, col = 0;
-        if (resid && cl < cvalid) {
-            lr = p.shared_lr ? 0 : blk.a0 + (cl >> p.lr_shift);
-            col = cl & (p.r - 1);
-        } else if (resid) {
-            lr = p.shared_lr ? 0 : blk.a0;
-        }
-        st.lv = lv + (int64_t)lr * p.L * p.r + col;
-    }
-
     Acc<T, D, CPAD> acc;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) acc.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -399,10 +501,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     acc.l = 0.0f;
 
     if (active) {
-        const int step = 32 * TG;
-        int tc = t0 + 32 * tg;
-        Chunk<T, D, CPAD> ca, cb;
-        load_chunk(ca, st, tc, n16, j4);
         for (; tc < t1; tc += 2 * step) {
             load_chunk(cb, st, tc + step, n16, j4);
             compute_chunk(acc, ca, qB, uH, uL, cl2, resid, tc, t1, causal, tq, j4);
@@ -491,144 +589,76 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
             p.p_ml[rec * 2 + 1] = l_run;
         }
     }
-}
 
-// ----------------------------------------------------------------- combine --
-
-// One wavefront per query row.  Loads every split's (max, sum) at once, merges
-// them with wavefront shuffles, then sums the weighted O and W partials and
-// applies Bv once.
-template <typename T, int D>
-__global__ __launch_bounds__(64) void combine_kernel(CombineParams p) {
-    constexpr int MAXS = 1024;
-    constexpr int DPL = D / 64;  // output columns per lane
-    __shared__ float s_w[MAXS];
-    __shared__ float s_wr[128];
-    const int R = blockIdx.x;  // (a * QL + t) * HQ + h
-    const int h = R % p.HQ;
-    const int at = R / p.HQ;
-    const int a = at / p.QL, t = at % p.QL;
-    const int k = h / p.g, hh = h % p.g;
-    const int64_t grow = (int64_t)a * p.rpa + (int64_t)t * p.g + hh;
-    const int64_t rec0 = ((int64_t)k * p.N * p.rpa + grow) * p.n_slots;
-    const int lane = threadIdx.x;
-    const int ns = p.n_slots;
-
-    float mv[MAXS / 64], lv[MAXS / 64];
-    float mx = -3.0e38f;
-#pragma unroll
-    for (int u = 0; u < MAXS / 64; ++u) {
-        const int s = lane + 64 * u;
-        mv[u] = -3.0e38f;
-        lv[u] = 0.0f;
-        if (s < ns) {
-            const float2 ml = *reinterpret_cast<const float2 *>(p.p_ml + (rec0 + s) * 2);
-            mv[u] = ml.x;
-            lv[u] = ml.y;
-        }
-        mx = fmaxf(mx, mv[u]);
-    }
-    mx = wave_max(mx);
-    float lsum = 0.0f;
-#pragma unroll
-    for (int u = 0; u < MAXS / 64; ++u) {
-        const int s = lane + 64 * u;
-        const float w = fexp2(mv[u] - mx);
-        if (s < ns) s_w[s] = w;
-        lsum += w * lv[u];
-    }
-    lsum = wave_sum(lsum);
+    // ---- completion tickets; the workgroup that completes an agent merges it
+    __shared__ int s_last[64];
+    __shared__ int s_nlast;
+    __threadfence();  // release this thread's partial stores (device scope)
     __syncthreads();
-
-    float o[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
-    const float *po = p.p_o + rec0 * D + DPL * lane;
-    int s = 0;
-    for (; s + 8 <= ns; s += 8) {
-        float v[8][DPL];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) v[u][e] = po[(int64_t)(s + u) * D + e];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) o[e] += s_w[s + u] * v[u][e];
-    }
-    for (; s < ns; ++s)
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] += s_w[s] * po[(int64_t)s * D + e];
-
-    if (p.r > 0) {
-        // W = sum over prefix splits of w_s W_s (lane j, and j + 64 when r = 128)
-        for (int j = lane; j < p.r; j += 64) {
-            float wj = 0.0f;
-            const float *pw = p.p_w + rec0 * p.r + j;
-            int s2 = 0;
-            for (; s2 + 8 <= p.n_ps; s2 += 8) {
-                float v[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) v[u] = pw[(int64_t)(s2 + u) * p.r];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) wj += s_w[s2 + u] * v[u];
-            }
-            for (; s2 < p.n_ps; ++s2) wj += s_w[s2] * pw[(int64_t)s2 * p.r];
-            s_wr[j] = wj;
+    if (threadIdx.x == 0) {
+        int a_lo, a_hi;
+        if (prefix) {
+            const RowBlock b0 = prefix_block(blk0, p.N, p.rpa, p.apb, p.bpa);
+            const RowBlock b1 = prefix_block(blk0 + nblk - 1, p.N, p.rpa, p.apb, p.bpa);
+            a_lo = b0.a0;
+            a_hi = b1.a0 + b1.na - 1;
+        } else {
+            a_lo = a_hi = agent_p;
         }
-        __syncthreads();
-        const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * p.r * p.HK * D + (int64_t)k * D + DPL * lane;
-        for (int j = 0; j < p.r; ++j) {
-            const float wj = s_wr[j];
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) o[e] += wj * (float)bv[(int64_t)j * p.HK * D + e];
+        int nl = 0;
+        for (int a = a_lo; a <= a_hi; ++a) {
+            const unsigned old = atomicAdd(p.cnt + (int64_t)k * p.N + a, 1u);
+            if (old + 1 == expected_tickets(p, a)) s_last[nl++] = a;
         }
+        s_nlast = nl;
     }
-    const float inv = 1.0f / lsum;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) p.out[(int64_t)R * D + DPL * lane + e] = o[e] * inv;
-    if (lane == 0 && p.lse) p.lse[R] = (mx + __builtin_log2f(lsum)) * 0.69314718055994530942f;
+    __syncthreads();
+    const int nl = s_nlast;
+    if (nl > 0) {
+        __threadfence();  // acquire: every item's partials of these agents are visible
+        float *wbuf = smem + (size_t)wave * (kMaxSlots + 128);
+        float *wr = wbuf + kMaxSlots;
+        for (int i = 0; i < nl; ++i) {
+            const int a = s_last[i];
+            for (int ria = wave; ria < p.rpa; ria += 4) merge_row<T, D>(p, k, a, ria, wbuf, wr, lane);
+        }
+        // Ready for the next call.  An atomic at device scope, like the tickets: a
+        // plain store could stay in this XCD's L2 while the next call's tickets
+        // are counted at the device-wide coherence point.
+        if (threadIdx.x == 0)
+            for (int i = 0; i < nl; ++i) atomicExch(p.cnt + (int64_t)k * p.N + s_last[i], 0u);
+    }
 }
 
 // ---------------------------------------------------------------- launchers --
 
 template <typename T>
-static hipError_t launch_decode_t(const DecodeParams &dp, const CombineParams &cp, int D, int cpad, size_t lds,
-                                  unsigned stages, hipStream_t st) {
+static hipError_t launch_decode_t(const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st) {
     const dim3 grid(8 * dp.per_xcd);
 #define RATTN_SPLIT(DD, CP) \
     hipLaunchKernelGGL((decode_split_kernel<T, DD, CP>), grid, dim3(256), lds, st, dp)
-    if (stages & 1u) {
-        if (D == 128) {
-            switch (cpad) {
-                case 0: RATTN_SPLIT(128, 0); break;
-                case 32: RATTN_SPLIT(128, 32); break;
-                case 64: RATTN_SPLIT(128, 64); break;
-                default: RATTN_SPLIT(128, 128); break;
-            }
-        } else {
-            switch (cpad) {
-                case 0: RATTN_SPLIT(64, 0); break;
-                case 32: RATTN_SPLIT(64, 32); break;
-                case 64: RATTN_SPLIT(64, 64); break;
-                default: RATTN_SPLIT(64, 128); break;
-            }
+    if (D == 128) {
+        switch (cpad) {
+            case 0: RATTN_SPLIT(128, 0); break;
+            case 32: RATTN_SPLIT(128, 32); break;
+            case 64: RATTN_SPLIT(128, 64); break;
+            default: RATTN_SPLIT(128, 128); break;
+        }
+    } else {
+        switch (cpad) {
+            case 0: RATTN_SPLIT(64, 0); break;
+            case 32: RATTN_SPLIT(64, 32); break;
+            case 64: RATTN_SPLIT(64, 64); break;
+            default: RATTN_SPLIT(64, 128); break;
         }
     }
 #undef RATTN_SPLIT
-    if (stages & 2u) {
-        if (D == 128)
-            hipLaunchKernelGGL((combine_kernel<T, 128>), dim3(dp.N * dp.QL * dp.HQ), dim3(64), 0, st, cp);
-        else
-            hipLaunchKernelGGL((combine_kernel<T, 64>), dim3(dp.N * dp.QL * dp.HQ), dim3(64), 0, st, cp);
-    }
     return hipGetLastError();
 }
 
-hipError_t launch_decode(int bf16_in, const DecodeParams &dp, const CombineParams &cp, int D, int cpad, size_t lds,
-                         unsigned stages, hipStream_t st) {
-    if (bf16_in) return launch_decode_t<bf16>(dp, cp, D, cpad, lds, stages, st);
-    return launch_decode_t<float>(dp, cp, D, cpad, lds, stages, st);
+hipError_t launch_decode(int bf16_in, const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st) {
+    if (bf16_in) return launch_decode_t<bf16>(dp, D, cpad, lds, st);
+    return launch_decode_t<float>(dp, D, cpad, lds, st);
 }
 
 }  // namespace rattn

@@ -59,14 +59,24 @@ RATTN_HD void block_row(const RowBlock &rb, int m, int rpa, int *agent, int *ria
     }
 }
 
+// Splits per query row the merge handles (weights staged in LDS).
+constexpr int kMaxSlots = 512;
+
+// The workspace starts with a header of completion counters of this fixed size,
+// whatever the shape of the call, so that no call's partials ever land on bytes
+// that another call (of another shape) counts with.  H_kv * N must fit.
+constexpr int64_t kCounterHeaderBytes = 64 * 1024;
+
 struct DecodeParams {
     const void *q, *kb, *vb;
     const int32_t *table;
-    const void *lk, *lv, *bk, *kp, *vp;
+    const void *lk, *lv, *bk, *bv, *kp, *vp;
+    float *out, *lse;
     float *p_ml;      // [H_kv, N*rpa, n_slots, 2]  running max (log2 units), sum of weights
     float *p_o;       // [H_kv, N*rpa, n_slots, d]  unnormalised P V_base (+ private P V)
     float *p_w;       // [H_kv, N*rpa, n_slots, r]  unnormalised P Lv
-    int64_t L, S;     // < 2^31 (validated on the host)
+    unsigned *cnt;    // [H_kv, N] completion tickets; zero between calls
+    int64_t L, S;     // < 2^30 (validated on the host)
     int N, QL, HQ, HK, g, r, lr_shift, rpa, apb, bpa, ps, shared_lr;
     int causal;       // private token j is visible to query token t only if j <= t
     float c;          // softmax scale * log2(e)
@@ -75,14 +85,6 @@ struct DecodeParams {
     int pb, n_prg, n_pv;
     int tok_pv;
     int n_slots, n_prefix_items, n_items, per_xcd;
-};
-
-struct CombineParams {
-    const float *p_ml, *p_o, *p_w;
-    const void *bv;
-    float *out, *lse;
-    int N, QL, HQ, HK, g, r, rpa, n_slots, n_ps;
-    int64_t S;
 };
 
 }  // namespace rattn

@@ -36,8 +36,13 @@ def run_gpu(case, x, lse=True):
     R = rattn()
     t = synth.to_torch(x, DEV)
     lse_t = torch.empty(t["q"].shape[:3], device=DEV, dtype=torch.float32) if lse else None
-    out = R.attend(t, mode=case.mode, shared_lr=case.shared_lr, prefix_len=case.prefix_len, lse=lse_t)
+    # the output starts as NaN, so a row the kernel never writes cannot pass
+    out = torch.full(tuple(t["q"].shape), float("nan"), device=DEV, dtype=torch.float32)
+    R.attend(t, mode=case.mode, shared_lr=case.shared_lr, prefix_len=case.prefix_len, lse=lse_t, out=out)
     torch.cuda.synchronize()
+    # every call leaves the completion-counter header of the workspace zero
+    ws = R.workspace_for(0, torch.device(DEV))
+    assert int(ws[: 64 * 1024].count_nonzero()) == 0, f"completion counters not reset after {case}"
     return out.cpu().numpy().astype(np.float64), (lse_t.cpu().numpy().astype(np.float64) if lse else None)
 
 
@@ -113,7 +118,7 @@ def test_full_depth_decode_sampled_layers():
     layers = [synth.make_inputs_torch(c, 4, l, DEV) for l in range(c.layers)]
     outs = [torch.empty(layers[0]["q"].shape, device=DEV, dtype=torch.float32) for _ in range(c.layers)]
     desc = R.describe(layers[0]["q"], layers[0]["k_base"], layers[0]["lk"], layers[0]["bk"])
-    ws = torch.empty(R.workspace_bytes(desc), device=DEV, dtype=torch.uint8)
+    ws = torch.zeros(R.workspace_bytes(desc), device=DEV, dtype=torch.uint8)  # zero-filled once
     for l in range(c.layers):
         R.attend(layers[l], out=outs[l], workspace=ws)
     torch.cuda.synchronize()
@@ -214,3 +219,24 @@ def test_shuffled_table_bitwise_equals_identity():
     got, _ = run_gpu(c, alias)
     exp, _ = oracle.attend(c, alias)
     parity.check(got, exp, "bf16", what="aliased pages")
+
+
+def test_workspace_reused_across_shapes():
+    """One zero-filled workspace serves calls of different shapes in turn: every call
+    leaves its completion counters zero (rattn.h workspace rule)."""
+    R = rattn()
+    cases = [synth.Case(4, 32, 8, 128, 16, 3000, priv_len=40, name="A"),
+             synth.Case(7, 8, 2, 64, 8, 900, name="B"),
+             synth.Case(4, 32, 8, 128, 16, 3000, priv_len=40, name="A again")]
+    xs = [synth.make_inputs(c, 40 + i, b_sigma=0.3) for i, c in enumerate(cases)]
+    nbytes = max(R.workspace_bytes(R.describe(*[synth.to_torch(x, DEV)[n] for n in ("q", "k_base", "lk", "bk")],
+                                              k_priv=synth.to_torch(x, DEV)["k_priv"])) for x in xs)
+    ws = torch.zeros(nbytes, device=DEV, dtype=torch.uint8)
+    for c, x in zip(cases, xs):
+        say(f"[gpu] shared workspace: {c.name}")
+        t = synth.to_torch(x, DEV)
+        got = R.attend(t, workspace=ws)
+        torch.cuda.synchronize()
+        exp, _ = oracle.attend(c, x)
+        parity.check(got.cpu().numpy().astype(np.float64), exp, "bf16", what=c.name)
+    assert int(ws[: 64 * 1024].count_nonzero()) == 0, "counter header not zero after the calls"
