@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu]
 
-One step = one rattn_decode call (a single kernel launch) over one
+One step = one rattn_decode call (split kernel, then combine) over one
 layer of the Llama-3-8B-shaped decode workload: 4 agents on a 32768-token shared
 prefix, H_q=32, H_kv=8, d=128, per-agent rank-16 residual caches, bf16 inputs,
 fp32 accumulation.  Inputs are seeded synthetic data already resident in HBM.
@@ -11,10 +11,11 @@ Several replicas of the input set are rotated so that each step reads its
 step.
 
 Prints one JSON line.  `value` is agent x context-token pairs per second (Gtok/s).
-`roofline` is for that kernel: its algorithmic bytes per launch (every input
-read once and the fp32 output written once) divided by its average duration,
-measured with HIP events recorded on the launch stream around the launch in
-every timed step.  `cpu_baseline` times the fp64 oracle
+`roofline` is for the split kernel, which carries all but the merge: its
+algorithmic bytes per launch (every input it must read once: base K/V,
+low-rank caches, private tokens, queries, up-projections Bk) divided by its
+average duration, measured with HIP events recorded on the launch stream
+around that launch in every timed step.  `cpu_baseline` times the fp64 oracle
 on the host cores.
 """
 from __future__ import annotations
@@ -83,7 +84,7 @@ def algorithmic_bytes(c):
     priv = 2 * c.n_agents * c.n_kv_heads * c.priv_len * c.head_dim * es
     table = 4 * c.n_table
     out = 4 * c.n_agents * c.q_len * c.n_q_heads * c.head_dim
-    split = base + resid + priv + q + table
+    split = base + resid + priv + q + table + bmat // 2
     return dict(base=base, resid=resid, bmat=bmat, q=q, priv=priv, table=table, out=out,
                 call=base + resid + bmat + q + priv + table + out, split=split)
 
@@ -184,7 +185,7 @@ def main():
                       block_table=sets[0]["block_table"], k_priv=sets[0]["k_priv"], prefix_len=case.prefix_len,
                       shared_lr=case.shared_lr)
     wsb = R.workspace_bytes(desc, op)
-    ws = torch.zeros(max(wsb, 256), device=dev, dtype=torch.uint8)  # zero-filled once (rattn.h)
+    ws = torch.empty(max(wsb, 256), device=dev, dtype=torch.uint8)
     outs = [torch.empty(tuple(s["q"].shape), device=dev, dtype=torch.float32) for s in sets]
     argv = []
     for s, o in zip(sets, outs):
@@ -197,15 +198,15 @@ def main():
     wsp, wss = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel())
     dref = ctypes.byref(desc)
     arefs = [ctypes.byref(a) for a in argv]
-    fn = lib.rattn_prefill_chunk if case.mode == "prefill" else lib.rattn_decode
+    fn = lib.rattn_attention_stages
 
-    def launch(i):
-        st = fn(dref, arefs[i], wsp, wss, sp)
+    def launch(i, stages):
+        st = fn(dref, op, arefs[i], wsp, wss, sp, stages)
         if st:
-            raise R.RattnError(st, fn.__name__)
+            raise R.RattnError(st, "rattn_attention_stages")
 
     # One step = all layers' calls (one call when layers == 1).  HIP events on the
-    # launch stream bracket every call of layer 0, which is one kernel launch.
+    # launch stream bracket the split launch of layer 0 and the whole step.
     hip = Hip()
     K, W = args.steps, args.warmup
     ev = [[hip.event() for _ in range(3)] for _ in range(K)]
@@ -215,9 +216,11 @@ def main():
             i = (k * layers + l) % n_sets
             if timed and l == 0:
                 hip.record(ev[k][0], sp)
-            launch(i)
-            if timed and l == 0:
+                launch(i, R.STAGE_SPLIT)
                 hip.record(ev[k][1], sp)
+                launch(i, R.STAGE_COMBINE)
+            else:
+                launch(i, R.STAGE_ALL)
         if timed:
             hip.record(ev[k][2], sp)
 
@@ -236,11 +239,11 @@ def main():
     pairs = pairs_per_call(case) * layers
     value = pairs / (ms_step / 1e3) / 1e9
     kern_avg = statistics.mean(kern_ms)
-    achieved = ab["call"] / (kern_avg / 1e3) / 1e9
+    achieved = ab["split"] / (kern_avg / 1e3) / 1e9
     traffic = traffic_from_counters(f"decode_cfg{args.config}")
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-            "kernel": "decode_split_kernel", "bytes_per_launch": ab["call"],
+            "kernel": "decode_split_kernel", "bytes_per_launch": ab["split"],
             "avg_launch_us": round(kern_avg * 1e3, 2), "median_launch_us": round(statistics.median(kern_ms) * 1e3, 2)}
     res = {
         "metric": METRIC, "value": round(value, 4), "unit": "Gtok/s", "n_gpus": 1, "steps": K, "warmup": W,

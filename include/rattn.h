@@ -109,21 +109,15 @@ int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes);
 /*
  * Decode: every one of the q_len query tokens of agent a attends the L prefix
  * tokens (base + agent a's residual) and all S private tokens of agent a.
- * One kernel launch: split-K over the context with an online softmax per split
- * (partials in the workspace); the last split to finish for an agent merges
- * that agent's rows and applies Bv once per query row (LRAgent,
+ * Two kernel launches on `stream`: split-K over the context with an online
+ * softmax per split (partials in the workspace), then a merge of the splits of
+ * every query row that also applies Bv once per row (LRAgent,
  * Flash-LoRA-Attention: B is applied once per query block).
  *
  * Workspace: at least rattn_workspace_bytes(desc, RATTN_OP_DECODE) bytes of
- * device memory, 256-byte aligned, ZERO-FILLED BEFORE ITS FIRST USE (for
- * example with a fill kernel once after allocation).  Its first 64 KiB hold
- * completion counters, one per (KV head, agent), so H_kv * N <= 16384
- * (RATTN_E_UNSUPPORTED otherwise).  No call writes anything else there, and
- * every call that completes leaves them zero again, so one workspace serves
- * any sequence of calls of any shapes whose size fits.  Calls that share a
- * workspace must not overlap in time (use one stream, or one workspace per
- * stream).  A call that does not complete (a fault) leaves the counters
- * undefined: zero the workspace again before reusing it.
+ * device memory, 256-byte aligned.  Its contents on entry do not matter and are
+ * scratch on exit; calls that share a workspace must not overlap in time (one
+ * stream, or one workspace per stream).
  */
 int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace, size_t workspace_bytes,
                  void *stream);
@@ -145,6 +139,24 @@ int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *wo
  */
 int rattn_gather_base(const rattn_desc *desc, const void *pool, const int32_t *block_table, void *dst,
                       void *stream);
+
+/*
+ * Runs selected launches of rattn_decode (op = RATTN_OP_DECODE) or
+ * rattn_prefill_chunk (op = RATTN_OP_PREFILL), in their fixed order:
+ *   RATTN_STAGE_SPLIT    per-split partial attention into the workspace;
+ *   RATTN_STAGE_COMBINE  merge of the splits, Bv applied, out and lse written.
+ * The combine reads what the split stage wrote into the same workspace (in this
+ * call, or in an earlier call on the same stream with the same descriptor and
+ * tensors).  stages == RATTN_STAGE_ALL is exactly rattn_decode /
+ * rattn_prefill_chunk.  Lets a caller time the launches separately.  Same
+ * validation and errors as the full calls; zero or bits outside
+ * RATTN_STAGE_ALL return RATTN_E_SHAPE.
+ */
+#define RATTN_STAGE_SPLIT 1u
+#define RATTN_STAGE_COMBINE 2u
+#define RATTN_STAGE_ALL 3u
+int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,
+                           size_t workspace_bytes, void *stream, unsigned stages);
 
 /* Work decomposition chosen for a decode call (host-only introspection; no HIP call). */
 typedef struct rattn_plan_info {

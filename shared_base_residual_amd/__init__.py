@@ -29,7 +29,9 @@ RATTN_OP_DECODE, RATTN_OP_PREFILL = 0, 1
 STATUS = {0: "RATTN_OK", -1: "RATTN_E_NULL", -2: "RATTN_E_SHAPE", -3: "RATTN_E_UNSUPPORTED",
           -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP"}
 EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
-           "rattn_decode_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error")
+           "rattn_decode_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error",
+           "rattn_attention_stages")
+STAGE_SPLIT, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
 
 
 class RattnError(RuntimeError):
@@ -81,10 +83,12 @@ def lib():
         L.rattn_prefill_chunk.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P, ctypes.c_size_t, P]
         L.rattn_gather_base.argtypes = [ctypes.POINTER(Desc), P, P, P, P]
         L.rattn_decode_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PlanInfo)]
+        L.rattn_attention_stages.argtypes = [ctypes.POINTER(Desc), I, ctypes.POINTER(Args), P, ctypes.c_size_t, P,
+                                             ctypes.c_uint]
         L.rattn_status_str.argtypes = [I]
         L.rattn_status_str.restype = ctypes.c_char_p
         for f in ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
-                  "rattn_decode_plan", "rattn_version", "rattn_last_hip_error"):
+                  "rattn_decode_plan", "rattn_version", "rattn_last_hip_error", "rattn_attention_stages"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -197,20 +201,20 @@ _workspaces = {}
 
 
 def workspace_for(nbytes: int, device):
-    """A zero-filled workspace of at least ``nbytes`` (cached per device and
-    stream).  The library leaves it zero-filled after every call."""
+    """A workspace of at least ``nbytes``, cached per device and stream (its
+    contents do not matter between calls)."""
     import torch
 
     key = (str(device), torch.cuda.current_stream(device).cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), device=device, dtype=torch.uint8)
+        ws = torch.empty(max(nbytes, 256), device=device, dtype=torch.uint8)
         _workspaces[key] = ws
     return ws
 
 
 def _run(fn_name, op, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_priv, shared_lr, out, lse,
-         workspace, sm_scale, prefix_len, stream, desc):
+         workspace, sm_scale, prefix_len, stream, desc, stages=None):
     import torch
 
     if desc is None:
@@ -232,7 +236,12 @@ def _run(fn_name, op, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_
                    "lse")])
     wsp = ctypes.c_void_p(workspace.data_ptr())
     wsb = ctypes.c_size_t(workspace.numel() * workspace.element_size())
-    st = getattr(lib(), fn_name)(ctypes.byref(desc), ctypes.byref(args), wsp, wsb, _stream(stream))
+    if stages is None:
+        st = getattr(lib(), fn_name)(ctypes.byref(desc), ctypes.byref(args), wsp, wsb, _stream(stream))
+    else:
+        st = lib().rattn_attention_stages(ctypes.byref(desc), op, ctypes.byref(args), wsp, wsb, _stream(stream),
+                                          stages)
+        fn_name = f"rattn_attention_stages({stages})"
     if st:
         raise RattnError(st, fn_name)
     return out
@@ -276,9 +285,9 @@ def gather_base(pool, block_table, prefix_len: int, *, out=None, stream=None):
 
 
 def attend(inputs: dict, *, mode: str = "decode", shared_lr=None, prefix_len=None, out=None, lse=None,
-           workspace=None, stream=None, desc=None):
+           workspace=None, stream=None, desc=None, stages=None):
     """Runs decode or prefill on a dict of device tensors named as in the layouts above.
-    A given ``workspace`` must be zero-filled before its first use (see rattn.h)."""
+    ``stages`` (a mask of STAGE_*) runs only those launches through rattn_attention_stages."""
     if mode == "decode":
         fn_name, op = "rattn_decode", RATTN_OP_DECODE
     else:
@@ -286,4 +295,4 @@ def attend(inputs: dict, *, mode: str = "decode", shared_lr=None, prefix_len=Non
     g = inputs.get
     return _run(fn_name, op, inputs["q"], g("k_base"), g("v_base"), g("lk"), g("lv"), g("bk"), g("bv"),
                 g("block_table"), g("k_priv"), g("v_priv"), shared_lr, out, lse, workspace, 0.0, prefix_len, stream,
-                desc)
+                desc, stages)

@@ -31,8 +31,12 @@ def hipcc() -> str:
 
 
 def flags():
+    # -amdgpu-mfma-vgpr-form: MFMA accumulators live in ordinary VGPRs (the
+    # kernels fit in 256), so the online-softmax rescale and the epilogue need no
+    # AGPR <-> VGPR copies.
     return ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-            "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-Wall", "-Wno-unused-function"]
+            "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+            "-Wall", "-Wno-unused-function"]
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:

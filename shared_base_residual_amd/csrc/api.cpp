@@ -10,7 +10,8 @@
 #include "internal.h"
 
 namespace rattn {
-hipError_t launch_decode(int bf16_in, const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st);
+hipError_t launch_decode(int bf16_in, const DecodeParams &dp, int D, int cpad, size_t lds, unsigned stages,
+                         hipStream_t st);
 hipError_t launch_gather(const void *pool, const int32_t *table, void *dst, int64_t L, int HK, int ps,
                          int row_bytes, hipStream_t st);
 }  // namespace rattn
@@ -19,7 +20,10 @@ namespace {
 
 thread_local int g_last_hip = 0;
 
-constexpr int kTargetItems = 256;   // split-kernel workgroups aimed for (one per CU)
+#ifndef RATTN_TARGET_ITEMS
+#define RATTN_TARGET_ITEMS 256
+#endif
+constexpr int kTargetItems = RATTN_TARGET_ITEMS;  // split-kernel workgroups aimed for
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t roundup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -63,7 +67,7 @@ struct Plan {
     rattn::DecodeParams dp;
     int cpad;
     size_t lds;
-    size_t off_cnt, off_ml, off_o, off_w, total;
+    size_t off_ml, off_o, off_w, total;
 };
 
 int make_plan(const rattn_desc *d, int op, Plan *pl) {
@@ -148,18 +152,77 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     p.n_items = (int)n_all;
     p.per_xcd = (int)cdiv(n_all, 8);
 
-    // Merge area of the split kernel: needed when some row group has fewer than
-    // four row blocks (several waves then share one block).
-    const bool share_pre = L > 0 && (p.n_blocks % 4 != 0);
-    const bool share_pv = S > 0 && (p.pb % 4 != 0);
+    // LDS staging ring.  A stage holds T tokens of keys and values and, for
+    // prefix items with a residual, the low-rank rows (Lk and Lv) of every agent
+    // the workgroup serves, as 16-byte chunks (rows padded to a power of two).
+    // T must give every wave whole 16-token steps: a row group of nblk blocks
+    // runs 4 / nblk waves per block.
+    const int es = (int)esize(d->dtype);
+    const int kv_row = D * es;  // bytes of one key (or value) row
+    auto tg_of = [](int nblk) { return 4 / nblk; };
+    auto pick = [&](int tg_max, int lr_row_bytes, int *T, int *nst, int *stage) {
+        for (int t = 64; t >= 16; t /= 2) {
+            if (t % (16 * tg_max)) continue;
+            const int sb = t * (2 * kv_row + 2 * lr_row_bytes);
+            const int n = rattn::kLdsBudget / sb;
+            if (n >= 3 || (t == 16 * tg_max && n >= 2)) {
+                *T = t;
+                *nst = n < 4 ? n : 4;
+                *stage = sb;
+                return true;
+            }
+        }
+        return false;
+    };
+    int lds_ring = 0;
+    if (L > 0) {
+        int tg_max = 1, ag_max = 1;
+        for (int rg = 0; rg < p.n_rg; ++rg) {
+            const int b0 = 4 * rg;
+            const int nb = p.n_blocks - b0 < 4 ? p.n_blocks - b0 : 4;
+            if (tg_of(nb) > tg_max) tg_max = tg_of(nb);
+            const rattn::RowBlock x0 = rattn::prefix_block(b0, N, rpa, p.apb, p.bpa);
+            const rattn::RowBlock x1 = rattn::prefix_block(b0 + nb - 1, N, rpa, p.apb, p.bpa);
+            const int na = x1.a0 + x1.na - x0.a0;
+            if (na > ag_max) ag_max = na;
+        }
+        int lr_row = 0;
+        p.lr_off32 = (int64_t)ag_max * L * r * es < (1ll << 31);
+        if (resid) {
+            const int chunks = (d->shared_lr ? r : ag_max * r) * es / 16;
+            lr_row = 16 * pow2ceil(chunks);
+        }
+        if (!pick(tg_max, lr_row, &p.T_pre, &p.nst_pre, &p.stage_bytes_pre)) return RATTN_E_UNSUPPORTED;
+        lds_ring = p.nst_pre * p.stage_bytes_pre;
+    }
+    if (S > 0) {
+        int tg_max = 1;
+        for (int g0 = 0; g0 < p.pb; g0 += 4) {
+            const int nb = p.pb - g0 < 4 ? p.pb - g0 : 4;
+            if (tg_of(nb) > tg_max) tg_max = tg_of(nb);
+        }
+        if (!pick(tg_max, 0, &p.T_pv, &p.nst_pv, &p.stage_bytes_pv)) return RATTN_E_UNSUPPORTED;
+        const int b = p.nst_pv * p.stage_bytes_pv;
+        if (b > lds_ring) lds_ring = b;
+    }
+    // After the ring, the token-group merge (four slots of per-lane state)
+    // reuses the same memory.
     const int cpl = pl->cpad > 0 ? pl->cpad / 16 : 1;
     const int per_lane = 4 * (D / 16) + 4 * cpl;
-    const size_t lds_merge = (share_pre || share_pv) ? (size_t)3 * (64 * per_lane + 32) * sizeof(float) : 0;
-    const size_t lds_final = (size_t)4 * (rattn::kMaxSlots + 128) * sizeof(float);
-    pl->lds = lds_merge > lds_final ? lds_merge : lds_final;
+    int lds = lds_ring;
+    const int lds_merge = 4 * (64 * per_lane + 32) * (int)sizeof(float);
+    if (lds_merge > lds) lds = lds_merge;
+    // The split's page-table entries.
+    p.table_lds_off = (lds + 15) & ~15;
+    if (d->page_size > 0 && L > 0) {
+        const int64_t pages = cdiv(p.tok_ps, d->page_size) + 1;
+        if (pages > rattn::kMaxPagesPerSplit) return RATTN_E_UNSUPPORTED;
+        lds = p.table_lds_off + (int)pages * 4;
+    }
+    if (lds > rattn::kLdsBudget) return RATTN_E_UNSUPPORTED;
+    pl->lds = (size_t)lds;
 
-    // Workspace: a fixed-size header of completion counters (zero between calls,
-    // never written by any call's partials), then the (max, sum), O and W partials.
+    // Workspace: the (max, sum), O and W partials of every (KV head, row, split).
     const int64_t rows_kv = (int64_t)HK * N * rpa;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -167,8 +230,6 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         off += (bytes + 255) & ~(size_t)255;
         return o;
     };
-    if ((int64_t)HK * N * (int64_t)sizeof(unsigned) > rattn::kCounterHeaderBytes) return RATTN_E_UNSUPPORTED;
-    pl->off_cnt = take((size_t)rattn::kCounterHeaderBytes);
     pl->off_ml = take((size_t)rows_kv * p.n_slots * 2 * sizeof(float));
     pl->off_o = take((size_t)rows_kv * p.n_slots * D * sizeof(float));
     pl->off_w = take(resid ? (size_t)rows_kv * p.n_slots * r * sizeof(float) : 0);
@@ -201,7 +262,9 @@ int hip_status(hipError_t e) {
     return RATTN_E_HIP;
 }
 
-int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_bytes, void *stream, int op) {
+int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_bytes, void *stream, int op,
+                  unsigned stages) {
+    if (stages == 0 || (stages & ~(unsigned)RATTN_STAGE_ALL)) return RATTN_E_SHAPE;
     int st = check_desc(d, op);
     if (st) return st;
     st = check_args(d, a);
@@ -227,12 +290,11 @@ int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_
     p.vp = a->v_priv;
     p.out = a->out;
     p.lse = a->lse;
-    p.cnt = reinterpret_cast<unsigned *>(w + pl.off_cnt);
     p.p_ml = reinterpret_cast<float *>(w + pl.off_ml);
     p.p_o = reinterpret_cast<float *>(w + pl.off_o);
     p.p_w = reinterpret_cast<float *>(w + pl.off_w);
     if (!(d->rank > 0 && d->prefix_len > 0)) p.r = 0;  // no residual without a prefix
-    return hip_status(rattn::launch_decode(d->dtype == RATTN_BF16, p, d->head_dim, pl.cpad, pl.lds,
+    return hip_status(rattn::launch_decode(d->dtype == RATTN_BF16, p, d->head_dim, pl.cpad, pl.lds, stages,
                                            static_cast<hipStream_t>(stream)));
 }
 
@@ -288,12 +350,18 @@ int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info) {
 
 int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace, size_t workspace_bytes,
                  void *stream) {
-    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_DECODE);
+    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_DECODE, RATTN_STAGE_ALL);
 }
 
 int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *workspace,
                         size_t workspace_bytes, void *stream) {
-    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_PREFILL);
+    return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_PREFILL, RATTN_STAGE_ALL);
+}
+
+int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,
+                           size_t workspace_bytes, void *stream, unsigned stages) {
+    if (op != RATTN_OP_DECODE && op != RATTN_OP_PREFILL) return RATTN_E_SHAPE;
+    return run_attention(desc, args, workspace, workspace_bytes, stream, op, stages);
 }
 
 int rattn_gather_base(const rattn_desc *d, const void *pool, const int32_t *block_table, void *dst,

@@ -1,110 +1,199 @@
-// decode.hip -- decode kernel of librattn (gfx950).
+// decode.hip -- split-K attention kernel of librattn (gfx950).
 //
 // Fused residual attention for N agents that share one base KV cache
 // (ForkKV Guide, "Fused ResidualAttention"; LRAgent, "Flash-LoRA-Attention"):
 //   score  s = scale * (q . K_base[j] + (q Bk_a^T) . Lk_a[j])
 //   output o = sum_j p_j V_base[j] + (sum_j p_j Lv_a[j]) Bv_a
-// One launch.  Each workgroup takes one (KV head, row group, context split):
-//   * it computes U = scale*log2(e) * q Bk_a^T for its query rows with MFMA;
-//   * it streams the base K/V tiles once for all agents' query rows (one MFMA
-//     contraction over the rows of every agent), adds the rank-r score
-//     correction with a second MFMA over the agents' Lk rows, runs an online
-//     softmax in the log2 domain and accumulates P V_base and P Lv.  Private
-//     tokens are extra work items with per-agent keys and no residual;
-//   * it writes its partial state (max, sum, O, W) to the workspace and takes a
-//     ticket on a per-(KV head, agent) counter; the workgroup that completes an
-//     agent merges that agent's rows: a log-sum-exp merge over the splits with
-//     wavefront shuffles, then o = (sum w O + (sum w W) Bv_a^(k)) / sum w l, so
-//     Bv is applied once per row, not per token.  It resets the counter to zero.
+// One launch.  Each workgroup (four waves) takes one (KV head, row group,
+// context split):
+//   * U = scale*log2(e) * q Bk_a^T for its query rows, with MFMA;
+//   * the split's tokens are streamed in tiles of T tokens through a ring of
+//     LDS stages filled by direct global->LDS loads (no registers in between,
+//     several tiles in flight).  A stage holds the tile's base keys and values
+//     and the low-rank rows (Lk, Lv) of every agent the workgroup serves, each
+//     read from HBM once and shared by all four waves;
+//   * each wave owns one 16-row MFMA row block (query rows of one or more
+//     agents) and a share of each tile's tokens: one MFMA contraction scores the
+//     base keys against all agents' rows, a second adds the rank-r correction
+//     over the agents' Lk rows; online softmax in the log2 domain; P V_base and
+//     P Lv accumulate in registers.  Private tokens (decode suffix, causal
+//     prefill chunk) are extra work items with per-agent keys and no residual;
+//   * the partial state (max, sum, O, W) of every row goes to the workspace.
+// A second, small kernel merges the splits of each query row (one wavefront per
+// row, a log-sum-exp merge with wavefront reductions) and applies Bv once per
+// row: o = (sum w O + (sum w W) Bv_a^(k)) / sum w l (LRAgent: B is applied once
+// per query block, not per token).
 //
-// Layout of the streaming loop (S^T formulation): the MFMA A operand is the key
-// tile (rows = 16 tokens), the B operand the query rows (columns = 16 query
-// rows), so the scores arrive with one query row per lane column and the
-// softmax statistics of a row live in the lanes that own it.  The value product
-// is O^T = V^T P^T, so P feeds the B operand straight from the score registers.
-// Every lane reads 16 contiguous bytes per key row and d/16 contiguous elements
-// per value row; the value tile needs no transpose through LDS.
+// Operand layout (S^T formulation): the MFMA A operand is the key tile (rows =
+// 16 tokens), the B operand the query rows (columns = 16 query rows), so the
+// scores arrive with one query row per lane column and the softmax statistics
+// of a row live in the lanes that own it.  The value product is O^T = V^T P^T
+// over 16-token steps (v_mfma_f32_16x16x16_bf16), so P feeds the B operand
+// straight from the score registers and each lane reads one contiguous
+// segment of a value row.
 //
-// Loads never branch: token indices beyond the split are clamped to its last
-// token (finite data) and those scores are masked to -inf, so their weights are
-// exactly zero.  Chunks are software-pipelined two deep.
+// Loads never branch on the data: token indices beyond the split are clamped
+// to its last token (finite data) and those scores are masked to -inf, so
+// their weights are exactly zero.
 #include "device.h"
 #include "internal.h"
 
 namespace rattn {
 
-template <typename T, int D, int CPAD>
-struct Chunk {
-    static constexpr int KS = D / 32;
-    static constexpr int VPL = D / 16;
-    static constexpr int CS = CPAD > 0 ? CPAD / 32 : 1;
-    static constexpr int CPL = CPAD > 0 ? CPAD / 16 : 1;
-    typename Ops<T>::frag k[2][KS];
-    Row<T, VPL> v[8];
-    typename Ops<T>::frag lk[2][CS];
-    Row<T, CPL> lv[8];
+// ------------------------------------------------------------- geometry --
+
+// Layout of one LDS stage, in 16-byte chunks: K rows, V rows, Lk rows, Lv rows.
+struct Geo {
+    int T;                    // tokens per stage
+    int nst;                  // stages in the ring
+    int cpr_kv, lg_kv;        // chunks per K (or V) row, its log2
+    int cpr_lr, cpa_lr, lg_lr;  // valid / allocated (power of two) chunks per Lk row
+    int ofs_v, ofs_lk, ofs_lv;  // region offsets (chunks)
+    int chunks;               // chunks per stage
+    int stage_bytes;          // stride between stages
 };
 
-// Per-lane, loop-invariant state of one work item's token stream.
-template <typename T, int D, int CPAD>
-struct Stream {
-    const T *kb, *vb;       // contiguous segment base, or paged pool
-    const int32_t *table;   // NULL: contiguous
-    int64_t page_stride;    // elements per physical page (all heads)
-    int64_t head_off;       // elements to this head inside a page
-    int ps;
-    int tlast;              // last valid token of the item
-    int tlast16;            // its 16-aligned tile start
-    const T *lk[Chunk<T, D, CPAD>::CS];  // this lane's low-rank column pointers (token 0)
-    const T *lv;
-    int r;
-    bool resid;
+__device__ inline int ilog2(int x) { return 31 - __builtin_clz(x); }
 
-    // First row of the 16-token tile starting at t16 (clamped into the item).
-    __device__ inline int tile_row0(int t16) const { return t16 < tlast16 ? t16 : tlast16; }
-    __device__ inline const T *tile_ptr(const T *base, int t16c) const {
-        if (table) {
-            const int64_t pg = table[t16c / ps];
-            return base + pg * page_stride + head_off + (int64_t)(t16c % ps) * D;
-        }
-        return base + (int64_t)t16c * D;
+// Where the tokens of a work item come from.
+template <typename T>
+struct Src {
+    const T *kb, *vb;         // contiguous: this head's rows; paged: pool + this head's offset
+    int64_t page_stride;      // paged: elements per physical page (0: contiguous)
+    int ps;                   // page size (paged)
+    int pg0;                  // first logical page of the split
+    const int *pages;         // LDS copy of the split's page-table entries (paged)
+    const T *lk, *lv;         // low-rank rows: first agent of the workgroup (or the shared one)
+    int64_t lr_agent_stride;  // elements between agents' low-rank caches
+    int r;                    // rank
+    int lr_es_shift;          // log2(r * sizeof(T) / 16): chunks per agent row
+    int tlast;                // last valid token of the item
+};
+
+template <typename T, int D>
+__device__ inline const T *kv_row(const Src<T> &s, const T *base, int tok) {
+    if (s.page_stride) {
+        const int64_t pg = s.pages[tok / s.ps - s.pg0];
+        return base + pg * s.page_stride + (int64_t)(tok % s.ps) * D;
     }
-};
+    return base + (int64_t)tok * D;
+}
 
-template <typename T, int D, int CPAD>
-__device__ inline void load_chunk(Chunk<T, D, CPAD> &ch, const Stream<T, D, CPAD> &st, int tc, int n16,
-                                  int j4) {
-    using O = Ops<T>;
-    constexpr int KS = Chunk<T, D, CPAD>::KS, VPL = Chunk<T, D, CPAD>::VPL, CS = Chunk<T, D, CPAD>::CS,
-                  CPL = Chunk<T, D, CPAD>::CPL;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        const int t16 = tc + 16 * c;
-        const int t16c = st.tile_row0(t16);
-        const T *kt = st.tile_ptr(st.kb, t16c);
-        const T *vt = st.tile_ptr(st.vb, t16c);
-        int tk = t16 + n16;
-        tk = tk < st.tlast ? tk : st.tlast;
-        const T *krow = kt + (tk - t16c) * D + 8 * j4;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) ch.k[c][s] = O::load8(krow + 32 * s);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int tv = t16 + 4 * j4 + i;
-            tv = tv < st.tlast ? tv : st.tlast;
-            ch.v[4 * c + i] = load_row<T, VPL>(vt + (tv - t16c) * D + VPL * n16);
-        }
-        if (CPAD > 0 && st.resid) {
-#pragma unroll
-            for (int s = 0; s < CS; ++s) ch.lk[c][s] = O::load8(st.lk[s] + (int64_t)tk * st.r);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int tv = t16 + 4 * j4 + i;
-                tv = tv < st.tlast ? tv : st.tlast;
-                ch.lv[4 * c + i] = load_row<T, CPL>(st.lv + (int64_t)tv * st.r);
+// Issues this wave's share of the direct loads that fill one stage with the
+// tile starting at token t0.  Instruction j (64 chunks) goes to wave j % 4.
+// General path: any tile (tokens past the item are clamped to its last one),
+// any region layout.
+template <typename T, int D>
+__device__ inline void fill_stage_any(const Geo &g, const Src<T> &s, int t0, char *stage, int wave, int lane) {
+    const int n_instr = (g.chunks + 63) >> 6;
+    for (int j = wave; j < n_instr; j += 4) {
+        const int q = 64 * j + lane;
+        if (q < g.chunks) {
+            const char *src;
+            if (q < g.ofs_lk) {
+                const bool isv = q >= g.ofs_v;
+                const int rel = isv ? q - g.ofs_v : q;
+                const int row = rel >> g.lg_kv;
+                const int c = swz(row, rel & (g.cpr_kv - 1), g.cpr_kv, g.lg_kv);
+                int tok = t0 + row;
+                tok = tok < s.tlast ? tok : s.tlast;
+                src = reinterpret_cast<const char *>(kv_row<T, D>(s, isv ? s.vb : s.kb, tok)) + 16 * c;
+            } else {
+                const bool isv = q >= g.ofs_lv;
+                const int rel = isv ? q - g.ofs_lv : q - g.ofs_lk;
+                const int row = rel >> g.lg_lr;
+                int c = swz(row, rel & (g.cpa_lr - 1), g.cpa_lr, g.lg_lr);
+                c = c < g.cpr_lr ? c : 0;  // allocated-only chunk: any valid data (never read)
+                int tok = t0 + row;
+                tok = tok < s.tlast ? tok : s.tlast;
+                const int agent = c >> s.lr_es_shift;
+                const int cin = c - (agent << s.lr_es_shift);
+                const T *base = (isv ? s.lv : s.lk) + agent * s.lr_agent_stride + (int64_t)tok * s.r;
+                src = reinterpret_cast<const char *>(base) + 16 * cin;
             }
+            dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(stage) + 1024 * j));
         }
     }
+}
+
+// Number of direct-load instructions a wave issues per stage.
+__device__ inline int fills_per_wave(const Geo &g, int wave) {
+    const int n_instr = (g.chunks + 63) >> 6;
+    return n_instr > wave ? (n_instr - wave + 3) >> 2 : 0;
+}
+
+// Lane constants of the fast fill.  For a full tile, the 64 chunks of one
+// direct-load instruction lie in one region (K, V, Lk or Lv) and within one
+// 16-row swizzle period, so the instruction's source is a wave-uniform base
+// plus a per-lane 32-bit offset, and the swizzle splits into a lane part and a
+// uniform part: swz(row0 + row, c) = swz(row, c) ^ swz(row0, 0) whenever row0
+// is a multiple of the rows per instruction and row is below it.
+struct FillLane {
+    uint32_t kv_rb;   // (lane's row in the instruction) * bytes per K/V row
+    uint32_t kv_pr;   // lane part of the K/V swizzle
+    uint32_t lr_rb;   // the same for the low-rank regions
+    uint32_t lr_pr;
+};
+
+__device__ inline uint32_t swz_uniform(int row0, int cpa, int lg) { return (uint32_t)swz(row0, 0, cpa, lg); }
+
+// Fills one stage with a full tile (every token of it below tlast) through the
+// fast path: per instruction a uniform base (SALU) and the lane's offset
+// (a few VALU).  Requires the regions to be whole instructions (see fast_ok).
+template <typename T, int D>
+__device__ inline void fill_stage_fast(const Geo &g, const Src<T> &s, const FillLane &fl, int t0, char *stage,
+                                       int wave) {
+    constexpr int ES = (int)sizeof(T);
+    const int n_instr = g.chunks >> 6;
+    const int nK = (g.T * g.cpr_kv) >> 6;
+    const int nL = (g.T * g.cpa_lr) >> 6;
+    const int rpi_kv = 64 >> g.lg_kv;
+    const int kv_bytes = D * ES;
+    const uint32_t lds0 = lds_addr(stage);
+    for (int j = wave; j < n_instr; j += 4) {
+        const char *base;
+        uint32_t off;
+        if (j < 2 * nK) {
+            const bool isv = j >= nK;
+            const int row0 = (j - (isv ? nK : 0)) * rpi_kv;
+            const int tok = t0 + row0;
+            base = reinterpret_cast<const char *>(kv_row<T, D>(s, isv ? s.vb : s.kb, tok));
+            off = fl.kv_rb + ((fl.kv_pr ^ swz_uniform(row0, g.cpr_kv, g.lg_kv)) << 4);
+        } else {
+            const bool isv = j >= 2 * nK + nL;
+            const int row0 = (j - 2 * nK - (isv ? nL : 0)) * (64 >> g.lg_lr);
+            base = reinterpret_cast<const char *>((isv ? s.lv : s.lk) + (int64_t)(t0 + row0) * s.r);
+            uint32_t c = fl.lr_pr ^ swz_uniform(row0, g.cpa_lr, g.lg_lr);
+            c = c < (uint32_t)g.cpr_lr ? c : 0u;  // allocated-only chunk: any valid data (never read)
+            const uint32_t agent = c >> s.lr_es_shift;
+            off = fl.lr_rb + agent * (uint32_t)(s.lr_agent_stride * ES) + ((c - (agent << s.lr_es_shift)) << 4);
+        }
+        (void)kv_bytes;
+        dma16s(uniform_ptr(base), off, __builtin_amdgcn_readfirstlane(lds0 + 1024 * j));
+    }
+}
+
+// Byte offsets (within a stage) of the LDS operands a lane reads in a 16-token
+// step, for the step's first row at 0; a step at row0 adds row0 * row bytes.
+// All rows a lane touches are row0 + x with x < 16, and row0 is a multiple of
+// 16, so the swizzle depends on x only.
+template <typename T, int D, int CPAD>
+struct ReadOfs {
+    static constexpr int ES = (int)sizeof(T);
+    static constexpr int FC = 8 * ES / 16;                                  // chunks per 8-element fragment
+    static constexpr int VB = (D / 16) * ES, VC = VB >= 16 ? VB / 16 : 1;  // a value-row segment
+    static constexpr int CPL = CPAD > 0 ? CPAD / 16 : 1;
+    static constexpr int LB = CPL * ES, LC = LB >= 16 ? LB / 16 : 1;        // a low-rank value segment
+    static constexpr int CSx = CPAD > 0 ? CPAD / 32 : 1;
+    uint32_t k[D / 32][FC];
+    uint32_t v[4][VC];
+    uint32_t lk[CSx][FC];
+    uint32_t lv[4][LC];
+};
+
+// Offset of element col of row x in a swizzled region starting at chunk rbase.
+__device__ inline uint32_t elem_ofs(int rbase, int x, int col_byte, int cpa, int lg) {
+    return (uint32_t)(16 * (rbase + (x << lg) + swz(x, col_byte >> 4, cpa, lg)) + (col_byte & 15));
 }
 
 template <typename T, int D, int CPAD>
@@ -114,109 +203,188 @@ struct Acc {
     float m, l;
 };
 
-// One 32-token chunk: scores, online softmax, value and low-rank value products.
+// Reads K consecutive elements whose chunks sit at base + ofs[c].
+template <typename T, int K, int NC>
+__device__ inline Row<T, K> lds_get(const char *base, const uint32_t (&ofs)[NC]) {
+    Row<T, K> out;
+    constexpr int B = K * (int)sizeof(T);
+    if constexpr (B >= 16) {
+#pragma unroll
+        for (int c = 0; c < B / 16; ++c)
+            __builtin_memcpy(reinterpret_cast<char *>(&out) + 16 * c, __builtin_assume_aligned(base + ofs[c], 16), 16);
+    } else {
+        __builtin_memcpy(&out, __builtin_assume_aligned(base + ofs[0], B), B);
+    }
+    return out;
+}
+
+// One 16-token step of one wave: scores for its row block, online softmax,
+// value and low-rank value products.  kvb / lrb: the stage plus row0 times the
+// K/V and low-rank row bytes; t: token of the step's first row; `masked`:
+// some token of the step may lie past t1 or (causal) past the row's position.
 template <typename T, int D, int CPAD>
-__device__ inline void compute_chunk(Acc<T, D, CPAD> &acc, const Chunk<T, D, CPAD> &ch,
-                                     const typename Ops<T>::frag *qB, const typename Ops<T>::frag *uH,
-                                     const typename Ops<T>::frag *uL, float cl2, bool resid, int tc,
-                                     int t1, bool causal, int tq, int j4) {
+__device__ inline void step16(Acc<T, D, CPAD> &acc, const ReadOfs<T, D, CPAD> &ro, const char *kvb, const char *lrb,
+                              int t, bool masked, const typename Ops<T>::frag *qB, const typename Ops<T>::frag *uH,
+                              const typename Ops<T>::frag *uL, float cl2, bool resid, int t1, bool causal, int tq,
+                              int j4) {
     using O = Ops<T>;
     using frag = typename O::frag;
-    constexpr int KS = Chunk<T, D, CPAD>::KS, VPL = Chunk<T, D, CPAD>::VPL, CS = CPAD / 32,
-                  CPL = CPAD / 16;
-    f32x4 sc[2];
+    using frag4 = typename O::frag4;
+    constexpr int KS = D / 32, VPL = D / 16;
+    constexpr int CS = CPAD / 32, CPL = CPAD / 16;
+
+    // S^T = K Q^T for 16 tokens x 16 query rows
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-        f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < KS; ++s) {
+        const Row<T, 8> kr = lds_get<T, 8>(kvb, ro.k[s]);
+        frag kf;
+        __builtin_memcpy(&kf, &kr, sizeof(kf));
+        a = O::mma(kf, qB[s], a);
+    }
+    a *= cl2;
+    if (CS > 0 && resid) {
 #pragma unroll
-        for (int s = 0; s < KS; ++s) a = O::mma(ch.k[c][s], qB[s], a);
-        a *= cl2;
-        if (CPAD > 0 && resid) {
-#pragma unroll
-            for (int s = 0; s < CS; ++s) {
-                a = O::mma(ch.lk[c][s], uH[s], a);
-                if constexpr (O::kSplitU) a = O::mma(ch.lk[c][s], uL[s], a);
-            }
+        for (int s = 0; s < CS; ++s) {
+            const Row<T, 8> lr = lds_get<T, 8>(lrb, ro.lk[s]);
+            frag lf;
+            __builtin_memcpy(&lf, &lr, sizeof(lf));
+            a = O::mma(lf, uH[s], a);
+            if constexpr (O::kSplitU) a = O::mma(lf, uL[s], a);
         }
+    }
+    if (masked) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int t = tc + 16 * c + 4 * j4 + i;
-            if (t >= t1 || (causal && t > tq)) a[i] = -__builtin_inff();
+            const int tt = t + 4 * j4 + i;
+            if (tt >= t1 || (causal && tt > tq)) a[i] = -__builtin_inff();
         }
-        sc[c] = a;
     }
-    float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                     fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+
+    // online softmax (log2 domain); the four lanes of a row are j4 = 0..3.
+    // The O and W accumulators are rescaled only on the steps where some row's
+    // reference max grows (a branch uniform over the wave); on the others
+    // alpha is exactly 1.
+    float mx = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(acc.m, mx);
-    const float alpha = fexp2(acc.m - m_new);
-    acc.m = m_new;
-    frag pB;
+    const bool grow = mx > acc.m + kRescaleSlack;
+    float alpha = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : acc.m;
+        alpha = fexp2(acc.m - m_new);
+        acc.m = m_new;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) acc.o[i] *= alpha;
+        if constexpr (CPAD > 0) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) acc.w[i] *= alpha;
+        }
+    }
+    frag4 pB;
     float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const float e = fexp2(sc[i >> 2][i & 3] - m_new);
+    for (int i = 0; i < 4; ++i) {
+        const float e = fexp2(a[i] - acc.m);
         psum += e;
-        O::set(pB, i, e);
+        O::set4(pB, i, e);
     }
     acc.l = acc.l * alpha + psum;
+
+    // O^T += V^T P^T: output tile jj holds d = VPL*m + jj in row m
+    Row<T, VPL> vr[4];
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) acc.o[i] *= alpha;
+    for (int i = 0; i < 4; ++i) vr[i] = lds_get<T, VPL>(kvb, ro.v[i]);
 #pragma unroll
     for (int jj = 0; jj < VPL; ++jj) {
-        frag vA;
+        frag4 vA;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) O::set_raw(vA, i, ch.v[i].e[jj]);
-        acc.o[jj] = O::mma(vA, pB, acc.o[jj]);
+        for (int i = 0; i < 4; ++i) O::set4_raw(vA, i, vr[i].e[jj]);
+        acc.o[jj] = O::mma16(vA, pB, acc.o[jj]);
     }
-    if (CPAD > 0 && resid) {
+    // W^T += Lv^T P^T over the block's residual columns
+    if constexpr (CPAD > 0) {
+        if (resid) {
+            Row<T, CPL> lr[4];
 #pragma unroll
-        for (int i = 0; i < CPL; ++i) acc.w[i] *= alpha;
+            for (int i = 0; i < 4; ++i) lr[i] = lds_get<T, CPL>(lrb, ro.lv[i]);
 #pragma unroll
-        for (int jj = 0; jj < CPL; ++jj) {
-            frag wA;
+            for (int jj = 0; jj < CPL; ++jj) {
+                frag4 wA;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) O::set_raw(wA, i, ch.lv[i].e[jj]);
-            acc.w[jj] = O::mma(wA, pB, acc.w[jj]);
+                for (int i = 0; i < 4; ++i) O::set4_raw(wA, i, lr[i].e[jj]);
+                acc.w[jj] = O::mma16(wA, pB, acc.w[jj]);
+            }
         }
     }
 }
 
 // ------------------------------------------------------------------- merge --
 
-// Expected completion tickets of (KV head, agent a): one per prefix item whose
-// row group holds some of a's rows, one per private item of a.
-__device__ inline unsigned expected_tickets(const DecodeParams &p, int a) {
-    unsigned e = 0;
-    if (p.n_ps > 0) {
-        int nrg = 1;
-        if (p.rpa > 16) nrg = (a * p.bpa + p.bpa - 1) / 4 - (a * p.bpa) / 4 + 1;
-        e += (unsigned)(p.n_ps * nrg);
-    }
-    if (p.n_pv > 0) e += (unsigned)(p.n_pv * p.n_prg);
-    return e;
-}
-
-// One wavefront merges the splits of one query row and writes out/lse.
-// wbuf: n_slots floats of LDS for the weights, wr: r floats for the merged W.
+// One wavefront merges the splits of one query row and writes out/lse.  Every
+// load of a batch is issued before any of it is used, so a batch costs one
+// memory round trip.  wbuf: n_slots floats of LDS for the weights.
+#define LDP(ptr) (*(ptr))
 template <typename T, int D>
-__device__ inline void merge_row(const DecodeParams &p, int k, int a, int ria, float *wbuf, float *wr, int lane) {
+__device__ inline void merge_row(const DecodeParams &p, int k, int a, int ria, float *wbuf, int lane) {
     constexpr int DPL = D / 64;
+    constexpr int SB = 32;  // slots per batch of O loads
     const int t = ria / p.g, hh = ria % p.g;
     const int64_t R = ((int64_t)a * p.QL + t) * p.HQ + (int64_t)k * p.g + hh;
     const int64_t rec0 = ((int64_t)k * p.N * p.rpa + (int64_t)a * p.rpa + ria) * p.n_slots;
-    const int ns = p.n_slots, r = p.r;
+    const int ns = p.n_slots, r = p.r, nps = p.n_ps;
+    const bool wres = r > 0 && nps > 0;
+
+    // batch 0: (max, sum) of every slot, O of the first SB slots, W of the first
+    // SB prefix slots, and this lane's Bv columns
+    constexpr int MLU = kMaxSlots / 64;
+    float mv[MLU], lv[MLU];
+#pragma unroll
+    for (int u = 0; u < MLU; ++u) {
+        const int s = lane + 64 * u;
+        const int sc = s < ns ? s : 0;
+        if (64 * u < ns) {
+            mv[u] = LDP(p.p_ml + (rec0 + sc) * 2);
+            lv[u] = LDP(p.p_ml + (rec0 + sc) * 2 + 1);
+        }
+    }
+    const float *po = p.p_o + rec0 * D + DPL * lane;
+    float ov[SB][DPL];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+        const int sc = u < ns ? u : ns - 1;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) ov[u][e] = LDP(po + (int64_t)sc * D + e);
+    }
+    // W: lane j (< r) and j + 64 when r = 128
+    float wv[2][SB];
+    if (wres) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int j = lane + 64 * h;
+            const int jc = j < r ? j : 0;
+#pragma unroll
+            for (int u = 0; u < SB; ++u) {
+                const int sc = u < nps ? u : nps - 1;
+                wv[h][u] = LDP(p.p_w + (rec0 + sc) * r + jc);
+            }
+        }
+    }
 
     float mx = -3.0e38f;
-    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, p.p_ml[(rec0 + s) * 2]);
+#pragma unroll
+    for (int u = 0; u < MLU; ++u)
+        if (64 * u < ns && lane + 64 * u < ns) mx = fmaxf(mx, mv[u]);
     mx = wave_max(mx);
     float lsum = 0.0f;
-    for (int s = lane; s < ns; s += 64) {
-        const float2 ml = *reinterpret_cast<const float2 *>(p.p_ml + (rec0 + s) * 2);
-        const float w = fexp2(ml.x - mx);
-        wbuf[s] = w;
-        lsum += w * ml.y;
+#pragma unroll
+    for (int u = 0; u < MLU; ++u) {
+        const int s = lane + 64 * u;
+        if (64 * u < ns && s < ns) {
+            const float w = fexp2(mv[u] - mx);
+            wbuf[s] = w;
+            lsum += w * lv[u];
+        }
     }
     lsum = wave_sum(lsum);
     __builtin_amdgcn_wave_barrier();
@@ -224,52 +392,67 @@ __device__ inline void merge_row(const DecodeParams &p, int k, int a, int ria, f
     float o[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
-    const float *po = p.p_o + rec0 * D + DPL * lane;
-    for (int s0 = 0; s0 < ns; s0 += 16) {
-        float v[16][DPL], wv[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < SB; ++u) {
+        const float w = u < ns ? wbuf[u] : 0.0f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] += w * ov[u][e];
+    }
+    for (int s0 = SB; s0 < ns; s0 += SB) {
+#pragma unroll
+        for (int u = 0; u < SB; ++u) {
             const int s = s0 + u;
             const int sc = s < ns ? s : ns - 1;
-            wv[u] = s < ns ? wbuf[sc] : 0.0f;
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) v[u][e] = po[(int64_t)sc * D + e];
+            for (int e = 0; e < DPL; ++e) ov[u][e] = LDP(po + (int64_t)sc * D + e);
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u)
+        for (int u = 0; u < SB; ++u) {
+            const float w = s0 + u < ns ? wbuf[s0 + u] : 0.0f;
 #pragma unroll
-            for (int e = 0; e < DPL; ++e) o[e] += wv[u] * v[u][e];
+            for (int e = 0; e < DPL; ++e) o[e] += w * ov[u][e];
+        }
     }
-    if (r > 0 && p.n_ps > 0) {
-        for (int j = lane; j < r; j += 64) {
-            float wj = 0.0f;
-            const float *pw = p.p_w + rec0 * r + j;
-            for (int s0 = 0; s0 < p.n_ps; s0 += 16) {
-                float v[16], wv[16];
+
+    if (wres) {
+        // merged W of this lane's residual columns, then o += W Bv^(k)
+        float wj[2] = {0.0f, 0.0f};
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int u = 0; u < SB; ++u) wj[h] += (u < nps ? wbuf[u] : 0.0f) * wv[h][u];
+        for (int s0 = SB; s0 < nps; s0 += SB) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int j = lane + 64 * h;
+                const int jc = j < r ? j : 0;
+#pragma unroll
+                for (int u = 0; u < SB; ++u) {
                     const int s = s0 + u;
-                    const int sc = s < p.n_ps ? s : p.n_ps - 1;
-                    wv[u] = s < p.n_ps ? wbuf[sc] : 0.0f;
-                    v[u] = pw[(int64_t)sc * r];
+                    const int sc = s < nps ? s : nps - 1;
+                    wv[h][u] = LDP(p.p_w + (rec0 + sc) * r + jc);
                 }
-#pragma unroll
-                for (int u = 0; u < 16; ++u) wj += wv[u] * v[u];
             }
-            wr[j] = wj;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int u = 0; u < SB; ++u) wj[h] += (s0 + u < nps ? wbuf[s0 + u] : 0.0f) * wv[h][u];
         }
-        __builtin_amdgcn_wave_barrier();
         const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * r * p.HK * D + (int64_t)k * D + DPL * lane;
+        const int64_t ldb = (int64_t)p.HK * D;
         for (int j0 = 0; j0 < r; j0 += 8) {
             float bvv[8][DPL];
 #pragma unroll
             for (int u = 0; u < 8; ++u)
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) bvv[u][e] = (float)bv[(int64_t)(j0 + u) * p.HK * D + e];
+                for (int e = 0; e < DPL; ++e) bvv[u][e] = (float)bv[(int64_t)(j0 + u) * ldb + e];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < 8; ++u) {
+                const int j = j0 + u;  // W of column j lives in lane j % 64, slot j / 64
+                const float wsel = __shfl(j < 64 ? wj[0] : wj[1], j & 63);
 #pragma unroll
-                for (int e = 0; e < DPL; ++e) o[e] += wr[j0 + u] * bvv[u][e];
+                for (int e = 0; e < DPL; ++e) o[e] += wsel * bvv[u][e];
+            }
         }
     }
     const float inv = 1.0f / lsum;
@@ -290,8 +473,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     constexpr int CS = CPAD / 32;
     constexpr int CSx = CS > 0 ? CS : 1;
     constexpr int CPLx = CPAD > 0 ? CPAD / 16 : 1;
+    constexpr int ES = (int)sizeof(T);
 
-    extern __shared__ float smem[];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -334,102 +518,176 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         slot = p.n_ps + s;
         prefix = false;
     }
+    if (t1 < t0) t1 = t0;  // an empty trailing split
     const bool resid = prefix && (CPAD > 0) && p.r > 0;
     const bool causal = !prefix && p.causal;
     const int TG = 4 / nblk;  // waves sharing one row block (token groups)
     const int rbi = wave / TG;
     const int tg = wave % TG;
-    const bool active = rbi < nblk && t0 < t1;
+
+    // Agents the workgroup serves.
+    int a_lo, a_hi;
+    if (prefix) {
+        const RowBlock b0 = prefix_block(blk0, p.N, p.rpa, p.apb, p.bpa);
+        const RowBlock b1 = prefix_block(blk0 + nblk - 1, p.N, p.rpa, p.apb, p.bpa);
+        a_lo = b0.a0;
+        a_hi = b1.a0 + b1.na - 1;
+    } else {
+        a_lo = a_hi = agent_p;
+    }
 
     // Row block of this wave.
     RowBlock blk;
     if (prefix) {
-        blk = prefix_block(blk0 + rbi, p.N, p.rpa, p.apb, p.bpa);
+        blk = prefix_block(blk0 + (rbi < nblk ? rbi : 0), p.N, p.rpa, p.apb, p.bpa);
     } else {
         blk.a0 = agent_p;
         blk.na = 1;
-        blk.f = p.rpa <= 16 ? 0 : 16 * (blk0 + rbi);
+        blk.f = p.rpa <= 16 ? 0 : 16 * (blk0 + (rbi < nblk ? rbi : 0));
         blk.nr = p.rpa - blk.f < 16 ? p.rpa - blk.f : 16;
     }
+    const bool wave_on = rbi < nblk;
     // Query row owned by this lane's column.
-    const bool vm = rbi < nblk && n16 < blk.nr;
+    const bool vm = wave_on && n16 < blk.nr;
     int agent_m = 0, ria = 0;
     if (vm) block_row(blk, n16, p.rpa, &agent_m, &ria);
     const int tq = ria / p.g, hh = ria % p.g;
     const int64_t qrow = ((int64_t)agent_m * p.QL + tq) * p.HQ + (int64_t)k * p.g + hh;
     const int64_t grow = (int64_t)agent_m * p.rpa + ria;
     const float cl2 = p.c;
-
-    const T *qp = static_cast<const T *>(p.q);
     const int cvalid = resid ? (p.shared_lr ? p.r : blk.na * p.r) : 0;
+    const int lr_col0 = resid && !p.shared_lr ? (blk.a0 - a_lo) * p.r : 0;  // block's first column in the tile
+
+    // ---- stage geometry and token source of this item
+    Geo g;
+    g.T = prefix ? p.T_pre : p.T_pv;
+    g.nst = prefix ? p.nst_pre : p.nst_pv;
+    g.stage_bytes = prefix ? p.stage_bytes_pre : p.stage_bytes_pv;
+    g.cpr_kv = D * ES / 16;
+    g.lg_kv = ilog2(g.cpr_kv);
+    if (resid) {
+        const int lrc = p.shared_lr ? p.r : (a_hi - a_lo + 1) * p.r;
+        g.cpr_lr = lrc * ES / 16;
+        g.lg_lr = g.cpr_lr > 1 ? 32 - __builtin_clz(g.cpr_lr - 1) : 0;
+        g.cpa_lr = 1 << g.lg_lr;
+    } else {
+        g.cpr_lr = 0;
+        g.cpa_lr = 1;
+        g.lg_lr = 0;
+    }
+    g.ofs_v = g.T * g.cpr_kv;
+    g.ofs_lk = 2 * g.T * g.cpr_kv;
+    g.ofs_lv = g.ofs_lk + (resid ? g.T * g.cpa_lr : 0);
+    g.chunks = g.ofs_lv + (resid ? g.T * g.cpa_lr : 0);
+
+    int *s_pages = reinterpret_cast<int *>(smem + p.table_lds_off);
+    Src<T> src;
+    src.tlast = t1 > t0 ? t1 - 1 : t0;
+    src.r = p.r > 0 ? p.r : 1;
+    src.lr_es_shift = p.r > 0 ? ilog2(p.r * ES / 16) : 0;
+    src.lk = src.lv = nullptr;
+    src.lr_agent_stride = 0;
+    src.page_stride = 0;
+    src.ps = 16;
+    src.pg0 = 0;
+    src.pages = s_pages;
+    if (prefix) {
+        src.kb = static_cast<const T *>(p.kb);
+        src.vb = static_cast<const T *>(p.vb);
+        if (p.ps > 0) {
+            src.page_stride = (int64_t)p.HK * p.ps * D;
+            src.ps = p.ps;
+            src.kb += (int64_t)k * p.ps * D;
+            src.vb += (int64_t)k * p.ps * D;
+            src.pg0 = t0 / p.ps;
+        } else {
+            src.kb += (int64_t)k * p.L * D;
+            src.vb += (int64_t)k * p.L * D;
+        }
+        if (resid) {
+            const int64_t a_lr = p.shared_lr ? 0 : a_lo;
+            src.lk = static_cast<const T *>(p.lk) + a_lr * p.L * p.r;
+            src.lv = static_cast<const T *>(p.lv) + a_lr * p.L * p.r;
+            src.lr_agent_stride = p.L * p.r;
+        }
+    } else {
+        const int64_t seg = ((int64_t)agent_p * p.HK + k) * p.S * D;
+        src.kb = static_cast<const T *>(p.kp) + seg;
+        src.vb = static_cast<const T *>(p.vp) + seg;
+    }
+    if (src.page_stride && t1 > t0) {
+        // the split's page-table entries, read once into LDS
+        const int npg = (t1 - 1) / p.ps - src.pg0 + 1;
+        for (int i = threadIdx.x; i < npg; i += 256) s_pages[i] = p.table[src.pg0 + i];
+        __syncthreads();
+    }
+
+    // Lane constants of the fast fill and of the step's LDS reads.
+    FillLane fl;
+    {
+        const int rin = lane >> g.lg_kv, pp = lane & (g.cpr_kv - 1);
+        fl.kv_rb = (uint32_t)(rin * D * ES);
+        fl.kv_pr = (uint32_t)swz(rin, pp, g.cpr_kv, g.lg_kv);
+        if (resid) {
+            const int rl = lane >> g.lg_lr, pl = lane & (g.cpa_lr - 1);
+            fl.lr_rb = (uint32_t)(rl * src.r * ES);
+            fl.lr_pr = (uint32_t)swz(rl, pl, g.cpa_lr, g.lg_lr);
+        } else {
+            fl.lr_rb = fl.lr_pr = 0;
+        }
+    }
+    // fast fill: every region a whole number of instructions, low-rank offsets in 32 bits
+    const bool fast_ok = (g.T * g.cpr_kv) % 64 == 0 && (!resid || (g.T * g.cpa_lr) % 64 == 0) &&
+                         (!resid || p.lr_off32);
+    ReadOfs<T, D, CPAD> ro;
+    {
+        using RO = ReadOfs<T, D, CPAD>;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int c = 0; c < RO::FC; ++c)
+                ro.k[s][c] = elem_ofs(0, n16, (32 * s + 8 * j4) * ES + 16 * c, g.cpr_kv, g.lg_kv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < RO::VC; ++c)
+                ro.v[i][c] = elem_ofs(g.ofs_v, 4 * j4 + i, VPL * n16 * ES + 16 * c, g.cpr_kv, g.lg_kv);
+#pragma unroll
+        for (int s = 0; s < RO::CSx; ++s) {
+            int col = 32 * s + 8 * j4;
+            col = lr_col0 + (col < cvalid ? col : 0);  // padding column: U is zero there
+#pragma unroll
+            for (int c = 0; c < RO::FC; ++c)
+                ro.lk[s][c] = resid ? elem_ofs(g.ofs_lk, n16, col * ES + 16 * c, g.cpa_lr, g.lg_lr) : 0u;
+        }
+        int colv = RO::CPL * n16;
+        colv = lr_col0 + (colv < cvalid ? colv : 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int c = 0; c < RO::LC; ++c)
+                ro.lv[i][c] = resid ? elem_ofs(g.ofs_lv, 4 * j4 + i, colv * ES + 16 * c, g.cpa_lr, g.lg_lr) : 0u;
+    }
+    const int kv_rowb = D * ES, lr_rowb = 16 * g.cpa_lr;
 
     // Query rows as the B operand of S^T = K Q^T.
+    const T *qp = static_cast<const T *>(p.q);
     frag qB[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) qB[s] = vm ? O::load8(qp + qrow * D + 32 * s + 8 * j4) : O::zero();
 
-    // Token stream of this item.
-    Stream<T, D, CPAD> st;
-    st.r = p.r;
-    st.resid = resid;
-    st.tlast = t1 - 1;
-    st.tlast16 = st.tlast & ~15;
-    if (prefix) {
-        st.kb = static_cast<const T *>(p.kb);
-        st.vb = static_cast<const T *>(p.vb);
-        if (p.ps > 0) {
-            st.table = p.table;
-            st.ps = p.ps;
-            st.page_stride = (int64_t)p.HK * p.ps * D;
-            st.head_off = (int64_t)k * p.ps * D;
-        } else {
-            st.table = nullptr;
-            st.ps = 16;
-            st.page_stride = 0;
-            st.head_off = 0;
-            st.kb += (int64_t)k * p.L * D;
-            st.vb += (int64_t)k * p.L * D;
-        }
-    } else {
-        const int64_t seg = ((int64_t)agent_p * p.HK + k) * p.S * D;
-        st.kb = static_cast<const T *>(p.kp) + seg;
-        st.vb = static_cast<const T *>(p.vp) + seg;
-        st.table = nullptr;
-        st.ps = 16;
-        st.page_stride = 0;
-        st.head_off = 0;
-    }
-    {
-        const T *lk = static_cast<const T *>(p.lk);
-        const T *lv = static_cast<const T *>(p.lv);
-#pragma unroll
-        for (int s = 0; s < CSx; ++s) {
-            const int cc = 32 * s + 8 * j4;
-            int lr = 0, col = 0;
-            if (resid && cc < cvalid) {
-                lr = p.shared_lr ? 0 : blk.a0 + (cc >> p.lr_shift);
-                col = cc & (p.r - 1);
-            } else if (resid) {
-                lr = p.shared_lr ? 0 : blk.a0;  // padding column: any finite data (U is zero there)
-            }
-            st.lk[s] = lk + (int64_t)lr * p.L * p.r + col;
-        }
-        const int cl = CPLx * n16;
-        int lr = 0, col = 0;
-        if (resid && cl < cvalid) {
-            lr = p.shared_lr ? 0 : blk.a0 + (cl >> p.lr_shift);
-            col = cl & (p.r - 1);
-        } else if (resid) {
-            lr = p.shared_lr ? 0 : blk.a0;
-        }
-        st.lv = lv + (int64_t)lr * p.L * p.r + col;
-    }
-
-    // First chunk's loads go out before U is computed.
-    Chunk<T, D, CPAD> ca, cb;
-    const int step = 32 * TG;
-    int tc = t0 + 32 * tg;
-    if (active) load_chunk(ca, st, tc, n16, j4);
+    // ---- start the ring: tiles 0 .. nst-2
+    const int n_tiles = (t1 - t0 + g.T - 1) / g.T;
+    const int fpw = fills_per_wave(g, wave);
+    auto fill = [&](int tile, int stage) {
+        const int tt = t0 + tile * g.T;
+        char *sp = smem + (size_t)stage * g.stage_bytes;
+        if (fast_ok && tt + g.T - 1 <= src.tlast)
+            fill_stage_fast<T, D>(g, src, fl, tt, sp, wave);
+        else
+            fill_stage_any<T, D>(g, src, tt, sp, wave, lane);
+    };
+    for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
 
     // U = scale*log2(e) * q Bk^T as the B operand of the rank-r score correction,
     // block-diagonal over the agents of the block (bf16 carries hi + lo halves).
@@ -442,7 +700,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         uH[s] = O::zero();
         uL[s] = O::zero();
     }
-    if (CPAD > 0 && resid && active) {
+    if (CPAD > 0 && resid && wave_on && n_tiles > 0) {
         const T *bk = static_cast<const T *>(p.bk);
         const int64_t ldb = (int64_t)p.HK * D;
         const int rmask = p.r - 1;
@@ -492,6 +750,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         }
     }
 
+    // Every register load (q, Bk) has landed on every path, so the compiler has
+    // nothing pending inside the ring loop and adds no waits of its own there.
+    wait_vmcnt(0);
+
     Acc<T, D, CPAD> acc;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) acc.o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -500,13 +762,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     acc.m = -1.0e30f;
     acc.l = 0.0f;
 
-    if (active) {
-        for (; tc < t1; tc += 2 * step) {
-            load_chunk(cb, st, tc + step, n16, j4);
-            compute_chunk(acc, ca, qB, uH, uL, cl2, resid, tc, t1, causal, tq, j4);
-            if (tc + step >= t1) break;
-            load_chunk(ca, st, tc + 2 * step, n16, j4);
-            compute_chunk(acc, cb, qB, uH, uL, cl2, resid, tc + step, t1, causal, tq, j4);
+    // ---- the ring: wait for tile i, refill the stage freed by tile i-1, compute tile i
+    const int spw = g.T / (16 * TG);  // 16-token steps per wave per tile
+    for (int i = 0; i < n_tiles; ++i) {
+        const int later = (n_tiles - 1 - i) < (g.nst - 2) ? (n_tiles - 1 - i) : (g.nst - 2);
+        wait_vmcnt(later * fpw);  // this wave's loads of tile i have landed
+        ring_barrier();           // ... everyone's, and everyone is done with tile i-1
+        if (i + g.nst - 1 < n_tiles) fill(i + g.nst - 1, (i + g.nst - 1) % g.nst);
+        if (wave_on) {
+            const char *st = smem + (size_t)(i % g.nst) * g.stage_bytes;
+            const int tt = t0 + i * g.T;
+            const bool masked = causal || tt + g.T > t1;
+            for (int u = 0; u < spw; ++u) {
+                const int row0 = 16 * (tg * spw + u);
+                step16<T, D, CPAD>(acc, ro, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked, qB, uH, uL,
+                                   cl2, resid, t1, causal, tq, j4);
+            }
         }
     }
     float m_run = acc.m, l_run = acc.l;
@@ -514,11 +785,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     l_run += __shfl_xor(l_run, 16);
     l_run += __shfl_xor(l_run, 32);
 
-    // ---- merge the token groups of a row block (same lane layout in every wave)
+    // ---- merge the token groups of a row block (same lane layout in every wave);
+    // the stages are free now (every load was awaited in the last iteration).
+    __syncthreads();
+    float *smf = reinterpret_cast<float *>(smem);
     constexpr int PER_LANE = 4 * VPL + 4 * CPLx;
-    // Waves 1..3 publish their state (wave 0 always has tg == 0): three slots.
     if (TG > 1) {
-        float *sm = smem + (size_t)(wave - 1) * (64 * PER_LANE + 32);
+        // waves with tg > 0 publish their state: one slot per wave
+        float *sm = smf + (size_t)wave * (64 * PER_LANE + 32);
         if (tg > 0) {
 #pragma unroll
             for (int jj = 0; jj < VPL; ++jj)
@@ -537,7 +811,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         if (tg == 0) {
             float mt = m_run;
             for (int w = 1; w < TG; ++w)
-                mt = fmaxf(mt, smem[(size_t)(wave + w - 1) * (64 * PER_LANE + 32) + 64 * PER_LANE + n16]);
+                mt = fmaxf(mt, smf[(size_t)(wave + w) * (64 * PER_LANE + 32) + 64 * PER_LANE + n16]);
             const float s0 = fexp2(m_run - mt);
             l_run *= s0;
 #pragma unroll
@@ -545,7 +819,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
             for (int jj = 0; jj < CPLx; ++jj) acc.w[jj] *= s0;
             for (int w = 1; w < TG; ++w) {
-                const float *sw = smem + (size_t)(wave + w - 1) * (64 * PER_LANE + 32);
+                const float *sw = smf + (size_t)(wave + w) * (64 * PER_LANE + 32);
                 const float sf = fexp2(sw[64 * PER_LANE + n16] - mt);
                 l_run += sf * sw[64 * PER_LANE + 16 + n16];
 #pragma unroll
@@ -584,81 +858,78 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                         p.p_w[rec * p.r + (c & (p.r - 1))] = acc.w[jj][i];
                 }
         }
-        if (j4 == 0) {
-            p.p_ml[rec * 2] = m_run;
-            p.p_ml[rec * 2 + 1] = l_run;
-        }
+        if (j4 == 0) *reinterpret_cast<float2 *>(p.p_ml + rec * 2) = float2{m_run, l_run};
     }
+}
 
-    // ---- completion tickets; the workgroup that completes an agent merges it
-    __shared__ int s_last[64];
-    __shared__ int s_nlast;
-    __threadfence();  // release this thread's partial stores (device scope)
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int a_lo, a_hi;
-        if (prefix) {
-            const RowBlock b0 = prefix_block(blk0, p.N, p.rpa, p.apb, p.bpa);
-            const RowBlock b1 = prefix_block(blk0 + nblk - 1, p.N, p.rpa, p.apb, p.bpa);
-            a_lo = b0.a0;
-            a_hi = b1.a0 + b1.na - 1;
-        } else {
-            a_lo = a_hi = agent_p;
-        }
-        int nl = 0;
-        for (int a = a_lo; a <= a_hi; ++a) {
-            const unsigned old = atomicAdd(p.cnt + (int64_t)k * p.N + a, 1u);
-            if (old + 1 == expected_tickets(p, a)) s_last[nl++] = a;
-        }
-        s_nlast = nl;
-    }
-    __syncthreads();
-    const int nl = s_nlast;
-    if (nl > 0) {
-        __threadfence();  // acquire: every item's partials of these agents are visible
-        float *wbuf = smem + (size_t)wave * (kMaxSlots + 128);
-        float *wr = wbuf + kMaxSlots;
-        for (int i = 0; i < nl; ++i) {
-            const int a = s_last[i];
-            for (int ria = wave; ria < p.rpa; ria += 4) merge_row<T, D>(p, k, a, ria, wbuf, wr, lane);
-        }
-        // Ready for the next call.  An atomic at device scope, like the tickets: a
-        // plain store could stay in this XCD's L2 while the next call's tickets
-        // are counted at the device-wide coherence point.
-        if (threadIdx.x == 0)
-            for (int i = 0; i < nl; ++i) atomicExch(p.cnt + (int64_t)k * p.N + s_last[i], 0u);
-    }
+
+// ---------------------------------------------------------------- combine --
+
+// One wavefront per query row: row R = (a * q_len + t) * H_q + h.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
+    __shared__ float wbuf[4][kMaxSlots];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t R = (int64_t)blockIdx.x * 4 + wave;
+    if (R >= (int64_t)p.N * p.QL * p.HQ) return;
+    const int h = (int)(R % p.HQ);
+    const int64_t at = R / p.HQ;
+    const int a = (int)(at / p.QL), t = (int)(at % p.QL);
+    const int k = h / p.g;
+    merge_row<T, D>(p, k, a, t * p.g + (h % p.g), wbuf[wave], lane);
 }
 
 // ---------------------------------------------------------------- launchers --
 
-template <typename T>
-static hipError_t launch_decode_t(const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st) {
-    const dim3 grid(8 * dp.per_xcd);
-#define RATTN_SPLIT(DD, CP) \
-    hipLaunchKernelGGL((decode_split_kernel<T, DD, CP>), grid, dim3(256), lds, st, dp)
-    if (D == 128) {
-        switch (cpad) {
-            case 0: RATTN_SPLIT(128, 0); break;
-            case 32: RATTN_SPLIT(128, 32); break;
-            case 64: RATTN_SPLIT(128, 64); break;
-            default: RATTN_SPLIT(128, 128); break;
-        }
-    } else {
-        switch (cpad) {
-            case 0: RATTN_SPLIT(64, 0); break;
-            case 32: RATTN_SPLIT(64, 32); break;
-            case 64: RATTN_SPLIT(64, 64); break;
-            default: RATTN_SPLIT(64, 128); break;
-        }
-    }
-#undef RATTN_SPLIT
+template <typename T, int D, int CP>
+static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t st) {
+    auto *fn = decode_split_kernel<T, D, CP>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3(8 * dp.per_xcd), dim3(256), lds, st, dp);
     return hipGetLastError();
 }
 
-hipError_t launch_decode(int bf16_in, const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st) {
-    if (bf16_in) return launch_decode_t<bf16>(dp, D, cpad, lds, st);
-    return launch_decode_t<float>(dp, D, cpad, lds, st);
+template <typename T>
+static hipError_t launch_split_t(const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st) {
+    if (D == 128) {
+        switch (cpad) {
+            case 0: return launch_split<T, 128, 0>(dp, lds, st);
+            case 32: return launch_split<T, 128, 32>(dp, lds, st);
+            case 64: return launch_split<T, 128, 64>(dp, lds, st);
+            default: return launch_split<T, 128, 128>(dp, lds, st);
+        }
+    }
+    switch (cpad) {
+        case 0: return launch_split<T, 64, 0>(dp, lds, st);
+        case 32: return launch_split<T, 64, 32>(dp, lds, st);
+        case 64: return launch_split<T, 64, 64>(dp, lds, st);
+        default: return launch_split<T, 64, 128>(dp, lds, st);
+    }
+}
+
+template <typename T>
+static hipError_t launch_combine_t(const DecodeParams &dp, int D, hipStream_t st) {
+    const int64_t rows = (int64_t)dp.N * dp.QL * dp.HQ;
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (D == 128)
+        hipLaunchKernelGGL((combine_kernel<T, 128>), grid, dim3(256), 0, st, dp);
+    else
+        hipLaunchKernelGGL((combine_kernel<T, 64>), grid, dim3(256), 0, st, dp);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(int bf16_in, const DecodeParams &dp, int D, int cpad, size_t lds, unsigned stages,
+                         hipStream_t st) {
+    hipError_t e = hipSuccess;
+    if (stages & 1u) {
+        e = bf16_in ? launch_split_t<bf16>(dp, D, cpad, lds, st) : launch_split_t<float>(dp, D, cpad, lds, st);
+        if (e != hipSuccess) return e;
+    }
+    if (stages & 2u) e = bf16_in ? launch_combine_t<bf16>(dp, D, st) : launch_combine_t<float>(dp, D, st);
+    return e;
 }
 
 }  // namespace rattn

@@ -8,6 +8,7 @@ namespace rattn {
 
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -62,6 +63,16 @@ struct Ops<bf16> {
     static __device__ inline f32x4 mma(const frag &a, const frag &b, f32x4 c) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
     }
+    // Half fragment: 4 k-values per lane over a 16-long contraction (lane l
+    // supplies k-slots 4*(l/16)..4*(l/16)+3), one v_mfma_f32_16x16x16_bf16.
+    struct frag4 {
+        bf16x4 v;
+    };
+    static __device__ inline void set4(frag4 &f, int i, float x) { f.v[i] = (bf16)x; }
+    static __device__ inline void set4_raw(frag4 &f, int i, bf16 x) { f.v[i] = x; }
+    static __device__ inline f32x4 mma16(const frag4 &a, const frag4 &b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, c, 0, 0, 0);
+    }
     static constexpr bool kSplitU = true;  // U is fed as bf16 hi + lo halves
 };
 
@@ -88,10 +99,111 @@ struct Ops<float> {
         for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.e[i], b.e[i], c, 0, 0, 0);
         return c;
     }
+    struct frag4 {
+        float e[4];
+    };
+    static __device__ inline void set4(frag4 &f, int i, float x) { f.e[i] = x; }
+    static __device__ inline void set4_raw(frag4 &f, int i, float x) { f.e[i] = x; }
+    static __device__ inline f32x4 mma16(const frag4 &a, const frag4 &b, f32x4 c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.e[i], b.e[i], c, 0, 0, 0);
+        return c;
+    }
     static constexpr bool kSplitU = false;
 };
 
 __device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Device-coherent (agent-scope) 4-byte store and load: on gfx950 these are
+// global_store/global_load with the device scope bit, so a value stored by one
+// XCD is read back by another without L2 writeback or invalidation.
+__device__ inline void st_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- staging through LDS ---------------------------------------------------
+//
+// Tiles are copied from global memory into LDS with gfx950's direct loads
+// (global_load_lds_dwordx4): one instruction moves 16 bytes per lane, lane l
+// landing at LDS byte (base + 16 l), with no registers in between.  Rows of a
+// tile are stored as 16-byte chunks, permuted within the row by an XOR with
+// bits of the row index so that the MFMA operand reads (16 rows at one column,
+// or one row across 16 lanes) touch distinct banks.
+
+// Physical chunk of logical chunk c in row `row` of a region whose rows hold
+// `cpa` (a power of two) chunks.  An involution: it also maps physical to logical.
+__device__ inline int swz(int row, int c, int cpa, int lg) {
+    return cpa >= 16 ? (c ^ (row & 15)) : (c ^ ((row >> (4 - lg)) & (cpa - 1)));
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ inline uint32_t lds_addr(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)p;
+}
+
+// One direct load: 16 bytes from gsrc (per lane) to LDS byte lds_base + 16*lane.
+// lds_base must be wave-uniform (it goes to M0).  Written as inline assembly so
+// that the compiler does not treat every later LDS read as dependent on it (it
+// would wait for all outstanding loads before each read); completion is awaited
+// explicitly with wait_vmcnt before the stage is read.  One wait state between
+// the M0 write and the load.
+__device__ inline void dma16(const void *gsrc, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// The same with a wave-uniform 64-bit base (SGPR pair) and a per-lane 32-bit
+// byte offset (the instruction's saddr form).
+__device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_base)
+                 : "memory", "m0");
+}
+
+// A pointer that is the same in every lane, moved to scalar registers.
+template <typename P>
+__device__ inline P *uniform_ptr(P *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (P *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt vmcnt(n) (n clamped to the 6-bit field), leaving the other counters.
+// The immediate must be a constant, hence the table.
+__device__ inline void wait_vmcnt(int n) {
+#define RATTN_VM(N) \
+    case N: __builtin_amdgcn_s_waitcnt(((N) & 15) | (((N) >> 4) << 14) | (7 << 4) | (15 << 8)); break;
+    switch (n < 63 ? (n > 0 ? n : 0) : 63) {
+        RATTN_VM(0) RATTN_VM(1) RATTN_VM(2) RATTN_VM(3) RATTN_VM(4) RATTN_VM(5) RATTN_VM(6) RATTN_VM(7)
+        RATTN_VM(8) RATTN_VM(9) RATTN_VM(10) RATTN_VM(11) RATTN_VM(12) RATTN_VM(13) RATTN_VM(14) RATTN_VM(15)
+        RATTN_VM(16) RATTN_VM(17) RATTN_VM(18) RATTN_VM(19) RATTN_VM(20) RATTN_VM(21) RATTN_VM(22) RATTN_VM(23)
+        RATTN_VM(24) RATTN_VM(25) RATTN_VM(26) RATTN_VM(27) RATTN_VM(28) RATTN_VM(29) RATTN_VM(30) RATTN_VM(31)
+        RATTN_VM(32) RATTN_VM(33) RATTN_VM(34) RATTN_VM(35) RATTN_VM(36) RATTN_VM(37) RATTN_VM(38) RATTN_VM(39)
+        RATTN_VM(40) RATTN_VM(41) RATTN_VM(42) RATTN_VM(43) RATTN_VM(44) RATTN_VM(45) RATTN_VM(46) RATTN_VM(47)
+        RATTN_VM(48) RATTN_VM(49) RATTN_VM(50) RATTN_VM(51) RATTN_VM(52) RATTN_VM(53) RATTN_VM(54) RATTN_VM(55)
+        RATTN_VM(56) RATTN_VM(57) RATTN_VM(58) RATTN_VM(59) RATTN_VM(60) RATTN_VM(61) RATTN_VM(62)
+        default: __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (15 << 8)); break;
+    }
+#undef RATTN_VM
+}
+
+// Workgroup barrier for the staging ring: waits for this wave's own LDS reads
+// (lgkmcnt(0)), then s_barrier.  No vmcnt(0): direct loads of later stages stay
+// in flight (their completion is awaited explicitly with wait_vmcnt).  The
+// empty asm statements keep the compiler from moving memory accesses across.
+__device__ inline void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 __device__ inline float wave_max(float v) {
 #pragma unroll

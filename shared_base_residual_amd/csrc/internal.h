@@ -62,10 +62,11 @@ RATTN_HD void block_row(const RowBlock &rb, int m, int rpa, int *agent, int *ria
 // Splits per query row the merge handles (weights staged in LDS).
 constexpr int kMaxSlots = 512;
 
-// The workspace starts with a header of completion counters of this fixed size,
-// whatever the shape of the call, so that no call's partials ever land on bytes
-// that another call (of another shape) counts with.  H_kv * N must fit.
-constexpr int64_t kCounterHeaderBytes = 64 * 1024;
+// Online softmax: the reference max of a row is raised when a score exceeds it
+// by more than this (log2 units).  Zero: the largest weight of a row is exactly
+// 1, which keeps its bf16 rounding error out of peaked rows; the accumulators
+// are still rescaled only on the steps where some row's max grows.
+constexpr float kRescaleSlack = 0.0f;
 
 struct DecodeParams {
     const void *q, *kb, *vb;
@@ -75,7 +76,6 @@ struct DecodeParams {
     float *p_ml;      // [H_kv, N*rpa, n_slots, 2]  running max (log2 units), sum of weights
     float *p_o;       // [H_kv, N*rpa, n_slots, d]  unnormalised P V_base (+ private P V)
     float *p_w;       // [H_kv, N*rpa, n_slots, r]  unnormalised P Lv
-    unsigned *cnt;    // [H_kv, N] completion tickets; zero between calls
     int64_t L, S;     // < 2^30 (validated on the host)
     int N, QL, HQ, HK, g, r, lr_shift, rpa, apb, bpa, ps, shared_lr;
     int causal;       // private token j is visible to query token t only if j <= t
@@ -85,6 +85,18 @@ struct DecodeParams {
     int pb, n_prg, n_pv;
     int tok_pv;
     int n_slots, n_prefix_items, n_items, per_xcd;
+    // LDS staging ring: tokens per stage, stages, bytes per stage (prefix items
+    // and private items), and where the split's page-table copy lives.
+    int T_pre, nst_pre, stage_bytes_pre;
+    int T_pv, nst_pv, stage_bytes_pv;
+    int table_lds_off;
+    int lr_off32;     // the low-rank rows a workgroup reads span < 2^31 bytes (fast fill usable)
 };
+
+// Dynamic LDS a split workgroup may use (gfx950: 160 KiB per workgroup, less
+// what the kernel declares statically).
+constexpr int kLdsBudget = 160 * 1024 - 1024;
+// Page-table entries of one split copied into LDS.
+constexpr int kMaxPagesPerSplit = 2048;
 
 }  // namespace rattn

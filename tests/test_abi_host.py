@@ -205,3 +205,16 @@ def test_gather_validation():
                                None) == E_SHAPE
     assert L.rattn_gather_base(ctypes.byref(cfg1_desc(page_size=16, n_phys_pages=4, prefix_len=0)), None,
                                None, None, None) == OK
+
+
+def test_stage_mask_validation():
+    """rattn_attention_stages accepts only a non-empty subset of split | combine,
+    and only the two ops; all checked before any HIP call."""
+    L = R.lib()
+    d = cfg1_desc()
+    _, need = ws(d)
+    a = args()
+    for stages in (0, 4, 7):
+        assert L.rattn_attention_stages(ctypes.byref(d), 0, ctypes.byref(a), FAKE, need, None, stages) == E_SHAPE
+    assert L.rattn_attention_stages(ctypes.byref(d), 5, ctypes.byref(a), FAKE, need, None, 1) == E_SHAPE
+    assert L.rattn_attention_stages(ctypes.byref(d), 0, ctypes.byref(a), FAKE, need - 1, None, 1) == E_WS

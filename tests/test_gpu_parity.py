@@ -40,9 +40,6 @@ def run_gpu(case, x, lse=True):
     out = torch.full(tuple(t["q"].shape), float("nan"), device=DEV, dtype=torch.float32)
     R.attend(t, mode=case.mode, shared_lr=case.shared_lr, prefix_len=case.prefix_len, lse=lse_t, out=out)
     torch.cuda.synchronize()
-    # every call leaves the completion-counter header of the workspace zero
-    ws = R.workspace_for(0, torch.device(DEV))
-    assert int(ws[: 64 * 1024].count_nonzero()) == 0, f"completion counters not reset after {case}"
     return out.cpu().numpy().astype(np.float64), (lse_t.cpu().numpy().astype(np.float64) if lse else None)
 
 
@@ -222,8 +219,8 @@ def test_shuffled_table_bitwise_equals_identity():
 
 
 def test_workspace_reused_across_shapes():
-    """One zero-filled workspace serves calls of different shapes in turn: every call
-    leaves its completion counters zero (rattn.h workspace rule)."""
+    """One workspace, never cleared, serves calls of different shapes in turn (its
+    contents on entry do not matter), and the stages run separately equal the call."""
     R = rattn()
     cases = [synth.Case(4, 32, 8, 128, 16, 3000, priv_len=40, name="A"),
              synth.Case(7, 8, 2, 64, 8, 900, name="B"),
@@ -231,7 +228,7 @@ def test_workspace_reused_across_shapes():
     xs = [synth.make_inputs(c, 40 + i, b_sigma=0.3) for i, c in enumerate(cases)]
     nbytes = max(R.workspace_bytes(R.describe(*[synth.to_torch(x, DEV)[n] for n in ("q", "k_base", "lk", "bk")],
                                               k_priv=synth.to_torch(x, DEV)["k_priv"])) for x in xs)
-    ws = torch.zeros(nbytes, device=DEV, dtype=torch.uint8)
+    ws = torch.full((nbytes,), 0x7F, device=DEV, dtype=torch.uint8)  # garbage, never cleared
     for c, x in zip(cases, xs):
         say(f"[gpu] shared workspace: {c.name}")
         t = synth.to_torch(x, DEV)
@@ -239,4 +236,8 @@ def test_workspace_reused_across_shapes():
         torch.cuda.synchronize()
         exp, _ = oracle.attend(c, x)
         parity.check(got.cpu().numpy().astype(np.float64), exp, "bf16", what=c.name)
-    assert int(ws[: 64 * 1024].count_nonzero()) == 0, "counter header not zero after the calls"
+        o2 = torch.full_like(got, float("nan"))
+        R.attend(t, workspace=ws, out=o2, stages=R.STAGE_SPLIT)
+        R.attend(t, workspace=ws, out=o2, stages=R.STAGE_COMBINE)
+        torch.cuda.synchronize()
+        assert torch.equal(got, o2), "split then combine differs from the full call"
