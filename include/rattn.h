@@ -114,6 +114,10 @@ int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes);
  * every query row that also applies Bv once per row (LRAgent,
  * Flash-LoRA-Attention: B is applied once per query block).
  *
+ * Limits (RATTN_E_UNSUPPORTED beyond them): the low-rank caches of the agents
+ * that share one 16-row MFMA block group (up to 4 blocks) must span less than
+ * 2 GiB (N_group * L * r * element size < 2^31).
+ *
  * Workspace: at least rattn_workspace_bytes(desc, RATTN_OP_DECODE) bytes of
  * device memory, 256-byte aligned.  Its contents on entry do not matter and are
  * scratch on exit; calls that share a workspace must not overlap in time (one

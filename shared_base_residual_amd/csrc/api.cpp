@@ -187,7 +187,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             if (na > ag_max) ag_max = na;
         }
         int lr_row = 0;
-        p.lr_off32 = (int64_t)ag_max * L * r * es < (1ll << 31);
+        // the stage fill addresses one workgroup's low-rank rows with 32-bit offsets
+        if (resid && (int64_t)(d->shared_lr ? 1 : ag_max) * L * r * es >= (1ll << 31)) return RATTN_E_UNSUPPORTED;
         if (resid) {
             const int chunks = (d->shared_lr ? r : ag_max * r) * es / 16;
             lr_row = 16 * pow2ceil(chunks);

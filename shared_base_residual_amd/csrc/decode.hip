@@ -79,97 +79,141 @@ __device__ inline const T *kv_row(const Src<T> &s, const T *base, int tok) {
     return base + (int64_t)tok * D;
 }
 
-// Issues this wave's share of the direct loads that fill one stage with the
-// tile starting at token t0.  Instruction j (64 chunks) goes to wave j % 4.
-// General path: any tile (tokens past the item are clamped to its last one),
-// any region layout.
-template <typename T, int D>
-__device__ inline void fill_stage_any(const Geo &g, const Src<T> &s, int t0, char *stage, int wave, int lane) {
-    const int n_instr = (g.chunks + 63) >> 6;
-    for (int j = wave; j < n_instr; j += 4) {
-        const int q = 64 * j + lane;
-        if (q < g.chunks) {
-            const char *src;
-            if (q < g.ofs_lk) {
-                const bool isv = q >= g.ofs_v;
-                const int rel = isv ? q - g.ofs_v : q;
-                const int row = rel >> g.lg_kv;
-                const int c = swz(row, rel & (g.cpr_kv - 1), g.cpr_kv, g.lg_kv);
-                int tok = t0 + row;
-                tok = tok < s.tlast ? tok : s.tlast;
-                src = reinterpret_cast<const char *>(kv_row<T, D>(s, isv ? s.vb : s.kb, tok)) + 16 * c;
-            } else {
-                const bool isv = q >= g.ofs_lv;
-                const int rel = isv ? q - g.ofs_lv : q - g.ofs_lk;
-                const int row = rel >> g.lg_lr;
-                int c = swz(row, rel & (g.cpa_lr - 1), g.cpa_lr, g.lg_lr);
-                c = c < g.cpr_lr ? c : 0;  // allocated-only chunk: any valid data (never read)
-                int tok = t0 + row;
-                tok = tok < s.tlast ? tok : s.tlast;
-                const int agent = c >> s.lr_es_shift;
-                const int cin = c - (agent << s.lr_es_shift);
-                const T *base = (isv ? s.lv : s.lk) + agent * s.lr_agent_stride + (int64_t)tok * s.r;
-                src = reinterpret_cast<const char *>(base) + 16 * cin;
-            }
-            dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(stage) + 1024 * j));
-        }
-    }
-}
+// ------------------------------------------------------------ stage fill --
+//
+// A stage holds four regions of the tile: K rows, V rows, Lk rows, Lv rows (the
+// last two only with a residual).  The tile's rows are cut into 16-row groups;
+// wave w fills group w % G (G = T / 16) of the regions r with
+// r % (4 / G) == w / G, so every wave of the workgroup fills a fixed part: one
+// page lookup and one uniform base per region and tile, and lane offsets that
+// depend on the lane only (the swizzle repeats every 16 rows).  Each direct load
+// moves 64 chunks of 16 bytes; a region row of cpa chunks gives 16 * cpa chunks
+// per group, ceil(16 * cpa / 64) loads (the last one partial when 16 * cpa < 64).
+// Lane offsets are 32-bit: the low-rank rows one workgroup reads span less than
+// 2^31 bytes (checked on the host).
 
-// Number of direct-load instructions a wave issues per stage.
-__device__ inline int fills_per_wave(const Geo &g, int wave) {
-    const int n_instr = (g.chunks + 63) >> 6;
-    return n_instr > wave ? (n_instr - wave + 3) >> 2 : 0;
-}
+constexpr int kMaxKvLoads = 8;   // direct loads per group of a K (or V) region (fp32, d = 128)
 
-// Lane constants of the fast fill.  For a full tile, the 64 chunks of one
-// direct-load instruction lie in one region (K, V, Lk or Lv) and within one
-// 16-row swizzle period, so the instruction's source is a wave-uniform base
-// plus a per-lane 32-bit offset, and the swizzle splits into a lane part and a
-// uniform part: swz(row0 + row, c) = swz(row, c) ^ swz(row0, 0) whenever row0
-// is a multiple of the rows per instruction and row is below it.
-struct FillLane {
-    uint32_t kv_rb;   // (lane's row in the instruction) * bytes per K/V row
-    uint32_t kv_pr;   // lane part of the K/V swizzle
-    uint32_t lr_rb;   // the same for the low-rank regions
-    uint32_t lr_pr;
+struct FillPlan {
+    int G, g;                 // groups per tile, this wave's group
+    bool rK, rV, rL, rLv;     // regions this wave fills
+    int n_kv, n_lr;           // loads per group of a K/V region, of an Lk/Lv region
+    int fpw;                  // loads this wave issues per stage
+    uint32_t kv_off[kMaxKvLoads];  // lane byte offset from the group's first K/V row
+    int kv_row[kMaxKvLoads];       // lane's row within the group (for clamping)
+    uint32_t lr_stride;            // bytes between agents' low-rank caches
 };
 
-__device__ inline uint32_t swz_uniform(int row0, int cpa, int lg) { return (uint32_t)swz(row0, 0, cpa, lg); }
-
-// Fills one stage with a full tile (every token of it below tlast) through the
-// fast path: per instruction a uniform base (SALU) and the lane's offset
-// (a few VALU).  Requires the regions to be whole instructions (see fast_ok).
 template <typename T, int D>
-__device__ inline void fill_stage_fast(const Geo &g, const Src<T> &s, const FillLane &fl, int t0, char *stage,
-                                       int wave) {
+__device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f, const Geo &g, const Src<T> &s, bool resid, int wave, int lane) {
     constexpr int ES = (int)sizeof(T);
-    const int n_instr = g.chunks >> 6;
-    const int nK = (g.T * g.cpr_kv) >> 6;
-    const int nL = (g.T * g.cpa_lr) >> 6;
-    const int rpi_kv = 64 >> g.lg_kv;
-    const int kv_bytes = D * ES;
-    const uint32_t lds0 = lds_addr(stage);
-    for (int j = wave; j < n_instr; j += 4) {
-        const char *base;
-        uint32_t off;
-        if (j < 2 * nK) {
-            const bool isv = j >= nK;
-            const int row0 = (j - (isv ? nK : 0)) * rpi_kv;
-            const int tok = t0 + row0;
-            base = reinterpret_cast<const char *>(kv_row<T, D>(s, isv ? s.vb : s.kb, tok));
-            off = fl.kv_rb + ((fl.kv_pr ^ swz_uniform(row0, g.cpr_kv, g.lg_kv)) << 4);
-        } else {
-            const bool isv = j >= 2 * nK + nL;
-            const int row0 = (j - 2 * nK - (isv ? nL : 0)) * (64 >> g.lg_lr);
-            base = reinterpret_cast<const char *>((isv ? s.lv : s.lk) + (int64_t)(t0 + row0) * s.r);
-            uint32_t c = fl.lr_pr ^ swz_uniform(row0, g.cpa_lr, g.lg_lr);
-            c = c < (uint32_t)g.cpr_lr ? c : 0u;  // allocated-only chunk: any valid data (never read)
-            const uint32_t agent = c >> s.lr_es_shift;
-            off = fl.lr_rb + agent * (uint32_t)(s.lr_agent_stride * ES) + ((c - (agent << s.lr_es_shift)) << 4);
+    f.G = g.T >> 4;
+    f.g = wave % f.G;
+    const int per = 4 / f.G, sel = wave / f.G;
+    f.rK = 0 % per == sel;
+    f.rV = 1 % per == sel;
+    f.rL = resid && 2 % per == sel;
+    f.rLv = resid && 3 % per == sel;
+    f.n_kv = (16 * g.cpr_kv) >> 6;
+    f.n_lr = resid ? ((16 * g.cpa_lr + 63) >> 6) : 0;
+    f.fpw = (f.rK ? f.n_kv : 0) + (f.rV ? f.n_kv : 0) + (f.rL ? f.n_lr : 0) + (f.rLv ? f.n_lr : 0);
+#pragma unroll
+    for (int i = 0; i < kMaxKvLoads; ++i) {
+        const int q = 64 * i + lane;
+        const int row = q >> g.lg_kv;
+        const int c = swz(row, q & (g.cpr_kv - 1), g.cpr_kv, g.lg_kv);
+        f.kv_row[i] = row;
+        f.kv_off[i] = (uint32_t)(row * D * ES + 16 * c);
+    }
+    f.lr_stride = (uint32_t)(s.lr_agent_stride * ES);
+}
+
+// Lane byte offset of low-rank load i of a group (agent, row and chunk), and the
+// lane's row within the group.  Computed per load: a workgroup issues few.
+template <typename T>
+__device__ inline uint32_t lr_lane_off(const FillPlan &f, const Geo &g, const Src<T> &s, int i, int lane, int *row_out) {
+    constexpr int ES = (int)sizeof(T);
+    const int q = 64 * i + lane;
+    const int row = q >> g.lg_lr;
+    int c = swz(row, q & (g.cpa_lr - 1), g.cpa_lr, g.lg_lr);
+    c = c < g.cpr_lr ? c : 0;  // allocated-only chunk: any valid data (never read)
+    const int agent = c >> s.lr_es_shift;
+    const int cin = c - (agent << s.lr_es_shift);
+    *row_out = row < 16 ? row : 15;
+    return (uint32_t)(row * s.r * ES + 16 * cin) + (uint32_t)agent * f.lr_stride;
+}
+
+// Issues this wave's loads of the tile starting at token t0 into `stage`.
+// clamp: rows past the item's last token read that token instead (the tail
+// tile); otherwise every row is valid and a uniform base per region serves.
+// Always the same number of loads per wave (f.fpw), which the ring's waits count.
+template <typename T, int D>
+__device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan &f, const Geo &g, const Src<T> &s, int t0, char *stage, bool clamp,
+                                  int lane) {
+    constexpr int ES = (int)sizeof(T);
+    const int tg0 = t0 + 16 * f.g;  // the group's first token
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(stage));
+    if (!clamp) {
+        if (f.rK || f.rV) {
+            const char *kb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tg0)));
+            const char *vb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tg0)));
+#pragma unroll
+            for (int i = 0; i < kMaxKvLoads; ++i) {
+                if (i < f.n_kv && f.rK)
+                    dma16s(kb, f.kv_off[i], lds0 + 16 * (16 * f.g * g.cpr_kv) + 1024 * i);
+            }
+#pragma unroll
+            for (int i = 0; i < kMaxKvLoads; ++i) {
+                if (i < f.n_kv && f.rV)
+                    dma16s(vb, f.kv_off[i], lds0 + 16 * (g.ofs_v + 16 * f.g * g.cpr_kv) + 1024 * i);
+            }
         }
-        (void)kv_bytes;
-        dma16s(uniform_ptr(base), off, __builtin_amdgcn_readfirstlane(lds0 + 1024 * j));
+        if (f.rL || f.rLv) {
+            const char *lk = uniform_ptr(reinterpret_cast<const char *>(s.lk + (int64_t)tg0 * s.r));
+            const char *lv = uniform_ptr(reinterpret_cast<const char *>(s.lv + (int64_t)tg0 * s.r));
+            const int nchunk = 16 * g.cpa_lr;  // chunks of one group of a low-rank region
+            for (int i = 0; i < f.n_lr; ++i) {
+                if (64 * i + lane < nchunk) {
+                    int row;
+                    const uint32_t off = lr_lane_off(f, g, s, i, lane, &row);
+                    if (f.rL) dma16s(lk, off, lds0 + 16 * (g.ofs_lk + 16 * f.g * g.cpa_lr) + 1024 * i);
+                    if (f.rLv) dma16s(lv, off, lds0 + 16 * (g.ofs_lv + 16 * f.g * g.cpa_lr) + 1024 * i);
+                }
+            }
+        }
+        return;
+    }
+    // tail tile: per-lane rows, clamped to the item's last token
+#pragma unroll
+    for (int i = 0; i < kMaxKvLoads; ++i) {
+        if (i < f.n_kv && (f.rK || f.rV)) {
+            int tok = tg0 + f.kv_row[i];
+            tok = tok < s.tlast ? tok : s.tlast;
+            const uint32_t rowoff = f.kv_off[i] - (uint32_t)(f.kv_row[i] * D * ES);  // chunk part
+            if (f.rK)
+                dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tok)) + rowoff,
+                      lds0 + 16 * (16 * f.g * g.cpr_kv) + 1024 * i);
+            if (f.rV)
+                dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tok)) + rowoff,
+                      lds0 + 16 * (g.ofs_v + 16 * f.g * g.cpr_kv) + 1024 * i);
+        }
+    }
+    // (the loads are issued K then V per i here; the count per wave is the same)
+    const int nchunk = 16 * g.cpa_lr;
+    for (int i = 0; i < f.n_lr; ++i) {
+        if ((f.rL || f.rLv) && 64 * i + lane < nchunk) {
+            int row;
+            const uint32_t off = lr_lane_off(f, g, s, i, lane, &row);
+            int tok = tg0 + row;
+            tok = tok < s.tlast ? tok : s.tlast;
+            const uint32_t rel = off - (uint32_t)(row * s.r * ES);  // agent and chunk part
+            if (f.rL)
+                dma16(reinterpret_cast<const char *>(s.lk + (int64_t)tok * s.r) + rel,
+                      lds0 + 16 * (g.ofs_lk + 16 * f.g * g.cpa_lr) + 1024 * i);
+            if (f.rLv)
+                dma16(reinterpret_cast<const char *>(s.lv + (int64_t)tok * s.r) + rel,
+                      lds0 + 16 * (g.ofs_lv + 16 * f.g * g.cpa_lr) + 1024 * i);
+        }
     }
 }
 
@@ -622,23 +666,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         __syncthreads();
     }
 
-    // Lane constants of the fast fill and of the step's LDS reads.
-    FillLane fl;
-    {
-        const int rin = lane >> g.lg_kv, pp = lane & (g.cpr_kv - 1);
-        fl.kv_rb = (uint32_t)(rin * D * ES);
-        fl.kv_pr = (uint32_t)swz(rin, pp, g.cpr_kv, g.lg_kv);
-        if (resid) {
-            const int rl = lane >> g.lg_lr, pl = lane & (g.cpa_lr - 1);
-            fl.lr_rb = (uint32_t)(rl * src.r * ES);
-            fl.lr_pr = (uint32_t)swz(rl, pl, g.cpa_lr, g.lg_lr);
-        } else {
-            fl.lr_rb = fl.lr_pr = 0;
-        }
-    }
-    // fast fill: every region a whole number of instructions, low-rank offsets in 32 bits
-    const bool fast_ok = (g.T * g.cpr_kv) % 64 == 0 && (!resid || (g.T * g.cpa_lr) % 64 == 0) &&
-                         (!resid || p.lr_off32);
+    // The fill plan of this wave and the lane offsets of the step's LDS reads.
+    FillPlan fp;
+    make_fill_plan<T, D>(fp, g, src, resid, wave, lane);
     ReadOfs<T, D, CPAD> ro;
     {
         using RO = ReadOfs<T, D, CPAD>;
@@ -676,18 +706,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < KS; ++s) qB[s] = vm ? O::load8(qp + qrow * D + 32 * s + 8 * j4) : O::zero();
 
-    // ---- start the ring: tiles 0 .. nst-2
     const int n_tiles = (t1 - t0 + g.T - 1) / g.T;
-    const int fpw = fills_per_wave(g, wave);
+    const int fpw = fp.fpw;
     auto fill = [&](int tile, int stage) {
         const int tt = t0 + tile * g.T;
-        char *sp = smem + (size_t)stage * g.stage_bytes;
-        if (fast_ok && tt + g.T - 1 <= src.tlast)
-            fill_stage_fast<T, D>(g, src, fl, tt, sp, wave);
-        else
-            fill_stage_any<T, D>(g, src, tt, sp, wave, lane);
+        fill_stage<T, D>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
     };
-    for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
 
     // U = scale*log2(e) * q Bk^T as the B operand of the rank-r score correction,
     // block-diagonal over the agents of the block (bf16 carries hi + lo halves).
@@ -700,11 +724,56 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
         uH[s] = O::zero();
         uL[s] = O::zero();
     }
-    if (CPAD > 0 && resid && wave_on && n_tiles > 0) {
+    if (CPAD > 0 && resid && wave_on && n_tiles > 0 && !p.shared_lr) {
+        // Per-agent caches: one Bk row per A-operand row; every load is issued
+        // before the first MFMA (one memory round trip).
         const T *bk = static_cast<const T *>(p.bk);
         const int64_t ldb = (int64_t)p.HK * D;
         const int rmask = p.r - 1;
-        const int na_loop = p.shared_lr ? blk.na : 1;
+        frag bkf[CSx][2][KS];
+#pragma unroll
+        for (int s = 0; s < CSx; ++s)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int crow = 32 * s + 8 * (n16 >> 2) + 4 * h + (n16 & 3);  // A-operand row
+                const bool okc = crow < cvalid;
+                const int arow = blk.a0 + (okc ? (crow >> p.lr_shift) : 0);
+                const int colr = okc ? (crow & rmask) : 0;
+                const T *brow = bk + ((int64_t)arow * p.r + colr) * ldb + (int64_t)k * D + 8 * j4;
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) bkf[s][h][s2] = O::load8(brow + 32 * s2);
+            }
+#pragma unroll
+        for (int s = 0; s < CSx; ++s) {
+            float uv[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s2 = 0; s2 < KS; ++s2) a = O::mma(bkf[s][h][s2], qB[s2], a);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = 32 * s + 8 * j4 + 4 * h + i;  // column this lane received
+                    const bool keep = vm && c < cvalid && blk.a0 + (c >> p.lr_shift) == agent_m;
+                    uv[4 * h + i] = keep ? a[i] * cl2 : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                O::set(uH[s], i, uv[i]);
+                if constexpr (O::kSplitU) {
+                    const float hi = (float)(bf16)uv[i];
+                    O::set(uL[s], i, uv[i] - hi);
+                }
+            }
+        }
+    }
+    if (CPAD > 0 && resid && wave_on && n_tiles > 0 && p.shared_lr) {
+        // One cache for all agents: each agent of the block has its own Bk.
+        const T *bk = static_cast<const T *>(p.bk);
+        const int64_t ldb = (int64_t)p.HK * D;
+        const int rmask = p.r - 1;
+        const int na_loop = blk.na;
 #pragma unroll
         for (int s = 0; s < CSx; ++s) {
             float uv[8];
@@ -753,6 +822,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     // Every register load (q, Bk) has landed on every path, so the compiler has
     // nothing pending inside the ring loop and adds no waits of its own there.
     wait_vmcnt(0);
+
+    // ---- start the ring: tiles 0 .. nst-2
+    for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
 
     Acc<T, D, CPAD> acc;
 #pragma unroll

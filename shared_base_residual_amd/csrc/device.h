@@ -151,6 +151,7 @@ __device__ inline uint32_t lds_addr(const void *p) {
 // explicitly with wait_vmcnt before the stage is read.  One wait state between
 // the M0 write and the load.
 __device__ inline void dma16(const void *gsrc, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                  :
                  : "v"(gsrc), "s"(lds_base)
@@ -160,6 +161,7 @@ __device__ inline void dma16(const void *gsrc, uint32_t lds_base) {
 // The same with a wave-uniform 64-bit base (SGPR pair) and a per-lane 32-bit
 // byte offset (the instruction's saddr form).
 __device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
                  : "v"(voff), "s"(sbase), "s"(lds_base)

@@ -90,7 +90,6 @@ struct DecodeParams {
     int T_pre, nst_pre, stage_bytes_pre;
     int T_pv, nst_pv, stage_bytes_pv;
     int table_lds_off;
-    int lr_off32;     // the low-rank rows a workgroup reads span < 2^31 bytes (fast fill usable)
 };
 
 // Dynamic LDS a split workgroup may use (gfx950: 160 KiB per workgroup, less
