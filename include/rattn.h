@@ -129,8 +129,12 @@ int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace
 /*
  * Chunked prefill: agent a appends a chunk of C = priv_len = q_len new tokens
  * whose keys/values are k_priv/v_priv[a]; chunk query t attends the L prefix
- * tokens and chunk tokens 0..t (causal).  Same residual algebra and the same
- * workspace rules as rattn_decode (op = RATTN_OP_PREFILL for its size).
+ * tokens and chunk tokens 0..t (causal).  Same residual algebra as
+ * rattn_decode.  bf16 calls run one kernel that streams the whole context per
+ * block of 256 query rows and writes out/lse directly (no workspace:
+ * rattn_workspace_bytes(desc, RATTN_OP_PREFILL) is 0, and `workspace` may be
+ * NULL); fp32 calls, and paged prefixes of more than 2048 pages, run the split
+ * and merge launches of rattn_decode with the causal mask (workspace as there).
  */
 int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *workspace,
                         size_t workspace_bytes, void *stream);

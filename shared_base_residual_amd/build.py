@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librattn.so")
-SOURCES = ["api.cpp", "decode.hip", "gather.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "gather.hip"]
 ARCH = "gfx950"
 
 

@@ -14,6 +14,7 @@ hipError_t launch_decode(int bf16_in, const DecodeParams &dp, int D, int cpad, s
                          hipStream_t st);
 hipError_t launch_gather(const void *pool, const int32_t *table, void *dst, int64_t L, int HK, int ps,
                          int row_bytes, hipStream_t st);
+hipError_t launch_prefill(const PrefillParams &pp, int D, int cpad, size_t lds, hipStream_t st);
 }  // namespace rattn
 
 namespace {
@@ -238,6 +239,86 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     return RATTN_OK;
 }
 
+// ---- chunked prefill through its own kernel (bf16; a paged prefix whose
+// table fits in LDS).  Other prefill calls run on the split kernel with the
+// causal mask.
+struct PrefillPlan {
+    rattn::PrefillParams pp;
+    int cpad;
+    size_t lds;
+};
+
+bool prefill_direct(const rattn_desc *d) {
+    if (d->dtype != RATTN_BF16) return false;
+    if (d->page_size > 0 && d->prefix_len > 0 &&
+        (d->prefix_len - 1) / d->page_size + 1 > rattn::kMaxPagesPerSplit)
+        return false;
+    return true;
+}
+
+int make_prefill_plan(const rattn_desc *d, PrefillPlan *pl) {
+    rattn::PrefillParams &p = pl->pp;
+    p = rattn::PrefillParams{};
+    const int N = d->n_agents, HK = d->n_kv_heads, g = d->n_q_heads / d->n_kv_heads, r = d->rank;
+    const int D = d->head_dim;
+    const int64_t L = d->prefix_len, S = d->priv_len;
+    const bool resid = r > 0 && L > 0;
+    p.L = L;
+    p.S = S;
+    p.N = N;
+    p.QL = d->q_len;
+    p.HQ = d->n_q_heads;
+    p.HK = HK;
+    p.g = g;
+    p.r = resid ? r : 0;
+    p.lr_shift = 0;
+    while (r > 0 && (1 << p.lr_shift) < r) ++p.lr_shift;
+    p.ps = d->page_size;
+    p.shared_lr = d->shared_lr;
+    const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
+    p.c = scale * 1.44269504088896340736f;
+    p.rpa = d->q_len * g;
+    p.n_qb = (int)cdiv(p.rpa, rattn::kPrefillRows);
+    const int64_t items = (int64_t)HK * N * p.n_qb;
+    if (items > (1ll << 30)) return RATTN_E_UNSUPPORTED;
+    p.n_items = (int)items;
+    p.per_xcd = (int)cdiv(items, 8);
+    pl->cpad = resid ? (pow2ceil(r) < 32 ? 32 : pow2ceil(r)) : 0;
+
+    // LDS rings: prefix tiles (keys, values and the low-rank rows), chunk tiles
+    // (keys and values); kPrefillTile keys per stage, up to 8 stages.
+    const int es = (int)esize(d->dtype);
+    const int T = rattn::kPrefillTile;
+    const int kv_chunks = D * es / 16;
+    const int lr_chunks = resid ? pow2ceil(r * es / 16) : 0;
+    p.stage_bytes_pre = T * 16 * (2 * kv_chunks + 2 * lr_chunks);
+    p.stage_bytes_ch = T * 16 * (2 * kv_chunks);
+    auto nst_for = [](int sb) {
+        const int n = rattn::kLdsBudget / sb;
+        return n < 8 ? n : 8;
+    };
+    p.nst_pre = nst_for(p.stage_bytes_pre);
+    p.nst_ch = nst_for(p.stage_bytes_ch);
+    if (p.nst_pre < 2 || p.nst_ch < 2) return RATTN_E_UNSUPPORTED;
+    int lds = p.nst_pre * p.stage_bytes_pre;
+    if (p.nst_ch * p.stage_bytes_ch > lds) lds = p.nst_ch * p.stage_bytes_ch;
+    p.table_lds_off = lds;
+    if (d->page_size > 0 && L > 0) lds += (int)((L - 1) / d->page_size + 1) * 4;
+    if (lds > rattn::kLdsBudget) {
+        // shrink the rings to make room for the page table
+        const int room = rattn::kLdsBudget - (lds - p.table_lds_off);
+        p.nst_pre = room / p.stage_bytes_pre < 8 ? room / p.stage_bytes_pre : 8;
+        p.nst_ch = room / p.stage_bytes_ch < 8 ? room / p.stage_bytes_ch : 8;
+        if (p.nst_pre < 2 || p.nst_ch < 2) return RATTN_E_UNSUPPORTED;
+        int ring = p.nst_pre * p.stage_bytes_pre;
+        if (p.nst_ch * p.stage_bytes_ch > ring) ring = p.nst_ch * p.stage_bytes_ch;
+        lds = lds - p.table_lds_off + ring;
+        p.table_lds_off = ring;
+    }
+    pl->lds = (size_t)lds;
+    return RATTN_OK;
+}
+
 int check_args(const rattn_desc *d, const rattn_args *a) {
     if (!a) return RATTN_E_NULL;
     const bool paged = d->page_size > 0;
@@ -270,6 +351,26 @@ int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_
     if (st) return st;
     st = check_args(d, a);
     if (st) return st;
+    if (op == RATTN_OP_PREFILL && prefill_direct(d)) {
+        PrefillPlan pp;
+        st = make_prefill_plan(d, &pp);
+        if (st) return st;
+        rattn::PrefillParams &q = pp.pp;
+        q.q = a->q;
+        q.kb = a->k_base;
+        q.vb = a->v_base;
+        q.table = a->block_table;
+        q.lk = a->lk;
+        q.lv = a->lv;
+        q.bk = a->bk;
+        q.bv = a->bv;
+        q.kp = a->k_priv;
+        q.vp = a->v_priv;
+        q.out = a->out;
+        q.lse = a->lse;
+        if (!(stages & RATTN_STAGE_SPLIT)) return RATTN_OK;  // no merge pass on this path
+        return hip_status(rattn::launch_prefill(q, d->head_dim, pp.cpad, pp.lds, static_cast<hipStream_t>(stream)));
+    }
     Plan pl;
     st = make_plan(d, op, &pl);
     if (st) return st;
@@ -324,6 +425,13 @@ int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes) {
     if (!bytes) return RATTN_E_NULL;
     int st = check_desc(desc, op);
     if (st) return st;
+    if (op == RATTN_OP_PREFILL && prefill_direct(desc)) {
+        PrefillPlan pp;
+        st = make_prefill_plan(desc, &pp);
+        if (st) return st;
+        *bytes = 0;  // the prefill kernel needs no workspace
+        return RATTN_OK;
+    }
     Plan pl;
     st = make_plan(desc, op, &pl);
     if (st) return st;

@@ -99,3 +99,28 @@ constexpr int kLdsBudget = 160 * 1024 - 1024;
 constexpr int kMaxPagesPerSplit = 2048;
 
 }  // namespace rattn
+
+namespace rattn {
+
+// Chunked prefill: one workgroup per (KV head, agent, block of 256 query rows
+// of that agent), no split of the context.  Waves own 64 rows each (four
+// 16-row MFMA blocks).
+constexpr int kPrefillRows = 256;
+constexpr int kPrefillTile = 32;  // keys per LDS stage
+
+struct PrefillParams {
+    const void *q, *kb, *vb;
+    const int32_t *table;
+    const void *lk, *lv, *bk, *bv, *kp, *vp;
+    float *out, *lse;
+    int64_t L, S;     // prefix tokens, chunk tokens (= q_len)
+    int N, QL, HQ, HK, g, r, lr_shift, ps, shared_lr;
+    float c;          // softmax scale * log2(e)
+    int rpa;          // query rows per agent per KV head (q_len * g)
+    int n_qb;         // row blocks per (agent, KV head)
+    int n_items, per_xcd;
+    int nst_pre, stage_bytes_pre, nst_ch, stage_bytes_ch;
+    int table_lds_off;
+};
+
+}  // namespace rattn

@@ -1,0 +1,493 @@
+// prefill.hip -- chunked-prefill kernel of librattn (gfx950).
+//
+// Agent a appends a chunk of C tokens with private keys and values; chunk query
+// t attends the shared prefix (base keys/values plus the rank-r residual) and
+// chunk tokens 0..t.  The residual algebra is the decode kernel's (ForkKV Guide,
+// "Fused ResidualAttention"; LRAgent, "Flash-LoRA-Attention"):
+//   score  s = scale * (q . K_base[j] + (q Bk_a^T) . Lk[j])
+//   output o = sum_j p_j V[j] + (sum_j p_j Lv[j]) Bv_a
+// With BaseLRShared (LRAgent, "Schemi di Condivisione": the down-projection A is
+// shared) Lk and Lv are one cache for every agent, so the score correction is
+// one dense rank-r MFMA contraction per key tile, like the base product.
+//
+// This is MFMA-bound work (thousands of query rows per KV head), so a workgroup
+// takes 256 query rows of one (KV head, agent) and streams the whole context
+// once: the prefix, then the chunk with the causal mask, through the same LDS
+// ring as the decode kernel (direct global->LDS loads, several tiles in
+// flight).  Each of the four waves owns 64 rows (four 16-row MFMA blocks), so
+// every key tile read from LDS feeds 64 rows, and every tile fetched into LDS
+// feeds all 256.  Workgroups of one KV head run on one XCD (workgroup i runs on
+// XCD i % 8), where they share its tiles through that XCD's L2.
+//
+// Per 32 keys and wave: S^T = K Q^T (keys as the A operand, query rows as B),
+// + Lk U^T (U = scale*log2(e) q Bk_a^T as bf16 hi + lo halves), online softmax
+// in the log2 domain, O^T += V^T P^T and W^T += Lv^T P^T with P straight from
+// the score registers.  At the end O^T += Bv^T W^T (W as hi + lo halves), so Bv
+// is applied once per row, and o = O / l is written.  No split-K, no workspace.
+#include "device.h"
+#include "internal.h"
+#include "stage.h"
+
+namespace rattn {
+
+template <typename T, int D, int CPAD>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+    using O = Ops<T>;
+    using frag = typename O::frag;
+    constexpr int KS = D / 32;
+    constexpr int VPL = D / 16;
+    constexpr int CS = CPAD / 32;
+    constexpr int CSx = CS > 0 ? CS : 1;
+    constexpr int CPL = CPAD / 16;
+    constexpr int CPLx = CPL > 0 ? CPL : 1;
+    constexpr int ES = (int)sizeof(T);
+    constexpr int NCB = 4;  // 16-row blocks per wave
+
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n16 = lane & 15;
+    const int j4 = lane >> 4;
+
+    const int bid = blockIdx.x;
+    const int li = (bid & 7) * p.per_xcd + (bid >> 3);
+    if (li >= p.n_items) return;
+    // items: KV head slowest, so that consecutive items (one XCD) share a head
+    const int per_head = p.N * p.n_qb;
+    const int k = li / per_head;
+    const int rest = li - k * per_head;
+    const int a = rest / p.n_qb;
+    const int qb = rest - a * p.n_qb;
+    const int R0 = qb * kPrefillRows + wave * (NCB * 16);  // this wave's first row within (a, k)
+
+    const bool resid = CPAD > 0 && p.r > 0 && p.L > 0;
+    const float cl2 = p.c;
+
+    // ---- this lane's query row in each block, and the query rows as B operands
+    const T *qp = static_cast<const T *>(p.q);
+    bool vm[NCB];
+    int tq[NCB];
+    int64_t qrow[NCB];
+    frag qB[NCB][KS];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const int ria = R0 + 16 * cb + n16;
+        vm[cb] = ria < p.rpa;
+        const int rr = vm[cb] ? ria : 0;
+        tq[cb] = rr / p.g;
+        const int hh = rr - tq[cb] * p.g;
+        qrow[cb] = ((int64_t)a * p.QL + tq[cb]) * p.HQ + (int64_t)k * p.g + hh;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            qB[cb][s] = vm[cb] ? O::load8(qp + qrow[cb] * D + 32 * s + 8 * j4) : O::zero();
+    }
+    // last chunk token any row of the workgroup may see
+    int rmax = qb * kPrefillRows + kPrefillRows - 1;
+    rmax = rmax < p.rpa - 1 ? rmax : p.rpa - 1;
+    const int t_hi = rmax / p.g + 1;  // chunk keys [0, t_hi)
+
+    // ---- U = scale*log2(e) q Bk_a^T as the B operand of the rank-r score
+    // correction (bf16 hi + lo halves).  U^T = Bk Q^T with MFMA; A-operand row
+    // rho of output tile 2s+h is residual column 32s + 8(rho/4) + 4h + rho%4, so
+    // each lane's results land in its own B-operand slots.  The Bk rows are the
+    // same for all four blocks.
+    frag uH[NCB][CSx], uL[NCB][CSx];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int s = 0; s < CSx; ++s) {
+            uH[cb][s] = O::zero();
+            uL[cb][s] = O::zero();
+        }
+    if constexpr (CPAD > 0) {
+        if (resid) {
+            const T *bk = static_cast<const T *>(p.bk) + (int64_t)a * p.r * p.HK * D + (int64_t)k * D + 8 * j4;
+            const int64_t ldb = (int64_t)p.HK * D;
+#pragma unroll
+            for (int s = 0; s < CSx; ++s) {
+                frag bkf[2][KS];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    int crow = 32 * s + 8 * (n16 >> 2) + 4 * h + (n16 & 3);
+                    crow = crow < p.r ? crow : 0;
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2) bkf[h][s2] = O::load8(bk + crow * ldb + 32 * s2);
+                }
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    float uv[8];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int s2 = 0; s2 < KS; ++s2) acc = O::mma(bkf[h][s2], qB[cb][s2], acc);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int c = 32 * s + 8 * j4 + 4 * h + i;
+                            uv[4 * h + i] = (vm[cb] && c < p.r) ? acc[i] * cl2 : 0.0f;
+                        }
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        O::set(uH[cb][s], i, uv[i]);
+                        const float hi = (float)(bf16)uv[i];
+                        O::set(uL[cb][s], i, uv[i] - hi);
+                    }
+                }
+            }
+        }
+    }
+    wait_vmcnt(0);  // every register load has landed: nothing pending inside the rings
+
+    f32x4 o[NCB][VPL], w[NCB][CPLx];
+    float m[NCB], l[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) o[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < CPLx; ++i) w[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[cb] = -1.0e30f;
+        l[cb] = 0.0f;
+    }
+
+    int *s_pages = reinterpret_cast<int *>(smem + p.table_lds_off);
+    const int kv_rowb = D * ES;
+
+    // ---- one phase: the prefix (with residual) or the chunk (causal)
+    for (int phase = 0; phase < 2; ++phase) {
+        const bool pre = phase == 0;
+        const int t0 = 0;
+        const int t1 = pre ? (int)p.L : t_hi;
+        if (t1 <= 0) continue;
+        const bool res = pre && resid;
+        Geo g;
+        g.T = kPrefillTile;
+        g.nst = pre ? p.nst_pre : p.nst_ch;
+        g.stage_bytes = pre ? p.stage_bytes_pre : p.stage_bytes_ch;
+        g.cpr_kv = D * ES / 16;
+        g.lg_kv = ilog2(g.cpr_kv);
+        if (res) {
+            g.cpr_lr = p.r * ES / 16;
+            g.lg_lr = g.cpr_lr > 1 ? 32 - __builtin_clz(g.cpr_lr - 1) : 0;
+            g.cpa_lr = 1 << g.lg_lr;
+        } else {
+            g.cpr_lr = 0;
+            g.cpa_lr = 1;
+            g.lg_lr = 0;
+        }
+        g.ofs_v = g.T * g.cpr_kv;
+        g.ofs_lk = 2 * g.T * g.cpr_kv;
+        g.ofs_lv = g.ofs_lk + (res ? g.T * g.cpa_lr : 0);
+        g.chunks = g.ofs_lv + (res ? g.T * g.cpa_lr : 0);
+
+        Src<T> src;
+        src.tlast = t1 - 1;
+        src.r = p.r > 0 ? p.r : 1;
+        src.lr_es_shift = p.r > 0 ? ilog2(p.r * ES / 16) : 0;
+        src.lk = src.lv = nullptr;
+        src.lr_agent_stride = 0;
+        src.page_stride = 0;
+        src.ps = 16;
+        src.pg0 = 0;
+        src.pages = s_pages;
+        if (pre) {
+            src.kb = static_cast<const T *>(p.kb);
+            src.vb = static_cast<const T *>(p.vb);
+            if (p.ps > 0) {
+                src.page_stride = (int64_t)p.HK * p.ps * D;
+                src.ps = p.ps;
+                src.kb += (int64_t)k * p.ps * D;
+                src.vb += (int64_t)k * p.ps * D;
+                const int npg = (t1 - 1) / p.ps + 1;
+                for (int i = threadIdx.x; i < npg; i += 256) s_pages[i] = p.table[i];
+                __syncthreads();
+            } else {
+                src.kb += (int64_t)k * p.L * D;
+                src.vb += (int64_t)k * p.L * D;
+            }
+            if (res) {
+                const int64_t a_lr = p.shared_lr ? 0 : a;
+                src.lk = static_cast<const T *>(p.lk) + a_lr * p.L * p.r;
+                src.lv = static_cast<const T *>(p.lv) + a_lr * p.L * p.r;
+                src.lr_agent_stride = p.L * p.r;
+            }
+        } else {
+            const int64_t seg = ((int64_t)a * p.HK + k) * p.S * D;
+            src.kb = static_cast<const T *>(p.kp) + seg;
+            src.vb = static_cast<const T *>(p.vp) + seg;
+        }
+
+        FillPlan fp;
+        make_fill_plan<T, D>(fp, g, src, res, wave, lane);
+        ReadOfs<T, D, CPAD> ro;
+        {
+            using RO = ReadOfs<T, D, CPAD>;
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+#pragma unroll
+                for (int c = 0; c < RO::FC; ++c)
+                    ro.k[s][c] = elem_ofs(0, n16, (32 * s + 8 * j4) * ES + 16 * c, g.cpr_kv, g.lg_kv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < RO::VC; ++c)
+                    ro.v[i][c] = elem_ofs(g.ofs_v, 4 * j4 + i, VPL * n16 * ES + 16 * c, g.cpr_kv, g.lg_kv);
+#pragma unroll
+            for (int s = 0; s < RO::CSx; ++s) {
+                int col = 32 * s + 8 * j4;
+                col = col < p.r ? col : 0;  // padding column: U is zero there
+#pragma unroll
+                for (int c = 0; c < RO::FC; ++c)
+                    ro.lk[s][c] = res ? elem_ofs(g.ofs_lk, n16, col * ES + 16 * c, g.cpa_lr, g.lg_lr) : 0u;
+            }
+            int colv = RO::CPL * n16;
+            colv = colv < p.r ? colv : 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int c = 0; c < RO::LC; ++c)
+                    ro.lv[i][c] = res ? elem_ofs(g.ofs_lv, 4 * j4 + i, colv * ES + 16 * c, g.cpa_lr, g.lg_lr) : 0u;
+        }
+        const int lr_rowb = 16 * g.cpa_lr;
+        const int n_tiles = (t1 - t0 + g.T - 1) / g.T;
+        const int fpw = fp.fpw;
+        auto fill = [&](int tile, int stage) {
+            const int tt = t0 + tile * g.T;
+            fill_stage<T, D>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
+        };
+        for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
+
+        for (int it = 0; it < n_tiles; ++it) {
+            const int later = (n_tiles - 1 - it) < (g.nst - 2) ? (n_tiles - 1 - it) : (g.nst - 2);
+            wait_vmcnt(later * fpw);
+            ring_barrier();
+            if (it + g.nst - 1 < n_tiles) fill(it + g.nst - 1, (it + g.nst - 1) % g.nst);
+            const char *st = smem + (size_t)(it % g.nst) * g.stage_bytes;
+            const int tt = t0 + it * g.T;
+            const bool masked = !pre || tt + g.T > t1;
+
+            // scores of the two 16-key halves for the four row blocks
+            f32x4 sc[NCB][2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                frag kf[KS];
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    const Row<T, 8> kr = lds_get<T, 8>(st + 16 * h * kv_rowb, ro.k[s]);
+                    __builtin_memcpy(&kf[s], &kr, sizeof(frag));
+                }
+                frag lkf[CSx];
+                if constexpr (CPAD > 0) {
+                    if (res) {
+#pragma unroll
+                        for (int s = 0; s < CS; ++s) {
+                            const Row<T, 8> lr = lds_get<T, 8>(st + 16 * h * lr_rowb, ro.lk[s]);
+                            __builtin_memcpy(&lkf[s], &lr, sizeof(frag));
+                        }
+                    }
+                }
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) acc = O::mma(kf[s], qB[cb][s], acc);
+                    acc *= cl2;
+                    if constexpr (CPAD > 0) {
+                        if (res) {
+#pragma unroll
+                            for (int s = 0; s < CS; ++s) {
+                                acc = O::mma(lkf[s], uH[cb][s], acc);
+                                acc = O::mma(lkf[s], uL[cb][s], acc);
+                            }
+                        }
+                    }
+                    sc[cb][h] = acc;
+                }
+            }
+            if (masked) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int key = tt + 16 * h + 4 * j4 + i;
+                            if (key >= t1 || (!pre && key > tq[cb])) sc[cb][h][i] = -__builtin_inff();
+                        }
+            }
+
+            // online softmax per block (log2 domain); P as the B operand over 32 keys:
+            // slots 0..3 = keys 4*j4+i of the first half, 4..7 = the second half
+            frag pB[NCB];
+            float alpha[NCB];
+            bool any_grow = false;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) {
+                float mx = fmaxf(fmaxf(fmaxf(sc[cb][0][0], sc[cb][0][1]), fmaxf(sc[cb][0][2], sc[cb][0][3])),
+                                 fmaxf(fmaxf(sc[cb][1][0], sc[cb][1][1]), fmaxf(sc[cb][1][2], sc[cb][1][3])));
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const bool grow = mx > m[cb] + kRescaleSlack;
+                const float m_new = grow ? mx : m[cb];
+                alpha[cb] = fexp2(m[cb] - m_new);
+                m[cb] = m_new;
+                any_grow = any_grow || grow;
+                float psum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float e = fexp2(sc[cb][i >> 2][i & 3] - m_new);
+                    psum += e;
+                    O::set(pB[cb], i, e);
+                }
+                l[cb] = l[cb] * alpha[cb] + psum;
+            }
+            if (__builtin_amdgcn_ballot_w64(any_grow)) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                    for (int i = 0; i < VPL; ++i) o[cb][i] *= alpha[cb];
+#pragma unroll
+                    for (int i = 0; i < CPLx; ++i) w[cb][i] *= alpha[cb];
+                }
+            }
+
+            // O^T += V^T P^T (tile jj holds d = VPL*m + jj in row m), shared V operand
+            Row<T, VPL> vr[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vr[4 * h + i] = lds_get<T, VPL>(st + 16 * h * kv_rowb, ro.v[i]);
+#pragma unroll
+            for (int jj = 0; jj < VPL; ++jj) {
+                frag vA;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) O::set_raw(vA, i, vr[i].e[jj]);
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) o[cb][jj] = O::mma(vA, pB[cb], o[cb][jj]);
+            }
+            // W^T += Lv^T P^T
+            if constexpr (CPAD > 0) {
+                if (res) {
+                    Row<T, CPL> lr[8];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) lr[4 * h + i] = lds_get<T, CPL>(st + 16 * h * lr_rowb, ro.lv[i]);
+#pragma unroll
+                    for (int jj = 0; jj < CPL; ++jj) {
+                        frag wA;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) O::set_raw(wA, i, lr[i].e[jj]);
+#pragma unroll
+                        for (int cb = 0; cb < NCB; ++cb) w[cb][jj] = O::mma(wA, pB[cb], w[cb][jj]);
+                    }
+                }
+            }
+        }
+        // the ring is drained (the last iteration waited for every load); every wave
+        // must be done reading before the next phase refills the stages
+        __syncthreads();
+    }
+
+    // ---- epilogue: O^T += Bv^T W^T, o = O / l, written with lse
+    // Bv rows for the epilogue: for d-tile jj and
+    // contraction step s, lane (n16, j4) needs Bv[kappa][VPL*n16 + jj] for the 8
+    // residual columns kappa = 4*CPL*j4 + 8*s + i, which are the columns whose W
+    // this lane holds.
+    constexpr int NBS = CPL / 2 > 0 ? CPL / 2 : 1;  // contraction steps of 8 columns per lane group
+    Row<T, VPL> bvr[NBS][8];
+    if constexpr (CPAD > 0) {
+        if (resid) {
+            const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * p.r * p.HK * D + (int64_t)k * D + VPL * n16;
+            const int64_t ldb = (int64_t)p.HK * D;
+#pragma unroll
+            for (int s = 0; s < NBS; ++s)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    int kap = 4 * CPL * j4 + 8 * s + i;
+                    kap = kap < p.r ? kap : 0;
+                    bvr[s][i] = load_row<T, VPL>(bv + kap * ldb);
+                }
+        }
+    }
+    const float LN2 = 0.69314718055994530942f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        float lr = l[cb];
+        lr += __shfl_xor(lr, 16);
+        lr += __shfl_xor(lr, 32);
+        if constexpr (CPAD > 0) {
+            if (resid) {
+                // B operand: this lane's W (row n16, columns 4*CPL*j4 + 8*s + i), hi + lo
+#pragma unroll
+                for (int s = 0; s < NBS; ++s) {
+                    frag wH, wL;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int cc = 8 * s + i;  // = CPL * i' + jj' of the W^T tiles
+                        // padding columns (c >= r) hold P Lv of a stand-in column: drop them
+                        const bool real = 4 * CPL * j4 + cc < p.r;
+                        const float x = real ? w[cb][cc % CPLx][cc / CPLx] : 0.0f;
+                        const float hi = (float)(bf16)x;
+                        O::set(wH, i, x);
+                        O::set(wL, i, x - hi);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < VPL; ++jj) {
+                        frag bA;
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) O::set_raw(bA, i, bvr[s][i].e[jj]);
+                        o[cb][jj] = O::mma(bA, wH, o[cb][jj]);
+                        o[cb][jj] = O::mma(bA, wL, o[cb][jj]);
+                    }
+                }
+            }
+        }
+        if (vm[cb]) {
+            const float inv = 1.0f / lr;
+            float *po = p.out + qrow[cb] * D + 4 * VPL * j4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float ov[VPL];
+#pragma unroll
+                for (int jj = 0; jj < VPL; ++jj) ov[jj] = o[cb][jj][i] * inv;
+#pragma unroll
+                for (int c4 = 0; c4 < VPL / 4; ++c4)
+                    *reinterpret_cast<f32x4 *>(po + VPL * i + 4 * c4) =
+                        f32x4{ov[4 * c4], ov[4 * c4 + 1], ov[4 * c4 + 2], ov[4 * c4 + 3]};
+            }
+            if (j4 == 0 && p.lse) p.lse[qrow[cb]] = (m[cb] + __builtin_log2f(lr)) * LN2;
+        }
+    }
+}
+
+template <typename T, int D, int CP>
+static hipError_t launch_prefill_one(const PrefillParams &pp, size_t lds, hipStream_t st) {
+    auto *fn = prefill_kernel<T, D, CP>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, dim3(8 * pp.per_xcd), dim3(256), lds, st, pp);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill(const PrefillParams &pp, int D, int cpad, size_t lds, hipStream_t st) {
+    if (D == 128) {
+        switch (cpad) {
+            case 0: return launch_prefill_one<bf16, 128, 0>(pp, lds, st);
+            case 32: return launch_prefill_one<bf16, 128, 32>(pp, lds, st);
+            case 64: return launch_prefill_one<bf16, 128, 64>(pp, lds, st);
+            default: return launch_prefill_one<bf16, 128, 128>(pp, lds, st);
+        }
+    }
+    switch (cpad) {
+        case 0: return launch_prefill_one<bf16, 64, 0>(pp, lds, st);
+        case 32: return launch_prefill_one<bf16, 64, 32>(pp, lds, st);
+        case 64: return launch_prefill_one<bf16, 64, 64>(pp, lds, st);
+        default: return launch_prefill_one<bf16, 64, 128>(pp, lds, st);
+    }
+}
+
+}  // namespace rattn
