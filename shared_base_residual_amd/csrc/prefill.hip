@@ -14,14 +14,15 @@
 // takes 256 query rows of one (KV head, agent) and streams the whole context
 // once: the prefix, then the chunk with the causal mask, through the same LDS
 // ring as the decode kernel (direct global->LDS loads, several tiles in
-// flight).  Each of the four waves owns 64 rows (four 16-row MFMA blocks), so
-// every key tile read from LDS feeds 64 rows, and every tile fetched into LDS
-// feeds all 256.  Workgroups of one KV head run on one XCD (workgroup i runs on
-// XCD i % 8), where they share its tiles through that XCD's L2.
+// flight).  Each of the eight waves (two per SIMD, so one wave's MFMAs overlap
+// the other's softmax) owns 32 rows (two 16-row MFMA blocks); every tile
+// fetched into LDS feeds all 256 rows.  Workgroups of one KV head run on one
+// XCD (workgroup i runs on XCD i % 8), where they share its tiles through that
+// XCD's L2.
 //
 // Per 32 keys and wave: S^T = K Q^T (keys as the A operand, query rows as B),
-// + Lk U^T (U = scale*log2(e) q Bk_a^T as bf16 hi + lo halves), online softmax
-// in the log2 domain, O^T += V^T P^T and W^T += Lv^T P^T with P straight from
+// + Lk U^T (U = q Bk_a^T as bf16 hi + lo halves), online softmax in the log2
+// domain with the scale folded into the exponent (exp2(s * scale*log2(e) - m)), O^T += V^T P^T and W^T += Lv^T P^T with P straight from
 // the score registers.  At the end O^T += Bv^T W^T (W as hi + lo halves), so Bv
 // is applied once per row, and o = O / l is written.  No split-K, no workspace.
 #include "device.h"
@@ -31,7 +32,7 @@
 namespace rattn {
 
 template <typename T, int D, int CPAD>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     using O = Ops<T>;
     using frag = typename O::frag;
     constexpr int KS = D / 32;
@@ -41,7 +42,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     constexpr int CPL = CPAD / 16;
     constexpr int CPLx = CPL > 0 ? CPL : 1;
     constexpr int ES = (int)sizeof(T);
-    constexpr int NCB = 4;  // 16-row blocks per wave
+    constexpr int NCB = 2;  // 16-row blocks per wave
+    constexpr int NW = kPrefillRows / (16 * NCB);  // waves per workgroup
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -87,11 +89,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
     rmax = rmax < p.rpa - 1 ? rmax : p.rpa - 1;
     const int t_hi = rmax / p.g + 1;  // chunk keys [0, t_hi)
 
-    // ---- U = scale*log2(e) q Bk_a^T as the B operand of the rank-r score
+    // ---- U = q Bk_a^T as the B operand of the rank-r score
     // correction (bf16 hi + lo halves).  U^T = Bk Q^T with MFMA; A-operand row
     // rho of output tile 2s+h is residual column 32s + 8(rho/4) + 4h + rho%4, so
     // each lane's results land in its own B-operand slots.  The Bk rows are the
-    // same for all four blocks.
+    // same for both blocks.
     frag uH[NCB][CSx], uL[NCB][CSx];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb)
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int c = 32 * s + 8 * j4 + 4 * h + i;
-                            uv[4 * h + i] = (vm[cb] && c < p.r) ? acc[i] * cl2 : 0.0f;
+                            uv[4 * h + i] = (vm[cb] && c < p.r) ? acc[i] : 0.0f;
                         }
                     }
 #pragma unroll
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                 src.kb += (int64_t)k * p.ps * D;
                 src.vb += (int64_t)k * p.ps * D;
                 const int npg = (t1 - 1) / p.ps + 1;
-                for (int i = threadIdx.x; i < npg; i += 256) s_pages[i] = p.table[i];
+                for (int i = threadIdx.x; i < npg; i += 64 * NW) s_pages[i] = p.table[i];
                 __syncthreads();
             } else {
                 src.kb += (int64_t)k * p.L * D;
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
         }
 
         FillPlan fp;
-        make_fill_plan<T, D>(fp, g, src, res, wave, lane);
+        make_fill_plan<T, D>(fp, g, src, res, wave, lane, NW);
         ReadOfs<T, D, CPAD> ro;
         {
             using RO = ReadOfs<T, D, CPAD>;
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
             const int tt = t0 + it * g.T;
             const bool masked = !pre || tt + g.T > t1;
 
-            // scores of the two 16-key halves for the four row blocks
+            // raw scores (unscaled) of the two 16-key halves for the row blocks
             f32x4 sc[NCB][2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -293,7 +295,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int s = 0; s < KS; ++s) acc = O::mma(kf[s], qB[cb][s], acc);
-                    acc *= cl2;
                     if constexpr (CPAD > 0) {
                         if (res) {
 #pragma unroll
@@ -329,6 +330,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                                  fmaxf(fmaxf(sc[cb][1][0], sc[cb][1][1]), fmaxf(sc[cb][1][2], sc[cb][1][3])));
                 mx = fmaxf(mx, __shfl_xor(mx, 16));
                 mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx *= cl2;  // scaled (log2 units); -inf stays -inf
                 const bool grow = mx > m[cb] + kRescaleSlack;
                 const float m_new = grow ? mx : m[cb];
                 alpha[cb] = fexp2(m[cb] - m_new);
@@ -337,7 +339,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p) {
                 float psum = 0.0f;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float e = fexp2(sc[cb][i >> 2][i & 3] - m_new);
+                    const float e = fexp2(__builtin_fmaf(sc[cb][i >> 2][i & 3], cl2, -m_new));
                     psum += e;
                     O::set(pB[cb], i, e);
                 }
@@ -469,7 +471,7 @@ static hipError_t launch_prefill_one(const PrefillParams &pp, size_t lds, hipStr
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(8 * pp.per_xcd), dim3(256), lds, st, pp);
+    hipLaunchKernelGGL(fn, dim3(8 * pp.per_xcd), dim3(kPrefillRows / 32 * 64), lds, st, pp);
     return hipGetLastError();
 }
 

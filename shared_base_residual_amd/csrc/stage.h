@@ -51,7 +51,7 @@ __device__ inline const T *kv_row(const Src<T> &s, const T *base, int tok) {
 // A stage holds four regions of the tile: K rows, V rows, Lk rows, Lv rows (the
 // last two only with a residual).  The tile's rows are cut into 16-row groups;
 // wave w fills group w % G (G = T / 16) of the regions r with
-// r % (4 / G) == w / G, so every wave of the workgroup fills a fixed part: one
+// (r * G + w % G) % nw == w (nw waves), so every wave fills a fixed part: one
 // page lookup and one uniform base per region and tile, and lane offsets that
 // depend on the lane only (the swizzle repeats every 16 rows).  Each direct load
 // moves 64 chunks of 16 bytes; a region row of cpa chunks gives 16 * cpa chunks
@@ -72,15 +72,18 @@ struct FillPlan {
 };
 
 template <typename T, int D>
-__device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f, const Geo &g, const Src<T> &s, bool resid, int wave, int lane) {
+__device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f, const Geo &g, const Src<T> &s,
+                                                                     bool resid, int wave, int lane, int nw = 4) {
     constexpr int ES = (int)sizeof(T);
+    // (group, region) pairs pi = region * G + group go round-robin to the waves:
+    // wave w fills the pairs with pi % nw == w (nw a multiple of G)
     f.G = g.T >> 4;
     f.g = wave % f.G;
-    const int per = 4 / f.G, sel = wave / f.G;
-    f.rK = 0 % per == sel;
-    f.rV = 1 % per == sel;
-    f.rL = resid && 2 % per == sel;
-    f.rLv = resid && 3 % per == sel;
+    auto mine = [&](int region) { return (region * f.G + f.g) % nw == wave; };
+    f.rK = mine(0);
+    f.rV = mine(1);
+    f.rL = resid && mine(2);
+    f.rLv = resid && mine(3);
     f.n_kv = (16 * g.cpr_kv) >> 6;
     f.n_lr = resid ? ((16 * g.cpa_lr + 63) >> 6) : 0;
     f.fpw = (f.rK ? f.n_kv : 0) + (f.rV ? f.n_kv : 0) + (f.rL ? f.n_lr : 0) + (f.rLv ? f.n_lr : 0);
