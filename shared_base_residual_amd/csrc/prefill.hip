@@ -22,8 +22,9 @@
 //
 // Per 32 keys and wave: S^T = K Q^T (keys as the A operand, query rows as B),
 // + Lk U^T (U = q Bk_a^T as bf16 hi + lo halves), online softmax in the log2
-// domain with the scale folded into the exponent (exp2(s * scale*log2(e) - m)), O^T += V^T P^T and W^T += Lv^T P^T with P straight from
-// the score registers.  At the end O^T += Bv^T W^T (W as hi + lo halves), so Bv
+// domain with the scale folded into the exponent (exp2(s * scale*log2(e) - m)),
+// O^T += V^T P^T and W^T += Lv^T P^T with P straight from the score registers.
+// At the end O^T += Bv^T W^T (W as hi + lo halves), so Bv
 // is applied once per row, and o = O / l is written.  No split-K, no workspace.
 #include "device.h"
 #include "internal.h"
