@@ -6,7 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/rattn.h"
+#include "rattn.h"
 #include "internal.h"
 
 namespace rattn {

@@ -114,6 +114,18 @@ struct Ops<float> {
 
 __device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane p supplies the address of 4 consecutive 16-bit elements x_p[0..3];
+// lane 4a + b receives {x_{4i+a}[b] : i = 0..3}.  With lane 4i + a pointing at
+// row i, columns c + 4a of a row-major tile, lane 4a + b gets column c + 4a + b
+// of rows 0..3: a 4-long column segment, as an MFMA operand wants it.
+__device__ inline bf16x4 lds_tr4(const void *p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(__attribute__((address_space(3))) char *)p);
+    return __builtin_bit_cast(bf16x4, v);
+}
+
 // Device-coherent (agent-scope) 4-byte store and load: on gfx950 these are
 // global_store/global_load with the device scope bit, so a value stored by one
 // XCD is read back by another without L2 writeback or invalidation.

@@ -106,7 +106,7 @@ namespace rattn {
 // of that agent), no split of the context.  Waves own 64 rows each (four
 // 16-row MFMA blocks).
 constexpr int kPrefillRows = 256;
-constexpr int kPrefillTile = 32;  // keys per LDS stage
+constexpr int kPrefillTile = 64;  // keys per LDS stage
 
 struct PrefillParams {
     const void *q, *kb, *vb;

@@ -253,6 +253,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                 for (int c = 0; c < RO::LC; ++c)
                     ro.lv[i][c] = res ? elem_ofs(g.ofs_lv, 4 * j4 + i, colv * ES + 16 * c, g.cpa_lr, g.lg_lr) : 0u;
         }
+        // transposed value reads: for d-tile jj, lane 4i + a of group j4 points at
+        // key row 4*j4 + i, columns 16*jj + 4a (the other 16 keys: +16 rows)
+        uint32_t vtr[VPL];
+#pragma unroll
+        for (int jj = 0; jj < VPL; ++jj)
+            vtr[jj] = elem_ofs(g.ofs_v, 4 * j4 + (n16 >> 2), 2 * (16 * jj + 4 * (n16 & 3)), g.cpr_kv, g.lg_kv);
         const int lr_rowb = 16 * g.cpa_lr;
         const int n_tiles = (t1 - t0 + g.T - 1) / g.T;
         const int fpw = fp.fpw;
@@ -271,122 +277,127 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
             const int tt = t0 + it * g.T;
             const bool masked = !pre || tt + g.T > t1;
 
-            // raw scores (unscaled) of the two 16-key halves for the row blocks
-            f32x4 sc[NCB][2];
+            // 32 keys at a time: two 16-key halves per step
+            for (int sub = 0; sub < g.T / 32; ++sub) {
+                const char *stk = st + 32 * sub * kv_rowb;
+                const char *stl = st + 32 * sub * lr_rowb;
+                const int tk = tt + 32 * sub;
+                // raw scores (unscaled) of the two 16-key halves for the row blocks
+                f32x4 sc[NCB][2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                frag kf[KS];
+                for (int h = 0; h < 2; ++h) {
+                    frag kf[KS];
 #pragma unroll
-                for (int s = 0; s < KS; ++s) {
-                    const Row<T, 8> kr = lds_get<T, 8>(st + 16 * h * kv_rowb, ro.k[s]);
-                    __builtin_memcpy(&kf[s], &kr, sizeof(frag));
-                }
-                frag lkf[CSx];
-                if constexpr (CPAD > 0) {
-                    if (res) {
-#pragma unroll
-                        for (int s = 0; s < CS; ++s) {
-                            const Row<T, 8> lr = lds_get<T, 8>(st + 16 * h * lr_rowb, ro.lk[s]);
-                            __builtin_memcpy(&lkf[s], &lr, sizeof(frag));
-                        }
+                    for (int s = 0; s < KS; ++s) {
+                        const Row<T, 8> kr = lds_get<T, 8>(stk + 16 * h * kv_rowb, ro.k[s]);
+                        __builtin_memcpy(&kf[s], &kr, sizeof(frag));
                     }
-                }
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < KS; ++s) acc = O::mma(kf[s], qB[cb][s], acc);
+                    frag lkf[CSx];
                     if constexpr (CPAD > 0) {
                         if (res) {
 #pragma unroll
                             for (int s = 0; s < CS; ++s) {
-                                acc = O::mma(lkf[s], uH[cb][s], acc);
-                                acc = O::mma(lkf[s], uL[cb][s], acc);
+                                const Row<T, 8> lr = lds_get<T, 8>(stl + 16 * h * lr_rowb, ro.lk[s]);
+                                __builtin_memcpy(&lkf[s], &lr, sizeof(frag));
                             }
                         }
                     }
-                    sc[cb][h] = acc;
-                }
-            }
-            if (masked) {
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int h = 0; h < 2; ++h)
+                        for (int s = 0; s < KS; ++s) acc = O::mma(kf[s], qB[cb][s], acc);
+                        if constexpr (CPAD > 0) {
+                            if (res) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int key = tt + 16 * h + 4 * j4 + i;
-                            if (key >= t1 || (!pre && key > tq[cb])) sc[cb][h][i] = -__builtin_inff();
+                                for (int s = 0; s < CS; ++s) {
+                                    acc = O::mma(lkf[s], uH[cb][s], acc);
+                                    acc = O::mma(lkf[s], uL[cb][s], acc);
+                                }
+                            }
                         }
-            }
-
-            // online softmax per block (log2 domain); P as the B operand over 32 keys:
-            // slots 0..3 = keys 4*j4+i of the first half, 4..7 = the second half
-            frag pB[NCB];
-            float alpha[NCB];
-            bool any_grow = false;
-#pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) {
-                float mx = fmaxf(fmaxf(fmaxf(sc[cb][0][0], sc[cb][0][1]), fmaxf(sc[cb][0][2], sc[cb][0][3])),
-                                 fmaxf(fmaxf(sc[cb][1][0], sc[cb][1][1]), fmaxf(sc[cb][1][2], sc[cb][1][3])));
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                mx *= cl2;  // scaled (log2 units); -inf stays -inf
-                const bool grow = mx > m[cb] + kRescaleSlack;
-                const float m_new = grow ? mx : m[cb];
-                alpha[cb] = fexp2(m[cb] - m_new);
-                m[cb] = m_new;
-                any_grow = any_grow || grow;
-                float psum = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float e = fexp2(__builtin_fmaf(sc[cb][i >> 2][i & 3], cl2, -m_new));
-                    psum += e;
-                    O::set(pB[cb], i, e);
-                }
-                l[cb] = l[cb] * alpha[cb] + psum;
-            }
-            if (__builtin_amdgcn_ballot_w64(any_grow)) {
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-                    for (int i = 0; i < VPL; ++i) o[cb][i] *= alpha[cb];
-#pragma unroll
-                    for (int i = 0; i < CPLx; ++i) w[cb][i] *= alpha[cb];
-                }
-            }
-
-            // O^T += V^T P^T (tile jj holds d = VPL*m + jj in row m), shared V operand
-            Row<T, VPL> vr[8];
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vr[4 * h + i] = lds_get<T, VPL>(st + 16 * h * kv_rowb, ro.v[i]);
-#pragma unroll
-            for (int jj = 0; jj < VPL; ++jj) {
-                frag vA;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) O::set_raw(vA, i, vr[i].e[jj]);
-#pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) o[cb][jj] = O::mma(vA, pB[cb], o[cb][jj]);
-            }
-            // W^T += Lv^T P^T
-            if constexpr (CPAD > 0) {
-                if (res) {
-                    Row<T, CPL> lr[8];
-#pragma unroll
-                    for (int h = 0; h < 2; ++h)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) lr[4 * h + i] = lds_get<T, CPL>(st + 16 * h * lr_rowb, ro.lv[i]);
-#pragma unroll
-                    for (int jj = 0; jj < CPL; ++jj) {
-                        frag wA;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) O::set_raw(wA, i, lr[i].e[jj]);
-#pragma unroll
-                        for (int cb = 0; cb < NCB; ++cb) w[cb][jj] = O::mma(wA, pB[cb], w[cb][jj]);
+                        sc[cb][h] = acc;
                     }
                 }
+                if (masked) {
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int key = tk + 16 * h + 4 * j4 + i;
+                                if (key >= t1 || (!pre && key > tq[cb])) sc[cb][h][i] = -__builtin_inff();
+                            }
+                }
+
+                // online softmax per block (log2 domain); P as the B operand over 32 keys:
+                // slots 0..3 = keys 4*j4+i of the first half, 4..7 = the second half
+                frag pB[NCB];
+                float alpha[NCB];
+                bool any_grow = false;
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    float mx = fmaxf(fmaxf(fmaxf(sc[cb][0][0], sc[cb][0][1]), fmaxf(sc[cb][0][2], sc[cb][0][3])),
+                                     fmaxf(fmaxf(sc[cb][1][0], sc[cb][1][1]), fmaxf(sc[cb][1][2], sc[cb][1][3])));
+                    mx = fmaxf(mx, __shfl_xor(mx, 16));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32));
+                    mx *= cl2;  // scaled (log2 units); -inf stays -inf
+                    const bool grow = mx > m[cb] + kRescaleSlack;
+                    const float m_new = grow ? mx : m[cb];
+                    alpha[cb] = fexp2(m[cb] - m_new);
+                    m[cb] = m_new;
+                    any_grow = any_grow || grow;
+                    float psum = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const float e = fexp2(__builtin_fmaf(sc[cb][i >> 2][i & 3], cl2, -m_new));
+                        psum += e;
+                        O::set(pB[cb], i, e);
+                    }
+                    l[cb] = l[cb] * alpha[cb] + psum;
+                }
+                if (__builtin_amdgcn_ballot_w64(any_grow)) {
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+                        for (int i = 0; i < VPL; ++i) o[cb][i] *= alpha[cb];
+#pragma unroll
+                        for (int i = 0; i < CPLx; ++i) w[cb][i] *= alpha[cb];
+                    }
+                }
+
+                // O^T += V^T P^T (tile jj holds d = 16*jj + m in row m), shared V
+                // operand read transposed from LDS: slots 0..3 = keys 4*j4+i of the
+                // first half, 4..7 = the second half, like P
+#pragma unroll
+                for (int jj = 0; jj < VPL; ++jj) {
+                    const bf16x4 v0 = lds_tr4(stk + vtr[jj]);
+                    const bf16x4 v1 = lds_tr4(stk + 16 * kv_rowb + vtr[jj]);
+                    frag vA;
+                    vA.v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) o[cb][jj] = O::mma(vA, pB[cb], o[cb][jj]);
+                }
+                // W^T += Lv^T P^T
+                if constexpr (CPAD > 0) {
+                    if (res) {
+                        Row<T, CPL> lr[8];
+#pragma unroll
+                        for (int h = 0; h < 2; ++h)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) lr[4 * h + i] = lds_get<T, CPL>(stl + 16 * h * lr_rowb, ro.lv[i]);
+#pragma unroll
+                        for (int jj = 0; jj < CPL; ++jj) {
+                            frag wA;
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) O::set_raw(wA, i, lr[i].e[jj]);
+#pragma unroll
+                            for (int cb = 0; cb < NCB; ++cb) w[cb][jj] = O::mma(wA, pB[cb], w[cb][jj]);
+                        }
+                    }
+                }
+        
             }
         }
         // the ring is drained (the last iteration waited for every load); every wave
@@ -395,24 +406,25 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     }
 
     // ---- epilogue: O^T += Bv^T W^T, o = O / l, written with lse
-    // Bv rows for the epilogue: for d-tile jj and
-    // contraction step s, lane (n16, j4) needs Bv[kappa][VPL*n16 + jj] for the 8
-    // residual columns kappa = 4*CPL*j4 + 8*s + i, which are the columns whose W
-    // this lane holds.
+    // Bv as the A operand of O^T += Bv^T W^T: for d-tile jj and contraction step
+    // s, lane (n16, j4) supplies Bv[kappa][16*jj + n16] for the 8 residual
+    // columns kappa = 4*CPL*j4 + 8*s + i, the columns whose W this lane holds.
     constexpr int NBS = CPL / 2 > 0 ? CPL / 2 : 1;  // contraction steps of 8 columns per lane group
-    Row<T, VPL> bvr[NBS][8];
+    frag bvf[NBS][VPL];
     if constexpr (CPAD > 0) {
         if (resid) {
-            const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * p.r * p.HK * D + (int64_t)k * D + VPL * n16;
+            const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * p.r * p.HK * D + (int64_t)k * D + n16;
             const int64_t ldb = (int64_t)p.HK * D;
 #pragma unroll
             for (int s = 0; s < NBS; ++s)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    int kap = 4 * CPL * j4 + 8 * s + i;
-                    kap = kap < p.r ? kap : 0;
-                    bvr[s][i] = load_row<T, VPL>(bv + kap * ldb);
-                }
+                for (int jj = 0; jj < VPL; ++jj)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        int kap = 4 * CPL * j4 + 8 * s + i;
+                        kap = kap < p.r ? kap : 0;
+                        O::set_raw(bvf[s][jj], i, bv[kap * ldb + 16 * jj]);
+                    }
         }
     }
     const float LN2 = 0.69314718055994530942f;
@@ -439,28 +451,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                     }
 #pragma unroll
                     for (int jj = 0; jj < VPL; ++jj) {
-                        frag bA;
-#pragma unroll
-                        for (int i = 0; i < 8; ++i) O::set_raw(bA, i, bvr[s][i].e[jj]);
-                        o[cb][jj] = O::mma(bA, wH, o[cb][jj]);
-                        o[cb][jj] = O::mma(bA, wL, o[cb][jj]);
+                        o[cb][jj] = O::mma(bvf[s][jj], wH, o[cb][jj]);
+                        o[cb][jj] = O::mma(bvf[s][jj], wL, o[cb][jj]);
                     }
                 }
             }
         }
         if (vm[cb]) {
             const float inv = 1.0f / lr;
-            float *po = p.out + qrow[cb] * D + 4 * VPL * j4;
+            // tile jj, element i of this lane: d = 16*jj + 4*j4 + i
+            float *po = p.out + qrow[cb] * D + 4 * j4;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float ov[VPL];
-#pragma unroll
-                for (int jj = 0; jj < VPL; ++jj) ov[jj] = o[cb][jj][i] * inv;
-#pragma unroll
-                for (int c4 = 0; c4 < VPL / 4; ++c4)
-                    *reinterpret_cast<f32x4 *>(po + VPL * i + 4 * c4) =
-                        f32x4{ov[4 * c4], ov[4 * c4 + 1], ov[4 * c4 + 2], ov[4 * c4 + 3]};
-            }
+            for (int jj = 0; jj < VPL; ++jj) *reinterpret_cast<f32x4 *>(po + 16 * jj) = o[cb][jj] * inv;
             if (j4 == 0 && p.lse) p.lse[qrow[cb]] = (m[cb] + __builtin_log2f(lr)) * LN2;
         }
     }
