@@ -150,6 +150,110 @@ __device__ inline void step16(Acc<T, D, CPAD> &acc, const ReadOfs<T, D, CPAD> &r
     }
 }
 
+// The bf16 step: the same contraction with every LDS operand read issued before
+// the first MFMA that needs it, raw (unscaled) scores with the scale folded into
+// the exponent, a VALU cross-lane maximum, and the value operands (V and Lv)
+// read with gfx950's transposing LDS read, so that output tile jj holds
+// d = 16*jj + m in row m (lane (n16, j4) holds d = 16*jj + 4*j4 + i).
+// vtr / wtr: lane offsets of the transposed V and Lv reads; U (uH, uL) is
+// unscaled.
+template <int D, int CPAD>
+__device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, D, CPAD> &ro, const uint32_t *vtr,
+                                   const uint32_t *wtr, const char *kvb, const char *lrb, int t, bool masked,
+                                   const Ops<bf16>::frag *qB, const Ops<bf16>::frag *uH, const Ops<bf16>::frag *uL,
+                                   float cl2, bool resid, int t1, bool causal, int tq, int j4) {
+    using O = Ops<bf16>;
+    using frag = O::frag;
+    using frag4 = O::frag4;
+    constexpr int KS = D / 32, VPL = D / 16;
+    constexpr int CS = CPAD / 32, CPL = CPAD / 16;
+    constexpr int CSx = CS > 0 ? CS : 1;
+
+    frag kf[KS], lf[CSx];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const Row<bf16, 8> kr = lds_get<bf16, 8>(kvb, ro.k[s]);
+        __builtin_memcpy(&kf[s], &kr, sizeof(frag));
+    }
+    if (CS > 0 && resid) {
+#pragma unroll
+        for (int s = 0; s < CS; ++s) {
+            const Row<bf16, 8> lr = lds_get<bf16, 8>(lrb, ro.lk[s]);
+            __builtin_memcpy(&lf[s], &lr, sizeof(frag));
+        }
+    }
+    // S^T = K Q^T + Lk U^T, raw
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) a = O::mma(kf[s], qB[s], a);
+    if (CS > 0 && resid) {
+#pragma unroll
+        for (int s = 0; s < CS; ++s) {
+            a = O::mma(lf[s], uH[s], a);
+            a = O::mma(lf[s], uL[s], a);
+        }
+    }
+    // value operands: issued now, consumed after the softmax
+    bf16x4 va[VPL];
+#pragma unroll
+    for (int jj = 0; jj < VPL; ++jj) va[jj] = lds_tr4(kvb + vtr[jj]);
+    bf16x4 wa[CPL > 0 ? CPL : 1];
+    if constexpr (CPL > 0) {
+        if (resid) {
+#pragma unroll
+            for (int jj = 0; jj < CPL; ++jj) wa[jj] = lds_tr4(lrb + wtr[jj]);
+        }
+    }
+    if (masked) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tt = t + 4 * j4 + i;
+            if (tt >= t1 || (causal && tt > tq)) a[i] = -__builtin_inff();
+        }
+    }
+
+    // online softmax (log2 domain, running max in scaled units)
+    float mx = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
+    mx = row_max4(mx) * cl2;  // -inf stays -inf
+    const bool grow = mx > acc.m + kRescaleSlack;
+    float alpha = 1.0f;
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mx : acc.m;
+        alpha = fexp2(acc.m - m_new);
+        acc.m = m_new;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) acc.o[i] *= alpha;
+        if constexpr (CPAD > 0) {
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) acc.w[i] *= alpha;
+        }
+    }
+    f32x4 ev;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ev[i] = fexp2(__builtin_fmaf(a[i], cl2, -acc.m));
+    frag4 pB;
+    pB.v = to_bf16x4(ev[0], ev[1], ev[2], ev[3]);
+    acc.l = acc.l * alpha + ((ev[0] + ev[1]) + (ev[2] + ev[3]));
+
+    // O^T += V^T P^T and W^T += Lv^T P^T
+#pragma unroll
+    for (int jj = 0; jj < VPL; ++jj) {
+        frag4 vA;
+        vA.v = va[jj];
+        acc.o[jj] = O::mma16(vA, pB, acc.o[jj]);
+    }
+    if constexpr (CPL > 0) {
+        if (resid) {
+#pragma unroll
+            for (int jj = 0; jj < CPL; ++jj) {
+                frag4 wA;
+                wA.v = wa[jj];
+                acc.w[jj] = O::mma16(wA, pB, acc.w[jj]);
+            }
+        }
+    }
+}
+
 // ------------------------------------------------------------------- merge --
 
 // One wavefront merges the splits of one query row and writes out/lse.  Every
@@ -456,6 +560,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     // The fill plan of this wave and the lane offsets of the step's LDS reads.
     FillPlan fp;
     make_fill_plan<T, D>(fp, g, src, resid, wave, lane);
+    // keys and values that no other workgroup reads are streamed past the caches
+    fp.kv_nt = prefix ? p.n_rg == 1 : p.n_prg == 1;
     ReadOfs<T, D, CPAD> ro;
     {
         using RO = ReadOfs<T, D, CPAD>;
@@ -486,6 +592,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 ro.lv[i][c] = resid ? elem_ofs(g.ofs_lv, 4 * j4 + i, colv * ES + 16 * c, g.cpa_lr, g.lg_lr) : 0u;
     }
     const int kv_rowb = D * ES, lr_rowb = 16 * g.cpa_lr;
+    // bf16 step: transposed value reads.  For d-tile jj, lane (4i + a, j4) points at
+    // row 4*j4 + i, columns 16*jj + 4a (residual columns of the block; padding
+    // columns read column 0 of the block, their W is dropped at the store).
+    uint32_t vtr[VPL], wtr[CPLx];
+#pragma unroll
+    for (int jj = 0; jj < VPL; ++jj)
+        vtr[jj] = elem_ofs(g.ofs_v, 4 * j4 + (n16 >> 2), ES * (16 * jj + 4 * (n16 & 3)), g.cpr_kv, g.lg_kv);
+#pragma unroll
+    for (int jj = 0; jj < CPLx; ++jj) {
+        int col = 16 * jj + 4 * (n16 & 3);
+        col = lr_col0 + (col < cvalid ? col : 0);
+        wtr[jj] = resid ? elem_ofs(g.ofs_lv, 4 * j4 + (n16 >> 2), ES * col, g.cpa_lr, g.lg_lr) : 0u;
+    }
 
     // Query rows as the B operand of S^T = K Q^T.
     const T *qp = static_cast<const T *>(p.q);
@@ -506,6 +625,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     // is residual column 32s + 8(rho/4) + 4h + rho%4, so that each lane's
     // results land in its own B-operand slots.
     frag uH[CSx], uL[CSx];
+    constexpr bool kBf16 = sizeof(T) == 2;
+    const float uscale = kBf16 ? 1.0f : cl2;  // the bf16 step folds the scale into the exponent
 #pragma unroll
     for (int s = 0; s < CSx; ++s) {
         uH[s] = O::zero();
@@ -542,7 +663,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                 for (int i = 0; i < 4; ++i) {
                     const int c = 32 * s + 8 * j4 + 4 * h + i;  // column this lane received
                     const bool keep = vm && c < cvalid && blk.a0 + (c >> p.lr_shift) == agent_m;
-                    uv[4 * h + i] = keep ? a[i] * cl2 : 0.0f;
+                    uv[4 * h + i] = keep ? a[i] * uscale : 0.0f;
                 }
             }
 #pragma unroll
@@ -591,7 +712,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
                             keep = keep && agent_m == blk.a0 + ai;
                         else
                             keep = keep && blk.a0 + (c >> p.lr_shift) == agent_m;
-                        if (keep) uv[4 * h + i] += a[i] * cl2;
+                        if (keep) uv[4 * h + i] += a[i] * uscale;
                     }
                 }
             }
@@ -634,8 +755,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
             const bool masked = causal || tt + g.T > t1;
             for (int u = 0; u < spw; ++u) {
                 const int row0 = 16 * (tg * spw + u);
-                step16<T, D, CPAD>(acc, ro, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked, qB, uH, uL,
-                                   cl2, resid, t1, causal, tq, j4);
+                if constexpr (kBf16)
+                    step16_bf16<D, CPAD>(acc, ro, vtr, wtr, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked,
+                                         qB, uH, uL, cl2, resid, t1, causal, tq, j4);
+                else
+                    step16<T, D, CPAD>(acc, ro, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked, qB, uH,
+                                       uL, cl2, resid, t1, causal, tq, j4);
             }
         }
     }
@@ -695,7 +820,26 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     }
 
     // ---- write this split's partial state of every valid row
-    if (tg == 0 && vm) {
+    if (kBf16 && tg == 0 && vm) {
+        // natural order: tile jj, element i of this lane is d (or c) = 16*jj + 4*j4 + i
+        const int64_t rec = ((int64_t)k * p.N * p.rpa + grow) * p.n_slots + slot;
+        float *po = p.p_o + rec * D + 4 * j4;
+#pragma unroll
+        for (int jj = 0; jj < VPL; ++jj) *reinterpret_cast<f32x4 *>(po + 16 * jj) = acc.o[jj];
+        if (resid) {
+            const int arel = agent_m - blk.a0;
+#pragma unroll
+            for (int jj = 0; jj < CPLx; ++jj)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = 16 * jj + 4 * j4 + i;
+                    if (c < cvalid && (p.shared_lr || (c >> p.lr_shift) == arel))
+                        p.p_w[rec * p.r + (c & (p.r - 1))] = acc.w[jj][i];
+                }
+        }
+        if (j4 == 0) *reinterpret_cast<float2 *>(p.p_ml + rec * 2) = float2{m_run, l_run};
+    }
+    if (!kBf16 && tg == 0 && vm) {
         const int64_t rec = ((int64_t)k * p.N * p.rpa + grow) * p.n_slots + slot;
         float ov[4 * VPL];
 #pragma unroll

@@ -9,7 +9,9 @@ namespace rattn {
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // K consecutive elements of one row, loaded with the widest aligned loads.
@@ -114,6 +116,13 @@ struct Ops<float> {
 
 __device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Four floats to bf16 (round to nearest even).
+__device__ inline bf16x4 to_bf16x4(float a, float b, float c, float d) {
+    const bf16x2 x = __builtin_convertvector(f32x2{a, b}, bf16x2);
+    const bf16x2 y = __builtin_convertvector(f32x2{c, d}, bf16x2);
+    return __builtin_shufflevector(x, y, 0, 1, 2, 3);
+}
+
 // gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane p supplies the address of 4 consecutive 16-bit elements x_p[0..3];
 // lane 4a + b receives {x_{4i+a}[b] : i = 0..3}.  With lane 4i + a pointing at
@@ -180,6 +189,26 @@ __device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_bas
                  : "memory", "m0");
 }
 
+// Streaming variants (nontemporal bit): for data read exactly once, such as
+// the base and private key/value rows.  On gfx950 the direct loads sustain
+// about 7.3 TB/s with the bit against 5.9 TB/s without it (a one-workgroup-
+// per-CU ring over 1 GiB); data that other workgroups re-read through L2 (the
+// low-rank rows) keeps the default policy.
+__device__ inline void dma16_nt(const void *gsrc, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(gsrc), "s"(lds_base)
+                 : "memory", "m0");
+}
+__device__ inline void dma16s_nt(const void *sbase, uint32_t voff, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds_base)
+                 : "memory", "m0");
+}
+
 // A pointer that is the same in every lane, moved to scalar registers.
 template <typename P>
 __device__ inline P *uniform_ptr(P *p) {
@@ -217,6 +246,17 @@ __device__ inline void ring_barrier() {
     __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// Maximum over the four lanes l, l^16, l^32, l^48 (the lanes that hold one
+// query row's scores), with gfx950's cross-lane swaps on the VALU instead of
+// two LDS round trips.  permlane32_swap(x, x) leaves (x[l mod 32], x[l mod 32 + 32])
+// in the two results; permlane16_swap does the same for 16-lane rows 0<->1 and 2<->3.
+__device__ inline float row_max4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 __device__ inline float wave_max(float v) {

@@ -69,6 +69,7 @@ struct FillPlan {
     uint32_t kv_off[kMaxKvLoads];  // lane byte offset from the group's first K/V row
     int kv_row[kMaxKvLoads];       // lane's row within the group (for clamping)
     uint32_t lr_stride;            // bytes between agents' low-rank caches
+    bool kv_nt;                    // K/V rows are read by this workgroup only: stream them
 };
 
 template <typename T, int D>
@@ -96,6 +97,7 @@ __device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f
         f.kv_off[i] = (uint32_t)(row * D * ES + 16 * c);
     }
     f.lr_stride = (uint32_t)(s.lr_agent_stride * ES);
+    f.kv_nt = false;
 }
 
 // Lane byte offset of low-rank load i of a group (agent, row and chunk), and the
@@ -127,15 +129,21 @@ __device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan 
         if (f.rK || f.rV) {
             const char *kb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tg0)));
             const char *vb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tg0)));
+            const uint32_t lk0 = lds0 + 16 * (16 * f.g * g.cpr_kv), lv0 = lds0 + 16 * (g.ofs_v + 16 * f.g * g.cpr_kv);
+            if (f.kv_nt) {
 #pragma unroll
-            for (int i = 0; i < kMaxKvLoads; ++i) {
-                if (i < f.n_kv && f.rK)
-                    dma16s(kb, f.kv_off[i], lds0 + 16 * (16 * f.g * g.cpr_kv) + 1024 * i);
-            }
+                for (int i = 0; i < kMaxKvLoads; ++i)
+                    if (i < f.n_kv && f.rK) dma16s_nt(kb, f.kv_off[i], lk0 + 1024 * i);
 #pragma unroll
-            for (int i = 0; i < kMaxKvLoads; ++i) {
-                if (i < f.n_kv && f.rV)
-                    dma16s(vb, f.kv_off[i], lds0 + 16 * (g.ofs_v + 16 * f.g * g.cpr_kv) + 1024 * i);
+                for (int i = 0; i < kMaxKvLoads; ++i)
+                    if (i < f.n_kv && f.rV) dma16s_nt(vb, f.kv_off[i], lv0 + 1024 * i);
+            } else {
+#pragma unroll
+                for (int i = 0; i < kMaxKvLoads; ++i)
+                    if (i < f.n_kv && f.rK) dma16s(kb, f.kv_off[i], lk0 + 1024 * i);
+#pragma unroll
+                for (int i = 0; i < kMaxKvLoads; ++i)
+                    if (i < f.n_kv && f.rV) dma16s(vb, f.kv_off[i], lv0 + 1024 * i);
             }
         }
         if (f.rL || f.rLv) {
@@ -160,6 +168,7 @@ __device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan 
             int tok = tg0 + f.kv_row[i];
             tok = tok < s.tlast ? tok : s.tlast;
             const uint32_t rowoff = f.kv_off[i] - (uint32_t)(f.kv_row[i] * D * ES);  // chunk part
+            // (the tail tile: the default policy serves)
             if (f.rK)
                 dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tok)) + rowoff,
                       lds0 + 16 * (16 * f.g * g.cpr_kv) + 1024 * i);
