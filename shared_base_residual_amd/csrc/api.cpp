@@ -151,78 +151,92 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     if (n_all > (1ll << 30)) return RATTN_E_UNSUPPORTED;
     p.n_prefix_items = (int)n_pre;
     p.n_items = (int)n_all;
-    p.per_xcd = (int)cdiv(n_all, 8);
+    p.pre_per = (int)cdiv(n_pre, 8);
+    p.pv_per = (int)cdiv(n_all - n_pre, 8);
+    p.per_xcd = p.pre_per + p.pv_per;
 
     // LDS staging ring.  A stage holds T tokens of keys and values and, for
     // prefix items with a residual, the low-rank rows (Lk and Lv) of every agent
     // the workgroup serves, as 16-byte chunks (rows padded to a power of two).
     // T must give every wave whole 16-token steps: a row group of nblk blocks
-    // runs 4 / nblk waves per block.
+    // runs nw / nblk waves per block.
     const int es = (int)esize(d->dtype);
     const int kv_row = D * es;  // bytes of one key (or value) row
-    auto tg_of = [](int nblk) { return 4 / nblk; };
-    auto pick = [&](int tg_max, int lr_row_bytes, int *T, int *nst, int *stage) {
-        for (int t = 64; t >= 16; t /= 2) {
-            if (t % (16 * tg_max)) continue;
-            const int sb = t * (2 * kv_row + 2 * lr_row_bytes);
-            const int n = rattn::kLdsBudget / sb;
-            if (n >= 3 || (t == 16 * tg_max && n >= 2)) {
-                *T = t;
-                *nst = n < 4 ? n : 4;
-                *stage = sb;
-                return true;
+    int ag_max = 1;             // agents of one prefix row group
+    for (int rg = 0; L > 0 && rg < p.n_rg; ++rg) {
+        const int b0 = 4 * rg;
+        const int nb = p.n_blocks - b0 < 4 ? p.n_blocks - b0 : 4;
+        const rattn::RowBlock x0 = rattn::prefix_block(b0, N, rpa, p.apb, p.bpa);
+        const rattn::RowBlock x1 = rattn::prefix_block(b0 + nb - 1, N, rpa, p.apb, p.bpa);
+        const int na = x1.a0 + x1.na - x0.a0;
+        if (na > ag_max) ag_max = na;
+    }
+    // the stage fill addresses one workgroup's low-rank rows with 32-bit offsets
+    if (resid && (int64_t)(d->shared_lr ? 1 : ag_max) * L * r * es >= (1ll << 31)) return RATTN_E_UNSUPPORTED;
+    const int lr_row = resid ? 16 * pow2ceil((d->shared_lr ? r : ag_max * r) * es / 16) : 0;
+
+    auto plan_lds = [&](int nw) -> bool {
+        p.nw = nw;
+        auto tg_of = [&](int nblk) { return nw / nblk; };
+        auto pick = [&](int tg_max, int lr_row_bytes, int *T, int *nst, int *stage) {
+            for (int t = 128; t >= 16; t /= 2) {
+                if (t % (16 * tg_max) || t > 16 * nw) continue;  // the fill gives each 16-row group one wave
+                const int sb = t * (2 * kv_row + 2 * lr_row_bytes);
+                const int n = rattn::kLdsBudget / sb;
+                if (n >= 3 || (t == 16 * tg_max && n >= 2)) {
+                    *T = t;
+                    *nst = n < 4 ? n : 4;
+                    *stage = sb;
+                    return true;
+                }
             }
+            return false;
+        };
+        int lds_ring = 0;
+        if (L > 0) {
+            int tg_max = 1;
+            for (int rg = 0; rg < p.n_rg; ++rg) {
+                const int nb = p.n_blocks - 4 * rg < 4 ? p.n_blocks - 4 * rg : 4;
+                if (tg_of(nb) > tg_max) tg_max = tg_of(nb);
+            }
+            if (!pick(tg_max, lr_row, &p.T_pre, &p.nst_pre, &p.stage_bytes_pre)) return false;
+            lds_ring = p.nst_pre * p.stage_bytes_pre;
         }
-        return false;
+        if (S > 0) {
+            int tg_max = 1;
+            for (int g0 = 0; g0 < p.pb; g0 += 4) {
+                const int nb = p.pb - g0 < 4 ? p.pb - g0 : 4;
+                if (tg_of(nb) > tg_max) tg_max = tg_of(nb);
+            }
+            if (!pick(tg_max, 0, &p.T_pv, &p.nst_pv, &p.stage_bytes_pv)) return false;
+            const int b = p.nst_pv * p.stage_bytes_pv;
+            if (b > lds_ring) lds_ring = b;
+        }
+        // After the ring, the token-group merge (one slot of per-lane state per
+        // wave) reuses the same memory.
+        const int cpl = pl->cpad > 0 ? pl->cpad / 16 : 1;
+        const int per_lane = 4 * (D / 16) + 4 * cpl;
+        int lds = lds_ring;
+        const int lds_merge = nw * (64 * per_lane + 32) * (int)sizeof(float);
+        if (lds_merge > lds) lds = lds_merge;
+        // The split's page-table entries.
+        p.table_lds_off = (lds + 15) & ~15;
+        if (d->page_size > 0 && L > 0) lds = p.table_lds_off + (int)(cdiv(p.tok_ps, d->page_size) + 1) * 4;
+        if (lds > rattn::kLdsBudget) return false;
+        pl->lds = (size_t)lds;
+        return true;
     };
-    int lds_ring = 0;
-    if (L > 0) {
-        int tg_max = 1, ag_max = 1;
-        for (int rg = 0; rg < p.n_rg; ++rg) {
-            const int b0 = 4 * rg;
-            const int nb = p.n_blocks - b0 < 4 ? p.n_blocks - b0 : 4;
-            if (tg_of(nb) > tg_max) tg_max = tg_of(nb);
-            const rattn::RowBlock x0 = rattn::prefix_block(b0, N, rpa, p.apb, p.bpa);
-            const rattn::RowBlock x1 = rattn::prefix_block(b0 + nb - 1, N, rpa, p.apb, p.bpa);
-            const int na = x1.a0 + x1.na - x0.a0;
-            if (na > ag_max) ag_max = na;
-        }
-        int lr_row = 0;
-        // the stage fill addresses one workgroup's low-rank rows with 32-bit offsets
-        if (resid && (int64_t)(d->shared_lr ? 1 : ag_max) * L * r * es >= (1ll << 31)) return RATTN_E_UNSUPPORTED;
-        if (resid) {
-            const int chunks = (d->shared_lr ? r : ag_max * r) * es / 16;
-            lr_row = 16 * pow2ceil(chunks);
-        }
-        if (!pick(tg_max, lr_row, &p.T_pre, &p.nst_pre, &p.stage_bytes_pre)) return RATTN_E_UNSUPPORTED;
-        lds_ring = p.nst_pre * p.stage_bytes_pre;
+    if (d->page_size > 0 && L > 0 && cdiv(p.tok_ps, d->page_size) + 1 > rattn::kMaxPagesPerSplit)
+        return RATTN_E_UNSUPPORTED;
+    // Eight waves (two per SIMD) when every prefix row group has at least two
+    // row blocks and the ring still fits; four otherwise.
+    int nb_min = 4;
+    for (int rg = 0; L > 0 && rg < p.n_rg; ++rg) {
+        const int nb = p.n_blocks - 4 * rg < 4 ? p.n_blocks - 4 * rg : 4;
+        if (nb < nb_min) nb_min = nb;
     }
-    if (S > 0) {
-        int tg_max = 1;
-        for (int g0 = 0; g0 < p.pb; g0 += 4) {
-            const int nb = p.pb - g0 < 4 ? p.pb - g0 : 4;
-            if (tg_of(nb) > tg_max) tg_max = tg_of(nb);
-        }
-        if (!pick(tg_max, 0, &p.T_pv, &p.nst_pv, &p.stage_bytes_pv)) return RATTN_E_UNSUPPORTED;
-        const int b = p.nst_pv * p.stage_bytes_pv;
-        if (b > lds_ring) lds_ring = b;
-    }
-    // After the ring, the token-group merge (four slots of per-lane state)
-    // reuses the same memory.
-    const int cpl = pl->cpad > 0 ? pl->cpad / 16 : 1;
-    const int per_lane = 4 * (D / 16) + 4 * cpl;
-    int lds = lds_ring;
-    const int lds_merge = 4 * (64 * per_lane + 32) * (int)sizeof(float);
-    if (lds_merge > lds) lds = lds_merge;
-    // The split's page-table entries.
-    p.table_lds_off = (lds + 15) & ~15;
-    if (d->page_size > 0 && L > 0) {
-        const int64_t pages = cdiv(p.tok_ps, d->page_size) + 1;
-        if (pages > rattn::kMaxPagesPerSplit) return RATTN_E_UNSUPPORTED;
-        lds = p.table_lds_off + (int)pages * 4;
-    }
-    if (lds > rattn::kLdsBudget) return RATTN_E_UNSUPPORTED;
-    pl->lds = (size_t)lds;
+    if (L == 0) nb_min = p.pb < 4 ? p.pb : 4;
+    if (!((nb_min >= 2 && plan_lds(8)) || plan_lds(4))) return RATTN_E_UNSUPPORTED;
 
     // Workspace: the (max, sum), O and W partials of every (KV head, row, split).
     const int64_t rows_kv = (int64_t)HK * N * rpa;

@@ -4,14 +4,14 @@
 // (ForkKV Guide, "Fused ResidualAttention"; LRAgent, "Flash-LoRA-Attention"):
 //   score  s = scale * (q . K_base[j] + (q Bk_a^T) . Lk_a[j])
 //   output o = sum_j p_j V_base[j] + (sum_j p_j Lv_a[j]) Bv_a
-// One launch.  Each workgroup (four waves) takes one (KV head, row group,
-// context split):
+// One launch.  Each workgroup (four or eight waves) takes one (KV head, row
+// group, context split):
 //   * U = scale*log2(e) * q Bk_a^T for its query rows, with MFMA;
 //   * the split's tokens are streamed in tiles of T tokens through a ring of
 //     LDS stages filled by direct global->LDS loads (no registers in between,
 //     several tiles in flight).  A stage holds the tile's base keys and values
 //     and the low-rank rows (Lk, Lv) of every agent the workgroup serves, each
-//     read from HBM once and shared by all four waves;
+//     read from HBM once and shared by all the waves;
 //   * each wave owns one 16-row MFMA row block (query rows of one or more
 //     agents) and a share of each tile's tokens: one MFMA contraction scores the
 //     base keys against all agents' rows, a second adds the rank-r correction
@@ -400,7 +400,7 @@ __device__ inline void merge_row(const DecodeParams &p, int k, int a, int ria, f
 // ------------------------------------------------------------ split kernel --
 
 template <typename T, int D, int CPAD>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
     using O = Ops<T>;
     using frag = typename O::frag;
     constexpr int KS = D / 32;
@@ -417,12 +417,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     const int n16 = lane & 15;
     const int j4 = lane >> 4;
 
-    // Workgroup i is dispatched to XCD i % 8.  Items are numbered KV-head fastest
-    // and laid out so that the KV heads of one (split, row group) run back to back
-    // on one XCD, where they share the low-rank rows through that XCD's L2.
+    // Workgroup i is dispatched to XCD i % 8.  Each XCD takes an equal share of
+    // the prefix items first, then an equal share of the private items.  Prefix
+    // items are numbered KV-head fastest, so the KV heads of one (split, row
+    // group) run back to back on one XCD, where they share the low-rank rows
+    // through that XCD's L2.
     const int bid = blockIdx.x;
-    const int li = (bid & 7) * p.per_xcd + (bid >> 3);
-    if (li >= p.n_items) return;
+    const int xcd = bid & 7, pos = bid >> 3;
+    int li;
+    if (pos < p.pre_per) {
+        li = xcd * p.pre_per + pos;
+        if (li >= p.n_prefix_items) return;
+    } else {
+        const int iv = xcd * p.pv_per + (pos - p.pre_per);
+        if (iv >= p.n_items - p.n_prefix_items) return;
+        li = p.n_prefix_items + iv;
+    }
 
     int k, slot, nblk, blk0, agent_p = 0;
     int t0, t1;
@@ -456,7 +466,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     if (t1 < t0) t1 = t0;  // an empty trailing split
     const bool resid = prefix && (CPAD > 0) && p.r > 0;
     const bool causal = !prefix && p.causal;
-    const int TG = 4 / nblk;  // waves sharing one row block (token groups)
+    const int TG = p.nw / nblk;  // waves sharing one row block (token groups)
     const int rbi = wave / TG;
     const int tg = wave % TG;
 
@@ -553,13 +563,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeParams p) {
     if (src.page_stride && t1 > t0) {
         // the split's page-table entries, read once into LDS
         const int npg = (t1 - 1) / p.ps - src.pg0 + 1;
-        for (int i = threadIdx.x; i < npg; i += 256) s_pages[i] = p.table[src.pg0 + i];
+        for (int i = threadIdx.x; i < npg; i += 64 * p.nw) s_pages[i] = p.table[src.pg0 + i];
         __syncthreads();
     }
 
     // The fill plan of this wave and the lane offsets of the step's LDS reads.
     FillPlan fp;
-    make_fill_plan<T, D>(fp, g, src, resid, wave, lane);
+    make_fill_plan<T, D>(fp, g, src, resid, wave, lane, p.nw);
     // keys and values that no other workgroup reads are streamed past the caches
     fp.kv_nt = prefix ? p.n_rg == 1 : p.n_prg == 1;
     ReadOfs<T, D, CPAD> ro;
@@ -891,7 +901,7 @@ static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t s
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(8 * dp.per_xcd), dim3(256), lds, st, dp);
+    hipLaunchKernelGGL(fn, dim3(8 * dp.per_xcd), dim3(64 * dp.nw), lds, st, dp);
     return hipGetLastError();
 }
 

@@ -85,6 +85,11 @@ struct DecodeParams {
     int pb, n_prg, n_pv;
     int tok_pv;
     int n_slots, n_prefix_items, n_items, per_xcd;
+    // Workgroup i runs on XCD i % 8, as its (i / 8)-th workgroup there.  Each XCD
+    // takes a contiguous share of the prefix items (pre_per of them), then a
+    // share of the private items (pv_per).
+    int pre_per, pv_per;
+    int nw;           // waves per workgroup (4 or 8)
     // LDS staging ring: tokens per stage, stages, bytes per stage (prefix items
     // and private items), and where the split's page-table copy lives.
     int T_pre, nst_pre, stage_bytes_pre;
