@@ -176,6 +176,8 @@ typedef struct rattn_plan_info {
     int32_t agents_per_block; /* agents whose query rows share one block */
     int32_t resid_cols;       /* residual columns per block, padded (0 if r == 0) */
     int32_t work_items;       /* workgroups of the split kernel */
+    int32_t heads_per_item;   /* KV heads one prefix workgroup serves (sharing its low-rank tile) */
+    int32_t waves;            /* waves per split workgroup (compute + load) */
 } rattn_plan_info;
 
 int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info);

@@ -254,153 +254,12 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     }
 }
 
-// ------------------------------------------------------------------- merge --
-
-// One wavefront merges the splits of one query row and writes out/lse.  Every
-// load of a batch is issued before any of it is used, so a batch costs one
-// memory round trip.  wbuf: n_slots floats of LDS for the weights.
-#define LDP(ptr) (*(ptr))
-template <typename T, int D>
-__device__ inline void merge_row(const DecodeParams &p, int k, int a, int ria, float *wbuf, int lane) {
-    constexpr int DPL = D / 64;
-    constexpr int SB = 32;  // slots per batch of O loads
-    const int t = ria / p.g, hh = ria % p.g;
-    const int64_t R = ((int64_t)a * p.QL + t) * p.HQ + (int64_t)k * p.g + hh;
-    const int64_t rec0 = ((int64_t)k * p.N * p.rpa + (int64_t)a * p.rpa + ria) * p.n_slots;
-    const int ns = p.n_slots, r = p.r, nps = p.n_ps;
-    const bool wres = r > 0 && nps > 0;
-
-    // batch 0: (max, sum) of every slot, O of the first SB slots, W of the first
-    // SB prefix slots, and this lane's Bv columns
-    constexpr int MLU = kMaxSlots / 64;
-    float mv[MLU], lv[MLU];
-#pragma unroll
-    for (int u = 0; u < MLU; ++u) {
-        const int s = lane + 64 * u;
-        const int sc = s < ns ? s : 0;
-        if (64 * u < ns) {
-            mv[u] = LDP(p.p_ml + (rec0 + sc) * 2);
-            lv[u] = LDP(p.p_ml + (rec0 + sc) * 2 + 1);
-        }
-    }
-    const float *po = p.p_o + rec0 * D + DPL * lane;
-    float ov[SB][DPL];
-#pragma unroll
-    for (int u = 0; u < SB; ++u) {
-        const int sc = u < ns ? u : ns - 1;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) ov[u][e] = LDP(po + (int64_t)sc * D + e);
-    }
-    // W: lane j (< r) and j + 64 when r = 128
-    float wv[2][SB];
-    if (wres) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int j = lane + 64 * h;
-            const int jc = j < r ? j : 0;
-#pragma unroll
-            for (int u = 0; u < SB; ++u) {
-                const int sc = u < nps ? u : nps - 1;
-                wv[h][u] = LDP(p.p_w + (rec0 + sc) * r + jc);
-            }
-        }
-    }
-
-    float mx = -3.0e38f;
-#pragma unroll
-    for (int u = 0; u < MLU; ++u)
-        if (64 * u < ns && lane + 64 * u < ns) mx = fmaxf(mx, mv[u]);
-    mx = wave_max(mx);
-    float lsum = 0.0f;
-#pragma unroll
-    for (int u = 0; u < MLU; ++u) {
-        const int s = lane + 64 * u;
-        if (64 * u < ns && s < ns) {
-            const float w = fexp2(mv[u] - mx);
-            wbuf[s] = w;
-            lsum += w * lv[u];
-        }
-    }
-    lsum = wave_sum(lsum);
-    __builtin_amdgcn_wave_barrier();
-
-    float o[DPL];
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = 0.0f;
-#pragma unroll
-    for (int u = 0; u < SB; ++u) {
-        const float w = u < ns ? wbuf[u] : 0.0f;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] += w * ov[u][e];
-    }
-    for (int s0 = SB; s0 < ns; s0 += SB) {
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-            const int s = s0 + u;
-            const int sc = s < ns ? s : ns - 1;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) ov[u][e] = LDP(po + (int64_t)sc * D + e);
-        }
-#pragma unroll
-        for (int u = 0; u < SB; ++u) {
-            const float w = s0 + u < ns ? wbuf[s0 + u] : 0.0f;
-#pragma unroll
-            for (int e = 0; e < DPL; ++e) o[e] += w * ov[u][e];
-        }
-    }
-
-    if (wres) {
-        // merged W of this lane's residual columns, then o += W Bv^(k)
-        float wj[2] = {0.0f, 0.0f};
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int u = 0; u < SB; ++u) wj[h] += (u < nps ? wbuf[u] : 0.0f) * wv[h][u];
-        for (int s0 = SB; s0 < nps; s0 += SB) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int j = lane + 64 * h;
-                const int jc = j < r ? j : 0;
-#pragma unroll
-                for (int u = 0; u < SB; ++u) {
-                    const int s = s0 + u;
-                    const int sc = s < nps ? s : nps - 1;
-                    wv[h][u] = LDP(p.p_w + (rec0 + sc) * r + jc);
-                }
-            }
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int u = 0; u < SB; ++u) wj[h] += (s0 + u < nps ? wbuf[s0 + u] : 0.0f) * wv[h][u];
-        }
-        const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * r * p.HK * D + (int64_t)k * D + DPL * lane;
-        const int64_t ldb = (int64_t)p.HK * D;
-        for (int j0 = 0; j0 < r; j0 += 8) {
-            float bvv[8][DPL];
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int e = 0; e < DPL; ++e) bvv[u][e] = (float)bv[(int64_t)(j0 + u) * ldb + e];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int j = j0 + u;  // W of column j lives in lane j % 64, slot j / 64
-                const float wsel = __shfl(j < 64 ? wj[0] : wj[1], j & 63);
-#pragma unroll
-                for (int e = 0; e < DPL; ++e) o[e] += wsel * bvv[u][e];
-            }
-        }
-    }
-    const float inv = 1.0f / lsum;
-#pragma unroll
-    for (int e = 0; e < DPL; ++e) p.out[R * D + DPL * lane + e] = o[e] * inv;
-    if (lane == 0 && p.lse) p.lse[R] = (mx + __builtin_log2f(lsum)) * 0.69314718055994530942f;
-    __builtin_amdgcn_wave_barrier();
-}
-
 // ------------------------------------------------------------ split kernel --
 
-template <typename T, int D, int CPAD>
-__global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
+// MAXW: most waves a workgroup of this instantiation runs (compute + load
+// waves): 8 leaves each wave up to 256 VGPRs, 12 up to 168.
+template <typename T, int D, int CPAD, int MAXW>
+__global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p) {
     using O = Ops<T>;
     using frag = typename O::frag;
     constexpr int KS = D / 32;
@@ -434,12 +293,15 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
         li = p.n_prefix_items + iv;
     }
 
-    int k, slot, nblk, blk0, agent_p = 0;
+    int k0, nh, slot, nblk, blk0, agent_p = 0;
     int t0, t1;
     bool prefix;
     if (li < p.n_prefix_items) {
-        k = li % p.HK;
-        const int rest = li / p.HK;
+        // prefix item: H KV heads starting at k0 (head groups fastest), one row group, one split
+        const int hg = li % p.n_hg;
+        k0 = hg * p.H;
+        nh = p.H;
+        const int rest = li / p.n_hg;
         const int rg = rest % p.n_rg;
         const int s = rest / p.n_rg;
         blk0 = rg * 4;
@@ -450,7 +312,8 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
         prefix = true;
     } else {
         const int l2 = li - p.n_prefix_items;
-        k = l2 % p.HK;
+        k0 = l2 % p.HK;
+        nh = 1;
         int rest = l2 / p.HK;
         const int s = rest % p.n_pv;
         rest /= p.n_pv;
@@ -466,9 +329,14 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
     if (t1 < t0) t1 = t0;  // an empty trailing split
     const bool resid = prefix && (CPAD > 0) && p.r > 0;
     const bool causal = !prefix && p.causal;
-    const int TG = p.nw / nblk;  // waves sharing one row block (token groups)
+    // Row tiles: nblk row blocks of each of the nh heads; TG waves share a tile
+    // (token groups).
+    const int TG = p.nw / (nh * nblk);
     const int rbi = wave / TG;
     const int tg = wave % TG;
+    const int hw = rbi < nh * nblk ? rbi / nblk : 0;  // this wave's head within the item
+    const int bw = rbi < nh * nblk ? rbi % nblk : 0;  // and its row block
+    const int k = k0 + hw;                            // this wave's KV head
 
     // Agents the workgroup serves.
     int a_lo, a_hi;
@@ -484,14 +352,15 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
     // Row block of this wave.
     RowBlock blk;
     if (prefix) {
-        blk = prefix_block(blk0 + (rbi < nblk ? rbi : 0), p.N, p.rpa, p.apb, p.bpa);
+        blk = prefix_block(blk0 + bw, p.N, p.rpa, p.apb, p.bpa);
     } else {
         blk.a0 = agent_p;
         blk.na = 1;
-        blk.f = p.rpa <= 16 ? 0 : 16 * (blk0 + (rbi < nblk ? rbi : 0));
+        blk.f = p.rpa <= 16 ? 0 : 16 * (blk0 + bw);
         blk.nr = p.rpa - blk.f < 16 ? p.rpa - blk.f : 16;
     }
-    const bool wave_on = rbi < nblk;
+    const bool compute_wave = wave < p.nw;  // the others only load
+    const bool wave_on = compute_wave && rbi < nh * nblk;
     // Query row owned by this lane's column.
     const bool vm = wave_on && n16 < blk.nr;
     int agent_m = 0, ria = 0;
@@ -511,27 +380,28 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
     g.cpr_kv = D * ES / 16;
     g.lg_kv = ilog2(g.cpr_kv);
     if (resid) {
-        const int lrc = p.shared_lr ? p.r : (a_hi - a_lo + 1) * p.r;
-        g.cpr_lr = lrc * ES / 16;
-        g.lg_lr = g.cpr_lr > 1 ? 32 - __builtin_clz(g.cpr_lr - 1) : 0;
-        g.cpa_lr = 1 << g.lg_lr;
+        g.cpa_lr = p.r * ES / 16;
+        g.lg_lr = ilog2(g.cpa_lr);
+        g.na_lr = p.shared_lr ? 1 : a_hi - a_lo + 1;
     } else {
-        g.cpr_lr = 0;
         g.cpa_lr = 1;
         g.lg_lr = 0;
+        g.na_lr = 0;
     }
-    g.ofs_v = g.T * g.cpr_kv;
-    g.ofs_lk = 2 * g.T * g.cpr_kv;
-    g.ofs_lv = g.ofs_lk + (resid ? g.T * g.cpa_lr : 0);
-    g.chunks = g.ofs_lv + (resid ? g.T * g.cpa_lr : 0);
+    g.lr_grp = 16 * g.na_lr * g.cpa_lr;
+    g.H = nh;
+    g.ofs_v = nh * g.T * g.cpr_kv;
+    g.ofs_lk = 2 * nh * g.T * g.cpr_kv;
+    g.ofs_lv = g.ofs_lk + (resid ? (g.T >> 4) * g.lr_grp : 0);
+    g.chunks = g.ofs_lv + (resid ? (g.T >> 4) * g.lr_grp : 0);
 
     int *s_pages = reinterpret_cast<int *>(smem + p.table_lds_off);
     Src<T> src;
     src.tlast = t1 > t0 ? t1 - 1 : t0;
     src.r = p.r > 0 ? p.r : 1;
-    src.lr_es_shift = p.r > 0 ? ilog2(p.r * ES / 16) : 0;
     src.lk = src.lv = nullptr;
     src.lr_agent_stride = 0;
+    src.head_stride = 0;
     src.page_stride = 0;
     src.ps = 16;
     src.pg0 = 0;
@@ -542,12 +412,14 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
         if (p.ps > 0) {
             src.page_stride = (int64_t)p.HK * p.ps * D;
             src.ps = p.ps;
-            src.kb += (int64_t)k * p.ps * D;
-            src.vb += (int64_t)k * p.ps * D;
+            src.kb += (int64_t)k0 * p.ps * D;
+            src.vb += (int64_t)k0 * p.ps * D;
+            src.head_stride = (int64_t)p.ps * D;
             src.pg0 = t0 / p.ps;
         } else {
-            src.kb += (int64_t)k * p.L * D;
-            src.vb += (int64_t)k * p.L * D;
+            src.kb += (int64_t)k0 * p.L * D;
+            src.vb += (int64_t)k0 * p.L * D;
+            src.head_stride = p.L * D;
         }
         if (resid) {
             const int64_t a_lr = p.shared_lr ? 0 : a_lo;
@@ -563,15 +435,17 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
     if (src.page_stride && t1 > t0) {
         // the split's page-table entries, read once into LDS
         const int npg = (t1 - 1) / p.ps - src.pg0 + 1;
-        for (int i = threadIdx.x; i < npg; i += 64 * p.nw) s_pages[i] = p.table[src.pg0 + i];
+        for (int i = threadIdx.x; i < npg; i += blockDim.x) s_pages[i] = p.table[src.pg0 + i];
         __syncthreads();
     }
 
     // The fill plan of this wave and the lane offsets of the step's LDS reads.
     FillPlan fp;
-    make_fill_plan<T, D>(fp, g, src, resid, wave, lane, p.nw);
+    make_fill_plan<T, D>(fp, g, src, resid, compute_wave ? p.np : wave - p.nw, lane, p.np);
     // keys and values that no other workgroup reads are streamed past the caches
     fp.kv_nt = prefix ? p.n_rg == 1 : p.n_prg == 1;
+    // this wave's head: its K and V regions of the stage (chunks)
+    const int kreg = hw * g.T * g.cpr_kv, vreg = g.ofs_v + hw * g.T * g.cpr_kv;
     ReadOfs<T, D, CPAD> ro;
     {
         using RO = ReadOfs<T, D, CPAD>;
@@ -579,19 +453,19 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int c = 0; c < RO::FC; ++c)
-                ro.k[s][c] = elem_ofs(0, n16, (32 * s + 8 * j4) * ES + 16 * c, g.cpr_kv, g.lg_kv);
+                ro.k[s][c] = elem_ofs(kreg, n16, (32 * s + 8 * j4) * ES + 16 * c, g.cpr_kv, g.lg_kv);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int c = 0; c < RO::VC; ++c)
-                ro.v[i][c] = elem_ofs(g.ofs_v, 4 * j4 + i, VPL * n16 * ES + 16 * c, g.cpr_kv, g.lg_kv);
+                ro.v[i][c] = elem_ofs(vreg, 4 * j4 + i, VPL * n16 * ES + 16 * c, g.cpr_kv, g.lg_kv);
 #pragma unroll
         for (int s = 0; s < RO::CSx; ++s) {
             int col = 32 * s + 8 * j4;
             col = lr_col0 + (col < cvalid ? col : 0);  // padding column: U is zero there
 #pragma unroll
             for (int c = 0; c < RO::FC; ++c)
-                ro.lk[s][c] = resid ? elem_ofs(g.ofs_lk, n16, col * ES + 16 * c, g.cpa_lr, g.lg_lr) : 0u;
+                ro.lk[s][c] = resid ? lr_ofs(g, g.ofs_lk, col >> p.lr_shift, n16, (col & (p.r - 1)) * ES + 16 * c) : 0u;
         }
         int colv = RO::CPL * n16;
         colv = lr_col0 + (colv < cvalid ? colv : 0);
@@ -599,21 +473,22 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int c = 0; c < RO::LC; ++c)
-                ro.lv[i][c] = resid ? elem_ofs(g.ofs_lv, 4 * j4 + i, colv * ES + 16 * c, g.cpa_lr, g.lg_lr) : 0u;
+                ro.lv[i][c] =
+                    resid ? lr_ofs(g, g.ofs_lv, colv >> p.lr_shift, 4 * j4 + i, (colv & (p.r - 1)) * ES + 16 * c) : 0u;
     }
-    const int kv_rowb = D * ES, lr_rowb = 16 * g.cpa_lr;
+    const int kv_rowb = D * ES, lr_rowb = 16 * g.na_lr * g.cpa_lr;  // a step at row0 starts row0 * these bytes in
     // bf16 step: transposed value reads.  For d-tile jj, lane (4i + a, j4) points at
     // row 4*j4 + i, columns 16*jj + 4a (residual columns of the block; padding
     // columns read column 0 of the block, their W is dropped at the store).
     uint32_t vtr[VPL], wtr[CPLx];
 #pragma unroll
     for (int jj = 0; jj < VPL; ++jj)
-        vtr[jj] = elem_ofs(g.ofs_v, 4 * j4 + (n16 >> 2), ES * (16 * jj + 4 * (n16 & 3)), g.cpr_kv, g.lg_kv);
+        vtr[jj] = elem_ofs(vreg, 4 * j4 + (n16 >> 2), ES * (16 * jj + 4 * (n16 & 3)), g.cpr_kv, g.lg_kv);
 #pragma unroll
     for (int jj = 0; jj < CPLx; ++jj) {
         int col = 16 * jj + 4 * (n16 & 3);
         col = lr_col0 + (col < cvalid ? col : 0);
-        wtr[jj] = resid ? elem_ofs(g.ofs_lv, 4 * j4 + (n16 >> 2), ES * col, g.cpa_lr, g.lg_lr) : 0u;
+        wtr[jj] = resid ? lr_ofs(g, g.ofs_lv, col >> p.lr_shift, 4 * j4 + (n16 >> 2), (col & (p.r - 1)) * ES) : 0u;
     }
 
     // Query rows as the B operand of S^T = K Q^T.
@@ -742,7 +617,8 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
     wait_vmcnt(0);
 
     // ---- start the ring: tiles 0 .. nst-2
-    for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
+    if (fp.fpw)
+        for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
 
     Acc<T, D, CPAD> acc;
 #pragma unroll
@@ -758,7 +634,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
         const int later = (n_tiles - 1 - i) < (g.nst - 2) ? (n_tiles - 1 - i) : (g.nst - 2);
         wait_vmcnt(later * fpw);  // this wave's loads of tile i have landed
         ring_barrier();           // ... everyone's, and everyone is done with tile i-1
-        if (i + g.nst - 1 < n_tiles) fill(i + g.nst - 1, (i + g.nst - 1) % g.nst);
+        if (fp.fpw && i + g.nst - 1 < n_tiles) fill(i + g.nst - 1, (i + g.nst - 1) % g.nst);
         if (wave_on) {
             const char *st = smem + (size_t)(i % g.nst) * g.stage_bytes;
             const int tt = t0 + i * g.T;
@@ -787,7 +663,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
     if (TG > 1) {
         // waves with tg > 0 publish their state: one slot per wave
         float *sm = smf + (size_t)wave * (64 * PER_LANE + 32);
-        if (tg > 0) {
+        if (compute_wave && tg > 0) {
 #pragma unroll
             for (int jj = 0; jj < VPL; ++jj)
 #pragma unroll
@@ -802,7 +678,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
             }
         }
         __syncthreads();
-        if (tg == 0) {
+        if (compute_wave && tg == 0) {
             float mt = m_run;
             for (int w = 1; w < TG; ++w)
                 mt = fmaxf(mt, smf[(size_t)(wave + w) * (64 * PER_LANE + 32) + 64 * PER_LANE + n16]);
@@ -878,30 +754,173 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeParams p) {
 
 // ---------------------------------------------------------------- combine --
 
-// One wavefront per query row: row R = (a * q_len + t) * H_q + h.
+// One workgroup (512 threads) per query row R = (a * q_len + t) * H_q + h: a
+// log-sum-exp merge of the row's split partials, then o += (sum w W) Bv_a^(k)
+// (Bv applied once per row), o /= sum w l.  The partial O rows of one query row
+// are contiguous ([n_slots][d] floats) and are read as float4 by all threads;
+// thread t always lands on column group t % (d/4), so it accumulates one float4
+// and the threads of a column group are summed through LDS at the end.  The
+// first batch of O, W and Bv loads is issued before the weight pass, so the
+// row costs about two memory round trips.
+constexpr int kCombineThreads = 512;
+static_assert(kMaxSlots <= kCombineThreads, "the merge gives each slot one thread");
+constexpr int kCombineBatch = 8;  // float4 loads of O per thread per batch
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeParams p) {
-    __shared__ float wbuf[4][kMaxSlots];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int64_t R = (int64_t)blockIdx.x * 4 + wave;
-    if (R >= (int64_t)p.N * p.QL * p.HQ) return;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p) {
+    constexpr int NT = kCombineThreads, NWV = NT / 64, D4 = D / 4, B = kCombineBatch;
+    __shared__ float s_w[kMaxSlots];
+    __shared__ f32x4 s_o[NT];
+    __shared__ float s_red[2 * NWV];
+    __shared__ f32x4 s_wp[NWV * 32];  // per-wave W column-group sums
+    __shared__ float s_wt[128];       // merged W (r <= 128)
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t R = blockIdx.x;
     const int h = (int)(R % p.HQ);
     const int64_t at = R / p.HQ;
     const int a = (int)(at / p.QL), t = (int)(at % p.QL);
-    const int k = h / p.g;
-    merge_row<T, D>(p, k, a, t * p.g + (h % p.g), wbuf[wave], lane);
+    const int k = h / p.g, ria = t * p.g + h % p.g;
+    const int64_t rec0 = ((int64_t)k * p.N * p.rpa + (int64_t)a * p.rpa + ria) * p.n_slots;
+    const int ns = p.n_slots, nps = p.n_ps, r = p.r;
+    const bool wres = r > 0 && nps > 0;
+    const int R4 = wres ? r / 4 : 1;  // 2 .. 32, divides NT
+
+    // this thread's slot statistics (one slot per thread: n_slots <= kMaxSlots = NT),
+    // loaded first: the weight pass waits for it alone
+    const float2 ml = tid < ns ? *reinterpret_cast<const float2 *>(p.p_ml + (rec0 + tid) * 2) : float2{-3.0e38f, 0.0f};
+    // first batch of O (float4 q = slot * D/4 + column group), W and Bv, issued now
+    const f32x4 *po = reinterpret_cast<const f32x4 *>(p.p_o + rec0 * D);
+    const int nq = ns * D4;
+    f32x4 ob[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        const int q = tid + u * NT;
+        ob[u] = q < nq ? po[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const f32x4 *pw = reinterpret_cast<const f32x4 *>(p.p_w + rec0 * (wres ? r : 0));
+    const int nqw = wres ? nps * R4 : 0;
+    f32x4 wb[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = tid + u * NT;
+        wb[u] = q < nqw ? pw[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // Bv column d = tid % D, rows j = tid / D + jstep * i (jstep = NT / D threads per column)
+    constexpr int JS = NT / D;  // 4 (d = 128) or 8 (d = 64)
+    const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * r * p.HK * D + (int64_t)k * D + (tid % D);
+    const int64_t ldb = (int64_t)p.HK * D;
+    float bvv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int j = tid / D + JS * u;
+        bvv[u] = (wres && j < r) ? (float)bv[(int64_t)j * ldb] : 0.0f;
+    }
+
+    // weights of the slots: w_s = exp2(m_s - M), L = sum w_s l_s
+    const float mloc = wave_max(ml.x);
+    if (lane == 0) s_red[wv] = mloc;
+    __syncthreads();
+    float M = s_red[0];
+#pragma unroll
+    for (int i = 1; i < NWV; ++i) M = fmaxf(M, s_red[i]);
+    const float w = tid < ns ? fexp2(ml.x - M) : 0.0f;
+    s_w[tid] = w;
+    const float lloc = wave_sum(w * ml.y);
+    if (lane == 0) s_red[NWV + wv] = lloc;
+    __syncthreads();
+    float Lsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) Lsum += s_red[NWV + i];
+
+    // O = sum_s w_s O_s
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+        const int q = tid + u * NT;
+        if (q < nq) acc += s_w[q / D4] * ob[u];
+    }
+    for (int q0 = B * NT; q0 < nq; q0 += B * NT) {
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int q = q0 + tid + u * NT;
+            ob[u] = q < nq ? po[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int q = q0 + tid + u * NT;
+            if (q < nq) acc += s_w[q / D4] * ob[u];
+        }
+    }
+    // W = sum over prefix slots of w_s W_s.  Thread t holds column group t % (r/4):
+    // reduce over the lanes of a wave that share it (xor shuffles), then over
+    // the waves through LDS, in a fixed order.
+    f32x4 wacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int q = tid + u * NT;
+        if (q < nqw) wacc += s_w[q / R4] * wb[u];
+    }
+    for (int q = tid + 2 * NT; q < nqw; q += NT) wacc += s_w[q / R4] * pw[q];
+    if (wres) {
+        for (int off = 32; off >= R4; off >>= 1)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) wacc[e] += __shfl_xor(wacc[e], off);
+        if (lane < R4) s_wp[wv * R4 + lane] = wacc;
+    }
+    // O: column group t % (d/4); lanes l and l ^ 32 share it (d/4 = 32) or
+    // l, l ^ 16, l ^ 32, l ^ 48 (d/4 = 16)
+    for (int off = 32; off >= D4; off >>= 1)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
+    if (lane < D4) s_o[wv * D4 + lane] = acc;
+    __syncthreads();
+    if (wres && tid < r) {
+        float x = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NWV; ++i) x += s_wp[i * R4 + (tid >> 2)][tid & 3];
+        s_wt[tid] = x;
+    }
+    __syncthreads();
+    // (W Bv)[d] over this thread's rows j of Bv
+    float wbv = 0.0f;
+    if (wres) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = tid / D + JS * u;
+            if (j < r) wbv += s_wt[j] * bvv[u];
+        }
+        for (int j = tid / D + 4 * JS; j < r; j += JS) wbv += s_wt[j] * (float)bv[(int64_t)j * ldb];
+    }
+    float *s_wbv = s_w;  // the weights are consumed: reuse for the per-thread W Bv terms
+    s_wbv[tid] = wbv;
+    __syncthreads();
+
+    // o[d] for d = tid (< D)
+    if (tid < D) {
+        const int c4 = tid >> 2, e = tid & 3;
+        float o = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NWV; ++i) o += s_o[i * D4 + c4][e];
+#pragma unroll
+        for (int i = 0; i < JS; ++i) o += s_wbv[tid + D * i];
+        p.out[R * D + tid] = o / Lsum;
+        if (tid == 0 && p.lse) p.lse[R] = (M + __builtin_log2f(Lsum)) * 0.69314718055994530942f;
+    }
 }
 
 // ---------------------------------------------------------------- launchers --
 
+template <typename T, int D, int CP, int W>
+struct SplitSlot {};
+
 template <typename T, int D, int CP>
 static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t st) {
-    auto *fn = decode_split_kernel<T, D, CP>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const bool w8 = dp.nw + dp.np <= 8;
+    auto *fn = w8 ? decode_split_kernel<T, D, CP, 8> : decode_split_kernel<T, D, CP, 12>;
+    const hipError_t e = w8 ? ensure_lds<SplitSlot<T, D, CP, 8>>(reinterpret_cast<const void *>(fn), (int)lds)
+                            : ensure_lds<SplitSlot<T, D, CP, 12>>(reinterpret_cast<const void *>(fn), (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(8 * dp.per_xcd), dim3(64 * dp.nw), lds, st, dp);
+    hipLaunchKernelGGL(fn, dim3(8 * dp.per_xcd), dim3(64 * (dp.nw + dp.np)), lds, st, dp);
     return hipGetLastError();
 }
 
@@ -926,11 +945,11 @@ static hipError_t launch_split_t(const DecodeParams &dp, int D, int cpad, size_t
 template <typename T>
 static hipError_t launch_combine_t(const DecodeParams &dp, int D, hipStream_t st) {
     const int64_t rows = (int64_t)dp.N * dp.QL * dp.HQ;
-    const dim3 grid((unsigned)((rows + 3) / 4));
+    const dim3 grid((unsigned)rows);
     if (D == 128)
-        hipLaunchKernelGGL((combine_kernel<T, 128>), grid, dim3(256), 0, st, dp);
+        hipLaunchKernelGGL((combine_kernel<T, 128>), grid, dim3(kCombineThreads), 0, st, dp);
     else
-        hipLaunchKernelGGL((combine_kernel<T, 64>), grid, dim3(256), 0, st, dp);
+        hipLaunchKernelGGL((combine_kernel<T, 64>), grid, dim3(kCombineThreads), 0, st, dp);
     return hipGetLastError();
 }
 

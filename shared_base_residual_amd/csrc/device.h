@@ -4,7 +4,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace rattn {
+
+// Raises kernel fn's dynamic-LDS limit to `lds` bytes on the current device.
+// The attribute call is costly on the launch path, so each (kernel, device)
+// remembers the largest limit set so far (Slot: one static table per kernel).
+template <typename Slot>
+inline hipError_t ensure_lds(const void *fn, int lds) {
+    static std::atomic<int> set[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (set[dev].load(std::memory_order_relaxed) >= lds) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess) {
+        int cur = set[dev].load(std::memory_order_relaxed);
+        while (cur < lds && !set[dev].compare_exchange_weak(cur, lds)) {
+        }
+    }
+    return e;
+}
 
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));

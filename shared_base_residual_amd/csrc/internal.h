@@ -81,6 +81,7 @@ struct DecodeParams {
     int causal;       // private token j is visible to query token t only if j <= t
     float c;          // softmax scale * log2(e)
     int n_blocks, n_rg, n_ps;
+    int H, n_hg;      // KV heads per prefix item (sharing its low-rank tile), head groups
     int tok_ps;
     int pb, n_prg, n_pv;
     int tok_pv;
@@ -89,7 +90,9 @@ struct DecodeParams {
     // takes a contiguous share of the prefix items (pre_per of them), then a
     // share of the private items (pv_per).
     int pre_per, pv_per;
-    int nw;           // waves per workgroup (4 or 8)
+    int nw;           // compute waves per workgroup (4 or 8)
+    int np;           // load waves per workgroup: they issue every direct load of the
+                      // ring and wait for it, so no compute wave stalls on issue
     // LDS staging ring: tokens per stage, stages, bytes per stage (prefix items
     // and private items), and where the split's page-table copy lives.
     int T_pre, nst_pre, stage_bytes_pre;

@@ -172,14 +172,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         g.cpr_kv = D * ES / 16;
         g.lg_kv = ilog2(g.cpr_kv);
         if (res) {
-            g.cpr_lr = p.r * ES / 16;
-            g.lg_lr = g.cpr_lr > 1 ? 32 - __builtin_clz(g.cpr_lr - 1) : 0;
-            g.cpa_lr = 1 << g.lg_lr;
+            g.cpa_lr = p.r * ES / 16;
+            g.lg_lr = ilog2(g.cpa_lr);
+            g.na_lr = 1;  // one agent's (or the shared) low-rank rows
         } else {
-            g.cpr_lr = 0;
             g.cpa_lr = 1;
             g.lg_lr = 0;
+            g.na_lr = 0;
         }
+        g.lr_grp = 16 * g.na_lr * g.cpa_lr;
+        g.H = 1;
         g.ofs_v = g.T * g.cpr_kv;
         g.ofs_lk = 2 * g.T * g.cpr_kv;
         g.ofs_lv = g.ofs_lk + (res ? g.T * g.cpa_lr : 0);
@@ -188,9 +190,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         Src<T> src;
         src.tlast = t1 - 1;
         src.r = p.r > 0 ? p.r : 1;
-        src.lr_es_shift = p.r > 0 ? ilog2(p.r * ES / 16) : 0;
         src.lk = src.lv = nullptr;
         src.lr_agent_stride = 0;
+        src.head_stride = 0;
         src.page_stride = 0;
         src.ps = 16;
         src.pg0 = 0;
@@ -222,8 +224,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
             src.vb = static_cast<const T *>(p.vp) + seg;
         }
 
-        FillPlan fp;
-        make_fill_plan<T, D>(fp, g, src, res, wave, lane, NW);
+        GroupFill fp;
+        make_group_fill<T, D>(fp, g, src, res, wave, lane, NW);
         ReadOfs<T, D, CPAD> ro;
         {
             using RO = ReadOfs<T, D, CPAD>;
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const int fpw = fp.fpw;
         auto fill = [&](int tile, int stage) {
             const int tt = t0 + tile * g.T;
-            fill_stage<T, D>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
+            fill_group<T, D>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
         };
         for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
 
@@ -469,10 +471,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 }
 
 template <typename T, int D, int CP>
+struct PrefillSlot {};
+
+template <typename T, int D, int CP>
 static hipError_t launch_prefill_one(const PrefillParams &pp, size_t lds, hipStream_t st) {
     auto *fn = prefill_kernel<T, D, CP>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const hipError_t e = ensure_lds<PrefillSlot<T, D, CP>>(reinterpret_cast<const void *>(fn), (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3(8 * pp.per_xcd), dim3(kPrefillRows / 32 * 64), lds, st, pp);
     return hipGetLastError();

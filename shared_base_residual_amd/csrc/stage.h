@@ -10,12 +10,20 @@ namespace rattn {
 // ------------------------------------------------------------- geometry --
 
 // Layout of one LDS stage, in 16-byte chunks: K rows, V rows, Lk rows, Lv rows.
+// K and V rows are token-major.  The low-rank regions are agent-major within
+// each 16-token group: group gg holds, for each agent a of the workgroup, that
+// agent's 16 rows (r elements each) back to back -- the same bytes as one
+// contiguous piece of the agent's cache, so each direct load reads contiguous
+// memory.
 struct Geo {
     int T;                    // tokens per stage
     int nst;                  // stages in the ring
     int cpr_kv, lg_kv;        // chunks per K (or V) row, its log2
-    int cpr_lr, cpa_lr, lg_lr;  // valid / allocated (power of two) chunks per Lk row
-    int ofs_v, ofs_lk, ofs_lv;  // region offsets (chunks)
+    int cpa_lr, lg_lr;        // chunks per low-rank row of one agent (r * sizeof(T) / 16), its log2
+    int na_lr;                // agents in the low-rank regions
+    int lr_grp;               // chunks of one 16-token group of a low-rank region (16 * na_lr * cpa_lr)
+    int H;                    // KV heads staged: K regions 0..H-1, then V regions, then Lk, Lv
+    int ofs_v, ofs_lk, ofs_lv;  // region offsets (chunks): V of head 0, Lk, Lv
     int chunks;               // chunks per stage
     int stage_bytes;          // stride between stages
 };
@@ -25,7 +33,8 @@ __device__ inline int ilog2(int x) { return 31 - __builtin_clz(x); }
 // Where the tokens of a work item come from.
 template <typename T>
 struct Src {
-    const T *kb, *vb;         // contiguous: this head's rows; paged: pool + this head's offset
+    const T *kb, *vb;         // contiguous: the first head's rows; paged: pool + that head's offset
+    int64_t head_stride;      // elements from one staged head to the next
     int64_t page_stride;      // paged: elements per physical page (0: contiguous)
     int ps;                   // page size (paged)
     int pg0;                  // first logical page of the split
@@ -33,7 +42,6 @@ struct Src {
     const T *lk, *lv;         // low-rank rows: first agent of the workgroup (or the shared one)
     int64_t lr_agent_stride;  // elements between agents' low-rank caches
     int r;                    // rank
-    int lr_es_shift;          // log2(r * sizeof(T) / 16): chunks per agent row
     int tlast;                // last valid token of the item
 };
 
@@ -48,114 +56,214 @@ __device__ inline const T *kv_row(const Src<T> &s, const T *base, int tok) {
 
 // ------------------------------------------------------------ stage fill --
 //
-// A stage holds four regions of the tile: K rows, V rows, Lk rows, Lv rows (the
-// last two only with a residual).  The tile's rows are cut into 16-row groups;
-// wave w fills group w % G (G = T / 16) of the regions r with
-// (r * G + w % G) % nw == w (nw waves), so every wave fills a fixed part: one
-// page lookup and one uniform base per region and tile, and lane offsets that
-// depend on the lane only (the swizzle repeats every 16 rows).  Each direct load
-// moves 64 chunks of 16 bytes; a region row of cpa chunks gives 16 * cpa chunks
-// per group, ceil(16 * cpa / 64) loads (the last one partial when 16 * cpa < 64).
-// Lane offsets are 32-bit: the low-rank rows one workgroup reads span less than
-// 2^31 bytes (checked on the host).
+// A stage holds the regions of one tile: the K rows of each staged head, the V
+// rows of each, and with a residual the Lk and Lv rows.  The tile's rows are cut
+// into 16-row groups (G = T / 16).  The (region, group) pairs pi = region * G +
+// group go round-robin to the nw filling waves: wave w fills the pairs with
+// pi % nw == w, each with one page lookup and one uniform base per tile and lane
+// offsets that depend on the lane only (the swizzle repeats every 16 rows).  Each
+// direct load moves 64 chunks of 16 bytes: a K/V group of 16 rows of cpr_kv chunks
+// takes 16 * cpr_kv / 64 loads, a low-rank group ceil(lr_grp / 64) (the last one
+// partial when lr_grp is not a multiple of 64).  Lane offsets are 32-bit: the
+// low-rank rows one workgroup reads span less than 2^31 bytes (checked on the host).
 
 constexpr int kMaxKvLoads = 8;   // direct loads per group of a K (or V) region (fp32, d = 128)
 
 struct FillPlan {
-    int G, g;                 // groups per tile, this wave's group
-    bool rK, rV, rL, rLv;     // regions this wave fills
+    int G;                    // groups per tile
+    int npairs;               // (region, group) pairs per tile
+    int w, nw;                // this wave's index among the nw filling waves (w >= nw: none)
     int n_kv, n_lr;           // loads per group of a K/V region, of an Lk/Lv region
     int fpw;                  // loads this wave issues per stage
-    uint32_t kv_off[kMaxKvLoads];  // lane byte offset from the group's first K/V row
-    int kv_row[kMaxKvLoads];       // lane's row within the group (for clamping)
-    uint32_t lr_stride;            // bytes between agents' low-rank caches
-    bool kv_nt;                    // K/V rows are read by this workgroup only: stream them
+    uint32_t lr_stride;       // bytes between agents' low-rank caches
+    bool kv_nt;               // K/V rows are read by this workgroup only: stream them
+    uint32_t kv_off[kMaxKvLoads];  // lane byte offset of K/V load i from the group's first row
+                                   // (only the first d * sizeof(T) / 64 are set and used)
 };
+
+// Lane byte offset of K/V load i of a group from the group's first row, and the
+// lane's row within the group.  Recomputed per load (a few integer operations)
+// rather than kept in registers.
+template <typename T, int D>
+__device__ inline uint32_t kv_lane_off(const Geo &g, int i, int lane, int *row_out) {
+    constexpr int ES = (int)sizeof(T);
+    const int q = 64 * i + lane;
+    const int row = q >> g.lg_kv;
+    const int c = swz(row, q & (g.cpr_kv - 1), g.cpr_kv, g.lg_kv);
+    *row_out = row;
+    return (uint32_t)(row * D * ES + 16 * c);
+}
 
 template <typename T, int D>
 __device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f, const Geo &g, const Src<T> &s,
-                                                                     bool resid, int wave, int lane, int nw = 4) {
+                                                                     bool resid, int wave, int lane, int nw) {
     constexpr int ES = (int)sizeof(T);
-    // (group, region) pairs pi = region * G + group go round-robin to the waves:
-    // wave w fills the pairs with pi % nw == w (nw a multiple of G)
     f.G = g.T >> 4;
-    f.g = wave % f.G;
-    auto mine = [&](int region) { return (region * f.G + f.g) % nw == wave; };
-    f.rK = mine(0);
-    f.rV = mine(1);
-    f.rL = resid && mine(2);
-    f.rLv = resid && mine(3);
+    const int nreg = 2 * g.H + (resid ? 2 : 0);
+    f.npairs = nreg * f.G;
+    f.w = wave < nw ? wave : f.npairs;  // a wave outside the filling set fills nothing
+    f.nw = nw;
     f.n_kv = (16 * g.cpr_kv) >> 6;
-    f.n_lr = resid ? ((16 * g.cpa_lr + 63) >> 6) : 0;
-    f.fpw = (f.rK ? f.n_kv : 0) + (f.rV ? f.n_kv : 0) + (f.rL ? f.n_lr : 0) + (f.rLv ? f.n_lr : 0);
-#pragma unroll
-    for (int i = 0; i < kMaxKvLoads; ++i) {
-        const int q = 64 * i + lane;
-        const int row = q >> g.lg_kv;
-        const int c = swz(row, q & (g.cpr_kv - 1), g.cpr_kv, g.lg_kv);
-        f.kv_row[i] = row;
-        f.kv_off[i] = (uint32_t)(row * D * ES + 16 * c);
-    }
+    f.n_lr = resid ? ((g.lr_grp + 63) >> 6) : 0;
+    f.fpw = 0;
+    for (int pi = f.w; pi < f.npairs; pi += nw) f.fpw += pi < 2 * g.H * f.G ? f.n_kv : f.n_lr;
     f.lr_stride = (uint32_t)(s.lr_agent_stride * ES);
     f.kv_nt = false;
+    constexpr int NKV = D * ES / 64;  // loads per K/V group: 16 rows of d elements
+#pragma unroll
+    for (int i = 0; i < NKV; ++i) {
+        int row;
+        f.kv_off[i] = kv_lane_off<T, D>(g, i, lane, &row);
+    }
 }
 
-// Lane byte offset of low-rank load i of a group (agent, row and chunk), and the
-// lane's row within the group.  Computed per load: a workgroup issues few.
-template <typename T>
-__device__ inline uint32_t lr_lane_off(const FillPlan &f, const Geo &g, const Src<T> &s, int i, int lane, int *row_out) {
-    constexpr int ES = (int)sizeof(T);
+// Lane byte offset of low-rank load i of a group (agent, row and chunk, from
+// the first agent's row of the group's first token), and the lane's row within
+// the group.  Chunk q of the group region is chunk q % cpa of row
+// (q / cpa) % 16 of agent q / (16 cpa).  Computed per load: a workgroup issues few.
+__device__ inline uint32_t lr_lane_off(uint32_t lr_stride, const Geo &g, int i, int lane, int *row_out) {
     const int q = 64 * i + lane;
-    const int row = q >> g.lg_lr;
-    int c = swz(row, q & (g.cpa_lr - 1), g.cpa_lr, g.lg_lr);
-    c = c < g.cpr_lr ? c : 0;  // allocated-only chunk: any valid data (never read)
-    const int agent = c >> s.lr_es_shift;
-    const int cin = c - (agent << s.lr_es_shift);
-    *row_out = row < 16 ? row : 15;
-    return (uint32_t)(row * s.r * ES + 16 * cin) + (uint32_t)agent * f.lr_stride;
+    const int a = q >> (4 + g.lg_lr);
+    const int qa = q & ((16 << g.lg_lr) - 1);
+    const int x = qa >> g.lg_lr;
+    const int c = swz(x, qa & (g.cpa_lr - 1), g.cpa_lr, g.lg_lr);
+    *row_out = x;
+    return (uint32_t)(16 * ((x << g.lg_lr) + c)) + (uint32_t)a * lr_stride;
+}
+
+// LDS byte offset of byte cb of agent a's row x in a low-rank region whose
+// group starts at chunk rbase (the same swizzle as the fill).
+__device__ inline uint32_t lr_ofs(const Geo &g, int rbase, int a, int x, int cb) {
+    return (uint32_t)(16 * (rbase + ((16 * a + x) << g.lg_lr) + swz(x, cb >> 4, g.cpa_lr, g.lg_lr)) + (cb & 15));
 }
 
 // Issues this wave's loads of the tile starting at token t0 into `stage`.
 // clamp: rows past the item's last token read that token instead (the tail
-// tile); otherwise every row is valid and a uniform base per region serves.
+// tile); otherwise every row is valid and a uniform base per pair serves.
 // Always the same number of loads per wave (f.fpw), which the ring's waits count.
 template <typename T, int D>
-__device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan &f, const Geo &g, const Src<T> &s, int t0, char *stage, bool clamp,
-                                  int lane) {
+__device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan &f, const Geo &g, const Src<T> &s,
+                                                                 int t0, char *stage, bool clamp, int lane) {
     constexpr int ES = (int)sizeof(T);
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(stage));
+    const int nkv = 2 * g.H * f.G;  // K/V pairs come first
+    for (int pi = f.w; pi < f.npairs; pi += f.nw) {
+        const int gg = pi & (f.G - 1);
+        const int tg0 = t0 + 16 * gg;  // the group's first token
+        if (pi < nkv) {
+            // K (region < H) or V rows of head region % H
+            const int region = pi / f.G;
+            const bool isv = region >= g.H;
+            const T *base = (isv ? s.vb : s.kb) + (int64_t)(isv ? region - g.H : region) * s.head_stride;
+            const uint32_t dst = lds0 + 16 * ((region * g.T + 16 * gg) * g.cpr_kv);
+            constexpr int NKV = D * ES / 64;
+            if (!clamp) {
+                const char *b = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, base, tg0)));
+                if (f.kv_nt) {
+#pragma unroll
+                    for (int i = 0; i < NKV; ++i) dma16s_nt(b, f.kv_off[i], dst + 1024 * i);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < NKV; ++i) dma16s(b, f.kv_off[i], dst + 1024 * i);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < NKV; ++i) {
+                    const int row = (64 * i + lane) >> g.lg_kv;
+                    int tok = tg0 + row;
+                    tok = tok < s.tlast ? tok : s.tlast;
+                    const uint32_t rowoff = f.kv_off[i] - (uint32_t)(row * D * ES);  // chunk part
+                    dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, base, tok)) + rowoff, dst + 1024 * i);
+                }
+            }
+        } else {
+            // Lk (first) or Lv rows of every agent of the workgroup
+            const bool isv = pi >= nkv + f.G;
+            const T *lbase = isv ? s.lv : s.lk;
+            const uint32_t dst = lds0 + 16 * ((isv ? g.ofs_lv : g.ofs_lk) + gg * g.lr_grp);
+            const char *b = uniform_ptr(reinterpret_cast<const char *>(lbase + (int64_t)tg0 * s.r));
+            for (int i = 0; i < f.n_lr; ++i) {
+                if (64 * i + lane < g.lr_grp) {
+                    int row;
+                    const uint32_t off = lr_lane_off(f.lr_stride, g, i, lane, &row);
+                    if (!clamp) {
+                        dma16s(b, off, dst + 1024 * i);
+                    } else {
+                        int tok = tg0 + row;
+                        tok = tok < s.tlast ? tok : s.tlast;
+                        const uint32_t rel = off - (uint32_t)(row * s.r * ES);  // agent and chunk part
+                        dma16(reinterpret_cast<const char *>(lbase + (int64_t)tok * s.r) + rel, dst + 1024 * i);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// The same fill for one staged head when every filling wave owns a single
+// 16-row group (nw a multiple of G): wave w fills group w % G of the regions r
+// with (r * G + w % G) % nw == w.  Fewer instructions per tile than the
+// general walk over pairs, for kernels whose filling waves also compute.
+struct GroupFill {
+    int g;                    // this wave's group
+    bool rK, rV, rL, rLv;     // regions it fills
+    int n_lr;                 // loads per group of an Lk/Lv region
+    int fpw;                  // loads per stage
+    uint32_t lr_stride;       // bytes between agents' low-rank caches
+    uint32_t kv_off[kMaxKvLoads];  // as in FillPlan
+};
+
+template <typename T, int D>
+__device__ __attribute__((always_inline)) inline void make_group_fill(GroupFill &f, const Geo &g, const Src<T> &s,
+                                                                       bool resid, int wave, int lane, int nw) {
+    constexpr int ES = (int)sizeof(T);
+    constexpr int NKV = D * ES / 64;
+    const int G = g.T >> 4;
+    f.g = wave % G;
+    auto mine = [&](int region) { return (region * G + f.g) % nw == wave; };
+    f.rK = mine(0);
+    f.rV = mine(1);
+    f.rL = resid && mine(2);
+    f.rLv = resid && mine(3);
+    f.n_lr = resid ? ((g.lr_grp + 63) >> 6) : 0;
+    f.fpw = (f.rK ? NKV : 0) + (f.rV ? NKV : 0) + (f.rL ? f.n_lr : 0) + (f.rLv ? f.n_lr : 0);
+#pragma unroll
+    for (int i = 0; i < NKV; ++i) {
+        int row;
+        f.kv_off[i] = kv_lane_off<T, D>(g, i, lane, &row);
+    }
+    f.lr_stride = (uint32_t)(s.lr_agent_stride * ES);
+}
+
+template <typename T, int D>
+__device__ __attribute__((always_inline)) inline void fill_group(const GroupFill &f, const Geo &g, const Src<T> &s,
+                                                                  int t0, char *stage, bool clamp, int lane) {
+    constexpr int ES = (int)sizeof(T);
+    constexpr int NKV = D * ES / 64;
     const int tg0 = t0 + 16 * f.g;  // the group's first token
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(stage));
+    const uint32_t lk0 = lds0 + 16 * (16 * f.g * g.cpr_kv), lv0 = lds0 + 16 * (g.ofs_v + 16 * f.g * g.cpr_kv);
+    const uint32_t ll0 = lds0 + 16 * (g.ofs_lk + f.g * g.lr_grp), lw0 = lds0 + 16 * (g.ofs_lv + f.g * g.lr_grp);
     if (!clamp) {
         if (f.rK || f.rV) {
             const char *kb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tg0)));
             const char *vb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tg0)));
-            const uint32_t lk0 = lds0 + 16 * (16 * f.g * g.cpr_kv), lv0 = lds0 + 16 * (g.ofs_v + 16 * f.g * g.cpr_kv);
-            if (f.kv_nt) {
 #pragma unroll
-                for (int i = 0; i < kMaxKvLoads; ++i)
-                    if (i < f.n_kv && f.rK) dma16s_nt(kb, f.kv_off[i], lk0 + 1024 * i);
+            for (int i = 0; i < NKV; ++i)
+                if (f.rK) dma16s(kb, f.kv_off[i], lk0 + 1024 * i);
 #pragma unroll
-                for (int i = 0; i < kMaxKvLoads; ++i)
-                    if (i < f.n_kv && f.rV) dma16s_nt(vb, f.kv_off[i], lv0 + 1024 * i);
-            } else {
-#pragma unroll
-                for (int i = 0; i < kMaxKvLoads; ++i)
-                    if (i < f.n_kv && f.rK) dma16s(kb, f.kv_off[i], lk0 + 1024 * i);
-#pragma unroll
-                for (int i = 0; i < kMaxKvLoads; ++i)
-                    if (i < f.n_kv && f.rV) dma16s(vb, f.kv_off[i], lv0 + 1024 * i);
-            }
+            for (int i = 0; i < NKV; ++i)
+                if (f.rV) dma16s(vb, f.kv_off[i], lv0 + 1024 * i);
         }
         if (f.rL || f.rLv) {
             const char *lk = uniform_ptr(reinterpret_cast<const char *>(s.lk + (int64_t)tg0 * s.r));
             const char *lv = uniform_ptr(reinterpret_cast<const char *>(s.lv + (int64_t)tg0 * s.r));
-            const int nchunk = 16 * g.cpa_lr;  // chunks of one group of a low-rank region
             for (int i = 0; i < f.n_lr; ++i) {
-                if (64 * i + lane < nchunk) {
+                if (64 * i + lane < g.lr_grp) {
                     int row;
-                    const uint32_t off = lr_lane_off(f, g, s, i, lane, &row);
-                    if (f.rL) dma16s(lk, off, lds0 + 16 * (g.ofs_lk + 16 * f.g * g.cpa_lr) + 1024 * i);
-                    if (f.rLv) dma16s(lv, off, lds0 + 16 * (g.ofs_lv + 16 * f.g * g.cpa_lr) + 1024 * i);
+                    const uint32_t off = lr_lane_off(f.lr_stride, g, i, lane, &row);
+                    if (f.rL) dma16s(lk, off, ll0 + 1024 * i);
+                    if (f.rLv) dma16s(lv, off, lw0 + 1024 * i);
                 }
             }
         }
@@ -163,35 +271,25 @@ __device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan 
     }
     // tail tile: per-lane rows, clamped to the item's last token
 #pragma unroll
-    for (int i = 0; i < kMaxKvLoads; ++i) {
-        if (i < f.n_kv && (f.rK || f.rV)) {
-            int tok = tg0 + f.kv_row[i];
+    for (int i = 0; i < NKV; ++i) {
+        if (f.rK || f.rV) {
+            const int row = (64 * i + lane) >> g.lg_kv;
+            int tok = tg0 + row;
             tok = tok < s.tlast ? tok : s.tlast;
-            const uint32_t rowoff = f.kv_off[i] - (uint32_t)(f.kv_row[i] * D * ES);  // chunk part
-            // (the tail tile: the default policy serves)
-            if (f.rK)
-                dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tok)) + rowoff,
-                      lds0 + 16 * (16 * f.g * g.cpr_kv) + 1024 * i);
-            if (f.rV)
-                dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tok)) + rowoff,
-                      lds0 + 16 * (g.ofs_v + 16 * f.g * g.cpr_kv) + 1024 * i);
+            const uint32_t rowoff = f.kv_off[i] - (uint32_t)(row * D * ES);  // chunk part
+            if (f.rK) dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tok)) + rowoff, lk0 + 1024 * i);
+            if (f.rV) dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tok)) + rowoff, lv0 + 1024 * i);
         }
     }
-    // (the loads are issued K then V per i here; the count per wave is the same)
-    const int nchunk = 16 * g.cpa_lr;
     for (int i = 0; i < f.n_lr; ++i) {
-        if ((f.rL || f.rLv) && 64 * i + lane < nchunk) {
+        if ((f.rL || f.rLv) && 64 * i + lane < g.lr_grp) {
             int row;
-            const uint32_t off = lr_lane_off(f, g, s, i, lane, &row);
+            const uint32_t off = lr_lane_off(f.lr_stride, g, i, lane, &row);
             int tok = tg0 + row;
             tok = tok < s.tlast ? tok : s.tlast;
             const uint32_t rel = off - (uint32_t)(row * s.r * ES);  // agent and chunk part
-            if (f.rL)
-                dma16(reinterpret_cast<const char *>(s.lk + (int64_t)tok * s.r) + rel,
-                      lds0 + 16 * (g.ofs_lk + 16 * f.g * g.cpa_lr) + 1024 * i);
-            if (f.rLv)
-                dma16(reinterpret_cast<const char *>(s.lv + (int64_t)tok * s.r) + rel,
-                      lds0 + 16 * (g.ofs_lv + 16 * f.g * g.cpa_lr) + 1024 * i);
+            if (f.rL) dma16(reinterpret_cast<const char *>(s.lk + (int64_t)tok * s.r) + rel, ll0 + 1024 * i);
+            if (f.rLv) dma16(reinterpret_cast<const char *>(s.lv + (int64_t)tok * s.r) + rel, lw0 + 1024 * i);
         }
     }
 }

@@ -138,7 +138,10 @@ def test_plan_covers_context(kw):
         assert p["resid_cols"] in (32, 64, 128)
     rg = -(-p["row_blocks"] // 4)
     pb = 1 if rpa <= 16 else -(-rpa // 16)
-    items = p["n_prefix_splits"] * rg * d.n_kv_heads + d.n_agents * (-(-pb // 4)) * p["n_priv_splits"] * d.n_kv_heads
+    H = p["heads_per_item"]
+    assert H >= 1 and d.n_kv_heads % H == 0 and (H == 1 or (d.rank and L))
+    items = (p["n_prefix_splits"] * rg * (d.n_kv_heads // H)
+             + d.n_agents * (-(-pb // 4)) * p["n_priv_splits"] * d.n_kv_heads)
     assert p["work_items"] == items
 
 
