@@ -25,6 +25,9 @@ thread_local int g_last_hip = 0;
 #define RATTN_TARGET_ITEMS 256
 #endif
 constexpr int kTargetItems = RATTN_TARGET_ITEMS;  // split-kernel workgroups aimed for
+#ifndef RATTN_LR_OWN
+#define RATTN_LR_OWN 0
+#endif
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t roundup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
@@ -93,6 +96,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     p.ps = d->page_size;
     p.shared_lr = d->shared_lr;
     p.causal = op == RATTN_OP_PREFILL;
+    p.lr_own = RATTN_LR_OWN;
     const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
     p.c = scale * 1.44269504088896340736f;
 
@@ -190,17 +194,21 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     auto max_fpw = [&](int T, int H, int lr_row_bytes, int np) {
         const int G = T / 16, nkv = 2 * H * G, npairs = nkv + (lr_row_bytes ? 2 * G : 0);
         const int n_kv = (16 * (kv_row / 16)) / 64, n_lr = (16 * (lr_row_bytes / 16) + 63) / 64;
+        const bool own = p.lr_own && lr_row_bytes && np >= 2;  // as make_fill_plan
         int mx = 0;
         for (int w = 0; w < np; ++w) {
             int f = 0;
-            for (int pi = w; pi < npairs; pi += np) f += pi < nkv ? n_kv : n_lr;
+            const int b = own ? (w == np - 1 ? nkv : w) : w, e = own && w < np - 1 ? nkv : npairs;
+            const int st = own ? (w == np - 1 ? 1 : np - 1) : np;
+            for (int pi = b; pi < e; pi += st) f += pi < nkv ? n_kv : n_lr;
             if (f > mx) mx = f;
         }
         return mx;
     };
     auto fit_vmcnt = [&](int T, int H, int lr_row_bytes, int *nst) {
-        // two load waves, four if needed, then fewer stages
-        for (int np = 2; np <= 4; np += 2) {
+        // two load waves (three when the low-rank rows have their own), four if
+        // needed, then fewer stages
+        for (int np = p.lr_own ? 3 : 2; np <= 4; np += 1) {
             const int f = max_fpw(T, H, lr_row_bytes, np);
             if (f * (*nst - 1) <= 63) {
                 if (np > p.np) p.np = np;
@@ -221,7 +229,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     // the prefix ring needs.
     auto plan_lds = [&](int nw, int min_nst) -> bool {
         p.nw = nw;
-        p.np = 2;
+        p.np = p.lr_own ? 3 : 2;
         auto pick = [&](int tg_max, int H, int lr_row_bytes, int need, int *T, int *nst, int *stage) {
             for (int t = 128; t >= 16; t /= 2) {
                 if (t % (16 * tg_max) || t > 16 * nw) continue;  // the fill gives each 16-row group one wave

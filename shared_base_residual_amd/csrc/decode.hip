@@ -441,7 +441,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
 
     // The fill plan of this wave and the lane offsets of the step's LDS reads.
     FillPlan fp;
-    make_fill_plan<T, D>(fp, g, src, resid, compute_wave ? p.np : wave - p.nw, lane, p.np);
+    make_fill_plan<T, D>(fp, g, src, resid, compute_wave ? p.np : wave - p.nw, lane, p.np, p.lr_own != 0);
     // keys and values that no other workgroup reads are streamed past the caches
     fp.kv_nt = prefix ? p.n_rg == 1 : p.n_prg == 1;
     // this wave's head: its K and V regions of the stage (chunks)
@@ -491,18 +491,27 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         wtr[jj] = resid ? lr_ofs(g, g.ofs_lv, col >> p.lr_shift, 4 * j4 + (n16 >> 2), (col & (p.r - 1)) * ES) : 0u;
     }
 
-    // Query rows as the B operand of S^T = K Q^T.
-    const T *qp = static_cast<const T *>(p.q);
-    frag qB[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qB[s] = vm ? O::load8(qp + qrow * D + 32 * s + 8 * j4) : O::zero();
-
     const int n_tiles = (t1 - t0 + g.T - 1) / g.T;
     const int fpw = fp.fpw;
     auto fill = [&](int tile, int stage) {
         const int tt = t0 + tile * g.T;
         fill_stage<T, D>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
     };
+    // ---- the load waves start the ring (tiles 0 .. nst-2) at once, while the
+    // compute waves load the query rows and form U
+    if (fpw)
+        for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
+
+    // Query rows as the B operand of S^T = K Q^T.
+    const T *qp = static_cast<const T *>(p.q);
+    frag qB[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qB[s] = O::zero();
+    if (wave_on) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            if (vm) qB[s] = O::load8(qp + qrow * D + 32 * s + 8 * j4);
+    }
 
     // U = scale*log2(e) * q Bk^T as the B operand of the rank-r score correction,
     // block-diagonal over the agents of the block (bf16 carries hi + lo halves).
@@ -612,13 +621,9 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         }
     }
 
-    // Every register load (q, Bk) has landed on every path, so the compiler has
-    // nothing pending inside the ring loop and adds no waits of its own there.
-    wait_vmcnt(0);
-
-    // ---- start the ring: tiles 0 .. nst-2
-    if (fp.fpw)
-        for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
+    // Every register load (q, Bk) of a compute wave has landed, so the compiler
+    // has nothing pending inside the ring loop and adds no waits of its own there.
+    if (compute_wave) wait_vmcnt(0);
 
     Acc<T, D, CPAD> acc;
 #pragma unroll

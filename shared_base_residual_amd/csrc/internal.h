@@ -93,6 +93,7 @@ struct DecodeParams {
     int nw;           // compute waves per workgroup (4 or 8)
     int np;           // load waves per workgroup: they issue every direct load of the
                       // ring and wait for it, so no compute wave stalls on issue
+    int lr_own;       // the last load wave fills only the low-rank regions
     // LDS staging ring: tokens per stage, stages, bytes per stage (prefix items
     // and private items), and where the split's page-table copy lives.
     int T_pre, nst_pre, stage_bytes_pre;

@@ -72,7 +72,7 @@ constexpr int kMaxKvLoads = 8;   // direct loads per group of a K (or V) region 
 struct FillPlan {
     int G;                    // groups per tile
     int npairs;               // (region, group) pairs per tile
-    int w, nw;                // this wave's index among the nw filling waves (w >= nw: none)
+    int pbeg, pend, pstep;    // the pairs this wave fills: pbeg, pbeg + pstep, ... < pend
     int n_kv, n_lr;           // loads per group of a K/V region, of an Lk/Lv region
     int fpw;                  // loads this wave issues per stage
     uint32_t lr_stride;       // bytes between agents' low-rank caches
@@ -94,19 +94,40 @@ __device__ inline uint32_t kv_lane_off(const Geo &g, int i, int lane, int *row_o
     return (uint32_t)(row * D * ES + 16 * c);
 }
 
+// wave: index among the nw filling waves (a wave with wave >= nw fills nothing).
+// lr_own: with a residual and nw >= 2, the last filling wave fills every
+// low-rank pair and the others share the K/V pairs, so that low-rank rows
+// (mostly L2 hits) do not queue behind HBM reads in one wave's load order.
 template <typename T, int D>
 __device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f, const Geo &g, const Src<T> &s,
-                                                                     bool resid, int wave, int lane, int nw) {
+                                                                     bool resid, int wave, int lane, int nw,
+                                                                     bool lr_own = false) {
     constexpr int ES = (int)sizeof(T);
     f.G = g.T >> 4;
-    const int nreg = 2 * g.H + (resid ? 2 : 0);
-    f.npairs = nreg * f.G;
-    f.w = wave < nw ? wave : f.npairs;  // a wave outside the filling set fills nothing
-    f.nw = nw;
+    const int nkv = 2 * g.H * f.G;
+    f.npairs = nkv + (resid ? 2 * f.G : 0);
+    if (wave >= nw) {
+        f.pbeg = f.pend = 0;
+        f.pstep = 1;
+    } else if (lr_own && resid && nw >= 2) {
+        if (wave == nw - 1) {
+            f.pbeg = nkv;
+            f.pend = f.npairs;
+            f.pstep = 1;
+        } else {
+            f.pbeg = wave;
+            f.pend = nkv;
+            f.pstep = nw - 1;
+        }
+    } else {
+        f.pbeg = wave;
+        f.pend = f.npairs;
+        f.pstep = nw;
+    }
     f.n_kv = (16 * g.cpr_kv) >> 6;
     f.n_lr = resid ? ((g.lr_grp + 63) >> 6) : 0;
     f.fpw = 0;
-    for (int pi = f.w; pi < f.npairs; pi += nw) f.fpw += pi < 2 * g.H * f.G ? f.n_kv : f.n_lr;
+    for (int pi = f.pbeg; pi < f.pend; pi += f.pstep) f.fpw += pi < nkv ? f.n_kv : f.n_lr;
     f.lr_stride = (uint32_t)(s.lr_agent_stride * ES);
     f.kv_nt = false;
     constexpr int NKV = D * ES / 64;  // loads per K/V group: 16 rows of d elements
@@ -147,7 +168,7 @@ __device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan 
     constexpr int ES = (int)sizeof(T);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(stage));
     const int nkv = 2 * g.H * f.G;  // K/V pairs come first
-    for (int pi = f.w; pi < f.npairs; pi += f.nw) {
+    for (int pi = f.pbeg; pi < f.pend; pi += f.pstep) {
         const int gg = pi & (f.G - 1);
         const int tg0 = t0 + 16 * gg;  // the group's first token
         if (pi < nkv) {
