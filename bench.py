@@ -11,12 +11,15 @@ Several replicas of the input set are rotated so that each step reads its
 step.
 
 Prints one JSON line.  `value` is agent x context-token pairs per second (Gtok/s).
-`roofline` is for the split kernel, which carries all but the merge: its
-algorithmic bytes per launch (every input it must read once: base K/V,
-low-rank caches, private tokens, queries, up-projections Bk) divided by its
-average duration, measured with HIP events recorded on the launch stream
-around that launch in every timed step.  `cpu_baseline` times the fp64 oracle
-on the host cores.
+`roofline` is for the split kernel, which carries all but the merge (for the
+prefill workload, the prefill kernel, which is the whole call): its algorithmic
+bytes (or flops) per launch divided by its average duration, measured with HIP
+events on the launch stream around K * layers back-to-back launches of it over
+the same rotated inputs, right after the timed steps.  `traffic` is the HBM
+bytes per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+(profiles/counters.json, written by shared_base_residual_amd/counters.py) when
+they were taken on the current library sources, else null.  `cpu_baseline`
+times the fp64 oracle on the host cores.
 """
 from __future__ import annotations
 
@@ -36,16 +39,12 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "agent x ctx-token attention throughput (Gtok/s) + achieved HBM GB/s, 1 GPU"
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "shared_base_residual_amd", "csrc", f)
-                  for f in ("decode.hip", "device.h", "internal.h")]
 
 
 def source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    from shared_base_residual_amd.build import source_hash as h
+
+    return h()
 
 
 class Hip:
@@ -222,40 +221,50 @@ def main():
         if st:
             raise R.RattnError(st, "rattn_attention_stages")
 
-    # One step = all layers' calls (one call when layers == 1).  HIP events on the
-    # launch stream bracket the split launch of layer 0 and the whole step.
+    # One step = all layers' calls (one call when layers == 1), each one
+    # rattn_attention_stages call of both launches (split, then merge).  The
+    # timed steps carry no instrumentation; HIP events on the launch stream
+    # bracket the K steps (GPU time per step).
     hip = Hip()
     K, W = args.steps, args.warmup
-    ev = [[hip.event() for _ in range(3)] for _ in range(K)]
 
-    def step(k, timed):
+    def step(k):
         for l in range(layers):
-            i = (k * layers + l) % n_sets
-            if timed and l == 0:
-                hip.record(ev[k][0], sp)
-                launch(i, R.STAGE_SPLIT)
-                hip.record(ev[k][1], sp)
-                launch(i, R.STAGE_COMBINE)
-            else:
-                launch(i, R.STAGE_ALL)
-        if timed:
-            hip.record(ev[k][2], sp)
+            launch((k * layers + l) % n_sets, R.STAGE_ALL)
 
     for k in range(W):
-        step(k, False)
+        step(k)
     torch.cuda.synchronize()
+    ev_a, ev_b = hip.event(), hip.event()
     t0 = time.perf_counter()
+    hip.record(ev_a, sp)
     for k in range(K):
-        step(k, True)
+        step(k)
+    hip.record(ev_b, sp)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    step_ms_ev = hip.elapsed_ms(ev_a, ev_b) / K
 
-    kern_ms = [hip.elapsed_ms(ev[k][0], ev[k][1]) for k in range(K)]
-    step_ms_ev = [hip.elapsed_ms(ev[k][0], ev[k][2]) for k in range(K)]
+    # The kernel behind the roofline (the split kernel; for prefill the one
+    # kernel of the call): the same inputs, launched back to back K * layers
+    # times between two HIP events on the launch stream, so that the average
+    # is the kernel's own duration (a per-launch event pair would add the
+    # event and submission latency of every launch).
+    n_k = K * layers
+    for i in range(min(n_k, 4)):
+        launch(i % n_sets, R.STAGE_SPLIT)
+    torch.cuda.synchronize()
+    ev_c, ev_d = hip.event(), hip.event()
+    hip.record(ev_c, sp)
+    for i in range(n_k):
+        launch(i % n_sets, R.STAGE_SPLIT)
+    hip.record(ev_d, sp)
+    torch.cuda.synchronize()
+    kern_avg = hip.elapsed_ms(ev_c, ev_d) / n_k
+
     ms_step = wall * 1e3 / K
     pairs = pairs_per_call(case) * layers
     value = pairs / (ms_step / 1e3) / 1e9
-    kern_avg = statistics.mean(kern_ms)
     if case.mode == "prefill" and case.dtype == "bf16":
         # MFMA-bound: the prefill kernel does the whole call (no merge launch)
         fl = algorithmic_flops(case)
@@ -265,7 +274,7 @@ def main():
                 "traffic": traffic_from_counters(f"prefill_cfg{args.config}"),
                 "kernel": "prefill_kernel", "flops_per_launch": fl,
                 "avg_launch_us": round(kern_avg * 1e3, 2),
-                "median_launch_us": round(statistics.median(kern_ms) * 1e3, 2)}
+                "launches_timed": n_k}
     else:
         achieved = ab["split"] / (kern_avg / 1e3) / 1e9
         traffic = traffic_from_counters(f"decode_cfg{args.config}")
@@ -273,7 +282,7 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": "decode_split_kernel", "bytes_per_launch": ab["split"],
                 "avg_launch_us": round(kern_avg * 1e3, 2),
-                "median_launch_us": round(statistics.median(kern_ms) * 1e3, 2)}
+                "launches_timed": n_k}
     res = {
         "metric": METRIC, "value": round(value, 4), "unit": "Gtok/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -283,7 +292,7 @@ def main():
                    "priv_len": case.priv_len, "q_len": case.q_len, "rank": case.rank, "page_size": case.page_size,
                    "shared_lr": case.shared_lr, "layers": layers, "mode": case.mode, "input_sets_rotated": n_sets},
         "hbm_gbps_call": round(ab["call"] * layers / (ms_step / 1e3) / 1e9, 1),
-        "gpu_ms_per_step_events": round(statistics.mean(step_ms_ev), 5),
+        "gpu_ms_per_step_events": round(step_ms_ev, 5),
         "roofline": roof,
     }
     if not args.no_cpu:

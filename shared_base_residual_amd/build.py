@@ -23,6 +23,20 @@ SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "gather.hip"]
 ARCH = "gfx950"
 
 
+def source_hash() -> str:
+    """Hash of every library source (kernels, host planner, public header): a
+    measurement taken on other sources no longer describes the built kernels."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)) + ["../../include/rattn.h"]:
+        path = os.path.normpath(os.path.join(CSRC, name))
+        if os.path.isfile(path):
+            with open(path, "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
