@@ -178,6 +178,8 @@ typedef struct rattn_plan_info {
     int32_t work_items;       /* workgroups of the split kernel */
     int32_t heads_per_item;   /* KV heads one prefix workgroup serves (sharing its low-rank tile) */
     int32_t waves;            /* waves per split workgroup (compute + load) */
+    int32_t masked;           /* 1: per-agent caches, several agents per block, residual columns = rank */
+    int32_t blocks_per_group; /* row blocks one prefix workgroup serves */
 } rattn_plan_info;
 
 int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info);

@@ -64,7 +64,8 @@ class PlanInfo(ctypes.Structure):
                 ("n_priv_splits", ctypes.c_int32), ("priv_split_len", ctypes.c_int64),
                 ("row_blocks", ctypes.c_int32), ("agents_per_block", ctypes.c_int32),
                 ("resid_cols", ctypes.c_int32), ("work_items", ctypes.c_int32),
-                ("heads_per_item", ctypes.c_int32), ("waves", ctypes.c_int32)]
+                ("heads_per_item", ctypes.c_int32), ("waves", ctypes.c_int32), ("masked", ctypes.c_int32),
+                ("blocks_per_group", ctypes.c_int32)]
 
 
 _lib = None

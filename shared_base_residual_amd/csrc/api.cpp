@@ -100,198 +100,242 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
     p.c = scale * 1.44269504088896340736f;
 
-    // Row blocks over the prefix.
-    if (rpa <= 16) {
-        int apb = 16 / rpa;
-        if (resid && !d->shared_lr) {
-            const int cap = d->dtype == RATTN_BF16 ? rattn::kMaxResidCols : rattn::kMaxResidColsF32;
-            const int by_cols = cap / r;
-            if (by_cols < apb) apb = by_cols;
-        }
-        if (apb > N) apb = N;
-        if (apb < 1) apb = 1;
-        p.apb = apb;
-        p.bpa = 1;
-        p.n_blocks = (int)cdiv(N, apb);
-        p.pb = 1;
-    } else {
-        p.apb = 1;
-        p.bpa = (int)cdiv(rpa, 16);
-        p.n_blocks = N * p.bpa;
-        p.pb = p.bpa;
-    }
-    p.n_rg = (int)cdiv(p.n_blocks, 4);
-    p.n_prg = (int)cdiv(p.pb, 4);
-    int cols = 0;
-    if (resid) cols = d->shared_lr ? r : (rpa <= 16 ? p.apb * r : r);
-    pl->cpad = resid ? (pow2ceil(cols) < 32 ? 32 : pow2ceil(cols)) : 0;
-    if (pl->cpad > rattn::kMaxResidColsHard) return RATTN_E_UNSUPPORTED;
-
-    const int es = (int)esize(d->dtype);
-    const int kv_row = D * es;  // bytes of one key (or value) row
-    int ag_max = 1;             // agents of one prefix row group
-    int nb_min = 4, nb_max = 1; // row blocks of the prefix row groups
-    for (int rg = 0; L > 0 && rg < p.n_rg; ++rg) {
-        const int b0 = 4 * rg;
-        const int nb = p.n_blocks - b0 < 4 ? p.n_blocks - b0 : 4;
-        const rattn::RowBlock x0 = rattn::prefix_block(b0, N, rpa, p.apb, p.bpa);
-        const rattn::RowBlock x1 = rattn::prefix_block(b0 + nb - 1, N, rpa, p.apb, p.bpa);
-        const int na = x1.a0 + x1.na - x0.a0;
-        if (na > ag_max) ag_max = na;
-        if (nb < nb_min) nb_min = nb;
-        if (nb > nb_max) nb_max = nb;
-    }
-    // the stage fill addresses one workgroup's low-rank rows with 32-bit offsets
-    if (resid && (int64_t)(d->shared_lr ? 1 : ag_max) * L * r * es >= (1ll << 31)) return RATTN_E_UNSUPPORTED;
-    // low-rank bytes per token of a stage: every agent of the row group (or the shared cache)
-    const int lr_row = resid ? (d->shared_lr ? 1 : ag_max) * r * es : 0;
-
-    // Context splits for H KV heads per prefix item.
-    auto plan_splits = [&](int H) -> int {
-        p.H = H;
-        p.n_hg = HK / H;
-        p.n_ps = 0;
-        p.n_pv = 0;
-        if (L > 0) {
-            const int64_t base = (int64_t)p.n_hg * p.n_rg;
-            int64_t n = cdiv(kTargetItems, base);
-            const int64_t nmax = cdiv(L, rattn::kSplitQuantum);
-            if (n > nmax) n = nmax;
-            if (n < 1) n = 1;
-            // n splits of a 128-multiple length; trailing splits may be empty, which
-            // keeps the split count (and the workspace) non-decreasing in L.
-            p.tok_ps = (int)roundup(cdiv(L, n), rattn::kSplitQuantum);
-            p.n_ps = (int)n;
-        }
-        if (S > 0) {
-            const int64_t base = (int64_t)N * HK * p.n_prg;
-            int64_t n = cdiv(kTargetItems, base);
-            const int64_t nmax = cdiv(S, rattn::kSplitQuantum);
-            if (n > nmax) n = nmax;
-            if (n < 1) n = 1;
-            p.tok_pv = (int)roundup(cdiv(S, n), rattn::kSplitQuantum);
-            p.n_pv = (int)n;
-        }
-        p.n_slots = p.n_ps + p.n_pv;
-        if (p.n_slots > rattn::kMaxSlots) return RATTN_E_UNSUPPORTED;
-        const int64_t n_pre = (int64_t)p.n_ps * p.n_rg * p.n_hg;
-        const int64_t n_all = n_pre + (int64_t)N * p.n_prg * p.n_pv * HK;
-        if (n_all > (1ll << 30)) return RATTN_E_UNSUPPORTED;
-        p.n_prefix_items = (int)n_pre;
-        p.n_items = (int)n_all;
-        p.pre_per = (int)cdiv(n_pre, 8);
-        p.pv_per = (int)cdiv(n_all - n_pre, 8);
-        p.per_xcd = p.pre_per + p.pv_per;
-        if (d->page_size > 0 && L > 0 && cdiv(p.tok_ps, d->page_size) + 1 > rattn::kMaxPagesPerSplit)
-            return RATTN_E_UNSUPPORTED;
-        return RATTN_OK;
-    };
-
-    // Loads the busiest of np load waves issues per stage (the fill plan's
-    // round-robin of (region, group) pairs over 2H K/V regions and, with a
-    // residual, the Lk and Lv regions); a wave may have at most 63 loads
-    // outstanding, and a ring keeps nst - 1 stages in flight.
-    auto max_fpw = [&](int T, int H, int lr_row_bytes, int np) {
-        const int G = T / 16, nkv = 2 * H * G, npairs = nkv + (lr_row_bytes ? 2 * G : 0);
-        const int n_kv = (16 * (kv_row / 16)) / 64, n_lr = (16 * (lr_row_bytes / 16) + 63) / 64;
-        const bool own = p.lr_own && lr_row_bytes && np >= 2;  // as make_fill_plan
-        int mx = 0;
-        for (int w = 0; w < np; ++w) {
-            int f = 0;
-            const int b = own ? (w == np - 1 ? nkv : w) : w, e = own && w < np - 1 ? nkv : npairs;
-            const int st = own ? (w == np - 1 ? 1 : np - 1) : np;
-            for (int pi = b; pi < e; pi += st) f += pi < nkv ? n_kv : n_lr;
-            if (f > mx) mx = f;
-        }
-        return mx;
-    };
-    auto fit_vmcnt = [&](int T, int H, int lr_row_bytes, int *nst) {
-        // two load waves (three when the low-rank rows have their own), four if
-        // needed, then fewer stages
-        for (int np = p.lr_own ? 3 : 2; np <= 4; np += 1) {
-            const int f = max_fpw(T, H, lr_row_bytes, np);
-            if (f * (*nst - 1) <= 63) {
-                if (np > p.np) p.np = np;
-                return true;
+    // The decomposition: the masked mode first where it applies, else (or when
+    // its ring does not fit) block-diagonal residual columns.
+    auto plan_rows = [&](bool mask_ok) -> int {
+        // Row blocks over the prefix.  bf16 per-agent caches of rank >= 32 put as many
+        // agents in a block as its 16 rows hold (the masked mode: U and W stay r
+        // columns wide); otherwise the agents of a block are bounded by the residual
+        // columns their block-diagonal U and W take.
+        const bool can_mask = mask_ok && resid && !d->shared_lr && d->dtype == RATTN_BF16 && r >= 32;
+        if (rpa <= 16) {
+            int apb = 16 / rpa;
+            if (resid && !d->shared_lr && !can_mask) {
+                const int cap = d->dtype == RATTN_BF16 ? rattn::kMaxResidCols : rattn::kMaxResidColsF32;
+                const int by_cols = cap / r;
+                if (by_cols < apb) apb = by_cols;
             }
+            if (apb > N) apb = N;
+            if (apb < 1) apb = 1;
+            p.apb = apb;
+            p.bpa = 1;
+            p.n_blocks = (int)cdiv(N, apb);
+            p.pb = 1;
+        } else {
+            p.apb = 1;
+            p.bpa = (int)cdiv(rpa, 16);
+            p.n_blocks = N * p.bpa;
+            p.pb = p.bpa;
         }
-        const int f = max_fpw(T, H, lr_row_bytes, 4);
-        p.np = 4;
-        while (*nst > 2 && f * (*nst - 1) > 63) --*nst;
-        return f * (*nst - 1) <= 63;
-    };
+        p.n_prg = (int)cdiv(p.pb, 4);
+        p.masked = can_mask && rpa <= 16 && p.apb > 1;
+        int cols = 0;
+        if (resid) cols = d->shared_lr || p.masked ? r : (rpa <= 16 ? p.apb * r : r);
+        pl->cpad = resid ? (pow2ceil(cols) < 32 ? 32 : pow2ceil(cols)) : 0;
+        if (pl->cpad > rattn::kMaxResidColsHard) return RATTN_E_UNSUPPORTED;
 
-    // LDS staging ring.  A stage holds T tokens of keys and values of the item's
-    // heads and, for prefix items with a residual, the low-rank rows (Lk and Lv)
-    // of every agent the workgroup serves (agent-major within each 16-token
-    // group).  T must give every wave whole 16-token steps: a row group of nblk
-    // blocks of H heads runs nw / (H nblk) waves per row tile.  min_nst: stages
-    // the prefix ring needs.
-    auto plan_lds = [&](int nw, int min_nst) -> bool {
-        p.nw = nw;
-        p.np = p.lr_own ? 3 : 2;
-        auto pick = [&](int tg_max, int H, int lr_row_bytes, int need, int *T, int *nst, int *stage) {
-            for (int t = 128; t >= 16; t /= 2) {
-                if (t % (16 * tg_max) || t > 16 * nw) continue;  // the fill gives each 16-row group one wave
-                const int sb = t * (2 * H * kv_row + 2 * lr_row_bytes);
-                const int n = rattn::kLdsBudget / sb;
-                if (n >= 3 || (t == 16 * tg_max && n >= need)) {
-                    *T = t;
-                    *nst = n < 4 ? n : 4;
-                    *stage = sb;
+        const int es = (int)esize(d->dtype);
+        const int kv_row = D * es;  // bytes of one key (or value) row
+        // Row groups of bpg blocks: the agents of a group, and the low-rank bytes per
+        // token a stage holds for them (or for the shared cache).
+        int ag_max = 1, nb_min = 4, nb_max = 1, lr_row = 0;
+        auto group_stats = [&](int bpg) -> int {
+            p.bpg = bpg;
+            p.n_rg = (int)cdiv(p.n_blocks, bpg);
+            ag_max = 1;
+            nb_min = bpg;
+            nb_max = 1;
+            for (int rg = 0; L > 0 && rg < p.n_rg; ++rg) {
+                const int b0 = bpg * rg;
+                const int nb = p.n_blocks - b0 < bpg ? p.n_blocks - b0 : bpg;
+                const rattn::RowBlock x0 = rattn::prefix_block(b0, N, rpa, p.apb, p.bpa);
+                const rattn::RowBlock x1 = rattn::prefix_block(b0 + nb - 1, N, rpa, p.apb, p.bpa);
+                const int na = x1.a0 + x1.na - x0.a0;
+                if (na > ag_max) ag_max = na;
+                if (nb < nb_min) nb_min = nb;
+                if (nb > nb_max) nb_max = nb;
+            }
+            // the stage fill addresses one workgroup's low-rank rows with 32-bit offsets
+            if (resid && (int64_t)(d->shared_lr ? 1 : ag_max) * L * r * es >= (1ll << 31)) return RATTN_E_UNSUPPORTED;
+            lr_row = resid ? (d->shared_lr ? 1 : ag_max) * r * es : 0;
+            return RATTN_OK;
+        };
+
+        // Context splits for H KV heads per prefix item.
+        auto plan_splits = [&](int H) -> int {
+            p.H = H;
+            p.n_hg = HK / H;
+            p.n_ps = 0;
+            p.n_pv = 0;
+            if (L > 0) {
+                const int64_t base = (int64_t)p.n_hg * p.n_rg;
+                int64_t n = cdiv(kTargetItems, base);
+                const int64_t nmax = cdiv(L, rattn::kSplitQuantum);
+                if (n > nmax) n = nmax;
+                if (n < 1) n = 1;
+                // n splits of a 128-multiple length; trailing splits may be empty, which
+                // keeps the split count (and the workspace) non-decreasing in L.
+                p.tok_ps = (int)roundup(cdiv(L, n), rattn::kSplitQuantum);
+                p.n_ps = (int)n;
+            }
+            if (S > 0) {
+                const int64_t base = (int64_t)N * HK * p.n_prg;
+                int64_t n = cdiv(kTargetItems, base);
+                const int64_t nmax = cdiv(S, rattn::kSplitQuantum);
+                if (n > nmax) n = nmax;
+                if (n < 1) n = 1;
+                p.tok_pv = (int)roundup(cdiv(S, n), rattn::kSplitQuantum);
+                p.n_pv = (int)n;
+            }
+            p.n_slots = p.n_ps + p.n_pv;
+            if (p.n_slots > rattn::kMaxSlots) return RATTN_E_UNSUPPORTED;
+            const int64_t n_pre = (int64_t)p.n_ps * p.n_rg * p.n_hg;
+            const int64_t n_all = n_pre + (int64_t)N * p.n_prg * p.n_pv * HK;
+            if (n_all > (1ll << 30)) return RATTN_E_UNSUPPORTED;
+            p.n_prefix_items = (int)n_pre;
+            p.n_items = (int)n_all;
+            p.pre_per = (int)cdiv(n_pre, 8);
+            p.pv_per = (int)cdiv(n_all - n_pre, 8);
+            p.per_xcd = p.pre_per + p.pv_per;
+            if (d->page_size > 0 && L > 0 && cdiv(p.tok_ps, d->page_size) + 1 > rattn::kMaxPagesPerSplit)
+                return RATTN_E_UNSUPPORTED;
+            return RATTN_OK;
+        };
+
+        // Loads the busiest of np load waves issues per stage (the fill plan's
+        // round-robin of (region, group) pairs over 2H K/V regions and, with a
+        // residual, the Lk and Lv regions); a wave may have at most 63 loads
+        // outstanding, and a ring keeps nst - 1 stages in flight.
+        auto max_fpw = [&](int T, int H, int lr_row_bytes, int np) {
+            const int G = T / 16, nkv = 2 * H * G, npairs = nkv + (lr_row_bytes ? 2 * G : 0);
+            const int n_kv = (16 * (kv_row / 16)) / 64, n_lr = (16 * (lr_row_bytes / 16) + 63) / 64;
+            const bool own = p.lr_own && lr_row_bytes && np >= 2;  // as make_fill_plan
+            int mx = 0;
+            for (int w = 0; w < np; ++w) {
+                int f = 0;
+                const int b = own ? (w == np - 1 ? nkv : w) : w, e = own && w < np - 1 ? nkv : npairs;
+                const int st = own ? (w == np - 1 ? 1 : np - 1) : np;
+                for (int pi = b; pi < e; pi += st) f += pi < nkv ? n_kv : n_lr;
+                if (f > mx) mx = f;
+            }
+            return mx;
+        };
+        auto fit_vmcnt = [&](int T, int H, int lr_row_bytes, int *nst) {
+            // two load waves (three when the low-rank rows have their own), four if
+            // needed, then fewer stages
+            for (int np = p.lr_own ? 3 : 2; np <= 4; np += 1) {
+                const int f = max_fpw(T, H, lr_row_bytes, np);
+                if (f * (*nst - 1) <= 63) {
+                    if (np > p.np) p.np = np;
                     return true;
                 }
             }
-            return false;
+            const int f = max_fpw(T, H, lr_row_bytes, 4);
+            p.np = 4;
+            while (*nst > 2 && f * (*nst - 1) > 63) --*nst;
+            return f * (*nst - 1) <= 63;
         };
-        int lds_ring = 0;
-        if (L > 0) {
-            if (p.H * nb_max > nw) return false;
-            const int tg_max = nw / (p.H * nb_min);
-            if (!pick(tg_max, p.H, lr_row, min_nst, &p.T_pre, &p.nst_pre, &p.stage_bytes_pre)) return false;
-            if (!fit_vmcnt(p.T_pre, p.H, lr_row, &p.nst_pre)) return false;
-            lds_ring = p.nst_pre * p.stage_bytes_pre;
-        }
-        if (S > 0) {
-            int tg_max = 1;
-            for (int g0 = 0; g0 < p.pb; g0 += 4) {
-                const int nb = p.pb - g0 < 4 ? p.pb - g0 : 4;
-                if (nw / nb > tg_max) tg_max = nw / nb;
-            }
-            if (!pick(tg_max, 1, 0, 2, &p.T_pv, &p.nst_pv, &p.stage_bytes_pv)) return false;
-            if (!fit_vmcnt(p.T_pv, 1, 0, &p.nst_pv)) return false;
-            const int b = p.nst_pv * p.stage_bytes_pv;
-            if (b > lds_ring) lds_ring = b;
-        }
-        // After the ring, the token-group merge (one slot of per-lane state per
-        // wave) reuses the same memory.
-        const int cpl = pl->cpad > 0 ? pl->cpad / 16 : 1;
-        const int per_lane = 4 * (D / 16) + 4 * cpl;
-        int lds = lds_ring;
-        const int lds_merge = nw * (64 * per_lane + 32) * (int)sizeof(float);
-        if (lds_merge > lds) lds = lds_merge;
-        // The split's page-table entries.
-        p.table_lds_off = (lds + 15) & ~15;
-        if (d->page_size > 0 && L > 0) lds = p.table_lds_off + (int)(cdiv(p.tok_ps, d->page_size) + 1) * 4;
-        if (lds > rattn::kLdsBudget) return false;
-        pl->lds = (size_t)lds;
-        return true;
-    };
 
-    // Several KV heads per prefix item share its staged low-rank rows (read once
-    // instead of once per head): the most heads whose row tiles fit eight waves
-    // and whose ring still keeps two or more tiles in flight.  Eight waves (two
-    // per SIMD) when an item has two or more row tiles, else four.
-    bool planned = false;
-    for (int H = 8; H >= 1 && !planned; H /= 2) {
-        if (HK % H || (H > 1 && !resid)) continue;
-        const int st = plan_splits(H);
-        if (st != RATTN_OK) return st;
-        const int tiles_min = L > 0 ? H * nb_min : (p.pb < 4 ? p.pb : 4);
-        const int need = H > 1 ? 3 : 2;
-        planned = (tiles_min >= 2 && plan_lds(8, need)) || plan_lds(4, need);
-    }
-    if (!planned) return RATTN_E_UNSUPPORTED;
+        // LDS staging ring.  A stage holds T tokens of keys and values of the item's
+        // heads and, for prefix items with a residual, the low-rank rows (Lk and Lv)
+        // of every agent the workgroup serves (agent-major within each 16-token
+        // group).  T must give every wave whole 16-token steps: a row group of nblk
+        // blocks of H heads runs nw / (H nblk) waves per row tile.  min_nst: stages
+        // the prefix ring needs.
+        auto plan_lds = [&](int nw, int min_nst) -> bool {
+            p.nw = nw;
+            p.np = p.lr_own ? 3 : 2;
+            auto pick = [&](int tg_max, int H, int lr_row_bytes, int need, int *T, int *nst, int *stage) {
+                for (int t = 128; t >= 16; t /= 2) {
+                    if (t % (16 * tg_max) || t > 16 * nw) continue;  // the fill gives each 16-row group one wave
+                    const int sb = t * (2 * H * kv_row + 2 * lr_row_bytes);
+                    const int n = rattn::kLdsBudget / sb;
+                    if (n >= 3 || (t == 16 * tg_max && n >= need)) {
+                        *T = t;
+                        *nst = n < 4 ? n : 4;
+                        *stage = sb;
+                        return true;
+                    }
+                }
+                return false;
+            };
+            int lds_ring = 0;
+            if (L > 0) {
+                if (p.H * nb_max > nw) return false;
+                const int tg_max = nw / (p.H * nb_min);
+                if (!pick(tg_max, p.H, lr_row, min_nst, &p.T_pre, &p.nst_pre, &p.stage_bytes_pre)) return false;
+                if (!fit_vmcnt(p.T_pre, p.H, lr_row, &p.nst_pre)) return false;
+                lds_ring = p.nst_pre * p.stage_bytes_pre;
+            }
+            if (S > 0) {
+                int tg_max = 1;
+                for (int g0 = 0; g0 < p.pb; g0 += 4) {
+                    const int nb = p.pb - g0 < 4 ? p.pb - g0 : 4;
+                    if (nw / nb > tg_max) tg_max = nw / nb;
+                }
+                if (!pick(tg_max, 1, 0, 2, &p.T_pv, &p.nst_pv, &p.stage_bytes_pv)) return false;
+                if (!fit_vmcnt(p.T_pv, 1, 0, &p.nst_pv)) return false;
+                const int b = p.nst_pv * p.stage_bytes_pv;
+                if (b > lds_ring) lds_ring = b;
+            }
+            // After the ring, the token-group merge (one slot of per-lane state per
+            // wave) reuses the same memory.
+            const int cpl = pl->cpad > 0 ? pl->cpad / 16 : 1;
+            const int per_lane = 4 * (D / 16) + 4 * cpl;
+            int lds = lds_ring;
+            const int lds_merge = nw * (64 * per_lane + 32) * (int)sizeof(float);
+            if (lds_merge > lds) lds = lds_merge;
+            // The split's page-table entries.
+            p.table_lds_off = (lds + 15) & ~15;
+            if (d->page_size > 0 && L > 0) lds = p.table_lds_off + (int)(cdiv(p.tok_ps, d->page_size) + 1) * 4;
+            if (lds > rattn::kLdsBudget) return false;
+            pl->lds = (size_t)lds;
+            return true;
+        };
+
+        // Several KV heads per prefix item share its staged low-rank rows (read once
+        // instead of once per head): the most heads whose row tiles fit eight waves
+        // and whose ring still keeps two or more tiles in flight.  Eight waves (two
+        // per SIMD) when an item has two or more row tiles, else four.
+        // Among the row-group sizes (4, 2 or 1 blocks) and head counts that plan,
+        // the one that reads the fewest bytes per context token into the
+        // workgroups: each row group reads the K/V of every head, each (head group,
+        // row group) its agents' low-rank rows.
+        bool planned = false;
+        int64_t best_cost = -1;
+        rattn::DecodeParams best;
+        size_t best_lds = 0;
+        for (int bpg = 4; bpg >= 1; bpg /= 2) {
+            if (bpg > 1 && bpg > p.n_blocks && bpg != 4) continue;
+            const int gs = group_stats(bpg);
+            if (gs != RATTN_OK) return gs;
+            bool ok = false;
+            for (int H = 8; H >= 1 && !ok; H /= 2) {
+                if (HK % H || (H > 1 && !resid)) continue;
+                const int st = plan_splits(H);
+                if (st != RATTN_OK) return st;
+                const int tiles_min = L > 0 ? H * nb_min : (p.pb < 4 ? p.pb : 4);
+                const int need = H > 1 ? 3 : 2;
+                ok = (tiles_min >= 2 && plan_lds(8, need)) || plan_lds(4, need);
+            }
+            if (!ok) continue;
+            const int64_t cost = (int64_t)p.n_rg * HK * 2 * kv_row + (int64_t)p.n_hg * p.n_rg * 2 * lr_row;
+            if (best_cost < 0 || cost < best_cost) {
+                best_cost = cost;
+                best = p;
+                best_lds = pl->lds;
+            }
+            planned = true;
+            if (L == 0 || !resid) break;  // nothing to trade
+        }
+        if (!planned) return RATTN_E_UNSUPPORTED;
+        p = best;
+        pl->lds = best_lds;
+        return RATTN_OK;
+    };
+    int pst = plan_rows(true);
+    if (pst != RATTN_OK) pst = plan_rows(false);
+    if (pst != RATTN_OK) return pst;
 
     // Workspace: the (max, sum), O and W partials of every (KV head, row, split).
     const int64_t rows_kv = (int64_t)HK * N * rpa;
@@ -525,6 +569,8 @@ int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info) {
     info->work_items = pl.dp.n_items;
     info->heads_per_item = pl.dp.H;
     info->waves = pl.dp.nw + pl.dp.np;
+    info->masked = pl.dp.masked;
+    info->blocks_per_group = pl.dp.bpg;
     return RATTN_OK;
 }
 

@@ -157,11 +157,18 @@ __device__ inline void step16(Acc<T, D, CPAD> &acc, const ReadOfs<T, D, CPAD> &r
 // d = 16*jj + m in row m (lane (n16, j4) holds d = 16*jj + 4*j4 + i).
 // vtr / wtr: lane offsets of the transposed V and Lv reads; U (uH, uL) is
 // unscaled.
-template <int D, int CPAD>
+// MASKED: the tile's rows belong to na agents with separate rank-CPAD caches;
+// the score correction runs per agent against that agent's Lk rows with U kept
+// only in the lanes of its rows, and W accumulates per agent with P kept only in
+// those lanes, so W (and U) hold CPAD columns whatever the number of agents.
+// arow: the agent (0 .. na-1 within the tile) of this lane's row, -1 if none;
+// ast: LDS bytes from one agent's low-rank rows to the next.
+template <int D, int CPAD, bool MASKED>
 __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, D, CPAD> &ro, const uint32_t *vtr,
                                    const uint32_t *wtr, const char *kvb, const char *lrb, int t, bool masked,
                                    const Ops<bf16>::frag *qB, const Ops<bf16>::frag *uH, const Ops<bf16>::frag *uL,
-                                   float cl2, bool resid, int t1, bool causal, int tq, int j4) {
+                                   float cl2, bool resid, int t1, bool causal, int tq, int j4, int na, int arow,
+                                   int ast) {
     using O = Ops<bf16>;
     using frag = O::frag;
     using frag4 = O::frag4;
@@ -187,10 +194,29 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
 #pragma unroll
     for (int s = 0; s < KS; ++s) a = O::mma(kf[s], qB[s], a);
     if (CS > 0 && resid) {
+        if constexpr (MASKED) {
+            const frag zf = O::zero();
+            for (int ag = 0; ag < na; ++ag) {
+                const bool mine = arow == ag;
+                if (ag > 0) {
 #pragma unroll
-        for (int s = 0; s < CS; ++s) {
-            a = O::mma(lf[s], uH[s], a);
-            a = O::mma(lf[s], uL[s], a);
+                    for (int s = 0; s < CS; ++s) {
+                        const Row<bf16, 8> lr = lds_get<bf16, 8>(lrb + ag * ast, ro.lk[s]);
+                        __builtin_memcpy(&lf[s], &lr, sizeof(frag));
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < CS; ++s) {
+                    a = O::mma(lf[s], mine ? uH[s] : zf, a);
+                    a = O::mma(lf[s], mine ? uL[s] : zf, a);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < CS; ++s) {
+                a = O::mma(lf[s], uH[s], a);
+                a = O::mma(lf[s], uL[s], a);
+            }
         }
     }
     // value operands: issued now, consumed after the softmax
@@ -244,11 +270,29 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     }
     if constexpr (CPL > 0) {
         if (resid) {
+            if constexpr (MASKED) {
+                frag4 pz;
+                pz.v = bf16x4{};
+                for (int ag = 0; ag < na; ++ag) {
+                    const frag4 pa = arow == ag ? pB : pz;
+                    if (ag > 0) {
 #pragma unroll
-            for (int jj = 0; jj < CPL; ++jj) {
-                frag4 wA;
-                wA.v = wa[jj];
-                acc.w[jj] = O::mma16(wA, pB, acc.w[jj]);
+                        for (int jj = 0; jj < CPL; ++jj) wa[jj] = lds_tr4(lrb + ag * ast + wtr[jj]);
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < CPL; ++jj) {
+                        frag4 wA;
+                        wA.v = wa[jj];
+                        acc.w[jj] = O::mma16(wA, pa, acc.w[jj]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < CPL; ++jj) {
+                    frag4 wA;
+                    wA.v = wa[jj];
+                    acc.w[jj] = O::mma16(wA, pB, acc.w[jj]);
+                }
             }
         }
     }
@@ -258,7 +302,10 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
 
 // MAXW: most waves a workgroup of this instantiation runs (compute + load
 // waves): 8 leaves each wave up to 256 VGPRs, 12 up to 168.
-template <typename T, int D, int CPAD, int MAXW>
+// MASKED (bf16, per-agent caches of rank CPAD >= 32 with several agents per
+// 16-row block): U and W hold CPAD columns and the rank-r products run per agent
+// of the block (see step16_bf16).
+template <typename T, int D, int CPAD, bool MASKED, int MAXW>
 __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p) {
     using O = Ops<T>;
     using frag = typename O::frag;
@@ -304,8 +351,8 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         const int rest = li / p.n_hg;
         const int rg = rest % p.n_rg;
         const int s = rest / p.n_rg;
-        blk0 = rg * 4;
-        nblk = p.n_blocks - blk0 < 4 ? p.n_blocks - blk0 : 4;
+        blk0 = rg * p.bpg;
+        nblk = p.n_blocks - blk0 < p.bpg ? p.n_blocks - blk0 : p.bpg;
         t0 = s * p.tok_ps;
         t1 = t0 + p.tok_ps < p.L ? t0 + p.tok_ps : (int)p.L;
         slot = s;
@@ -365,6 +412,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     const bool vm = wave_on && n16 < blk.nr;
     int agent_m = 0, ria = 0;
     if (vm) block_row(blk, n16, p.rpa, &agent_m, &ria);
+    const int arow_m = agent_m - blk.a0;  // the row's agent within the block
     const int tq = ria / p.g, hh = ria % p.g;
     const int64_t qrow = ((int64_t)agent_m * p.QL + tq) * p.HQ + (int64_t)k * p.g + hh;
     const int64_t grow = (int64_t)agent_m * p.rpa + ria;
@@ -526,7 +574,53 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         uH[s] = O::zero();
         uL[s] = O::zero();
     }
-    if (CPAD > 0 && resid && wave_on && n_tiles > 0 && !p.shared_lr) {
+    if (MASKED && resid && wave_on && n_tiles > 0) {
+        // Per-agent caches, one agent at a time: U^T = Bk_a Q^T for every row of
+        // the block, kept in the lanes of agent a's rows (the columns are that
+        // agent's own, so every lane ends with its own agent's U).
+        const T *bk = static_cast<const T *>(p.bk);
+        const int64_t ldb = (int64_t)p.HK * D;
+        float uv[CSx][8];
+#pragma unroll
+        for (int s = 0; s < CSx; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) uv[s][i] = 0.0f;
+        for (int ag = 0; ag < blk.na; ++ag) {
+            frag bkf[CSx][2][KS];
+#pragma unroll
+            for (int s = 0; s < CSx; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int crow = 32 * s + 8 * (n16 >> 2) + 4 * h + (n16 & 3);  // A-operand row (< CPAD = r)
+                    const T *brow = bk + ((int64_t)(blk.a0 + ag) * p.r + crow) * ldb + (int64_t)k * D + 8 * j4;
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2) bkf[s][h][s2] = O::load8(brow + 32 * s2);
+                }
+            const bool keep = vm && arow_m == ag;
+#pragma unroll
+            for (int s = 0; s < CSx; ++s)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s2 = 0; s2 < KS; ++s2) a = O::mma(bkf[s][h][s2], qB[s2], a);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (keep) uv[s][4 * h + i] = a[i] * uscale;
+                }
+        }
+#pragma unroll
+        for (int s = 0; s < CSx; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                O::set(uH[s], i, uv[s][i]);
+                if constexpr (O::kSplitU) {
+                    const float hi = (float)(bf16)uv[s][i];
+                    O::set(uL[s], i, uv[s][i] - hi);
+                }
+            }
+    }
+    if (!MASKED && CPAD > 0 && resid && wave_on && n_tiles > 0 && !p.shared_lr) {
         // Per-agent caches: one Bk row per A-operand row; every load is issued
         // before the first MFMA (one memory round trip).
         const T *bk = static_cast<const T *>(p.bk);
@@ -647,8 +741,9 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
             for (int u = 0; u < spw; ++u) {
                 const int row0 = 16 * (tg * spw + u);
                 if constexpr (kBf16)
-                    step16_bf16<D, CPAD>(acc, ro, vtr, wtr, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked,
-                                         qB, uH, uL, cl2, resid, t1, causal, tq, j4);
+                    step16_bf16<D, CPAD, MASKED>(acc, ro, vtr, wtr, st + row0 * kv_rowb, st + row0 * lr_rowb,
+                                                 tt + row0, masked, qB, uH, uL, cl2, resid, t1, causal, tq, j4,
+                                                 blk.na, vm ? arow_m : -1, 256 * g.cpa_lr);
                 else
                     step16<T, D, CPAD>(acc, ro, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked, qB, uH,
                                        uL, cl2, resid, t1, causal, tq, j4);
@@ -724,7 +819,8 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int c = 16 * jj + 4 * j4 + i;
-                    if (c < cvalid && (p.shared_lr || (c >> p.lr_shift) == arel))
+                    // masked: every column is this row's own agent's
+                    if (c < cvalid && (MASKED || p.shared_lr || (c >> p.lr_shift) == arel))
                         p.p_w[rec * p.r + (c & (p.r - 1))] = acc.w[jj][i];
                 }
         }
@@ -915,15 +1011,15 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 
 // ---------------------------------------------------------------- launchers --
 
-template <typename T, int D, int CP, int W>
+template <typename T, int D, int CP, bool M, int W>
 struct SplitSlot {};
 
-template <typename T, int D, int CP>
+template <typename T, int D, int CP, bool M>
 static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t st) {
     const bool w8 = dp.nw + dp.np <= 8;
-    auto *fn = w8 ? decode_split_kernel<T, D, CP, 8> : decode_split_kernel<T, D, CP, 12>;
-    const hipError_t e = w8 ? ensure_lds<SplitSlot<T, D, CP, 8>>(reinterpret_cast<const void *>(fn), (int)lds)
-                            : ensure_lds<SplitSlot<T, D, CP, 12>>(reinterpret_cast<const void *>(fn), (int)lds);
+    auto *fn = w8 ? decode_split_kernel<T, D, CP, M, 8> : decode_split_kernel<T, D, CP, M, 12>;
+    const hipError_t e = w8 ? ensure_lds<SplitSlot<T, D, CP, M, 8>>(reinterpret_cast<const void *>(fn), (int)lds)
+                            : ensure_lds<SplitSlot<T, D, CP, M, 12>>(reinterpret_cast<const void *>(fn), (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3(8 * dp.per_xcd), dim3(64 * (dp.nw + dp.np)), lds, st, dp);
     return hipGetLastError();
@@ -931,19 +1027,35 @@ static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t s
 
 template <typename T>
 static hipError_t launch_split_t(const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st) {
+    if constexpr (sizeof(T) == 2) {
+        if (dp.masked) {  // per-agent caches of rank cpad >= 32, several agents per block
+            if (D == 128) {
+                switch (cpad) {
+                    case 32: return launch_split<T, 128, 32, true>(dp, lds, st);
+                    case 64: return launch_split<T, 128, 64, true>(dp, lds, st);
+                    default: return launch_split<T, 128, 128, true>(dp, lds, st);
+                }
+            }
+            switch (cpad) {
+                case 32: return launch_split<T, 64, 32, true>(dp, lds, st);
+                case 64: return launch_split<T, 64, 64, true>(dp, lds, st);
+                default: return launch_split<T, 64, 128, true>(dp, lds, st);
+            }
+        }
+    }
     if (D == 128) {
         switch (cpad) {
-            case 0: return launch_split<T, 128, 0>(dp, lds, st);
-            case 32: return launch_split<T, 128, 32>(dp, lds, st);
-            case 64: return launch_split<T, 128, 64>(dp, lds, st);
-            default: return launch_split<T, 128, 128>(dp, lds, st);
+            case 0: return launch_split<T, 128, 0, false>(dp, lds, st);
+            case 32: return launch_split<T, 128, 32, false>(dp, lds, st);
+            case 64: return launch_split<T, 128, 64, false>(dp, lds, st);
+            default: return launch_split<T, 128, 128, false>(dp, lds, st);
         }
     }
     switch (cpad) {
-        case 0: return launch_split<T, 64, 0>(dp, lds, st);
-        case 32: return launch_split<T, 64, 32>(dp, lds, st);
-        case 64: return launch_split<T, 64, 64>(dp, lds, st);
-        default: return launch_split<T, 64, 128>(dp, lds, st);
+        case 0: return launch_split<T, 64, 0, false>(dp, lds, st);
+        case 32: return launch_split<T, 64, 32, false>(dp, lds, st);
+        case 64: return launch_split<T, 64, 64, false>(dp, lds, st);
+        default: return launch_split<T, 64, 128, false>(dp, lds, st);
     }
 }
 

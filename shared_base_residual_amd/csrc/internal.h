@@ -82,6 +82,8 @@ struct DecodeParams {
     float c;          // softmax scale * log2(e)
     int n_blocks, n_rg, n_ps;
     int H, n_hg;      // KV heads per prefix item (sharing its low-rank tile), head groups
+    int bpg;          // 16-row blocks per prefix row group (1, 2 or 4)
+    int masked;       // per-agent caches, several agents per block, U and W r columns wide
     int tok_ps;
     int pb, n_prg, n_pv;
     int tok_pv;

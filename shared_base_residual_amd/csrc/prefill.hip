@@ -342,22 +342,18 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                 for (int cb = 0; cb < NCB; ++cb) {
                     float mx = fmaxf(fmaxf(fmaxf(sc[cb][0][0], sc[cb][0][1]), fmaxf(sc[cb][0][2], sc[cb][0][3])),
                                      fmaxf(fmaxf(sc[cb][1][0], sc[cb][1][1]), fmaxf(sc[cb][1][2], sc[cb][1][3])));
-                    mx = fmaxf(mx, __shfl_xor(mx, 16));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32));
-                    mx *= cl2;  // scaled (log2 units); -inf stays -inf
+                    mx = row_max4(mx) * cl2;  // scaled (log2 units); -inf stays -inf
                     const bool grow = mx > m[cb] + kRescaleSlack;
                     const float m_new = grow ? mx : m[cb];
                     alpha[cb] = fexp2(m[cb] - m_new);
                     m[cb] = m_new;
                     any_grow = any_grow || grow;
-                    float psum = 0.0f;
+                    float e[8];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float e = fexp2(__builtin_fmaf(sc[cb][i >> 2][i & 3], cl2, -m_new));
-                        psum += e;
-                        O::set(pB[cb], i, e);
-                    }
-                    l[cb] = l[cb] * alpha[cb] + psum;
+                    for (int i = 0; i < 8; ++i) e[i] = fexp2(__builtin_fmaf(sc[cb][i >> 2][i & 3], cl2, -m_new));
+                    pB[cb].v = __builtin_shufflevector(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]),
+                                                       0, 1, 2, 3, 4, 5, 6, 7);
+                    l[cb] = l[cb] * alpha[cb] + (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
                 }
                 if (__builtin_amdgcn_ballot_w64(any_grow)) {
 #pragma unroll

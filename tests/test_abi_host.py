@@ -132,11 +132,14 @@ def test_plan_covers_context(kw):
     if rpa <= 16:
         assert p["agents_per_block"] * rpa <= 16
         if d.rank and not d.shared_lr and L:
-            assert p["agents_per_block"] * d.rank <= p["resid_cols"] <= 128
+            if p["masked"]:  # U and W are the rank wide, several agents per block
+                assert d.dtype == 1 and d.rank >= 32 and p["resid_cols"] == d.rank and p["agents_per_block"] > 1
+            else:
+                assert p["agents_per_block"] * d.rank <= p["resid_cols"] <= 128
         assert p["row_blocks"] * p["agents_per_block"] >= d.n_agents
     if d.rank and L:
         assert p["resid_cols"] in (32, 64, 128)
-    rg = -(-p["row_blocks"] // 4)
+    rg = -(-p["row_blocks"] // p["blocks_per_group"])
     pb = 1 if rpa <= 16 else -(-rpa // 16)
     H = p["heads_per_item"]
     assert H >= 1 and d.n_kv_heads % H == 0 and (H == 1 or (d.rank and L))

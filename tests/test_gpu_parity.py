@@ -152,6 +152,7 @@ EDGE = [
                name="prefill shared ragged"),
     synth.Case(2, 4, 2, 64, 8, 300, priv_len=20, q_len=20, mode="prefill", dtype="f32", name="prefill fp32"),
     synth.Case(17, 4, 1, 128, 8, 129, name="17 agents g=4"),
+    synth.Case(9, 8, 2, 128, 32, 1500, priv_len=17, name="several agents per block, r=32, ragged last block"),
 ]
 
 
