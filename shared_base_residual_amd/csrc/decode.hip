@@ -585,8 +585,8 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         for (int s = 0; s < CSx; ++s)
 #pragma unroll
             for (int i = 0; i < 8; ++i) uv[s][i] = 0.0f;
-        for (int ag = 0; ag < blk.na; ++ag) {
-            frag bkf[CSx][2][KS];
+        // two agents' Bk rows in flight: the next agent's loads overlap this one's MFMAs
+        auto load_bk = [&](frag (&bkf)[CSx][2][KS], int ag) {
 #pragma unroll
             for (int s = 0; s < CSx; ++s)
 #pragma unroll
@@ -596,6 +596,8 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
 #pragma unroll
                     for (int s2 = 0; s2 < KS; ++s2) bkf[s][h][s2] = O::load8(brow + 32 * s2);
                 }
+        };
+        auto use_bk = [&](const frag (&bkf)[CSx][2][KS], int ag) {
             const bool keep = vm && arow_m == ag;
 #pragma unroll
             for (int s = 0; s < CSx; ++s)
@@ -608,6 +610,22 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
                     for (int i = 0; i < 4; ++i)
                         if (keep) uv[s][4 * h + i] = a[i] * uscale;
                 }
+        };
+        if constexpr (CSx <= 2) {
+            frag bk0[CSx][2][KS], bk1[CSx][2][KS];
+            load_bk(bk0, 0);
+            for (int ag = 0; ag < blk.na; ag += 2) {
+                if (ag + 1 < blk.na) load_bk(bk1, ag + 1);
+                use_bk(bk0, ag);
+                if (ag + 2 < blk.na) load_bk(bk0, ag + 2);
+                if (ag + 1 < blk.na) use_bk(bk1, ag + 1);
+            }
+        } else {  // rank 128: one agent at a time (registers)
+            frag bk0[CSx][2][KS];
+            for (int ag = 0; ag < blk.na; ++ag) {
+                load_bk(bk0, ag);
+                use_bk(bk0, ag);
+            }
         }
 #pragma unroll
         for (int s = 0; s < CSx; ++s)
