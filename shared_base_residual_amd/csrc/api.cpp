@@ -221,9 +221,15 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             return mx;
         };
         auto fit_vmcnt = [&](int T, int H, int lr_row_bytes, int *nst) {
-            // two load waves (three when the low-rank rows have their own), four if
-            // needed, then fewer stages
-            for (int np = p.lr_own ? 3 : 2; np <= 4; np += 1) {
+            // Two load waves (three when the low-rank rows have their own), four
+            // when a tile takes 40 or more loads: on gfx950 a wave's direct loads
+            // are back-pressured at issue, so large tiles stream faster from more
+            // waves.  More if the outstanding-load limit needs them, then fewer stages.
+            const int G = T / 16;
+            const int tile_loads = 2 * H * G * ((16 * (kv_row / 16)) / 64) +
+                                   (lr_row_bytes ? 2 * G * ((16 * (lr_row_bytes / 16) + 63) / 64) : 0);
+            const int np0 = tile_loads >= 40 && p.nw + 4 <= 12 ? 4 : (p.lr_own ? 3 : 2);
+            for (int np = np0; np <= 4; np += 1) {
                 const int f = max_fpw(T, H, lr_row_bytes, np);
                 if (f * (*nst - 1) <= 63) {
                     if (np > p.np) p.np = np;
