@@ -315,24 +315,27 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             if (bpg > 1 && bpg > p.n_blocks && bpg != 4) continue;
             const int gs = group_stats(bpg);
             if (gs != RATTN_OK) return gs;
-            bool ok = false;
-            for (int H = 8; H >= 1 && !ok; H /= 2) {
+            for (int H = 8; H >= 1; H /= 2) {
                 if (HK % H || (H > 1 && !resid)) continue;
                 const int st = plan_splits(H);
                 if (st != RATTN_OK) return st;
                 const int tiles_min = L > 0 ? H * nb_min : (p.pb < 4 ? p.pb : 4);
                 const int need = H > 1 ? 3 : 2;
-                ok = (tiles_min >= 2 && plan_lds(8, need)) || plan_lds(4, need);
+                const bool ok = (tiles_min >= 2 && plan_lds(8, need)) || plan_lds(4, need);
+                if (!ok) continue;
+                // Preference: a prefix tile of 32 or more tokens (the per-tile
+                // synchronisation is a large share of a tile's time), then the
+                // fewest bytes staged per context token, then more heads per item.
+                const int64_t bytes = (int64_t)p.n_rg * HK * 2 * kv_row + (int64_t)p.n_hg * p.n_rg * 2 * lr_row;
+                const int64_t cost = (L > 0 && p.T_pre < 32 ? (int64_t)1 << 40 : 0) + bytes * 16 + (8 - p.H);
+                if (best_cost < 0 || cost < best_cost) {
+                    best_cost = cost;
+                    best = p;
+                    best_lds = pl->lds;
+                }
+                planned = true;
             }
-            if (!ok) continue;
-            const int64_t cost = (int64_t)p.n_rg * HK * 2 * kv_row + (int64_t)p.n_hg * p.n_rg * 2 * lr_row;
-            if (best_cost < 0 || cost < best_cost) {
-                best_cost = cost;
-                best = p;
-                best_lds = pl->lds;
-            }
-            planned = true;
-            if (L == 0 || !resid) break;  // nothing to trade
+            if (planned && (L == 0 || !resid)) break;  // nothing to trade
         }
         if (!planned) return RATTN_E_UNSUPPORTED;
         p = best;
