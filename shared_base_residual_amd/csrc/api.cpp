@@ -345,6 +345,15 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     int pst = plan_rows(true);
     if (pst != RATTN_OK) pst = plan_rows(false);
     if (pst != RATTN_OK) return pst;
+    p.fd_hg = rattn::make_fastdiv(p.n_hg);
+    p.fd_rg = rattn::make_fastdiv(p.n_rg);
+    p.fd_hk = rattn::make_fastdiv(p.HK);
+    p.fd_pv = rattn::make_fastdiv(p.n_pv);
+    p.fd_prg = rattn::make_fastdiv(p.n_prg);
+    p.fd_rpa = rattn::make_fastdiv(p.rpa);
+    p.fd_bpa = rattn::make_fastdiv(p.bpa);
+    p.fd_g = rattn::make_fastdiv(p.g);
+    p.fd_ps = rattn::make_fastdiv(p.ps);
 
     // Workspace: the (max, sum), O and W partials of every (KV head, row, split).
     const int64_t rows_kv = (int64_t)HK * N * rpa;
@@ -396,6 +405,7 @@ int make_prefill_plan(const rattn_desc *d, PrefillPlan *pl) {
     p.lr_shift = 0;
     while (r > 0 && (1 << p.lr_shift) < r) ++p.lr_shift;
     p.ps = d->page_size;
+    p.fd_ps = rattn::make_fastdiv(p.ps);
     p.shared_lr = d->shared_lr;
     const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
     p.c = scale * 1.44269504088896340736f;

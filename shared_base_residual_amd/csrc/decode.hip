@@ -317,6 +317,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     constexpr int ES = (int)sizeof(T);
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
+    touch_params<DecodeParams>();
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -345,12 +346,12 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     bool prefix;
     if (li < p.n_prefix_items) {
         // prefix item: H KV heads starting at k0 (head groups fastest), one row group, one split
-        const int hg = li % p.n_hg;
+        const int rest = fdiv(li, p.fd_hg);
+        const int hg = li - rest * p.n_hg;
         k0 = hg * p.H;
         nh = p.H;
-        const int rest = li / p.n_hg;
-        const int rg = rest % p.n_rg;
-        const int s = rest / p.n_rg;
+        const int s = fdiv(rest, p.fd_rg);
+        const int rg = rest - s * p.n_rg;
         blk0 = rg * p.bpg;
         nblk = p.n_blocks - blk0 < p.bpg ? p.n_blocks - blk0 : p.bpg;
         t0 = s * p.tok_ps;
@@ -359,13 +360,13 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         prefix = true;
     } else {
         const int l2 = li - p.n_prefix_items;
-        k0 = l2 % p.HK;
+        int rest = fdiv(l2, p.fd_hk);
+        k0 = l2 - rest * p.HK;
         nh = 1;
-        int rest = l2 / p.HK;
-        const int s = rest % p.n_pv;
-        rest /= p.n_pv;
-        const int prg = rest % p.n_prg;
-        agent_p = rest / p.n_prg;
+        const int r2 = fdiv(rest, p.fd_pv);
+        const int s = rest - r2 * p.n_pv;
+        agent_p = fdiv(r2, p.fd_prg);
+        const int prg = r2 - agent_p * p.n_prg;
         blk0 = prg * 4;
         nblk = p.pb - blk0 < 4 ? p.pb - blk0 : 4;
         t0 = s * p.tok_pv;
@@ -376,49 +377,16 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     if (t1 < t0) t1 = t0;  // an empty trailing split
     const bool resid = prefix && (CPAD > 0) && p.r > 0;
     const bool causal = !prefix && p.causal;
-    // Row tiles: nblk row blocks of each of the nh heads; TG waves share a tile
-    // (token groups).
-    const int TG = p.nw / (nh * nblk);
-    const int rbi = wave / TG;
-    const int tg = wave % TG;
-    const int hw = rbi < nh * nblk ? rbi / nblk : 0;  // this wave's head within the item
-    const int bw = rbi < nh * nblk ? rbi % nblk : 0;  // and its row block
-    const int k = k0 + hw;                            // this wave's KV head
-
     // Agents the workgroup serves.
     int a_lo, a_hi;
     if (prefix) {
-        const RowBlock b0 = prefix_block(blk0, p.N, p.rpa, p.apb, p.bpa);
-        const RowBlock b1 = prefix_block(blk0 + nblk - 1, p.N, p.rpa, p.apb, p.bpa);
+        const RowBlock b0 = prefix_block(blk0, p.N, p.rpa, p.apb, p.fd_bpa);
+        const RowBlock b1 = prefix_block(blk0 + nblk - 1, p.N, p.rpa, p.apb, p.fd_bpa);
         a_lo = b0.a0;
         a_hi = b1.a0 + b1.na - 1;
     } else {
         a_lo = a_hi = agent_p;
     }
-
-    // Row block of this wave.
-    RowBlock blk;
-    if (prefix) {
-        blk = prefix_block(blk0 + bw, p.N, p.rpa, p.apb, p.bpa);
-    } else {
-        blk.a0 = agent_p;
-        blk.na = 1;
-        blk.f = p.rpa <= 16 ? 0 : 16 * (blk0 + bw);
-        blk.nr = p.rpa - blk.f < 16 ? p.rpa - blk.f : 16;
-    }
-    const bool compute_wave = wave < p.nw;  // the others only load
-    const bool wave_on = compute_wave && rbi < nh * nblk;
-    // Query row owned by this lane's column.
-    const bool vm = wave_on && n16 < blk.nr;
-    int agent_m = 0, ria = 0;
-    if (vm) block_row(blk, n16, p.rpa, &agent_m, &ria);
-    const int arow_m = agent_m - blk.a0;  // the row's agent within the block
-    const int tq = ria / p.g, hh = ria % p.g;
-    const int64_t qrow = ((int64_t)agent_m * p.QL + tq) * p.HQ + (int64_t)k * p.g + hh;
-    const int64_t grow = (int64_t)agent_m * p.rpa + ria;
-    const float cl2 = p.c;
-    const int cvalid = resid ? (p.shared_lr ? p.r : blk.na * p.r) : 0;
-    const int lr_col0 = resid && !p.shared_lr ? (blk.a0 - a_lo) * p.r : 0;  // block's first column in the tile
 
     // ---- stage geometry and token source of this item
     Geo g;
@@ -451,7 +419,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     src.lr_agent_stride = 0;
     src.head_stride = 0;
     src.page_stride = 0;
-    src.ps = 16;
+    src.fps = p.fd_ps;
     src.pg0 = 0;
     src.pages = s_pages;
     if (prefix) {
@@ -459,11 +427,10 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         src.vb = static_cast<const T *>(p.vb);
         if (p.ps > 0) {
             src.page_stride = (int64_t)p.HK * p.ps * D;
-            src.ps = p.ps;
             src.kb += (int64_t)k0 * p.ps * D;
             src.vb += (int64_t)k0 * p.ps * D;
             src.head_stride = (int64_t)p.ps * D;
-            src.pg0 = t0 / p.ps;
+            src.pg0 = fdiv(t0, p.fd_ps);
         } else {
             src.kb += (int64_t)k0 * p.L * D;
             src.vb += (int64_t)k0 * p.L * D;
@@ -476,23 +443,78 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
             src.lr_agent_stride = p.L * p.r;
         }
     } else {
-        const int64_t seg = ((int64_t)agent_p * p.HK + k) * p.S * D;
+        const int64_t seg = ((int64_t)agent_p * p.HK + k0) * p.S * D;  // one head per private item
         src.kb = static_cast<const T *>(p.kp) + seg;
         src.vb = static_cast<const T *>(p.vp) + seg;
     }
     if (src.page_stride && t1 > t0) {
         // the split's page-table entries, read once into LDS
-        const int npg = (t1 - 1) / p.ps - src.pg0 + 1;
+        const int npg = fdiv(t1 - 1, p.fd_ps) - src.pg0 + 1;
         for (int i = threadIdx.x; i < npg; i += blockDim.x) s_pages[i] = p.table[src.pg0 + i];
         __syncthreads();
     }
 
-    // The fill plan of this wave and the lane offsets of the step's LDS reads.
+    // The fill plan of this wave.
+    const bool compute_wave = wave < p.nw;  // the others only load
     FillPlan fp;
     make_fill_plan<T, D>(fp, g, src, resid, compute_wave ? p.np : wave - p.nw, lane, p.np, p.lr_own != 0);
     // keys and values that no other workgroup reads are streamed past the caches
     fp.kv_nt = prefix ? p.n_rg == 1 : p.n_prg == 1;
-    // this wave's head: its K and V regions of the stage (chunks)
+    const int n_tiles = (t1 - t0 + g.T - 1) >> ilog2(g.T);  // T is a power of two
+    const int fpw = fp.fpw;
+    auto fill = [&](int tile, int stage) {
+        const int tt = t0 + tile * g.T;
+        fill_stage<T, D>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
+    };
+    // ---- the load waves start the ring (tiles 0 .. nst-2) at once, before the
+    // compute waves set up their rows, load the queries and form U
+    if (fpw)
+        for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
+    // Row tiles: nblk row blocks of each of the nh heads; TG waves share a tile
+    // (token groups).
+    const int TG = small_div(p.nw, nh * nblk);
+    const int rbi = small_div(wave, TG);
+    const int tg = wave - rbi * TG;
+    const int hw = rbi < nh * nblk ? small_div(rbi, nblk) : 0;  // this wave's head within the item
+    const int bw = rbi < nh * nblk ? rbi - hw * nblk : 0;         // and its row block
+    const int k = k0 + hw;                            // this wave's KV head
+
+    // Row block of this wave.
+    RowBlock blk;
+    if (prefix) {
+        blk = prefix_block(blk0 + bw, p.N, p.rpa, p.apb, p.fd_bpa);
+    } else {
+        blk.a0 = agent_p;
+        blk.na = 1;
+        blk.f = p.rpa <= 16 ? 0 : 16 * (blk0 + bw);
+        blk.nr = p.rpa - blk.f < 16 ? p.rpa - blk.f : 16;
+    }
+    const bool wave_on = compute_wave && rbi < nh * nblk;
+    // Query row owned by this lane's column.
+    const bool vm = wave_on && n16 < blk.nr;
+    int agent_m = 0, ria = 0;
+    if (vm) block_row(blk, n16, p.fd_rpa, &agent_m, &ria);
+    const int arow_m = agent_m - blk.a0;  // the row's agent within the block
+    const int tq = fdiv(ria, p.fd_g), hh = ria - tq * p.g;
+    const int64_t qrow = ((int64_t)agent_m * p.QL + tq) * p.HQ + (int64_t)k * p.g + hh;
+    const int64_t grow = (int64_t)agent_m * p.rpa + ria;
+    const float cl2 = p.c;
+    const int cvalid = resid ? (p.shared_lr ? p.r : blk.na * p.r) : 0;
+    const int lr_col0 = resid && !p.shared_lr ? (blk.a0 - a_lo) * p.r : 0;  // block's first column in the tile
+
+    // Query rows as the B operand of S^T = K Q^T.
+    const T *qp = static_cast<const T *>(p.q);
+    frag qB[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qB[s] = O::zero();
+    if (wave_on) {
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            if (vm) qB[s] = O::load8(qp + qrow * D + 32 * s + 8 * j4);
+    }
+
+    // ---- lane offsets of this wave's LDS reads: its head's K and V regions
+    // of the stage (chunks)
     const int kreg = hw * g.T * g.cpr_kv, vreg = g.ofs_v + hw * g.T * g.cpr_kv;
     ReadOfs<T, D, CPAD> ro;
     {
@@ -537,28 +559,6 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         int col = 16 * jj + 4 * (n16 & 3);
         col = lr_col0 + (col < cvalid ? col : 0);
         wtr[jj] = resid ? lr_ofs(g, g.ofs_lv, col >> p.lr_shift, 4 * j4 + (n16 >> 2), (col & (p.r - 1)) * ES) : 0u;
-    }
-
-    const int n_tiles = (t1 - t0 + g.T - 1) / g.T;
-    const int fpw = fp.fpw;
-    auto fill = [&](int tile, int stage) {
-        const int tt = t0 + tile * g.T;
-        fill_stage<T, D>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
-    };
-    // ---- the load waves start the ring (tiles 0 .. nst-2) at once, while the
-    // compute waves load the query rows and form U
-    if (fpw)
-        for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
-
-    // Query rows as the B operand of S^T = K Q^T.
-    const T *qp = static_cast<const T *>(p.q);
-    frag qB[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) qB[s] = O::zero();
-    if (wave_on) {
-#pragma unroll
-        for (int s = 0; s < KS; ++s)
-            if (vm) qB[s] = O::load8(qp + qrow * D + 32 * s + 8 * j4);
     }
 
     // U = scale*log2(e) * q Bk^T as the B operand of the rank-r score correction,
@@ -893,6 +893,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     __shared__ float s_red[2 * NWV];
     __shared__ f32x4 s_wp[NWV * 32];  // per-wave W column-group sums
     __shared__ float s_wt[128];       // merged W (r <= 128)
+    touch_params<DecodeParams>();
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t R = blockIdx.x;
     const int h = (int)(R % p.HQ);

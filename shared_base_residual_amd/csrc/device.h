@@ -240,6 +240,22 @@ __device__ inline P *uniform_ptr(P *p) {
     return (P *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Requests every 64-byte line of the kernel's parameter block (a struct P
+// passed by value, at the start of the kernel argument segment) at once and
+// waits for them together.  The compiler reads parameter fields lazily, with a
+// wait after each batch; without this, each batch that touches a new line is a
+// separate round trip to memory at the start of every workgroup.
+template <typename P>
+__device__ __attribute__((always_inline)) inline void touch_params() {
+    constexpr int kLines = (int)((sizeof(P) + 63) / 64);
+    typedef const __attribute__((address_space(4))) uint32_t kword;
+    kword *ka = (kword *)__builtin_amdgcn_kernarg_segment_ptr();
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < kLines; ++i) acc ^= ka[16 * i];
+    asm volatile("" ::"s"(acc));
+}
+
 // s_waitcnt vmcnt(n) (n clamped to the 6-bit field), leaving the other counters.
 // The immediate must be a constant, hence the table.
 __device__ inline void wait_vmcnt(int n) {

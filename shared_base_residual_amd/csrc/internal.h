@@ -11,6 +11,34 @@
 
 namespace rattn {
 
+// Division of a non-negative int n < 2^31 by a divisor d >= 1 fixed at plan
+// time, as one multiply and shift: with l = ceil(log2 d) and
+// m = floor(2^(32+l) / d) + 1, floor(n * m / 2^(32+l)) = floor(n / d), because
+// the excess n * (m - 2^(32+l)/d) / 2^(32+l) is below n / 2^(32+l) < 2^(-1-l)
+// <= 1 / (2d) (the round-up method of Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994).  m < 2^33, so n * m fits in
+// 64 bits.  Kernels take these instead of runtime divisions, which cost a long
+// dependent instruction sequence each at the start of every workgroup.
+struct FastDiv {
+    uint64_t m;
+    int sh;  // 32 + l
+    int d;
+};
+
+// Host side; a divisor below 1 (an empty dimension) is taken as 1.
+inline FastDiv make_fastdiv(int d) {
+    FastDiv f;
+    if (d < 1) d = 1;
+    int l = 0;
+    while ((1ll << l) < (long long)d) ++l;
+    f.d = d;
+    f.sh = 32 + l;  // <= 63
+    f.m = ((uint64_t)1 << f.sh) / (uint64_t)d + 1;
+    return f;
+}
+
+RATTN_HD int fdiv(int n, const FastDiv &f) { return (int)(((uint64_t)(uint32_t)n * f.m) >> f.sh); }
+
 // Largest padded residual width (agents sharing a row block times r) a decode
 // row block is given when r allows; bounds the split kernel's registers
 // (bf16 / fp32 inputs).  r = 128 still runs, with 128 columns.
@@ -48,11 +76,39 @@ RATTN_HD RowBlock prefix_block(int b, int n_agents, int rpa, int apb, int bpa) {
     return rb;
 }
 
+// The same with the divisions by bpa and rpa as FastDiv.
+RATTN_HD RowBlock prefix_block(int b, int n_agents, int rpa, int apb, const FastDiv &bpa) {
+    RowBlock rb;
+    if (rpa <= 16) {
+        rb.a0 = b * apb;
+        rb.na = n_agents - rb.a0 < apb ? n_agents - rb.a0 : apb;
+        rb.f = 0;
+        rb.nr = rb.na * rpa;
+    } else {
+        rb.a0 = fdiv(b, bpa);
+        rb.na = 1;
+        rb.f = 16 * (b - rb.a0 * bpa.d);
+        rb.nr = rpa - rb.f < 16 ? rpa - rb.f : 16;
+    }
+    return rb;
+}
+
 // Agent and row-within-agent of row m (< nr) of a block.
 RATTN_HD void block_row(const RowBlock &rb, int m, int rpa, int *agent, int *ria) {
     if (rpa <= 16) {
         *agent = rb.a0 + m / rpa;
         *ria = m % rpa;
+    } else {
+        *agent = rb.a0;
+        *ria = rb.f + m;
+    }
+}
+
+RATTN_HD void block_row(const RowBlock &rb, int m, const FastDiv &rpa, int *agent, int *ria) {
+    if (rpa.d <= 16) {
+        const int a = fdiv(m, rpa);
+        *agent = rb.a0 + a;
+        *ria = m - a * rpa.d;
     } else {
         *agent = rb.a0;
         *ria = rb.f + m;
@@ -101,6 +157,8 @@ struct DecodeParams {
     int T_pre, nst_pre, stage_bytes_pre;
     int T_pv, nst_pv, stage_bytes_pv;
     int table_lds_off;
+    // the same divisors for one multiply each (see FastDiv)
+    FastDiv fd_hg, fd_rg, fd_hk, fd_pv, fd_prg, fd_rpa, fd_bpa, fd_g, fd_ps;
 };
 
 // Dynamic LDS a split workgroup may use (gfx950: 160 KiB per workgroup, less
@@ -132,6 +190,7 @@ struct PrefillParams {
     int n_items, per_xcd;
     int nst_pre, stage_bytes_pre, nst_ch, stage_bytes_ch;
     int table_lds_off;
+    FastDiv fd_ps;    // page size
 };
 
 }  // namespace rattn

@@ -34,6 +34,7 @@ namespace rattn {
 
 template <typename T, int D, int CPAD>
 __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
+    touch_params<PrefillParams>();
     using O = Ops<T>;
     using frag = typename O::frag;
     constexpr int KS = D / 32;
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         src.lr_agent_stride = 0;
         src.head_stride = 0;
         src.page_stride = 0;
-        src.ps = 16;
+        src.fps = p.fd_ps;
         src.pg0 = 0;
         src.pages = s_pages;
         if (pre) {
@@ -202,10 +203,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
             src.vb = static_cast<const T *>(p.vb);
             if (p.ps > 0) {
                 src.page_stride = (int64_t)p.HK * p.ps * D;
-                src.ps = p.ps;
                 src.kb += (int64_t)k * p.ps * D;
                 src.vb += (int64_t)k * p.ps * D;
-                const int npg = (t1 - 1) / p.ps + 1;
+                const int npg = fdiv(t1 - 1, p.fd_ps) + 1;
                 for (int i = threadIdx.x; i < npg; i += 64 * NW) s_pages[i] = p.table[i];
                 __syncthreads();
             } else {

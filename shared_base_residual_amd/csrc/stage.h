@@ -29,6 +29,12 @@ struct Geo {
 };
 
 __device__ inline int ilog2(int x) { return 31 - __builtin_clz(x); }
+// n / d for small non-negative n and d >= 1 (wave counts, a dozen or so), by counting.
+__device__ inline int small_div(int n, int d) {
+    int q = 0;
+    for (int x = d; x <= n; x += d) ++q;
+    return q;
+}
 
 // Where the tokens of a work item come from.
 template <typename T>
@@ -36,7 +42,7 @@ struct Src {
     const T *kb, *vb;         // contiguous: the first head's rows; paged: pool + that head's offset
     int64_t head_stride;      // elements from one staged head to the next
     int64_t page_stride;      // paged: elements per physical page (0: contiguous)
-    int ps;                   // page size (paged)
+    FastDiv fps;              // page size (paged)
     int pg0;                  // first logical page of the split
     const int *pages;         // LDS copy of the split's page-table entries (paged)
     const T *lk, *lv;         // low-rank rows: first agent of the workgroup (or the shared one)
@@ -48,8 +54,9 @@ struct Src {
 template <typename T, int D>
 __device__ inline const T *kv_row(const Src<T> &s, const T *base, int tok) {
     if (s.page_stride) {
-        const int64_t pg = s.pages[tok / s.ps - s.pg0];
-        return base + pg * s.page_stride + (int64_t)(tok % s.ps) * D;
+        const int lp = fdiv(tok, s.fps);
+        const int64_t pg = s.pages[lp - s.pg0];
+        return base + pg * s.page_stride + (int64_t)(tok - lp * s.fps.d) * D;
     }
     return base + (int64_t)tok * D;
 }
@@ -70,7 +77,7 @@ __device__ inline const T *kv_row(const Src<T> &s, const T *base, int tok) {
 constexpr int kMaxKvLoads = 8;   // direct loads per group of a K (or V) region (fp32, d = 128)
 
 struct FillPlan {
-    int G;                    // groups per tile
+    int G, lgG;               // groups per tile (a power of two), its log2
     int npairs;               // (region, group) pairs per tile
     int pbeg, pend, pstep;    // the pairs this wave fills: pbeg, pbeg + pstep, ... < pend
     int n_kv, n_lr;           // loads per group of a K/V region, of an Lk/Lv region
@@ -104,6 +111,7 @@ __device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f
                                                                      bool lr_own = false) {
     constexpr int ES = (int)sizeof(T);
     f.G = g.T >> 4;
+    f.lgG = ilog2(f.G);
     const int nkv = 2 * g.H * f.G;
     f.npairs = nkv + (resid ? 2 * f.G : 0);
     if (wave >= nw) {
@@ -173,7 +181,7 @@ __device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan 
         const int tg0 = t0 + 16 * gg;  // the group's first token
         if (pi < nkv) {
             // K (region < H) or V rows of head region % H
-            const int region = pi / f.G;
+            const int region = pi >> f.lgG;
             const bool isv = region >= g.H;
             const T *base = (isv ? s.vb : s.kb) + (int64_t)(isv ? region - g.H : region) * s.head_stride;
             const uint32_t dst = lds0 + 16 * ((region * g.T + 16 * gg) * g.cpr_kv);
