@@ -251,11 +251,13 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         auto plan_lds = [&](int nw, int min_nst) -> bool {
             p.nw = nw;
             p.np = p.lr_own ? 3 : 2;
+            // the split's page-table entries sit after the ring
+            const int table_bytes = d->page_size > 0 && L > 0 ? (int)(cdiv(p.tok_ps, d->page_size) + 1) * 4 + 16 : 0;
             auto pick = [&](int tg_max, int H, int lr_row_bytes, int need, int *T, int *nst, int *stage) {
                 for (int t = 128; t >= 16; t /= 2) {
                     if (t % (16 * tg_max) || t > 16 * nw) continue;  // the fill gives each 16-row group one wave
                     const int sb = t * (2 * H * kv_row + 2 * lr_row_bytes);
-                    const int n = rattn::kLdsBudget / sb;
+                    const int n = (rattn::kSplitLds - table_bytes) / sb;
                     if (n >= 3 || (t == 16 * tg_max && n >= need)) {
                         *T = t;
                         *nst = n < 4 ? n : 4;
@@ -294,7 +296,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             // The split's page-table entries.
             p.table_lds_off = (lds + 15) & ~15;
             if (d->page_size > 0 && L > 0) lds = p.table_lds_off + (int)(cdiv(p.tok_ps, d->page_size) + 1) * 4;
-            if (lds > rattn::kLdsBudget) return false;
+            if (lds > rattn::kSplitLds) return false;
             pl->lds = (size_t)lds;
             return true;
         };

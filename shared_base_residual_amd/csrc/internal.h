@@ -161,9 +161,10 @@ struct DecodeParams {
     FastDiv fd_hg, fd_rg, fd_hk, fd_pv, fd_prg, fd_rpa, fd_bpa, fd_g, fd_ps;
 };
 
-// Dynamic LDS a split workgroup may use (gfx950: 160 KiB per workgroup, less
-// what the kernel declares statically).
+// Dynamic LDS a workgroup may use (gfx950: 160 KiB per workgroup, less what
+// the kernel declares statically).  The split kernel declares none.
 constexpr int kLdsBudget = 160 * 1024 - 1024;
+constexpr int kSplitLds = 160 * 1024;
 // Page-table entries of one split copied into LDS.
 constexpr int kMaxPagesPerSplit = 2048;
 
