@@ -259,7 +259,8 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     for (int i = 0; i < 4; ++i) ev[i] = fexp2(__builtin_fmaf(a[i], cl2, -acc.m));
     frag4 pB;
     pB.v = to_bf16x4(ev[0], ev[1], ev[2], ev[3]);
-    acc.l = acc.l * alpha + ((ev[0] + ev[1]) + (ev[2] + ev[3]));
+    const f32x4 pr = __builtin_convertvector(pB.v, f32x4);  // the weights the product uses
+    acc.l = acc.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
 
     // O^T += V^T P^T and W^T += Lv^T P^T
 #pragma unroll

@@ -118,11 +118,14 @@ RATTN_HD void block_row(const RowBlock &rb, int m, const FastDiv &rpa, int *agen
 // Splits per query row the merge handles (weights staged in LDS).
 constexpr int kMaxSlots = 512;
 
-// Online softmax: the reference max of a row is raised when a score exceeds it
-// by more than this (log2 units).  Zero: the largest weight of a row is exactly
-// 1, which keeps its bf16 rounding error out of peaked rows; the accumulators
-// are still rescaled only on the steps where some row's max grows.
-constexpr float kRescaleSlack = 0.0f;
+// Online softmax: the reference max of a row is raised only when a score
+// exceeds it by more than this (log2 units), so weights stay below 2^4 and most
+// steps skip the rescale of the accumulators (a step rescales when any of its
+// rows' max grows, which for a fresh row max is nearly every early step).  The
+// bf16 kernels add a row's weights into its sum as rounded to bf16, exactly as
+// the P V product sees them, so a row dominated by one key still normalises to
+// that key's value.
+constexpr float kRescaleSlack = 4.0f;
 
 struct DecodeParams {
     const void *q, *kb, *vb;

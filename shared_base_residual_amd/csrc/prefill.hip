@@ -351,9 +351,11 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                     float e[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) e[i] = fexp2(__builtin_fmaf(sc[cb][i >> 2][i & 3], cl2, -m_new));
-                    pB[cb].v = __builtin_shufflevector(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]),
-                                                       0, 1, 2, 3, 4, 5, 6, 7);
-                    l[cb] = l[cb] * alpha[cb] + (((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7])));
+                    const bf16x4 p0 = to_bf16x4(e[0], e[1], e[2], e[3]), p1 = to_bf16x4(e[4], e[5], e[6], e[7]);
+                    pB[cb].v = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
+                    // the row sum takes the weights as rounded for the product
+                    const f32x4 r0 = __builtin_convertvector(p0, f32x4), r1 = __builtin_convertvector(p1, f32x4);
+                    l[cb] = l[cb] * alpha[cb] + (((r0[0] + r0[1]) + (r0[2] + r0[3])) + ((r1[0] + r1[1]) + (r1[2] + r1[3])));
                 }
                 if (__builtin_amdgcn_ballot_w64(any_grow)) {
 #pragma unroll
