@@ -894,6 +894,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     __shared__ float s_red[2 * NWV];
     __shared__ f32x4 s_wp[NWV * 32];  // per-wave W column-group sums
     __shared__ float s_wt[128];       // merged W (r <= 128)
+    __shared__ float s_wbv[NWV * D];  // per-wave (W Bv) column sums
     touch_params<DecodeParams>();
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t R = blockIdx.x;
@@ -926,15 +927,17 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
         const int q = tid + u * NT;
         wb[u] = q < nqw ? pw[q] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // Bv column d = tid % D, rows j = tid / D + jstep * i (jstep = NT / D threads per column)
-    constexpr int JS = NT / D;  // 4 (d = 128) or 8 (d = 64)
-    const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * r * p.HK * D + (int64_t)k * D + (tid % D);
+    // Bv rows: thread t takes columns 8 (t % CPR) .. + 7 of rows j = t / CPR + RPR u
+    // (CPR = D / 8 threads per row, RPR = NT / CPR rows per round), every row of
+    // Bv_a^(k) in one batch of 16-byte loads
+    constexpr int CPR = D / 8, RPR = NT / CPR, NU = kMaxResidColsHard / RPR;
+    const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * r * p.HK * D + (int64_t)k * D + 8 * (tid % CPR);
     const int64_t ldb = (int64_t)p.HK * D;
-    float bvv[4];
+    Row<T, 8> bvr[NU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int j = tid / D + JS * u;
-        bvv[u] = (wres && j < r) ? (float)bv[(int64_t)j * ldb] : 0.0f;
+    for (int u = 0; u < NU; ++u) {
+        const int j = tid / CPR + RPR * u;
+        bvr[u] = (wres && j < r) ? load_row<T, 8>(bv + (int64_t)j * ldb) : zero_row<T, 8>();
     }
 
     // weights of the slots: w_s = exp2(m_s - M), L = sum w_s l_s
@@ -1002,18 +1005,29 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
         s_wt[tid] = x;
     }
     __syncthreads();
-    // (W Bv)[d] over this thread's rows j of Bv
-    float wbv = 0.0f;
+    // (W Bv) over this thread's rows j of Bv, for its 8 columns; summed over the
+    // lanes of a wave that share the columns (xor shuffles), then over the waves
+    float wbv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wbv[i] = 0.0f;
     if (wres) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = tid / D + JS * u;
-            if (j < r) wbv += s_wt[j] * bvv[u];
+        for (int u = 0; u < NU; ++u) {
+            const int j = tid / CPR + RPR * u;
+            if (j < r) {
+                const float wj = s_wt[j];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) wbv[i] += wj * (float)bvr[u].e[i];
+            }
         }
-        for (int j = tid / D + 4 * JS; j < r; j += JS) wbv += s_wt[j] * (float)bv[(int64_t)j * ldb];
+#pragma unroll
+        for (int off = CPR; off < 64; off <<= 1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wbv[i] += __shfl_xor(wbv[i], off);
     }
-    float *s_wbv = s_w;  // the weights are consumed: reuse for the per-thread W Bv terms
-    s_wbv[tid] = wbv;
+    if (lane < CPR)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_wbv[wv * D + 8 * lane + i] = wbv[i];
     __syncthreads();
 
     // o[d] for d = tid (< D)
@@ -1022,8 +1036,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
         float o = 0.0f;
 #pragma unroll
         for (int i = 0; i < NWV; ++i) o += s_o[i * D4 + c4][e];
+        if (wres)
 #pragma unroll
-        for (int i = 0; i < JS; ++i) o += s_wbv[tid + D * i];
+            for (int i = 0; i < NWV; ++i) o += s_wbv[i * D + tid];
         p.out[R * D + tid] = o / Lsum;
         if (tid == 0 && p.lse) p.lse[R] = (M + __builtin_log2f(Lsum)) * 0.69314718055994530942f;
     }
