@@ -420,36 +420,28 @@ int make_prefill_plan(const rattn_desc *d, PrefillPlan *pl) {
     pl->cpad = resid ? (pow2ceil(r) < 32 ? 32 : pow2ceil(r)) : 0;
 
     // LDS rings: prefix tiles (keys, values and the low-rank rows), chunk tiles
-    // (keys and values); kPrefillTile keys per stage, up to 8 stages.
+    // (keys and values); T keys per stage, two to eight stages, the split's
+    // page-table entries after them.  128-key stages halve the ring's
+    // synchronisation per key against 64-key ones; 64 when 128 leaves no room.
     const int es = (int)esize(d->dtype);
-    const int T = rattn::kPrefillTile;
     const int kv_chunks = D * es / 16;
     const int lr_chunks = resid ? pow2ceil(r * es / 16) : 0;
-    p.stage_bytes_pre = T * 16 * (2 * kv_chunks + 2 * lr_chunks);
-    p.stage_bytes_ch = T * 16 * (2 * kv_chunks);
-    auto nst_for = [](int sb) {
-        const int n = rattn::kLdsBudget / sb;
-        return n < 8 ? n : 8;
-    };
-    p.nst_pre = nst_for(p.stage_bytes_pre);
-    p.nst_ch = nst_for(p.stage_bytes_ch);
-    if (p.nst_pre < 2 || p.nst_ch < 2) return RATTN_E_UNSUPPORTED;
-    int lds = p.nst_pre * p.stage_bytes_pre;
-    if (p.nst_ch * p.stage_bytes_ch > lds) lds = p.nst_ch * p.stage_bytes_ch;
-    p.table_lds_off = lds;
-    if (d->page_size > 0 && L > 0) lds += (int)((L - 1) / d->page_size + 1) * 4;
-    if (lds > rattn::kLdsBudget) {
-        // shrink the rings to make room for the page table
-        const int room = rattn::kLdsBudget - (lds - p.table_lds_off);
+    const int table_bytes = d->page_size > 0 && L > 0 ? (int)((L - 1) / d->page_size + 1) * 4 : 0;
+    auto plan_tile = [&](int T) -> bool {
+        p.T = T;
+        p.stage_bytes_pre = T * 16 * (2 * kv_chunks + 2 * lr_chunks);
+        p.stage_bytes_ch = T * 16 * (2 * kv_chunks);
+        const int room = rattn::kSplitLds - table_bytes;
         p.nst_pre = room / p.stage_bytes_pre < 8 ? room / p.stage_bytes_pre : 8;
         p.nst_ch = room / p.stage_bytes_ch < 8 ? room / p.stage_bytes_ch : 8;
-        if (p.nst_pre < 2 || p.nst_ch < 2) return RATTN_E_UNSUPPORTED;
+        if (p.nst_pre < 2 || p.nst_ch < 2) return false;
         int ring = p.nst_pre * p.stage_bytes_pre;
         if (p.nst_ch * p.stage_bytes_ch > ring) ring = p.nst_ch * p.stage_bytes_ch;
-        lds = lds - p.table_lds_off + ring;
         p.table_lds_off = ring;
-    }
-    pl->lds = (size_t)lds;
+        pl->lds = (size_t)(ring + table_bytes);
+        return true;
+    };
+    if (!plan_tile(128) && !plan_tile(64) && !plan_tile(32)) return RATTN_E_UNSUPPORTED;
     return RATTN_OK;
 }
 

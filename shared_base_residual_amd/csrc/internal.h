@@ -165,7 +165,7 @@ struct DecodeParams {
 };
 
 // Dynamic LDS a workgroup may use (gfx950: 160 KiB per workgroup, less what
-// the kernel declares statically).  The split kernel declares none.
+// the kernel declares statically).  The split and prefill kernels declare none.
 constexpr int kLdsBudget = 160 * 1024 - 1024;
 constexpr int kSplitLds = 160 * 1024;
 // Page-table entries of one split copied into LDS.
@@ -179,7 +179,6 @@ namespace rattn {
 // of that agent), no split of the context.  Waves own 64 rows each (four
 // 16-row MFMA blocks).
 constexpr int kPrefillRows = 256;
-constexpr int kPrefillTile = 64;  // keys per LDS stage
 
 struct PrefillParams {
     const void *q, *kb, *vb;
@@ -192,6 +191,7 @@ struct PrefillParams {
     int rpa;          // query rows per agent per KV head (q_len * g)
     int n_qb;         // row blocks per (agent, KV head)
     int n_items, per_xcd;
+    int T;            // keys per LDS stage (128, else 64 when the page table leaves no room)
     int nst_pre, stage_bytes_pre, nst_ch, stage_bytes_ch;
     int table_lds_off;
     FastDiv fd_ps;    // page size

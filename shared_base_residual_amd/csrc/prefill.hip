@@ -167,7 +167,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         if (t1 <= 0) continue;
         const bool res = pre && resid;
         Geo g;
-        g.T = kPrefillTile;
+        g.T = p.T;
         g.nst = pre ? p.nst_pre : p.nst_ch;
         g.stage_bytes = pre ? p.stage_bytes_pre : p.stage_bytes_ch;
         g.cpr_kv = D * ES / 16;
