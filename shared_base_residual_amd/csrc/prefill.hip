@@ -274,7 +274,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
             const int later = (n_tiles - 1 - it) < (g.nst - 2) ? (n_tiles - 1 - it) : (g.nst - 2);
             wait_vmcnt(later * fpw);
             ring_barrier();
-            if (it + g.nst - 1 < n_tiles) fill(it + g.nst - 1, (it + g.nst - 1) % g.nst);
             const char *st = smem + (size_t)(it % g.nst) * g.stage_bytes;
             const int tt = t0 + it * g.T;
             const bool masked = !pre || tt + g.T > t1;
@@ -321,6 +320,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                         sc[cb][h] = acc;
                     }
                 }
+                // this wave's share of the refill (stage of tile it - 1, free since the
+                // barrier), issued behind the score products of one 32-key step, a
+                // different step per wave: the direct loads of all eight waves at one
+                // point would queue at the CU's address unit and stall every wave
+                if (sub == (wave & (g.T / 32 - 1)) && it + g.nst - 1 < n_tiles)
+                    fill(it + g.nst - 1, (it + g.nst - 1) % g.nst);
                 if (masked) {
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb)
