@@ -45,7 +45,8 @@ template <typename T, int D, int CPAD>
 struct Acc {
     f32x4 o[D / 16];
     f32x4 w[CPAD > 0 ? CPAD / 16 : 1];
-    float m, l;
+    float m, l;  // l: this lane's share of the row's weight sum (fp32 step)
+    f32x4 ls;    // bf16 step: the row's weight sum in every element (a ones-row product)
 };
 
 // Reads K consecutive elements whose chunks sit at base + ofs[c].
@@ -253,14 +254,20 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
 #pragma unroll
             for (int i = 0; i < CPL; ++i) acc.w[i] *= alpha;
         }
+        acc.ls *= alpha;
     }
     f32x4 ev;
 #pragma unroll
     for (int i = 0; i < 4; ++i) ev[i] = fexp2(__builtin_fmaf(a[i], cl2, -acc.m));
     frag4 pB;
     pB.v = to_bf16x4(ev[0], ev[1], ev[2], ev[3]);
-    const f32x4 pr = __builtin_convertvector(pB.v, f32x4);  // the weights the product uses
-    acc.l = acc.l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    // row sums on the matrix unit: a ones operand against P^T adds each row's
+    // weights exactly as the P V product takes them (bf16), over all 16 tokens
+    {
+        frag4 ones;
+        ones.v = bf16x4{(bf16)1.0f, (bf16)1.0f, (bf16)1.0f, (bf16)1.0f};
+        acc.ls = O::mma16(ones, pB, acc.ls);
+    }
 
     // O^T += V^T P^T and W^T += Lv^T P^T
 #pragma unroll
@@ -745,6 +752,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     for (int i = 0; i < CPLx; ++i) acc.w[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     acc.m = -1.0e30f;
     acc.l = 0.0f;
+    acc.ls = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // ---- the ring: wait for tile i, refill the stage freed by tile i-1, compute tile i
     const int spw = g.T / (16 * TG);  // 16-token steps per wave per tile
@@ -769,10 +777,15 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
             }
         }
     }
-    float m_run = acc.m, l_run = acc.l;
-    // Sum of weights over the four lanes that share this query row.
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    float m_run = acc.m, l_run;
+    if constexpr (kBf16) {
+        l_run = acc.ls[0];  // already the whole row's sum
+    } else {
+        // sum of weights over the four lanes that share this query row
+        l_run = acc.l;
+        l_run += __shfl_xor(l_run, 16);
+        l_run += __shfl_xor(l_run, 32);
+    }
 
     // ---- merge the token groups of a row block (same lane layout in every wave);
     // the stages are free now (every load was awaited in the last iteration).

@@ -144,8 +144,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     }
     wait_vmcnt(0);  // every register load has landed: nothing pending inside the rings
 
-    f32x4 o[NCB][VPL], w[NCB][CPLx];
-    float m[NCB], l[NCB];
+    // l: each row's weight sum, in every element (a ones-row product, below)
+    f32x4 o[NCB][VPL], w[NCB][CPLx], l[NCB];
+    float m[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
@@ -153,7 +154,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < CPLx; ++i) w[cb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[cb] = -1.0e30f;
-        l[cb] = 0.0f;
+        l[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     int *s_pages = reinterpret_cast<int *>(smem + p.table_lds_off);
@@ -356,11 +357,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                     float e[8];
 #pragma unroll
                     for (int i = 0; i < 8; ++i) e[i] = fexp2(__builtin_fmaf(sc[cb][i >> 2][i & 3], cl2, -m_new));
-                    const bf16x4 p0 = to_bf16x4(e[0], e[1], e[2], e[3]), p1 = to_bf16x4(e[4], e[5], e[6], e[7]);
-                    pB[cb].v = __builtin_shufflevector(p0, p1, 0, 1, 2, 3, 4, 5, 6, 7);
-                    // the row sum takes the weights as rounded for the product
-                    const f32x4 r0 = __builtin_convertvector(p0, f32x4), r1 = __builtin_convertvector(p1, f32x4);
-                    l[cb] = l[cb] * alpha[cb] + (((r0[0] + r0[1]) + (r0[2] + r0[3])) + ((r1[0] + r1[1]) + (r1[2] + r1[3])));
+                    pB[cb].v = __builtin_shufflevector(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]),
+                                                       0, 1, 2, 3, 4, 5, 6, 7);
                 }
                 if (__builtin_amdgcn_ballot_w64(any_grow)) {
 #pragma unroll
@@ -369,7 +367,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                         for (int i = 0; i < VPL; ++i) o[cb][i] *= alpha[cb];
 #pragma unroll
                         for (int i = 0; i < CPLx; ++i) w[cb][i] *= alpha[cb];
+                        l[cb] *= alpha[cb];
                     }
+                }
+                // row sums on the matrix unit: a ones operand against P^T adds each
+                // row's weights exactly as the P V product takes them (bf16)
+                {
+                    frag ones;
+                    ones.v = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) l[cb] = O::mma(ones, pB[cb], l[cb]);
                 }
 
                 // O^T += V^T P^T (tile jj holds d = 16*jj + m in row m), shared V
@@ -435,9 +442,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     const float LN2 = 0.69314718055994530942f;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-        float lr = l[cb];
-        lr += __shfl_xor(lr, 16);
-        lr += __shfl_xor(lr, 32);
+        const float lr = l[cb][0];  // the whole row's sum
         if constexpr (CPAD > 0) {
             if (resid) {
                 // B operand: this lane's W (row n16, columns 4*CPL*j4 + 8*s + i), hi + lo
