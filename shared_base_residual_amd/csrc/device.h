@@ -290,6 +290,21 @@ __device__ inline void ring_barrier() {
 // query row's scores), with gfx950's cross-lane swaps on the VALU instead of
 // two LDS round trips.  permlane32_swap(x, x) leaves (x[l mod 32], x[l mod 32 + 32])
 // in the two results; permlane16_swap does the same for 16-lane rows 0<->1 and 2<->3.
+// Maximum of scores (finite or -inf, never NaN) as one v_med3_f32: the median of
+// (a, b, +inf) is max(a, b).  fmaxf would first quiet each operand (IEEE mode),
+// two extra instructions per maximum on the softmax's critical path.  pinf is
+// +inf read from the kernel parameters: with a literal +inf the compiler turns
+// the median back into fmaxf.
+__device__ inline float smax(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
+
+__device__ inline float row_max4(float x, float pinf) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = smax(__uint_as_float(a[0]), __uint_as_float(a[1]), pinf);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return smax(__uint_as_float(b[0]), __uint_as_float(b[1]), pinf);
+}
+
+// The same with fmaxf (the prefill kernel measured faster with it).
 __device__ inline float row_max4(float x) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
