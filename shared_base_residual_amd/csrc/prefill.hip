@@ -262,6 +262,15 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int jj = 0; jj < VPL; ++jj)
             vtr[jj] = elem_ofs(g.ofs_v, 4 * j4 + (n16 >> 2), 2 * (16 * jj + 4 * (n16 & 3)), g.cpr_kv, g.lg_kv);
+        // the same for the Lv rows: residual column tile jj, columns 16*jj + 4a
+        // (padding columns c >= r read column 0; their W is dropped at the end)
+        uint32_t wtr[CPLx];
+#pragma unroll
+        for (int jj = 0; jj < CPLx; ++jj) {
+            int col = 16 * jj + 4 * (n16 & 3);
+            col = col < p.r ? col : 0;
+            wtr[jj] = res ? elem_ofs(g.ofs_lv, 4 * j4 + (n16 >> 2), 2 * col, g.cpa_lr, g.lg_lr) : 0u;
+        }
         const int lr_rowb = 16 * g.cpa_lr;
         const int n_tiles = (t1 - t0 + g.T - 1) / g.T;
         const int fpw = fp.fpw;
@@ -391,19 +400,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) o[cb][jj] = O::mma(vA, pB[cb], o[cb][jj]);
                 }
-                // W^T += Lv^T P^T
+                // W^T += Lv^T P^T (tile jj holds c = 16*jj + m in row m), Lv read
+                // transposed like V
                 if constexpr (CPAD > 0) {
                     if (res) {
-                        Row<T, CPL> lr[8];
-#pragma unroll
-                        for (int h = 0; h < 2; ++h)
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) lr[4 * h + i] = lds_get<T, CPL>(stl + 16 * h * lr_rowb, ro.lv[i]);
 #pragma unroll
                         for (int jj = 0; jj < CPL; ++jj) {
+                            const bf16x4 w0 = lds_tr4(stl + wtr[jj]);
+                            const bf16x4 w1 = lds_tr4(stl + 16 * lr_rowb + wtr[jj]);
                             frag wA;
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) O::set_raw(wA, i, lr[i].e[jj]);
+                            wA.v = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
                             for (int cb = 0; cb < NCB; ++cb) w[cb][jj] = O::mma(wA, pB[cb], w[cb][jj]);
                         }
@@ -420,7 +426,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     // ---- epilogue: O^T += Bv^T W^T, o = O / l, written with lse
     // Bv as the A operand of O^T += Bv^T W^T: for d-tile jj and contraction step
     // s, lane (n16, j4) supplies Bv[kappa][16*jj + n16] for the 8 residual
-    // columns kappa = 4*CPL*j4 + 8*s + i, the columns whose W this lane holds.
+    // columns kappa = 16*(2s + i/4) + 4*j4 + i%4 (i < 8), the columns whose W
+    // this lane holds (W^T tiles 2s and 2s + 1).
     constexpr int NBS = CPL / 2 > 0 ? CPL / 2 : 1;  // contraction steps of 8 columns per lane group
     frag bvf[NBS][VPL];
     if constexpr (CPAD > 0) {
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                 for (int jj = 0; jj < VPL; ++jj)
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        int kap = 4 * CPL * j4 + 8 * s + i;
+                        int kap = 16 * (2 * s + (i >> 2)) + 4 * j4 + (i & 3);
                         kap = kap < p.r ? kap : 0;
                         O::set_raw(bvf[s][jj], i, bv[kap * ldb + 16 * jj]);
                     }
@@ -445,16 +452,16 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const float lr = l[cb][0];  // the whole row's sum
         if constexpr (CPAD > 0) {
             if (resid) {
-                // B operand: this lane's W (row n16, columns 4*CPL*j4 + 8*s + i), hi + lo
+                // B operand: this lane's W (row n16, columns 16*(2s + i/4) + 4*j4 + i%4), hi + lo
 #pragma unroll
                 for (int s = 0; s < NBS; ++s) {
                     frag wH, wL;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
-                        const int cc = 8 * s + i;  // = CPL * i' + jj' of the W^T tiles
+                        const int jt = 2 * s + (i >> 2);  // W^T tile
                         // padding columns (c >= r) hold P Lv of a stand-in column: drop them
-                        const bool real = 4 * CPL * j4 + cc < p.r;
-                        const float x = real ? w[cb][cc % CPLx][cc / CPLx] : 0.0f;
+                        const bool real = jt < CPLx && 16 * jt + 4 * j4 + (i & 3) < p.r;
+                        const float x = real ? w[cb][jt < CPLx ? jt : 0][i & 3] : 0.0f;
                         const float hi = (float)(bf16)x;
                         O::set(wH, i, x);
                         O::set(wL, i, x - hi);
