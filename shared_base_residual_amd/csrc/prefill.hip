@@ -391,15 +391,20 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                 // O^T += V^T P^T (tile jj holds d = 16*jj + m in row m), shared V
                 // operand read transposed from LDS: slots 0..3 = keys 4*j4+i of the
                 // first half, 4..7 = the second half, like P
+                // (every V read issued before the first product: the scores are dead
+                // by now, so their registers hold the operands and the LDS latency
+                // is paid once per step)
+                frag vA[VPL];
 #pragma unroll
                 for (int jj = 0; jj < VPL; ++jj) {
                     const bf16x4 v0 = lds_tr4(stk + vtr[jj]);
                     const bf16x4 v1 = lds_tr4(stk + 16 * kv_rowb + vtr[jj]);
-                    frag vA;
-                    vA.v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-#pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) o[cb][jj] = O::mma(vA, pB[cb], o[cb][jj]);
+                    vA[jj].v = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
                 }
+#pragma unroll
+                for (int jj = 0; jj < VPL; ++jj)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) o[cb][jj] = O::mma(vA[jj], pB[cb], o[cb][jj]);
                 // W^T += Lv^T P^T (tile jj holds c = 16*jj + m in row m), Lv read
                 // transposed like V
                 if constexpr (CPAD > 0) {
