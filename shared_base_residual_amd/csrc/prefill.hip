@@ -331,10 +331,12 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                     }
                 }
                 // this wave's share of the refill (stage of tile it - 1, free since the
-                // barrier), issued behind the score products of one 32-key step, a
-                // different step per wave: the direct loads of all eight waves at one
-                // point would queue at the CU's address unit and stall every wave
-                if (sub == (wave & (g.T / 32 - 1)) && it + g.nst - 1 < n_tiles)
+                // barrier), issued behind the score products of the first or second
+                // 32-key step (odd waves the second): the direct loads of all eight
+                // waves at one point would queue at the CU's address unit and stall
+                // every wave, and later steps leave the two-stage ring too little
+                // time to land them
+                if (sub == (wave & 1 & (g.T / 32 - 1)) && it + g.nst - 1 < n_tiles)
                     fill(it + g.nst - 1, (it + g.nst - 1) % g.nst);
                 if (masked) {
 #pragma unroll
