@@ -954,7 +954,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     }
 
     // weights of the slots: w_s = exp2(m_s - M), L = sum w_s l_s
-    const float mloc = wave_max(ml.x);
+    const float mloc = lane_max64(ml.x);
     if (lane == 0) s_red[wv] = mloc;
     __syncthreads();
     float M = s_red[0];
@@ -962,7 +962,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     for (int i = 1; i < NWV; ++i) M = fmaxf(M, s_red[i]);
     const float w = tid < ns ? fexp2(ml.x - M) : 0.0f;
     s_w[tid] = w;
-    const float lloc = wave_sum(w * ml.y);
+    const float lloc = lane_group_sum(w * ml.y, 1);
     if (lane == 0) s_red[NWV + wv] = lloc;
     __syncthreads();
     float Lsum = 0.0f;
@@ -999,16 +999,14 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     }
     for (int q = tid + 2 * NT; q < nqw; q += NT) wacc += s_w[q / R4] * pw[q];
     if (wres) {
-        for (int off = 32; off >= R4; off >>= 1)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wacc[e] += __shfl_xor(wacc[e], off);
+        for (int e = 0; e < 4; ++e) wacc[e] = lane_group_sum(wacc[e], R4);
         if (lane < R4) s_wp[wv * R4 + lane] = wacc;
     }
     // O: column group t % (d/4); lanes l and l ^ 32 share it (d/4 = 32) or
     // l, l ^ 16, l ^ 32, l ^ 48 (d/4 = 16)
-    for (int off = 32; off >= D4; off >>= 1)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], off);
+    for (int e = 0; e < 4; ++e) acc[e] = lane_group_sum(acc[e], D4);
     if (lane < D4) s_o[wv * D4 + lane] = acc;
     __syncthreads();
     if (wres && tid < r) {
@@ -1034,9 +1032,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
             }
         }
 #pragma unroll
-        for (int off = CPR; off < 64; off <<= 1)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) wbv[i] += __shfl_xor(wbv[i], off);
+        for (int i = 0; i < 8; ++i) wbv[i] = lane_group_sum(wbv[i], CPR);
     }
     if (lane < CPR)
 #pragma unroll

@@ -312,6 +312,38 @@ __device__ inline float row_max4(float x) {
     return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
+// Sum over the lanes l' of the wave with l' = l (mod g), g a power of two in
+// 1..32, every such lane receiving it; all steps on the VALU: DPP rotations by 8
+// and 4 within 16-lane rows (after the first, the values repeat with period 8,
+// so a rotation adds the same partner as an xor would), quad permutes for 2 and
+// 1, and the gfx950 lane swaps across rows (16) and halves (32).  No LDS round
+// trip, unlike __shfl_xor.
+template <int CTRL>
+__device__ inline float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ inline float lane_group_sum(float x, int g) {
+    if (g <= 8) x += dpp_mov<0x128>(x);  // row_ror:8
+    if (g <= 4) x += dpp_mov<0x124>(x);  // row_ror:4
+    if (g <= 2) x += dpp_mov<0x4E>(x);   // quad_perm [2,3,0,1]
+    if (g <= 1) x += dpp_mov<0xB1>(x);   // quad_perm [1,0,3,2]
+    if (g <= 16) {
+        const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    }
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+__device__ inline float lane_max64(float x) {
+    x = fmaxf(x, dpp_mov<0x128>(x));
+    x = fmaxf(x, dpp_mov<0x124>(x));
+    x = fmaxf(x, dpp_mov<0x4E>(x));
+    x = fmaxf(x, dpp_mov<0xB1>(x));
+    return row_max4(x);
+}
+
 __device__ inline float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
