@@ -324,7 +324,11 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
                 if (st != RATTN_OK) return st;
                 const int tiles_min = L > 0 ? H * nb_min : (p.pb < 4 ? p.pb : 4);
                 const int need = H > 1 ? 3 : 2;
-                const bool ok = (tiles_min >= 2 && plan_lds(8, need)) || plan_lds(4, need);
+                // Eight compute waves run the twelve-wave kernel (168 registers a
+                // lane), whose wider residual variants spill to scratch: only up to
+                // 32 residual columns (64 at d = 64) for bf16, none for fp32 at d = 128.
+                const int cpad8 = d->dtype == RATTN_BF16 ? (D == 64 ? 64 : 32) : (D == 64 ? 64 : 0);
+                const bool ok = (tiles_min >= 2 && pl->cpad <= cpad8 && plan_lds(8, need)) || plan_lds(4, need);
                 if (!ok) continue;
                 // Preference: a prefix tile of 32 or more tokens (the per-tile
                 // synchronisation is a large share of a tile's time), then the
