@@ -361,6 +361,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     p.fd_bpa = rattn::make_fastdiv(p.bpa);
     p.fd_g = rattn::make_fastdiv(p.g);
     p.fd_ps = rattn::make_fastdiv(p.ps);
+    p.fd_hq = rattn::make_fastdiv(p.HQ);
+    p.fd_ql = rattn::make_fastdiv(p.QL);
 
     // Workspace: the (max, sum), O and W partials of every (KV head, row, split).
     const int64_t rows_kv = (int64_t)HK * N * rpa;

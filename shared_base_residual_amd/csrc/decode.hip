@@ -910,11 +910,10 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     __shared__ float s_wbv[NWV * D];  // per-wave (W Bv) column sums
     touch_params<DecodeParams>();
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int64_t R = blockIdx.x;
-    const int h = (int)(R % p.HQ);
-    const int64_t at = R / p.HQ;
-    const int a = (int)(at / p.QL), t = (int)(at % p.QL);
-    const int k = h / p.g, ria = t * p.g + h % p.g;
+    const int R = blockIdx.x;  // (agent, query token, query head), < 2^31
+    const int at = fdiv(R, p.fd_hq), h = R - at * p.HQ;
+    const int a = fdiv(at, p.fd_ql), t = at - a * p.QL;
+    const int k = fdiv(h, p.fd_g), ria = t * p.g + (h - k * p.g);
     const int64_t rec0 = ((int64_t)k * p.N * p.rpa + (int64_t)a * p.rpa + ria) * p.n_slots;
     const int ns = p.n_slots, nps = p.n_ps, r = p.r;
     const bool wres = r > 0 && nps > 0;
@@ -954,27 +953,43 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     }
 
     // weights of the slots: w_s = exp2(m_s - M), L = sum w_s l_s
-    const float mloc = lane_max64(ml.x);
-    if (lane == 0) s_red[wv] = mloc;
-    __syncthreads();
-    float M = s_red[0];
+    float M, Lsum;
+    const float *sw;  // w of slot s at sw[s]
+    if (ns <= 64) {
+        // every wave forms all of them from the first 64 slots' statistics
+        // (lane = slot), into a block of its own: no workgroup barrier
+        const float2 m1 = lane < ns ? (wv == 0 ? ml : *reinterpret_cast<const float2 *>(p.p_ml + (rec0 + lane) * 2))
+                                    : float2{-3.0e38f, 0.0f};
+        M = lane_max64(m1.x);
+        const float w1 = lane < ns ? fexp2(m1.x - M) : 0.0f;
+        Lsum = lane_group_sum(w1 * m1.y, 1);
+        s_w[wv * 64 + lane] = w1;
+        __builtin_amdgcn_wave_barrier();
+        sw = s_w + wv * 64;
+    } else {
+        const float mloc = lane_max64(ml.x);
+        if (lane == 0) s_red[wv] = mloc;
+        __syncthreads();
+        M = s_red[0];
 #pragma unroll
-    for (int i = 1; i < NWV; ++i) M = fmaxf(M, s_red[i]);
-    const float w = tid < ns ? fexp2(ml.x - M) : 0.0f;
-    s_w[tid] = w;
-    const float lloc = lane_group_sum(w * ml.y, 1);
-    if (lane == 0) s_red[NWV + wv] = lloc;
-    __syncthreads();
-    float Lsum = 0.0f;
+        for (int i = 1; i < NWV; ++i) M = fmaxf(M, s_red[i]);
+        const float w = tid < ns ? fexp2(ml.x - M) : 0.0f;
+        s_w[tid] = w;
+        const float lloc = lane_group_sum(w * ml.y, 1);
+        if (lane == 0) s_red[NWV + wv] = lloc;
+        __syncthreads();
+        Lsum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NWV; ++i) Lsum += s_red[NWV + i];
+        for (int i = 0; i < NWV; ++i) Lsum += s_red[NWV + i];
+        sw = s_w;
+    }
 
     // O = sum_s w_s O_s
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < B; ++u) {
         const int q = tid + u * NT;
-        if (q < nq) acc += s_w[q / D4] * ob[u];
+        if (q < nq) acc += sw[q / D4] * ob[u];
     }
     for (int q0 = B * NT; q0 < nq; q0 += B * NT) {
 #pragma unroll
@@ -985,7 +1000,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 #pragma unroll
         for (int u = 0; u < B; ++u) {
             const int q = q0 + tid + u * NT;
-            if (q < nq) acc += s_w[q / D4] * ob[u];
+            if (q < nq) acc += sw[q / D4] * ob[u];
         }
     }
     // W = sum over prefix slots of w_s W_s.  Thread t holds column group t % (r/4):
@@ -995,9 +1010,9 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int q = tid + u * NT;
-        if (q < nqw) wacc += s_w[q / R4] * wb[u];
+        if (q < nqw) wacc += sw[q / R4] * wb[u];
     }
-    for (int q = tid + 2 * NT; q < nqw; q += NT) wacc += s_w[q / R4] * pw[q];
+    for (int q = tid + 2 * NT; q < nqw; q += NT) wacc += sw[q / R4] * pw[q];
     if (wres) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) wacc[e] = lane_group_sum(wacc[e], R4);

@@ -163,6 +163,7 @@ struct DecodeParams {
     int table_lds_off;
     // the same divisors for one multiply each (see FastDiv)
     FastDiv fd_hg, fd_rg, fd_hk, fd_pv, fd_prg, fd_rpa, fd_bpa, fd_g, fd_ps;
+    FastDiv fd_hq, fd_ql;  // query heads, query tokens (the merge's row index)
 };
 
 // Dynamic LDS a workgroup may use (gfx950: 160 KiB per workgroup, less what
