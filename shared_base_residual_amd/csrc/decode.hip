@@ -846,15 +846,26 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         for (int jj = 0; jj < VPL; ++jj) *reinterpret_cast<f32x4 *>(po + 16 * jj) = acc.o[jj];
         if (resid) {
             const int arel = agent_m - blk.a0;
+            if constexpr (MASKED) {
+                // every column is this row's own agent's (element stores: measured
+                // faster here than the vector form below, through the schedule of the
+                // whole kernel rather than the stores themselves)
 #pragma unroll
-            for (int jj = 0; jj < CPLx; ++jj)
+                for (int jj = 0; jj < CPLx; ++jj)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int c = 16 * jj + 4 * j4 + i;
-                    // masked: every column is this row's own agent's
-                    if (c < cvalid && (MASKED || p.shared_lr || (c >> p.lr_shift) == arel))
-                        p.p_w[rec * p.r + (c & (p.r - 1))] = acc.w[jj][i];
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = 16 * jj + 4 * j4 + i;
+                        if (c < cvalid) p.p_w[rec * p.r + (c & (p.r - 1))] = acc.w[jj][i];
+                    }
+            } else {
+                // the lane's four columns c0 .. c0 + 3 of tile jj belong to one agent (r >= 8)
+#pragma unroll
+                for (int jj = 0; jj < CPLx; ++jj) {
+                    const int c0 = 16 * jj + 4 * j4;
+                    if (c0 < cvalid && (p.shared_lr || (c0 >> p.lr_shift) == arel))
+                        *reinterpret_cast<f32x4 *>(p.p_w + rec * p.r + (c0 & (p.r - 1))) = acc.w[jj];
                 }
+            }
         }
         if (j4 == 0) *reinterpret_cast<float2 *>(p.p_ml + rec * 2) = float2{m_run, l_run};
     }
