@@ -153,6 +153,15 @@ EDGE = [
     synth.Case(2, 4, 2, 64, 8, 300, priv_len=20, q_len=20, mode="prefill", dtype="f32", name="prefill fp32"),
     synth.Case(17, 4, 1, 128, 8, 129, name="17 agents g=4"),
     synth.Case(9, 8, 2, 128, 32, 1500, priv_len=17, name="several agents per block, r=32, ragged last block"),
+    # prefill: a paged prefix (the page table leaves room for 64-key stages only),
+    # padding residual columns (r = 16 in 32-column tiles), and r = 64 (two
+    # contraction steps in the Bv epilogue)
+    synth.Case(2, 8, 2, 128, 32, 1000, priv_len=40, q_len=40, page_size=16, n_phys_pages=80, mode="prefill",
+               name="paged prefill"),
+    synth.Case(2, 8, 2, 128, 16, 700, priv_len=50, q_len=50, mode="prefill", name="prefill r=16 ragged"),
+    synth.Case(2, 8, 2, 128, 64, 300, priv_len=30, q_len=30, mode="prefill", name="prefill r=64"),
+    # more than 64 splits per row: the merge's weight pass across waves
+    synth.Case(2, 4, 1, 128, 16, 40000, name="more than 64 splits"),
 ]
 
 
