@@ -258,7 +258,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
                 for (int t = 128; t >= 16; t /= 2) {
                     if (t % (16 * tg_max) || t > 16 * nw) continue;  // the fill gives each 16-row group one wave
                     const int sb = t * (2 * H * kv_row + 2 * lr_row_bytes);
-                    const int n = (rattn::kSplitLds - table_bytes) / sb;
+                    const int n = (rattn::kLdsMax - table_bytes) / sb;
                     if (n >= 3 || (t == 16 * tg_max && n >= need)) {
                         *T = t;
                         *nst = n < 4 ? n : 4;
@@ -297,7 +297,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             // The split's page-table entries.
             p.table_lds_off = (lds + 15) & ~15;
             if (d->page_size > 0 && L > 0) lds = p.table_lds_off + (int)(cdiv(p.tok_ps, d->page_size) + 1) * 4;
-            if (lds > rattn::kSplitLds) return false;
+            if (lds > rattn::kLdsMax) return false;
             pl->lds = (size_t)lds;
             return true;
         };
@@ -438,7 +438,7 @@ int make_prefill_plan(const rattn_desc *d, PrefillPlan *pl) {
         p.T = T;
         p.stage_bytes_pre = T * 16 * (2 * kv_chunks + 2 * lr_chunks);
         p.stage_bytes_ch = T * 16 * (2 * kv_chunks);
-        const int room = rattn::kSplitLds - table_bytes;
+        const int room = rattn::kLdsMax - table_bytes;
         p.nst_pre = room / p.stage_bytes_pre < 8 ? room / p.stage_bytes_pre : 8;
         p.nst_ch = room / p.stage_bytes_ch < 8 ? room / p.stage_bytes_ch : 8;
         if (p.nst_pre < 2 || p.nst_ch < 2) return false;

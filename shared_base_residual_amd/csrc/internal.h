@@ -166,10 +166,9 @@ struct DecodeParams {
     FastDiv fd_hq, fd_ql;  // query heads, query tokens (the merge's row index)
 };
 
-// Dynamic LDS a workgroup may use (gfx950: 160 KiB per workgroup, less what
-// the kernel declares statically).  The split and prefill kernels declare none.
-constexpr int kLdsBudget = 160 * 1024 - 1024;
-constexpr int kSplitLds = 160 * 1024;
+// Dynamic LDS a split or prefill workgroup may use: all of gfx950's 160 KiB per
+// workgroup (neither kernel declares static LDS).
+constexpr int kLdsMax = 160 * 1024;
 // Page-table entries of one split copied into LDS.
 constexpr int kMaxPagesPerSplit = 2048;
 
