@@ -190,10 +190,17 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
             __builtin_memcpy(&lf[s], &lr, sizeof(frag));
         }
     }
-    // S^T = K Q^T + Lk U^T, raw
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    // S^T = K Q^T + Lk U^T, raw, in two independent accumulator chains (even
+    // and odd contraction steps, U hi and U lo) so that consecutive MFMAs do not
+    // wait for each other's results; summed once at the end
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) a = O::mma(kf[s], qB[s], a);
+    for (int s = 0; s < KS; ++s) {
+        if (s & 1)
+            a2 = O::mma(kf[s], qB[s], a2);
+        else
+            a = O::mma(kf[s], qB[s], a);
+    }
     if (CS > 0 && resid) {
         if constexpr (MASKED) {
             const frag zf = O::zero();
@@ -209,17 +216,18 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
 #pragma unroll
                 for (int s = 0; s < CS; ++s) {
                     a = O::mma(lf[s], mine ? uH[s] : zf, a);
-                    a = O::mma(lf[s], mine ? uL[s] : zf, a);
+                    a2 = O::mma(lf[s], mine ? uL[s] : zf, a2);
                 }
             }
         } else {
 #pragma unroll
             for (int s = 0; s < CS; ++s) {
                 a = O::mma(lf[s], uH[s], a);
-                a = O::mma(lf[s], uL[s], a);
+                a2 = O::mma(lf[s], uL[s], a2);
             }
         }
     }
+    a += a2;
     // value operands: issued now, consumed after the softmax
     bf16x4 va[VPL];
 #pragma unroll
