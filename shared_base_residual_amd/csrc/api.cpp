@@ -99,7 +99,6 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     p.lr_own = RATTN_LR_OWN;
     const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
     p.c = scale * 1.44269504088896340736f;
-    p.pinf = __builtin_inff();
 
     // The decomposition: the masked mode first where it applies, else (or when
     // its ring does not fit) block-diagonal residual columns.

@@ -169,7 +169,7 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
                                    const uint32_t *wtr, const char *kvb, const char *lrb, int t, bool masked,
                                    const Ops<bf16>::frag *qB, const Ops<bf16>::frag *uH, const Ops<bf16>::frag *uL,
                                    float cl2, bool resid, int t1, bool causal, int tq, int j4, int na, int arow,
-                                   int ast, float pinf) {
+                                   int ast) {
     using O = Ops<bf16>;
     using frag = O::frag;
     using frag4 = O::frag4;
@@ -248,8 +248,8 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     }
 
     // online softmax (log2 domain, running max in scaled units)
-    float mx = smax(smax(a[0], a[1], pinf), smax(a[2], a[3], pinf), pinf);
-    mx = row_max4(mx, pinf) * cl2;  // -inf stays -inf
+    float mx = amax3(a[0], a[1], amax(a[2], a[3]));  // scores are finite or -inf
+    mx = row_max4(mx) * cl2;  // -inf stays -inf
     const bool grow = mx > acc.m + kRescaleSlack;
     float alpha = 1.0f;
     if (__builtin_amdgcn_ballot_w64(grow)) {
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
                 if constexpr (kBf16)
                     step16_bf16<D, CPAD, MASKED>(acc, ro, vtr, wtr, st + row0 * kv_rowb, st + row0 * lr_rowb,
                                                  tt + row0, masked, qB, uH, uL, cl2, resid, t1, causal, tq, j4,
-                                                 blk.na, vm ? arow_m : -1, 256 * g.cpa_lr, p.pinf);
+                                                 blk.na, vm ? arow_m : -1, 256 * g.cpa_lr);
                 else
                     step16<T, D, CPAD>(acc, ro, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked, qB, uH,
                                        uL, cl2, resid, t1, causal, tq, j4);

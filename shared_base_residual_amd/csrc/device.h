@@ -286,30 +286,29 @@ __device__ inline void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Maxima of values that are never NaN (scores: finite or -inf), as v_max_f32 /
+// v_max3_f32 written out.  fmaxf would first quiet each operand (IEEE mode), a
+// v_max_f32 of the operand with itself, on the softmax's critical path.
+__device__ inline float amax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ inline float amax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 // Maximum over the four lanes l, l^16, l^32, l^48 (the lanes that hold one
 // query row's scores), with gfx950's cross-lane swaps on the VALU instead of
 // two LDS round trips.  permlane32_swap(x, x) leaves (x[l mod 32], x[l mod 32 + 32])
 // in the two results; permlane16_swap does the same for 16-lane rows 0<->1 and 2<->3.
-// Maximum of scores (finite or -inf, never NaN) as one v_med3_f32: the median of
-// (a, b, +inf) is max(a, b).  fmaxf would first quiet each operand (IEEE mode),
-// two extra instructions per maximum on the softmax's critical path.  pinf is
-// +inf read from the kernel parameters: with a literal +inf the compiler turns
-// the median back into fmaxf.
-__device__ inline float smax(float a, float b, float pinf) { return __builtin_amdgcn_fmed3f(a, b, pinf); }
-
-__device__ inline float row_max4(float x, float pinf) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = smax(__uint_as_float(a[0]), __uint_as_float(a[1]), pinf);
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return smax(__uint_as_float(b[0]), __uint_as_float(b[1]), pinf);
-}
-
-// The same with fmaxf (the prefill kernel measured faster with it).
 __device__ inline float row_max4(float x) {
     const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    x = amax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+    return amax(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // Sum over the lanes l' of the wave with l' = l (mod g), g a power of two in

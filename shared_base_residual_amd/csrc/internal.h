@@ -139,7 +139,6 @@ struct DecodeParams {
     int N, QL, HQ, HK, g, r, lr_shift, rpa, apb, bpa, ps, shared_lr;
     int causal;       // private token j is visible to query token t only if j <= t
     float c;          // softmax scale * log2(e)
-    float pinf;       // +inf (an operand the compiler cannot fold)
     int n_blocks, n_rg, n_ps;
     int H, n_hg;      // KV heads per prefix item (sharing its low-rank tile), head groups
     int bpg;          // 16-row blocks per prefix row group (1, 2 or 4)

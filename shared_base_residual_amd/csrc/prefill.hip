@@ -357,8 +357,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                 bool any_grow = false;
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
-                    float mx = fmaxf(fmaxf(fmaxf(sc[cb][0][0], sc[cb][0][1]), fmaxf(sc[cb][0][2], sc[cb][0][3])),
-                                     fmaxf(fmaxf(sc[cb][1][0], sc[cb][1][1]), fmaxf(sc[cb][1][2], sc[cb][1][3])));
+                    // (scores are finite or -inf, never NaN)
+                    float mx = amax3(amax3(sc[cb][0][0], sc[cb][0][1], sc[cb][0][2]),
+                                     amax3(sc[cb][0][3], sc[cb][1][0], sc[cb][1][1]), amax(sc[cb][1][2], sc[cb][1][3]));
                     mx = row_max4(mx) * cl2;  // scaled (log2 units); -inf stays -inf
                     const bool grow = mx > m[cb] + kRescaleSlack;
                     const float m_new = grow ? mx : m[cb];
