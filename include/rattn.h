@@ -30,6 +30,10 @@
  *     rattn_status is returned and nothing is launched when validation fails.
  *     A failed launch returns RATTN_E_HIP.  Faults during execution surface at
  *     the caller's next synchronisation.
+ *   - Inputs are finite.  The kernels take every score to be finite or -inf (a
+ *     masked key), so a NaN or infinity in q, the caches or the projections
+ *     gives unspecified outputs.  Pool pages that the block table does not
+ *     reference are never read and may hold anything.
  *   - Block-table entries must lie in [0, n_phys_pages); this is not checked on
  *     the device (an out-of-range entry is undefined behaviour).  Duplicate
  *     entries (aliased pages) are allowed.

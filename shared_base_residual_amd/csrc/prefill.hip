@@ -423,7 +423,6 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                         }
                     }
                 }
-        
             }
         }
         // the ring is drained (the last iteration waited for every load); every wave
