@@ -157,16 +157,6 @@ __device__ inline bf16x4 lds_tr4(const void *p) {
     return __builtin_bit_cast(bf16x4, v);
 }
 
-// Device-coherent (agent-scope) 4-byte store and load: on gfx950 these are
-// global_store/global_load with the device scope bit, so a value stored by one
-// XCD is read back by another without L2 writeback or invalidation.
-__device__ inline void st_coherent(float *p, float v) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline float ld_coherent(const float *p) {
-    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ---- staging through LDS ---------------------------------------------------
 //
 // Tiles are copied from global memory into LDS with gfx950's direct loads
@@ -216,13 +206,6 @@ __device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_bas
 // about 7.3 TB/s with the bit against 5.9 TB/s without it (a one-workgroup-
 // per-CU ring over 1 GiB); data that other workgroups re-read through L2 (the
 // low-rank rows) keeps the default policy.
-__device__ inline void dma16_nt(const void *gsrc, uint32_t lds_base) {
-    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-                 :
-                 : "v"(gsrc), "s"(lds_base)
-                 : "memory", "m0");
-}
 __device__ inline void dma16s_nt(const void *sbase, uint32_t voff, uint32_t lds_base) {
     lds_base = __builtin_amdgcn_readfirstlane(lds_base);
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
@@ -341,18 +324,6 @@ __device__ inline float lane_max64(float x) {
     x = fmaxf(x, dpp_mov<0x4E>(x));
     x = fmaxf(x, dpp_mov<0xB1>(x));
     return row_max4(x);
-}
-
-__device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
-}
-
-__device__ inline float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
 }
 
 }  // namespace rattn

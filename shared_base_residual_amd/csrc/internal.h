@@ -94,16 +94,6 @@ RATTN_HD RowBlock prefix_block(int b, int n_agents, int rpa, int apb, const Fast
 }
 
 // Agent and row-within-agent of row m (< nr) of a block.
-RATTN_HD void block_row(const RowBlock &rb, int m, int rpa, int *agent, int *ria) {
-    if (rpa <= 16) {
-        *agent = rb.a0 + m / rpa;
-        *ria = m % rpa;
-    } else {
-        *agent = rb.a0;
-        *ria = rb.f + m;
-    }
-}
-
 RATTN_HD void block_row(const RowBlock &rb, int m, const FastDiv &rpa, int *agent, int *ria) {
     if (rpa.d <= 16) {
         const int a = fdiv(m, rpa);
