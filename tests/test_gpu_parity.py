@@ -162,6 +162,11 @@ EDGE = [
     synth.Case(2, 8, 2, 128, 64, 300, priv_len=30, q_len=30, mode="prefill", name="prefill r=64"),
     # more than 64 splits per row: the merge's weight pass across waves
     synth.Case(2, 4, 1, 128, 16, 40000, name="more than 64 splits"),
+    # one row per agent (g = 1, r = 32): the masked ring does not fit, so blocks of
+    # two agents with block-diagonal residual columns
+    synth.Case(16, 4, 4, 128, 32, 600, priv_len=5, name="g=1 r=32, two agents per block"),
+    # masked blocks of more than four agents: eight, then two (g = 2, r = 64, d = 64)
+    synth.Case(10, 4, 2, 64, 64, 500, name="masked, 8 + 2 agents per block, d=64"),
 ]
 
 
