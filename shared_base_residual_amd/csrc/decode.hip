@@ -159,9 +159,10 @@ __device__ inline void step16(Acc<T, D, CPAD> &acc, const ReadOfs<T, D, CPAD> &r
 // vtr / wtr: lane offsets of the transposed V and Lv reads; U (uH, uL) is
 // unscaled.
 // MASKED: the tile's rows belong to na agents with separate rank-CPAD caches;
-// the score correction runs per agent against that agent's Lk rows with U kept
-// only in the lanes of its rows, and W accumulates per agent with P kept only in
-// those lanes, so W (and U) hold CPAD columns whatever the number of agents.
+// the score correction runs per agent (that agent's Lk rows against every row's
+// U) and is added only in the lanes of that agent's rows, and W accumulates per
+// agent with P kept only in those lanes, so W (and U) hold CPAD columns whatever
+// the number of agents.
 // arow: the agent (0 .. na-1 within the tile) of this lane's row, -1 if none;
 // ast: LDS bytes from one agent's low-rank rows to the next.
 template <int D, int CPAD, bool MASKED>
@@ -203,9 +204,9 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     }
     if (CS > 0 && resid) {
         if constexpr (MASKED) {
-            const frag zf = O::zero();
+            // agent ag's Lk rows against every row's U, kept (times 1.0, else 0.0:
+            // the products are finite) only in the lanes of agent ag's rows
             for (int ag = 0; ag < na; ++ag) {
-                const bool mine = arow == ag;
                 if (ag > 0) {
 #pragma unroll
                     for (int s = 0; s < CS; ++s) {
@@ -213,11 +214,15 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
                         __builtin_memcpy(&lf[s], &lr, sizeof(frag));
                     }
                 }
+                f32x4 t = {0.f, 0.f, 0.f, 0.f}, t2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < CS; ++s) {
-                    a = O::mma(lf[s], mine ? uH[s] : zf, a);
-                    a2 = O::mma(lf[s], mine ? uL[s] : zf, a2);
+                    t = O::mma(lf[s], uH[s], t);
+                    t2 = O::mma(lf[s], uL[s], t2);
                 }
+                const float keep = arow == ag ? 1.0f : 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = __builtin_fmaf(t[i] + t2[i], keep, a[i]);
             }
         } else {
 #pragma unroll
