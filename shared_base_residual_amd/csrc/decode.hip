@@ -780,10 +780,15 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
             const bool masked = causal || tt + g.T > t1;
             for (int u = 0; u < spw; ++u) {
                 const int row0 = 16 * (tg * spw + u);
-                if constexpr (kBf16)
-                    step16_bf16<D, CPAD, MASKED>(acc, ro, vtr, wtr, st + row0 * kv_rowb, st + row0 * lr_rowb,
+                if constexpr (kBf16) {
+                    // the step's stage offsets as opaque wave-uniform values: one add per
+                    // operand read, rather than per-read offsets advanced every step
+                    const int ko = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * kv_rowb);
+                    const int lo = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * lr_rowb);
+                    step16_bf16<D, CPAD, MASKED>(acc, ro, vtr, wtr, smem + ko, smem + lo,
                                                  tt + row0, masked, qB, uH, uL, cl2, resid, t1, causal, tq, j4,
                                                  blk.na, vm ? arow_m : -1, 256 * g.cpa_lr);
+                }
                 else
                     step16<T, D, CPAD>(acc, ro, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked, qB, uH,
                                        uL, cl2, resid, t1, causal, tq, j4);
