@@ -99,11 +99,14 @@ def _sample_rows(case, n, seed):
     return m
 
 
-def test_shared_lr_chunked_prefill_sampled():
+@pytest.mark.parametrize("variant", ["base", "stress"])
+def test_shared_lr_chunked_prefill_sampled(variant):
     c = synth.CONFIGS[3]
-    x = synth.make_inputs(c, 3)
+    kw = synth.STRESS if variant == "stress" else {}
+    seed = 3 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0)
+    x = synth.make_inputs(c, seed, **kw)
     mask = _sample_rows(c, 48, 0)
-    compare(c, x, with_b0=True, row_mask=mask, what="BaseLRShared prefill (sampled rows)")
+    compare(c, x, with_b0=(variant == "base"), row_mask=mask, what=f"BaseLRShared prefill {variant} (sampled rows)")
 
 
 def test_full_depth_decode_sampled_layers():
