@@ -136,8 +136,10 @@ int rattn_oracle_attend(const oracle_shape *s, const oracle_inputs *in, const ui
         double *K = (double *)malloc(sizeof(double) * (size_t)(NT * D));
         double *V = (double *)malloc(sizeof(double) * (size_t)(NT * D));
         double *sc = (double *)malloc(sizeof(double) * (size_t)NT);
-        if (!K || !V || !sc) {
-            free(K); free(V); free(sc);
+        double *qv = (double *)malloc(sizeof(double) * (size_t)D);
+        double *ov = (double *)malloc(sizeof(double) * (size_t)D);
+        if (!K || !V || !sc || !qv || !ov) {
+            free(K); free(V); free(sc); free(qv); free(ov);
 #pragma omp atomic write
             failed = 1;
             continue;
@@ -191,10 +193,11 @@ int rattn_oracle_attend(const oracle_shape *s, const oracle_inputs *in, const ui
 #else
                 const int64_t nk = s->causal ? L + t + 1 : NT;
 #endif
+                for (int dd = 0; dd < D; ++dd) qv[dd] = ld(in->q, row * D + dd, el);
                 double mx = -INFINITY;
                 for (int64_t j = 0; j < nk; ++j) {
                     double dot = 0.0;
-                    for (int dd = 0; dd < D; ++dd) dot += ld(in->q, row * D + dd, el) * K[j * D + dd];
+                    for (int dd = 0; dd < D; ++dd) dot += qv[dd] * K[j * D + dd];
                     sc[j] = scale * dot;
                     if (sc[j] > mx) mx = sc[j];
                 }
@@ -203,11 +206,12 @@ int rattn_oracle_attend(const oracle_shape *s, const oracle_inputs *in, const ui
                     sc[j] = exp(sc[j] - mx); /* unnormalised weight */
                     sum += sc[j];
                 }
-                for (int dd = 0; dd < D; ++dd) {
-                    double o = 0.0;
-                    for (int64_t j = 0; j < nk; ++j) o += sc[j] * V[j * D + dd];
-                    out[row * D + dd] = o / sum;
-                }
+                /* o[dd] = sum_j p_j V[j][dd], each sum taken over j in order (the
+                 * j loop outside walks V row by row) */
+                for (int dd = 0; dd < D; ++dd) ov[dd] = 0.0;
+                for (int64_t j = 0; j < nk; ++j)
+                    for (int dd = 0; dd < D; ++dd) ov[dd] += sc[j] * V[j * D + dd];
+                for (int dd = 0; dd < D; ++dd) out[row * D + dd] = ov[dd] / sum;
 #if ORACLE_MUTANT == 9
                 if (lse) lse[row] = log(sum); /* mistake: max term missing */
 #else
@@ -218,6 +222,8 @@ int rattn_oracle_attend(const oracle_shape *s, const oracle_inputs *in, const ui
         free(K);
         free(V);
         free(sc);
+        free(qv);
+        free(ov);
     }
     return failed ? -2 : 0;
 }
