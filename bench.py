@@ -1,31 +1,36 @@
 """Benchmark of fused residual attention over a shared base KV cache on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 1] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4] [--sub 1,2,3] [--no-cpu]
 
-One step = one rattn_decode call (split kernel, then combine) over one
-layer of the Llama-3-8B-shaped decode workload: 4 agents on a 32768-token shared
-prefix, H_q=32, H_kv=8, d=128, per-agent rank-16 residual caches, bf16 inputs,
-fp32 accumulation.  Inputs are seeded synthetic data already resident in HBM.
-Several replicas of the input set are rotated so that each step reads its
-143 MB from HBM, not from the 256 MB Infinity Cache left warm by the previous
-step.
+Headline workload (default): the 70B-shaped full-depth decode step, 80 layers of
+H_q=64, H_kv=8, d=128 over a 65536-token shared prefix, 8 agents with per-agent
+rank-16 residual caches, bf16 inputs, fp32 accumulation (24.2 GB of inputs,
+resident in HBM, drawn on the device).  One step = the 80 layers' rattn_decode
+calls (split kernel, then merge) back to back on one stream.  The other
+workloads (8B-shaped decode, paged copy-on-write decode, BaseLRShared chunked
+prefill) follow as sub-records in the same JSON line, each with its own
+roofline.  For the single-layer workloads several replicas of the inputs are
+rotated so that each step reads from HBM, not from the 256 MB Infinity Cache
+left warm by the previous step.
 
-Prints one JSON line.  `value` is agent x context-token pairs per second (Gtok/s).
-`roofline` is for the split kernel, which carries all but the merge (for the
-prefill workload, the prefill kernel, which is the whole call): its algorithmic
-bytes (or flops) per launch divided by its average duration, measured with HIP
-events on the launch stream around K * layers back-to-back launches of it over
-the same rotated inputs, right after the timed steps.  `traffic` is the HBM
-bytes per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+Prints one JSON line.  `value` is agent x context-token pairs per second
+(Gtok/s) over the timed steps (wall clock, K steps bracketed by device
+synchronisations).  `roofline` is for the kernel that carries the call (the
+split kernel for decode, the prefill kernel for prefill): algorithmic bytes (or
+flops) per launch over its average duration, measured with HIP events on the
+launch stream around K * layers back-to-back launches after a warm-up that runs
+until the launch time is stable; `frac_timed_steps` is the same ratio for the
+whole call over the timed steps.  `achievable` is the read rate of an HBM probe
+kernel measured in the same run (libhbm_probe.so).  `traffic` is the HBM bytes
+per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters
 (profiles/counters.json, written by shared_base_residual_amd/counters.py) when
 they were taken on the current library sources, else null.  `cpu_baseline`
-times the fp64 oracle on the host cores.
+times the fp64 oracle on the host cores over a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import statistics
@@ -41,10 +46,25 @@ METRIC = "agent x ctx-token attention throughput (Gtok/s) + achieved HBM GB/s, 1
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 
 
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
 def source_hash() -> str:
     from shared_base_residual_amd.build import source_hash as h
 
     return h()
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 class Hip:
@@ -71,6 +91,26 @@ class Hip:
         assert self.h.hipEventSynchronize(b) == 0
         assert self.h.hipEventElapsedTime(ctypes.byref(t), a, b) == 0
         return t.value
+
+    def time_ms(self, fn, n, stream):
+        """Average ms of fn() over n back-to-back calls, between two events."""
+        a, b = self.event(), self.event()
+        self.record(a, stream)
+        for i in range(n):
+            fn(i)
+        self.record(b, stream)
+        return self.elapsed_ms(a, b) / n
+
+
+def stable_ms(hip, fn, n, stream, tol=0.01, max_batches=40):
+    """Runs batches of n back-to-back calls until two consecutive batch averages
+    agree within tol (clocks and caches settled); returns the batch averages."""
+    hist = []
+    for _ in range(max_batches):
+        hist.append(hip.time_ms(fn, n, stream))
+        if len(hist) >= 3 and abs(hist[-1] - hist[-2]) <= tol * hist[-1] and abs(hist[-2] - hist[-3]) <= tol * hist[-2]:
+            break
+    return hist
 
 
 def algorithmic_bytes(c):
@@ -114,8 +154,9 @@ def pairs_per_call(c):
 def cpu_baseline(case, seed, budget_s=12.0):
     """The fp64 oracle, as it stands, on the host cores, over a bounded sample of
     the workload: the whole call for the decode workloads that finish in seconds,
-    one agent's rows otherwise; repeated until about `budget_s` seconds of work
-    have been timed.  The rate is scaled by the fraction of rows computed."""
+    one agent's rows of one layer otherwise; repeated until about `budget_s`
+    seconds of work have been timed.  The rate is scaled by the fraction of rows
+    computed (and, for the multi-layer workload, counts one layer's pairs)."""
     import numpy as np
 
     import oracle
@@ -138,12 +179,12 @@ def cpu_baseline(case, seed, budget_s=12.0):
             break
     t = statistics.median(times)
     return {"value": round(pairs_per_call(case) * frac / t / 1e9, 6), "unit": "Gtok/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{what} ({case.name}, one layer), {len(times)} runs, median {t:.3f} s, fp64, "
                       f"{threads} threads"}
 
 
-def traffic_from_counters(kernel_key, launches_per_step=1):
+def traffic_from_counters(kernel_key):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources."""
     if not os.path.exists(COUNTERS):
@@ -156,50 +197,65 @@ def traffic_from_counters(kernel_key, launches_per_step=1):
     return ent.get("bytes_per_launch")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1)
-    ap.add_argument("--replicas", type=int, default=0, help="input sets rotated (0: auto)")
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--seed", type=int, default=None)
-    args = ap.parse_args()
+def hbm_probe(hip, stream, dev):
+    """Read bandwidth two streaming readers reach over a 4 GiB buffer (each byte
+    read once per launch): plain vector loads and direct loads into LDS, over a
+    few launch shapes; the best is `achievable`."""
+    import torch
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU "
-              "path: run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+    from shared_base_residual_amd.build import PROBE_LIB
 
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.hbm_probe_vec.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.hbm_probe_lds.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, device=dev, dtype=torch.int32)
+    sink = torch.zeros(1 << 16, device=dev, dtype=torch.int32)
+    res = {}
+    shapes = [("vec", b, 0) for b in (2048, 4096, 8192)] + [("lds", b, w) for b in (256, 512, 1024) for w in (4, 8)]
+    for kind, blocks, waves in shapes:
+        if kind == "vec":
+            fn = lambda i: lib.hbm_probe_vec(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, stream)
+        else:
+            fn = lambda i: lib.hbm_probe_lds(buf.data_ptr(), nbytes, sink.data_ptr(), blocks, waves, stream)
+        assert fn(0) == 0
+        ms = min(hip.time_ms(fn, 4, stream) for _ in range(3))
+        res[f"{kind}:{blocks}" + (f"x{waves}w" if waves else "")] = round(nbytes / (ms / 1e3) / 1e9, 1)
+    torch.cuda.synchronize()
+    del buf, sink
+    best = max(res, key=res.get)
+    return {"achievable": res[best], "unit": "GB/s", "reader": best, "buffer_bytes": nbytes, "all": res}
+
+
+def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None):
+    """Times one workload; returns its record (without cpu_baseline)."""
     import torch
 
     import shared_base_residual_amd as R
     import synth
 
-    R.lib()
-    case = synth.CONFIGS[args.config]
-    seed = args.config if args.seed is None else args.seed
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
+    case = synth.CONFIGS[config]
+    seed = config if seed is None else seed
     ab = algorithmic_bytes(case)
     layers = case.layers
     op = R.RATTN_OP_PREFILL if case.mode == "prefill" else R.RATTN_OP_DECODE
+    say(f"[bench] {case.name}: drawing inputs")
 
     # ---- inputs resident in HBM
-    if layers > 1 or args.config == 4:
+    if layers > 1:
         sets = [synth.make_inputs_torch(case, seed, l, dev) for l in range(layers)]
         n_sets = layers
     else:
         x = synth.make_inputs(case, seed)
         base = synth.to_torch(x, dev)
-        per_set = ab["call"]
-        reps = args.replicas or max(1, min(8, -(-1024 * 2 ** 20 // per_set)))
+        reps = replicas or max(1, min(8, -(-1024 * 2 ** 20 // ab["call"])))
         sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(reps - 1)]
         n_sets = reps
     desc = R.describe(sets[0]["q"], sets[0]["k_base"], sets[0]["lk"], sets[0]["bk"],
                       block_table=sets[0]["block_table"], k_priv=sets[0]["k_priv"], prefix_len=case.prefix_len,
                       shared_lr=case.shared_lr)
+    kernel = R.kernel_of(desc, op)
     wsb = R.workspace_bytes(desc, op)
     ws = torch.empty(max(wsb, 256), device=dev, dtype=torch.uint8)
     outs = [torch.empty(tuple(s["q"].shape), device=dev, dtype=torch.float32) for s in sets]
@@ -208,7 +264,6 @@ def main():
         t = dict(s, out=o, lse=None)
         R._check_tensors(desc, t)
         argv.append(R.Args(*[None if t[n] is None else t[n].data_ptr() for n, _ in R.Args._fields_]))
-    stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     lib = R.lib()
     wsp, wss = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel())
@@ -217,23 +272,24 @@ def main():
     fn = lib.rattn_attention_stages
 
     def launch(i, stages):
-        st = fn(dref, op, arefs[i], wsp, wss, sp, stages)
+        st = fn(dref, op, arefs[i % n_sets], wsp, wss, sp, stages)
         if st:
             raise R.RattnError(st, "rattn_attention_stages")
 
     # One step = all layers' calls (one call when layers == 1), each one
-    # rattn_attention_stages call of both launches (split, then merge).  The
-    # timed steps carry no instrumentation; HIP events on the launch stream
-    # bracket the K steps (GPU time per step).
-    hip = Hip()
-    K, W = args.steps, args.warmup
-
+    # rattn_attention_stages call of all its launches.
     def step(k):
         for l in range(layers):
-            launch((k * layers + l) % n_sets, R.STAGE_ALL)
+            launch(k * layers + l, R.STAGE_ALL)
 
     for k in range(W):
         step(k)
+    torch.cuda.synchronize()
+    # warm until the per-call time is stable (clocks settle over the first
+    # launches), then the timed steps: K steps between two synchronisations
+    # (wall clock), with HIP events on the launch stream around them
+    per_batch = max(8, layers)
+    warm = stable_ms(hip, lambda i: launch(i, R.STAGE_ALL), per_batch, sp)
     torch.cuda.synchronize()
     ev_a, ev_b = hip.event(), hip.event()
     t0 = time.perf_counter()
@@ -246,44 +302,40 @@ def main():
     step_ms_ev = hip.elapsed_ms(ev_a, ev_b) / K
 
     # The kernel behind the roofline (the split kernel; for prefill the one
-    # kernel of the call): the same inputs, launched back to back K * layers
-    # times between two HIP events on the launch stream, so that the average
-    # is the kernel's own duration (a per-launch event pair would add the
-    # event and submission latency of every launch).
+    # kernel of the call), launched back to back K * layers times between two
+    # HIP events on the launch stream after its own stabilising warm-up, so that
+    # the average is the kernel's own steady duration.
     n_k = K * layers
-    for i in range(min(n_k, 4)):
-        launch(i % n_sets, R.STAGE_SPLIT)
+    stable_ms(hip, lambda i: launch(i, R.STAGE_SPLIT), per_batch, sp)
+    kern_avg = hip.time_ms(lambda i: launch(i, R.STAGE_SPLIT), n_k, sp)
     torch.cuda.synchronize()
-    ev_c, ev_d = hip.event(), hip.event()
-    hip.record(ev_c, sp)
-    for i in range(n_k):
-        launch(i % n_sets, R.STAGE_SPLIT)
-    hip.record(ev_d, sp)
-    torch.cuda.synchronize()
-    kern_avg = hip.elapsed_ms(ev_c, ev_d) / n_k
 
     ms_step = wall * 1e3 / K
     pairs = pairs_per_call(case) * layers
     value = pairs / (ms_step / 1e3) / 1e9
-    if case.mode == "prefill" and case.dtype == "bf16":
-        # MFMA-bound: the prefill kernel does the whole call (no merge launch)
+    call_ms = step_ms_ev / layers  # one call, from the timed steps' events
+    if kernel[0] == "prefill":
         fl = algorithmic_flops(case)
         achieved = fl / (kern_avg / 1e3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                "traffic": traffic_from_counters(f"prefill_cfg{args.config}"),
-                "kernel": "prefill_kernel", "flops_per_launch": fl,
-                "avg_launch_us": round(kern_avg * 1e3, 2),
-                "launches_timed": n_k}
+                "traffic": traffic_from_counters(f"prefill_cfg{config}"),
+                "kernel": "prefill_kernel", "flops_per_launch": fl, "avg_launch_us": round(kern_avg * 1e3, 2),
+                "launches_timed": n_k,
+                "frac_timed_steps": round(fl / (call_ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
     else:
         achieved = ab["split"] / (kern_avg / 1e3) / 1e9
-        traffic = traffic_from_counters(f"decode_cfg{args.config}")
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_counters(f"decode_cfg{config}"),
                 "kernel": "decode_split_kernel", "bytes_per_launch": ab["split"],
-                "avg_launch_us": round(kern_avg * 1e3, 2),
-                "launches_timed": n_k}
-    res = {
+                "avg_launch_us": round(kern_avg * 1e3, 2), "launches_timed": n_k,
+                # the whole call (split + merge) over the timed steps
+                "frac_timed_steps": round(ab["call"] / (call_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        if probe:
+            roof["achievable"] = probe["achievable"]
+            roof["frac_of_achievable"] = round(achieved / probe["achievable"], 4)
+    roof["instantiation"] = list(kernel)
+    rec = {
         "metric": METRIC, "value": round(value, 4), "unit": "Gtok/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": case.dtype, "data": "synthetic (seeded N(0,1) caches and queries, N(0,0.05^2) up-projections)",
@@ -293,10 +345,58 @@ def main():
                    "shared_lr": case.shared_lr, "layers": layers, "mode": case.mode, "input_sets_rotated": n_sets},
         "hbm_gbps_call": round(ab["call"] * layers / (ms_step / 1e3) / 1e9, 1),
         "gpu_ms_per_step_events": round(step_ms_ev, 5),
+        "warmup_call_ms": [round(x, 5) for x in warm],
         "roofline": roof,
     }
+    del sets, outs, ws
+    torch.cuda.empty_cache()
+    say(f"[bench] {case.name}: {rec['value']} Gtok/s, kernel {roof['avg_launch_us']} us, frac {roof['frac']}")
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=4, help="headline workload (synth.CONFIGS index)")
+    ap.add_argument("--sub", default="1,2,3", help="workloads measured as sub-records ('' for none)")
+    ap.add_argument("--replicas", type=int, default=0, help="input sets rotated (0: auto)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--seed", type=int, default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU "
+              "path: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import shared_base_residual_amd as R
+
+    R.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    hip = Hip()
+    probe = None if args.no_probe else hbm_probe(hip, ctypes.c_void_p(stream.cuda_stream), dev)
+    if probe:
+        say(f"[bench] HBM probe: {probe['achievable']} GB/s ({probe['reader']})")
+    res = measure(args.config, args.steps, args.warmup, dev, hip, stream, args.replicas, args.seed, probe)
+    subs = [int(s) for s in args.sub.split(",") if s.strip() and int(s) != args.config]
+    if subs:
+        res["sub_records"] = [measure(c, args.steps, args.warmup, dev, hip, stream, args.replicas, None, probe)
+                              for c in subs]
+    if probe:
+        res["hbm_probe"] = probe
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(case, seed)
+        import synth
+
+        say("[bench] cpu baseline")
+        res["cpu_baseline"] = cpu_baseline(synth.CONFIGS[args.config],
+                                           args.config if args.seed is None else args.seed)
     print(json.dumps(res), flush=True)
 
 

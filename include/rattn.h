@@ -134,11 +134,20 @@ int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace
  * Chunked prefill: agent a appends a chunk of C = priv_len = q_len new tokens
  * whose keys/values are k_priv/v_priv[a]; chunk query t attends the L prefix
  * tokens and chunk tokens 0..t (causal).  Same residual algebra as
- * rattn_decode.  bf16 calls run one kernel that streams the whole context per
- * block of 256 query rows and writes out/lse directly (no workspace:
+ * rattn_decode (ForkKV Guide, "Mathematical Formulation of ResidualAttention";
+ * LRAgent, "Flash-LoRA-Attention").  With shared_lr = 1 this is LRAgent's
+ * BaseLRShared scheme ("Schemi di Condivisione"): the down-projection A is
+ * shared, so one low-rank cache Lk/Lv ([1, L, r]) serves every agent's chunk
+ * and only Bk/Bv differ per agent; with shared_lr = 0 it is BaseShared (one
+ * low-rank cache per agent).
+ * bf16 calls run one kernel that streams the whole context per block of 256
+ * query rows (128 for d = 128 with r >= 64, and for d = 64 with r = 128) and
+ * writes out/lse directly (no workspace:
  * rattn_workspace_bytes(desc, RATTN_OP_PREFILL) is 0, and `workspace` may be
  * NULL); fp32 calls, and paged prefixes of more than 2048 pages, run the split
  * and merge launches of rattn_decode with the causal mask (workspace as there).
+ * fp32 with d = 128 and r = 128 returns RATTN_E_UNSUPPORTED (here and in
+ * rattn_decode).
  */
 int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *workspace,
                         size_t workspace_bytes, void *stream);
@@ -146,8 +155,17 @@ int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *wo
 /*
  * Copies the logical base cache of a paged pool into dst [H_kv, L, d] (same
  * dtype): dst[k][j] = pool[block_table[j / page_size]][k][j % page_size].
+ * The block table is the list of bCache block pointers that the base-tier
+ * lookup of the ForkKV Guide's DualRadixTree returns for a matched prefix
+ * ("Two-Tier Lookup Mechanics", Tier 1), stored as physical page indices; the
+ * pages are shared and immutable ("The Copy-on-Write Paradigm", "The
+ * Disaggregated Memory Layout"), so several tables may name one page.
  * Byte-exact.  Uses desc->n_kv_heads, head_dim, prefix_len, page_size,
- * n_phys_pages, dtype.
+ * n_phys_pages, dtype.  pool, block_table and dst are device pointers (pool
+ * and dst 16-byte aligned, the table 4-byte aligned); dst must not overlap
+ * the pool.  Entries outside [0, n_phys_pages) are undefined behaviour.
+ * prefix_len = 0 returns RATTN_OK and launches nothing; page_size must be a
+ * positive multiple of 16 (else RATTN_E_UNSUPPORTED).
  */
 int rattn_gather_base(const rattn_desc *desc, const void *pool, const int32_t *block_table, void *dst,
                       void *stream);
@@ -170,7 +188,10 @@ int rattn_gather_base(const rattn_desc *desc, const void *pool, const int32_t *b
 int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,
                            size_t workspace_bytes, void *stream, unsigned stages);
 
-/* Work decomposition chosen for a decode call (host-only introspection; no HIP call). */
+/* Work decomposition chosen for a call (host-only introspection; no HIP call).
+ * The kernel that runs is determined by (dtype, head_dim, path, resid_cols,
+ * masked, waves): path 0 is the split kernel (waves > 8 selects its twelve-wave
+ * form) followed by the merge; path 1 is the prefill kernel. */
 typedef struct rattn_plan_info {
     int32_t n_prefix_splits;  /* context splits of the prefix */
     int64_t prefix_split_len; /* tokens per prefix split */
@@ -179,14 +200,20 @@ typedef struct rattn_plan_info {
     int32_t row_blocks;       /* 16-row MFMA blocks per KV head over the prefix */
     int32_t agents_per_block; /* agents whose query rows share one block */
     int32_t resid_cols;       /* residual columns per block, padded (0 if r == 0) */
-    int32_t work_items;       /* workgroups of the split kernel */
+    int32_t work_items;       /* workgroups of the split (or prefill) kernel */
     int32_t heads_per_item;   /* KV heads one prefix workgroup serves (sharing its low-rank tile) */
-    int32_t waves;            /* waves per split workgroup (compute + load) */
+    int32_t waves;            /* waves per workgroup (compute + load) */
     int32_t masked;           /* 1: per-agent caches, several agents per block, residual columns = rank */
     int32_t blocks_per_group; /* row blocks one prefix workgroup serves */
+    int32_t path;             /* 0: split kernel + merge; 1: prefill kernel (no workspace) */
+    int32_t rows_per_item;    /* path 1: query rows of one (KV head, agent) per workgroup; else 0 */
 } rattn_plan_info;
 
+/* The plan of rattn_decode (rattn_decode_plan) or of rattn_prefill_chunk
+ * (rattn_prefill_plan) for this descriptor.  Same validation as the calls;
+ * a rattn_status is returned and *info written on success. */
 int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info);
+int rattn_prefill_plan(const rattn_desc *desc, rattn_plan_info *info);
 
 const char *rattn_status_str(int status);
 int rattn_version(void);

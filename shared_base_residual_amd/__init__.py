@@ -29,7 +29,7 @@ RATTN_OP_DECODE, RATTN_OP_PREFILL = 0, 1
 STATUS = {0: "RATTN_OK", -1: "RATTN_E_NULL", -2: "RATTN_E_SHAPE", -3: "RATTN_E_UNSUPPORTED",
           -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP"}
 EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
-           "rattn_decode_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error",
+           "rattn_decode_plan", "rattn_prefill_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error",
            "rattn_attention_stages")
 STAGE_SPLIT, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
 
@@ -65,7 +65,7 @@ class PlanInfo(ctypes.Structure):
                 ("row_blocks", ctypes.c_int32), ("agents_per_block", ctypes.c_int32),
                 ("resid_cols", ctypes.c_int32), ("work_items", ctypes.c_int32),
                 ("heads_per_item", ctypes.c_int32), ("waves", ctypes.c_int32), ("masked", ctypes.c_int32),
-                ("blocks_per_group", ctypes.c_int32)]
+                ("blocks_per_group", ctypes.c_int32), ("path", ctypes.c_int32), ("rows_per_item", ctypes.c_int32)]
 
 
 _lib = None
@@ -85,12 +85,14 @@ def lib():
         L.rattn_prefill_chunk.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P, ctypes.c_size_t, P]
         L.rattn_gather_base.argtypes = [ctypes.POINTER(Desc), P, P, P, P]
         L.rattn_decode_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PlanInfo)]
+        L.rattn_prefill_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PlanInfo)]
         L.rattn_attention_stages.argtypes = [ctypes.POINTER(Desc), I, ctypes.POINTER(Args), P, ctypes.c_size_t, P,
                                              ctypes.c_uint]
         L.rattn_status_str.argtypes = [I]
         L.rattn_status_str.restype = ctypes.c_char_p
         for f in ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
-                  "rattn_decode_plan", "rattn_version", "rattn_last_hip_error", "rattn_attention_stages"):
+                  "rattn_decode_plan", "rattn_prefill_plan", "rattn_version", "rattn_last_hip_error",
+                  "rattn_attention_stages"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -116,6 +118,28 @@ def decode_plan(desc: Desc) -> dict:
     if st:
         raise RattnError(st, "rattn_decode_plan")
     return {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+
+
+def prefill_plan(desc: Desc) -> dict:
+    info = PlanInfo()
+    st = lib().rattn_prefill_plan(ctypes.byref(desc), ctypes.byref(info))
+    if st:
+        raise RattnError(st, "rattn_prefill_plan")
+    return {f: getattr(info, f) for f, _ in PlanInfo._fields_}
+
+
+def plan(desc: Desc, op: int = RATTN_OP_DECODE) -> dict:
+    return prefill_plan(desc) if op == RATTN_OP_PREFILL else decode_plan(desc)
+
+
+def kernel_of(desc: Desc, op: int = RATTN_OP_DECODE) -> tuple:
+    """The kernel instantiation a call runs: ("split", dtype, d, residual columns,
+    masked, twelve-wave form) or ("prefill", dtype, d, residual columns)."""
+    p = plan(desc, op)
+    dt = "bf16" if desc.dtype == RATTN_BF16 else "f32"
+    if p["path"] == 1:
+        return ("prefill", dt, desc.head_dim, p["resid_cols"])
+    return ("split", dt, desc.head_dim, p["resid_cols"], bool(p["masked"]), p["waves"] > 8)
 
 
 def _ptr(t):
@@ -202,15 +226,27 @@ def _check_tensors(desc: Desc, tensors: dict):
 _workspaces = {}
 
 
-def workspace_for(nbytes: int, device):
-    """A workspace of at least ``nbytes``, cached per device and stream (its
-    contents do not matter between calls)."""
+def _ws_key(device, stream) -> tuple:
+    """Cache key of a workspace: the device and the HIP stream the call is
+    launched on (two streams never share one, since calls that share a
+    workspace must not overlap)."""
+    return (str(device), int(stream.cuda_stream))
+
+
+def workspace_for(nbytes: int, device, stream=None):
+    """A workspace of at least ``nbytes`` for calls launched on ``stream`` (the
+    current stream when None), cached per (device, stream); its contents do not
+    matter between calls.  It is allocated while that stream is current, so the
+    caching allocator ties it to the stream the kernels run on: a buffer
+    replaced by a larger one is reused only by work ordered after them."""
     import torch
 
-    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = _ws_key(device, s)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), device=device, dtype=torch.uint8)
+        with torch.cuda.stream(s):
+            ws = torch.empty(max(nbytes, 256), device=device, dtype=torch.uint8)
         _workspaces[key] = ws
     return ws
 
@@ -229,7 +265,7 @@ def _run(fn_name, op, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_
     _check_tensors(desc, tensors)
     nbytes = workspace_bytes(desc, op)
     if workspace is None:
-        workspace = workspace_for(nbytes, q.device)
+        workspace = workspace_for(nbytes, q.device, stream)
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise RattnError(-4, f"{fn_name}: workspace has {workspace.numel() * workspace.element_size()} bytes, "
                              f"needs {nbytes}")

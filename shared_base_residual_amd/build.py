@@ -20,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librattn.so")
 SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "gather.hip"]
+# the benchmark's HBM read-bandwidth probe: a library of its own, not librattn
+PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
+PROBE_SOURCES = ["hbm_probe.hip"]
 ARCH = "gfx950"
 
 
@@ -29,7 +32,7 @@ def source_hash() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)) + ["../../include/rattn.h"]:
+    for name in sorted(set(os.listdir(CSRC)) - set(PROBE_SOURCES)) + ["../../include/rattn.h"]:
         path = os.path.normpath(os.path.join(CSRC, name))
         if os.path.isfile(path):
             with open(path, "rb") as f:
@@ -70,13 +73,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         return obj
 
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    n = len(SOURCES)
+    for lib, lib_objs in ((LIB, objs[:n]), (PROBE_LIB, objs[n:])):
+        tmp = lib + ".tmp"
+        cmd = [cc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *lib_objs, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
     return LIB
 
 

@@ -133,6 +133,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         if (resid) cols = d->shared_lr || p.masked ? r : (rpa <= 16 ? p.apb * r : r);
         pl->cpad = resid ? (pow2ceil(cols) < 32 ? 32 : pow2ceil(cols)) : 0;
         if (pl->cpad > rattn::kMaxResidColsHard) return RATTN_E_UNSUPPORTED;
+        if (!rattn::split_ok(d->dtype == RATTN_BF16, D, pl->cpad)) return RATTN_E_UNSUPPORTED;
 
         const int es = (int)esize(d->dtype);
         const int kv_row = D * es;  // bytes of one key (or value) row
@@ -324,10 +325,9 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
                 const int tiles_min = L > 0 ? H * nb_min : (p.pb < 4 ? p.pb : 4);
                 const int need = H > 1 ? 3 : 2;
                 // Eight compute waves run the twelve-wave kernel (168 registers a
-                // lane), whose wider residual variants spill to scratch: only up to
-                // 32 residual columns (64 at d = 64) for bf16, none for fp32 at d = 128.
-                const int cpad8 = d->dtype == RATTN_BF16 ? (D == 64 ? 64 : 32) : (D == 64 ? 64 : 0);
-                const bool ok = (tiles_min >= 2 && pl->cpad <= cpad8 && plan_lds(8, need)) || plan_lds(4, need);
+                // lane), whose wider residual variants would spill to scratch.
+                const bool wide = rattn::split_wide_ok(d->dtype == RATTN_BF16, D, pl->cpad);
+                const bool ok = (tiles_min >= 2 && wide && plan_lds(8, need)) || plan_lds(4, need);
                 if (!ok) continue;
                 // Preference: a prefix tile of 32 or more tokens (the per-tile
                 // synchronisation is a large share of a tile's time), then the
@@ -418,12 +418,12 @@ int make_prefill_plan(const rattn_desc *d, PrefillPlan *pl) {
     const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
     p.c = scale * 1.44269504088896340736f;
     p.rpa = d->q_len * g;
-    p.n_qb = (int)cdiv(p.rpa, rattn::kPrefillRows);
+    pl->cpad = resid ? (pow2ceil(r) < 32 ? 32 : pow2ceil(r)) : 0;
+    p.n_qb = (int)cdiv(p.rpa, rattn::prefill_rows(D, pl->cpad));
     const int64_t items = (int64_t)HK * N * p.n_qb;
     if (items > (1ll << 30)) return RATTN_E_UNSUPPORTED;
     p.n_items = (int)items;
     p.per_xcd = (int)cdiv(items, 8);
-    pl->cpad = resid ? (pow2ceil(r) < 32 ? 32 : pow2ceil(r)) : 0;
 
     // LDS rings: prefix tiles (keys, values and the low-rank rows), chunk tiles
     // (keys and values); T keys per stage, two to eight stages, the split's
@@ -532,6 +532,24 @@ int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_
                                            static_cast<hipStream_t>(stream)));
 }
 
+void fill_plan_info(const Plan &pl, rattn_plan_info *info) {
+    *info = rattn_plan_info{};
+    info->n_prefix_splits = pl.dp.n_ps;
+    info->prefix_split_len = pl.dp.tok_ps;
+    info->n_priv_splits = pl.dp.n_pv;
+    info->priv_split_len = pl.dp.tok_pv;
+    info->row_blocks = pl.dp.n_blocks;
+    info->agents_per_block = pl.dp.apb;
+    info->resid_cols = pl.cpad;
+    info->work_items = pl.dp.n_items;
+    info->heads_per_item = pl.dp.H;
+    info->waves = pl.dp.nw + pl.dp.np;
+    info->masked = pl.dp.masked;
+    info->blocks_per_group = pl.dp.bpg;
+    info->path = 0;
+    info->rows_per_item = 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -578,18 +596,36 @@ int rattn_decode_plan(const rattn_desc *desc, rattn_plan_info *info) {
     Plan pl;
     st = make_plan(desc, RATTN_OP_DECODE, &pl);
     if (st) return st;
-    info->n_prefix_splits = pl.dp.n_ps;
-    info->prefix_split_len = pl.dp.tok_ps;
-    info->n_priv_splits = pl.dp.n_pv;
-    info->priv_split_len = pl.dp.tok_pv;
-    info->row_blocks = pl.dp.n_blocks;
-    info->agents_per_block = pl.dp.apb;
-    info->resid_cols = pl.cpad;
-    info->work_items = pl.dp.n_items;
-    info->heads_per_item = pl.dp.H;
-    info->waves = pl.dp.nw + pl.dp.np;
-    info->masked = pl.dp.masked;
-    info->blocks_per_group = pl.dp.bpg;
+    fill_plan_info(pl, info);
+    return RATTN_OK;
+}
+
+int rattn_prefill_plan(const rattn_desc *desc, rattn_plan_info *info) {
+    if (!info) return RATTN_E_NULL;
+    int st = check_desc(desc, RATTN_OP_PREFILL);
+    if (st) return st;
+    if (prefill_direct(desc)) {
+        PrefillPlan pp;
+        st = make_prefill_plan(desc, &pp);
+        if (st) return st;
+        *info = rattn_plan_info{};
+        info->n_prefix_splits = desc->prefix_len > 0 ? 1 : 0;
+        info->prefix_split_len = desc->prefix_len;
+        info->row_blocks = (int)((pp.pp.rpa + 15) / 16);
+        info->agents_per_block = 1;
+        info->resid_cols = pp.cpad;
+        info->work_items = pp.pp.n_items;
+        info->heads_per_item = 1;
+        info->waves = rattn::kPrefillWaves;
+        info->blocks_per_group = rattn::prefill_blocks_per_wave(desc->head_dim, pp.cpad) * rattn::kPrefillWaves;
+        info->path = 1;
+        info->rows_per_item = rattn::prefill_rows(desc->head_dim, pp.cpad);
+        return RATTN_OK;
+    }
+    Plan pl;
+    st = make_plan(desc, RATTN_OP_PREFILL, &pl);
+    if (st) return st;
+    fill_plan_info(pl, info);
     return RATTN_OK;
 }
 

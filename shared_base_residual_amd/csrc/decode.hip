@@ -1092,7 +1092,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
         if (wres)
 #pragma unroll
             for (int i = 0; i < NWV; ++i) o += s_wbv[i * D + tid];
-        p.out[R * D + tid] = o / Lsum;
+        p.out[(int64_t)R * D + tid] = o / Lsum;  // R * D reaches 2^35 within the row limit
         if (tid == 0 && p.lse) p.lse[R] = (M + __builtin_log2f(Lsum)) * 0.69314718055994530942f;
     }
 }
@@ -1102,15 +1102,29 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 template <typename T, int D, int CP, bool M, int W>
 struct SplitSlot {};
 
-template <typename T, int D, int CP, bool M>
-static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t st) {
-    const bool w8 = dp.nw + dp.np <= 8;
-    auto *fn = w8 ? decode_split_kernel<T, D, CP, M, 8> : decode_split_kernel<T, D, CP, M, 12>;
-    const hipError_t e = w8 ? ensure_lds<SplitSlot<T, D, CP, M, 8>>(reinterpret_cast<const void *>(fn), (int)lds)
-                            : ensure_lds<SplitSlot<T, D, CP, M, 12>>(reinterpret_cast<const void *>(fn), (int)lds);
+template <typename T, int D, int CP, bool M, int W>
+static hipError_t launch_split_w(const DecodeParams &dp, size_t lds, hipStream_t st) {
+    auto *fn = decode_split_kernel<T, D, CP, M, W>;
+    const hipError_t e = ensure_lds<SplitSlot<T, D, CP, M, W>>(reinterpret_cast<const void *>(fn), (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3(8 * dp.per_xcd), dim3(64 * (dp.nw + dp.np)), lds, st, dp);
     return hipGetLastError();
+}
+
+// Only the instantiations that fit in registers (split_ok, split_wide_ok) exist;
+// the planner never asks for another.
+template <typename T, int D, int CP, bool M>
+static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t st) {
+    constexpr bool kBf = sizeof(T) == 2;
+    if constexpr (!split_ok(kBf, D, CP)) {
+        return hipErrorInvalidValue;
+    } else {
+        if (dp.nw + dp.np <= 8) return launch_split_w<T, D, CP, M, 8>(dp, lds, st);
+        if constexpr (split_wide_ok(kBf, D, CP))
+            return launch_split_w<T, D, CP, M, 12>(dp, lds, st);
+        else
+            return hipErrorInvalidValue;
+    }
 }
 
 template <typename T>

@@ -178,27 +178,26 @@ __device__ inline uint32_t lds_addr(const void *p) {
 }
 
 // One direct load: 16 bytes from gsrc (per lane) to LDS byte lds_base + 16*lane.
-// lds_base must be wave-uniform (it goes to M0).  Written as inline assembly so
-// that the compiler does not treat every later LDS read as dependent on it (it
-// would wait for all outstanding loads before each read); completion is awaited
-// explicitly with wait_vmcnt before the stage is read.  One wait state between
-// the M0 write and the load.
+// lds_base must be wave-uniform: it is an M0 input operand ("{m0}"), so the
+// compiler itself writes M0 and knows it is live here.  Written as inline
+// assembly so that the compiler does not treat every later LDS read as
+// dependent on it (it would wait for all outstanding loads before each read);
+// completion is awaited explicitly with wait_vmcnt before the stage is read.
+// One wait state (s_nop 0) between the M0 write and the load, which the
+// compiler cannot see inside the statement.
 __device__ inline void dma16(const void *gsrc, uint32_t lds_base) {
     lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gsrc), "s"(lds_base)
-                 : "memory", "m0");
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(gsrc), "{m0}"(lds_base) : "memory");
 }
 
 // The same with a wave-uniform 64-bit base (SGPR pair) and a per-lane 32-bit
 // byte offset (the instruction's saddr form).
 __device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_base) {
     lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(voff), "s"(sbase), "s"(lds_base)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(sbase), "{m0}"(lds_base)
+                 : "memory");
 }
 
 // Streaming variants (nontemporal bit): for data read exactly once, such as
@@ -208,10 +207,10 @@ __device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_bas
 // low-rank rows) keeps the default policy.
 __device__ inline void dma16s_nt(const void *sbase, uint32_t voff, uint32_t lds_base) {
     lds_base = __builtin_amdgcn_readfirstlane(lds_base);
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :
-                 : "v"(voff), "s"(sbase), "s"(lds_base)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(sbase), "{m0}"(lds_base)
+                 : "memory");
 }
 
 // A pointer that is the same in every lane, moved to scalar registers.

@@ -45,6 +45,16 @@ RATTN_HD int fdiv(int n, const FastDiv &f) { return (int)(((uint64_t)(uint32_t)n
 constexpr int kMaxResidCols = 64;
 constexpr int kMaxResidColsF32 = 32;
 constexpr int kMaxResidColsHard = 128;
+// Split-kernel instantiations whose registers fit without spilling to scratch:
+// eight compute waves run the twelve-wave kernel (168 registers a lane), which
+// holds up to 32 residual columns (64 at d = 64) for bf16 inputs, and none at
+// d = 128 (64 at d = 64) for fp32; the eight-wave kernel (256 registers) holds
+// every width except fp32 at d = 128 with 128 columns.  The planner keeps to
+// these and the launcher instantiates nothing else.
+RATTN_HD constexpr bool split_wide_ok(bool bf16, int D, int cpad) {
+    return bf16 ? cpad <= (D == 64 ? 64 : 32) : cpad <= (D == 64 ? 64 : 0);
+}
+RATTN_HD constexpr bool split_ok(bool bf16, int D, int cpad) { return bf16 || D == 64 || cpad <= 64; }
 // Context tokens per split are a multiple of this (4 waves x 32-token chunks),
 // which also keeps every 16-token MFMA tile inside one 16-aligned page.
 constexpr int kSplitQuantum = 128;
@@ -165,10 +175,16 @@ constexpr int kMaxPagesPerSplit = 2048;
 
 namespace rattn {
 
-// Chunked prefill: one workgroup per (KV head, agent, block of 256 query rows
-// of that agent), no split of the context.  Waves own 64 rows each (four
-// 16-row MFMA blocks).
-constexpr int kPrefillRows = 256;
+// Chunked prefill: one workgroup of eight waves per (KV head, agent, block of
+// query rows of that agent), no split of the context.  A wave owns one or two
+// 16-row MFMA blocks: two where the accumulators of both fit in registers, one
+// for the wide residual widths (d = 128 with 64 or more residual columns, d = 64
+// with 128), whose two-block form would spill to scratch.
+constexpr int kPrefillWaves = 8;
+RATTN_HD constexpr int prefill_blocks_per_wave(int D, int cpad) {
+    return (D == 128 ? cpad >= 64 : cpad >= 128) ? 1 : 2;
+}
+RATTN_HD constexpr int prefill_rows(int D, int cpad) { return 16 * kPrefillWaves * prefill_blocks_per_wave(D, cpad); }
 
 struct PrefillParams {
     const void *q, *kb, *vb;

@@ -16,9 +16,11 @@
 // ring as the decode kernel (direct global->LDS loads, several tiles in
 // flight).  Each of the eight waves (two per SIMD, so one wave's MFMAs overlap
 // the other's softmax) owns 32 rows (two 16-row MFMA blocks); every tile
-// fetched into LDS feeds all 256 rows.  Workgroups of one KV head run on one
-// XCD (workgroup i runs on XCD i % 8), where they share its tiles through that
-// XCD's L2.
+// fetched into LDS feeds all 256 rows.  With wide residuals (d = 128 and 64 or
+// more residual columns, d = 64 and 128) a wave owns one block and a workgroup
+// 128 rows, so that the accumulators stay in registers.  Workgroups of one KV
+// head run on one XCD (workgroup i runs on XCD i % 8), where they share its
+// tiles through that XCD's L2.
 //
 // Per 32 keys and wave: S^T = K Q^T (keys as the A operand, query rows as B),
 // + Lk U^T (U = q Bk_a^T as bf16 hi + lo halves), online softmax in the log2
@@ -44,8 +46,9 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     constexpr int CPL = CPAD / 16;
     constexpr int CPLx = CPL > 0 ? CPL : 1;
     constexpr int ES = (int)sizeof(T);
-    constexpr int NCB = 2;  // 16-row blocks per wave
-    constexpr int NW = kPrefillRows / (16 * NCB);  // waves per workgroup
+    constexpr int NCB = prefill_blocks_per_wave(D, CPAD);  // 16-row blocks per wave
+    constexpr int NW = kPrefillWaves;
+    constexpr int ROWS = prefill_rows(D, CPAD);  // query rows per workgroup
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     const int rest = li - k * per_head;
     const int a = rest / p.n_qb;
     const int qb = rest - a * p.n_qb;
-    const int R0 = qb * kPrefillRows + wave * (NCB * 16);  // this wave's first row within (a, k)
+    const int R0 = qb * ROWS + wave * (NCB * 16);  // this wave's first row within (a, k)
 
     const bool resid = CPAD > 0 && p.r > 0 && p.L > 0;
     const float cl2 = p.c;
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
             qB[cb][s] = vm[cb] ? O::load8(qp + qrow[cb] * D + 32 * s + 8 * j4) : O::zero();
     }
     // last chunk token any row of the workgroup may see
-    int rmax = qb * kPrefillRows + kPrefillRows - 1;
+    int rmax = qb * ROWS + ROWS - 1;
     rmax = rmax < p.rpa - 1 ? rmax : p.rpa - 1;
     const int t_hi = rmax / p.g + 1;  // chunk keys [0, t_hi)
 
@@ -436,32 +439,26 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
     // columns kappa = 16*(2s + i/4) + 4*j4 + i%4 (i < 8), the columns whose W
     // this lane holds (W^T tiles 2s and 2s + 1).
     constexpr int NBS = CPL / 2 > 0 ? CPL / 2 : 1;  // contraction steps of 8 columns per lane group
-    frag bvf[NBS][VPL];
+    // one contraction step's Bv operands at a time (all of them at once would
+    // hold NBS * d / 16 fragments in registers)
     if constexpr (CPAD > 0) {
         if (resid) {
             const T *bv = static_cast<const T *>(p.bv) + (int64_t)a * p.r * p.HK * D + (int64_t)k * D + n16;
             const int64_t ldb = (int64_t)p.HK * D;
 #pragma unroll
-            for (int s = 0; s < NBS; ++s)
+            for (int s = 0; s < NBS; ++s) {
+                frag bvf[VPL];
 #pragma unroll
                 for (int jj = 0; jj < VPL; ++jj)
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         int kap = 16 * (2 * s + (i >> 2)) + 4 * j4 + (i & 3);
                         kap = kap < p.r ? kap : 0;
-                        O::set_raw(bvf[s][jj], i, bv[kap * ldb + 16 * jj]);
+                        O::set_raw(bvf[jj], i, bv[kap * ldb + 16 * jj]);
                     }
-        }
-    }
-    const float LN2 = 0.69314718055994530942f;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-        const float lr = l[cb][0];  // the whole row's sum
-        if constexpr (CPAD > 0) {
-            if (resid) {
-                // B operand: this lane's W (row n16, columns 16*(2s + i/4) + 4*j4 + i%4), hi + lo
-#pragma unroll
-                for (int s = 0; s < NBS; ++s) {
+                for (int cb = 0; cb < NCB; ++cb) {
+                    // B operand: this lane's W (row n16, columns 16*(2s + i/4) + 4*j4 + i%4), hi + lo
                     frag wH, wL;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
@@ -475,12 +472,17 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                     }
 #pragma unroll
                     for (int jj = 0; jj < VPL; ++jj) {
-                        o[cb][jj] = O::mma(bvf[s][jj], wH, o[cb][jj]);
-                        o[cb][jj] = O::mma(bvf[s][jj], wL, o[cb][jj]);
+                        o[cb][jj] = O::mma(bvf[jj], wH, o[cb][jj]);
+                        o[cb][jj] = O::mma(bvf[jj], wL, o[cb][jj]);
                     }
                 }
             }
         }
+    }
+    const float LN2 = 0.69314718055994530942f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        const float lr = l[cb][0];  // the whole row's sum
         if (vm[cb]) {
             const float inv = 1.0f / lr;
             // tile jj, element i of this lane: d = 16*jj + 4*j4 + i
@@ -500,7 +502,7 @@ static hipError_t launch_prefill_one(const PrefillParams &pp, size_t lds, hipStr
     auto *fn = prefill_kernel<T, D, CP>;
     const hipError_t e = ensure_lds<PrefillSlot<T, D, CP>>(reinterpret_cast<const void *>(fn), (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(8 * pp.per_xcd), dim3(kPrefillRows / 32 * 64), lds, st, pp);
+    hipLaunchKernelGGL(fn, dim3(8 * pp.per_xcd), dim3(64 * kPrefillWaves), lds, st, pp);
     return hipGetLastError();
 }
 

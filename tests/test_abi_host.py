@@ -224,3 +224,23 @@ def test_stage_mask_validation():
         assert L.rattn_attention_stages(ctypes.byref(d), 0, ctypes.byref(a), FAKE, need, None, stages) == E_SHAPE
     assert L.rattn_attention_stages(ctypes.byref(d), 5, ctypes.byref(a), FAKE, need, None, 1) == E_SHAPE
     assert L.rattn_attention_stages(ctypes.byref(d), 0, ctypes.byref(a), FAKE, need - 1, None, 1) == E_WS
+
+
+def test_row_limit_and_output_index():
+    """The merge writes out[row * d + column] with a 64-bit index; the row
+    count a call may have is bounded at 2^28 (d = 128 gives 2^35 elements)."""
+    assert ws(cfg1_desc(n_agents=2 ** 21, n_q_heads=256, n_kv_heads=8, prefix_len=16))[0] == E_UNSUP
+    st, n = ws(cfg1_desc(n_agents=2 ** 15, n_q_heads=128, n_kv_heads=8, prefix_len=16, rank=0))
+    assert st == OK and n > 0  # 2^22 rows: planned, index well inside 64 bits
+
+
+def test_workspace_cache_key_is_the_launch_stream():
+    """Calls launched on different streams never share a cached workspace (the
+    key is the stream the call is launched on, not the current stream)."""
+    class S:
+        def __init__(self, h):
+            self.cuda_stream = h
+
+    assert R._ws_key("cuda:0", S(1)) != R._ws_key("cuda:0", S(2))
+    assert R._ws_key("cuda:0", S(1)) == R._ws_key("cuda:0", S(1))
+    assert R._ws_key("cuda:0", S(1)) != R._ws_key("cuda:1", S(1))

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 import synth
+from tests import kernel_paths as KP
 from tests import parity
 
 torch = pytest.importorskip("torch")
@@ -43,17 +44,34 @@ def run_gpu(case, x, lse=True):
     return out.cpu().numpy().astype(np.float64), (lse_t.cpu().numpy().astype(np.float64) if lse else None)
 
 
-def ref(case, x, **kw):
-    return oracle.attend(case, x, **kw)
+def ref(case, x, row_mask=None, what=""):
+    """The oracle's output; large workloads are computed a few agents at a time
+    (row masks), with a progress line after each group."""
+    rows = case.n_agents * case.q_len * case.n_q_heads
+    keys = case.prefix_len + case.priv_len
+    if row_mask is not None or rows * keys < 2 ** 28:
+        return oracle.attend(case, x, row_mask=row_mask)
+    out = np.full((case.n_agents, case.q_len, case.n_q_heads, case.head_dim), np.nan)
+    lse = np.full((case.n_agents, case.q_len, case.n_q_heads), np.nan)
+    step = max(1, case.n_agents // 4)
+    for a0 in range(0, case.n_agents, step):
+        m = np.zeros(lse.shape, bool)
+        m[a0:a0 + step] = True
+        o, l = oracle.attend(case, x, row_mask=m)
+        out[a0:a0 + step] = o[a0:a0 + step]
+        lse[a0:a0 + step] = l[a0:a0 + step]
+        say(f"[gpu] {what}: oracle rows of agents {a0}..{min(a0 + step, case.n_agents) - 1} done")
+    return out, lse
 
 
 def compare(case, x, *, with_b0=False, what="", row_mask=None):
     say(f"[gpu] {what}: {case}")
     got, got_lse = run_gpu(case, x)
-    exp, exp_lse = ref(case, x, row_mask=row_mask)
+    exp, exp_lse = ref(case, x, row_mask=row_mask, what=what)
     b0 = None
     if with_b0:
-        b0, _ = ref(case, dict(x, bk=np.zeros_like(x["bk"]), bv=np.zeros_like(x["bv"])), row_mask=row_mask)
+        b0, _ = ref(case, dict(x, bk=np.zeros_like(x["bk"]), bv=np.zeros_like(x["bv"])), row_mask=row_mask,
+                    what=what + " (B = 0)")
     s = parity.check(got, exp, case.dtype, b0, what)
     m = ~np.isnan(exp_lse)
     assert np.abs(got_lse[m] - exp_lse[m]).max() <= 2e-3 * max(1.0, np.abs(exp_lse[m]).max()), what
@@ -89,50 +107,64 @@ def test_paged_cow_decode(variant):
     assert np.all(np.isfinite(got)), "NaN-poisoned unused pages reached the output"
 
 
-def _sample_rows(case, n, seed):
-    rng = np.random.default_rng(seed)
-    m = np.zeros((case.n_agents, case.q_len, case.n_q_heads), bool)
-    idx = rng.choice(m.size, size=min(n, m.size), replace=False)
-    m.reshape(-1)[idx] = True
-    # always include the first and last chunk positions of some agent
-    m[0, 0, 0] = m[-1, -1, -1] = True
-    return m
-
-
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("variant", ["base", "stress"])
-def test_shared_lr_chunked_prefill_sampled(variant):
+def test_shared_lr_chunked_prefill_all_rows(variant):
+    """The full BaseLRShared prefill (32 agents x 256-token chunks, L = 16384):
+    every one of the 262,144 query rows against the oracle."""
     c = synth.CONFIGS[3]
     kw = synth.STRESS if variant == "stress" else {}
     seed = 3 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0)
     x = synth.make_inputs(c, seed, **kw)
-    mask = _sample_rows(c, 48, 0)
-    compare(c, x, with_b0=(variant == "base"), row_mask=mask, what=f"BaseLRShared prefill {variant} (sampled rows)")
+    compare(c, x, with_b0=(variant == "base"), what=f"BaseLRShared prefill {variant} (all rows)")
 
 
-def test_full_depth_decode_sampled_layers():
-    """All 80 layers run back to back on one stream (as timed); sampled layers and
-    rows are checked against the oracle."""
+FULL_DEPTH_CHECKED = (0, 11, 23, 35, 47, 59, 71, 79)
+
+
+@pytest.mark.timeout(1200)
+def test_full_depth_decode_all_rows_of_eight_layers():
+    """All 80 layers run back to back on one stream, as timed.  Every row of
+    eight layers (first and last among them) is checked against the oracle,
+    per layer and aggregated over the eight layers' elements, lse included."""
     R = rattn()
     c = synth.CONFIGS[4]
     say(f"[gpu] 70B full-depth decode: generating {c.layers} layers on the device")
     layers = [synth.make_inputs_torch(c, 4, l, DEV) for l in range(c.layers)]
     outs = [torch.empty(layers[0]["q"].shape, device=DEV, dtype=torch.float32) for _ in range(c.layers)]
+    lses = [torch.empty(layers[0]["q"].shape[:3], device=DEV, dtype=torch.float32) for _ in range(c.layers)]
     desc = R.describe(layers[0]["q"], layers[0]["k_base"], layers[0]["lk"], layers[0]["bk"])
     ws = torch.zeros(R.workspace_bytes(desc), device=DEV, dtype=torch.uint8)  # zero-filled once
     for l in range(c.layers):
-        R.attend(layers[l], out=outs[l], workspace=ws)
+        R.attend(layers[l], out=outs[l], lse=lses[l], workspace=ws)
     torch.cuda.synchronize()
     say("[gpu] 70B full-depth decode: ran all layers")
-    errs = []
-    for l in (0, 41, 79):
+    gots, exps, b0s = [], [], []
+    for l in FULL_DEPTH_CHECKED:
         x = {k: synth.torch_to_numpy(v) for k, v in layers[l].items()}
-        mask = _sample_rows(c, 24, l)
-        exp, _ = oracle.attend(c, x, row_mask=mask)
-        b0, _ = oracle.attend(c, dict(x, bk=np.zeros_like(x["bk"]), bv=np.zeros_like(x["bv"])), row_mask=mask)
+        exp, exp_lse = oracle.attend(c, x)
+        b0, _ = oracle.attend(c, dict(x, bk=np.zeros_like(x["bk"]), bv=np.zeros_like(x["bv"])))
         got = outs[l].cpu().numpy().astype(np.float64)
-        errs.append(parity.check(got, exp, "bf16", b0, f"layer {l}"))
-        say(f"[gpu] layer {l}: {errs[-1]}")
+        got_lse = lses[l].cpu().numpy().astype(np.float64)
+        s = parity.check(got, exp, "bf16", b0, f"layer {l}")
+        assert np.abs(got_lse - exp_lse).max() <= 2e-3 * max(1.0, np.abs(exp_lse).max()), f"layer {l} lse"
+        say(f"[gpu] layer {l}: {s}")
+        gots.append(got)
+        exps.append(exp)
+        b0s.append(b0)
+    s = parity.check(np.stack(gots), np.stack(exps), "bf16", np.stack(b0s), "eight layers together")
+    say(f"[gpu] layers {FULL_DEPTH_CHECKED} together: {s}")
     del layers
+
+
+# --------------------------------------------- every kernel instantiation --
+
+@pytest.mark.parametrize("key,case", KP.PATHS, ids=[c.name for _, c in KP.PATHS])
+def test_kernel_path(key, case):
+    """One workload per kernel instantiation the library can launch (the host
+    test in test_kernel_paths.py pins that each reaches its instantiation)."""
+    x = synth.make_inputs(case, 77, b_sigma=0.3, q_scale=2.0)
+    compare(case, x, what=f"{case.name} {key}")
 
 
 # ------------------------------------------------------------ edge cases --
