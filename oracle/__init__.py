@@ -13,7 +13,11 @@ Contents
   * ``gather_base`` -- logical base cache from a paged pool and its table
                        (numpy indexing, byte-exact);
   * ``brute``       -- the same definition in 40-digit decimal arithmetic, for
-                       tiny shapes (pins the C code).
+                       tiny shapes (pins the C code);
+  * ``cache_write`` -- the cache-write path upstream of attention: the rank-r
+                       projection L = X A that fills the low-rank caches, the
+                       logical rows of a paged pool, and the copy-on-write
+                       rules an append of new base rows must obey.
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against facts the
 pages and the mathematics fix (brute force, closed forms, invariants, library

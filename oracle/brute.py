@@ -76,3 +76,17 @@ def to_float(out, lse):
     o = np.array([[[[float(x) for x in row] for row in th] for th in at] for at in out])
     l = np.array([[[float(x) for x in th] for th in at] for at in lse])
     return o, l
+
+
+def lr_project(x, a_t):
+    """40-digit decimal L = X A for tiny shapes (the same definition as
+    oracle.cache_write.lr_project: A given as [r, d_in]; one output set per
+    X or A set, a single set being shared).  Returns nested lists of Decimal
+    [n][t][c]."""
+    X = _widen(np.asarray(x))
+    A = _widen(np.asarray(a_t))
+    nx, na = X.shape[0], A.shape[0]
+    n_out = max(nx, na)
+    with decimal.localcontext(_CTX):
+        return [[[sum((X[0 if nx == 1 else n, t, k] * A[0 if na == 1 else n, c, k] for k in range(X.shape[2])),
+                      Decimal(0)) for c in range(A.shape[1])] for t in range(X.shape[1])] for n in range(n_out)]
