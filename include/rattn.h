@@ -59,7 +59,8 @@ typedef enum rattn_status {
     RATTN_E_UNSUPPORTED = -3, /* valid, but outside what the kernels implement */
     RATTN_E_WORKSPACE = -4,   /* workspace NULL or smaller than rattn_workspace_bytes */
     RATTN_E_ALIGN = -5,       /* a pointer is not 16-byte aligned */
-    RATTN_E_HIP = -6          /* a HIP runtime call or kernel launch failed */
+    RATTN_E_HIP = -6,         /* a HIP runtime call or kernel launch failed */
+    RATTN_E_SCRATCH = -7      /* rattn_decode_noalloc: the call needs more than its static buffer */
 } rattn_status;
 
 typedef enum rattn_dtype {
@@ -129,6 +130,24 @@ int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes);
  */
 int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/*
+ * rattn_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops or harnesses that forbid allocation): the same
+ * computation and kernels, with the split partials kept in a static device
+ * buffer of RATTN_NOALLOC_SCRATCH_BYTES (32 MiB) instead of a caller
+ * workspace.  Each GPU the library runs on holds its own such buffer until the
+ * process ends.  The call allocates and frees nothing; its first call on a
+ * device looks up that device's buffer address once (hipGetSymbolAddress).
+ * The buffer needs no clearing (the split launch writes every partial the
+ * merge reads).  Every call on one GPU shares that GPU's buffer: calls that
+ * overlap in time on one GPU (other streams, other threads) race and give
+ * wrong results; order them (one stream per GPU).  Returns RATTN_E_SCRATCH,
+ * launching nothing, when rattn_workspace_bytes(desc, RATTN_OP_DECODE) exceeds
+ * RATTN_NOALLOC_SCRATCH_BYTES; other errors as rattn_decode.
+ */
+#define RATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int rattn_decode_noalloc(const rattn_desc *desc, const rattn_args *args, void *stream);
 
 /*
  * Chunked prefill: agent a appends a chunk of C = priv_len = q_len new tokens

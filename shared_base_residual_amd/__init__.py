@@ -27,10 +27,11 @@ LIB_PATH = os.path.join(HERE, "librattn.so")
 RATTN_F32, RATTN_BF16 = 0, 1
 RATTN_OP_DECODE, RATTN_OP_PREFILL = 0, 1
 STATUS = {0: "RATTN_OK", -1: "RATTN_E_NULL", -2: "RATTN_E_SHAPE", -3: "RATTN_E_UNSUPPORTED",
-          -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP"}
+          -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP", -7: "RATTN_E_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
            "rattn_decode_plan", "rattn_prefill_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error",
-           "rattn_attention_stages")
+           "rattn_attention_stages", "rattn_decode_noalloc")
 STAGE_SPLIT, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
 
 
@@ -88,11 +89,12 @@ def lib():
         L.rattn_prefill_plan.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(PlanInfo)]
         L.rattn_attention_stages.argtypes = [ctypes.POINTER(Desc), I, ctypes.POINTER(Args), P, ctypes.c_size_t, P,
                                              ctypes.c_uint]
+        L.rattn_decode_noalloc.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P]
         L.rattn_status_str.argtypes = [I]
         L.rattn_status_str.restype = ctypes.c_char_p
         for f in ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
                   "rattn_decode_plan", "rattn_prefill_plan", "rattn_version", "rattn_last_hip_error",
-                  "rattn_attention_stages"):
+                  "rattn_attention_stages", "rattn_decode_noalloc"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -301,6 +303,26 @@ def prefill_chunk(q, k_base, v_base, lk=None, lv=None, bk=None, bv=None, *, bloc
     tokens 0..t (k_priv/v_priv hold the chunk's own keys and values)."""
     return _run("rattn_prefill_chunk", RATTN_OP_PREFILL, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv,
                 v_priv, shared_lr, out, lse, workspace, sm_scale, prefix_len, stream, desc)
+
+
+def decode_noalloc(inputs: dict, *, shared_lr=None, prefix_len=None, out, lse=None, stream=None, desc=None):
+    """rattn_decode_noalloc on a dict of device tensors (named as in the layouts
+    above): rattn_decode with the library's static scratch buffer instead of a
+    workspace.  ``out`` (and ``lse``) are the caller's; nothing is allocated."""
+    g = inputs.get
+    if desc is None:
+        desc = describe(inputs["q"], g("k_base"), g("lk"), g("bk"), block_table=g("block_table"),
+                        k_priv=g("k_priv"), prefix_len=prefix_len, shared_lr=shared_lr)
+    tensors = dict(q=inputs["q"], k_base=g("k_base"), v_base=g("v_base"), block_table=g("block_table"), lk=g("lk"),
+                   lv=g("lv"), bk=g("bk"), bv=g("bv"), k_priv=g("k_priv"), v_priv=g("v_priv"), out=out, lse=lse)
+    _check_tensors(desc, tensors)
+    args = Args(*[_ptr(tensors[n]) for n in
+                  ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out",
+                   "lse")])
+    st = lib().rattn_decode_noalloc(ctypes.byref(desc), ctypes.byref(args), _stream(stream))
+    if st:
+        raise RattnError(st, "rattn_decode_noalloc")
+    return out
 
 
 def gather_base(pool, block_table, prefix_len: int, *, out=None, stream=None):

@@ -15,7 +15,10 @@ hipError_t launch_decode(int bf16_in, const DecodeParams &dp, int D, int cpad, s
 hipError_t launch_gather(const void *pool, const int32_t *table, void *dst, int64_t L, int HK, int ps,
                          int row_bytes, hipStream_t st);
 hipError_t launch_prefill(const PrefillParams &pp, int D, int cpad, size_t lds, hipStream_t st);
+hipError_t noalloc_scratch(void **ptr);
 }  // namespace rattn
+
+static_assert(rattn::kNoAllocScratchBytes == RATTN_NOALLOC_SCRATCH_BYTES, "static scratch size in the header");
 
 namespace {
 
@@ -567,6 +570,7 @@ const char *rattn_status_str(int s) {
         case RATTN_E_WORKSPACE: return "workspace missing or too small";
         case RATTN_E_ALIGN: return "misaligned pointer";
         case RATTN_E_HIP: return "HIP runtime error";
+        case RATTN_E_SCRATCH: return "call needs more than the static scratch buffer holds";
         default: return "unknown status";
     }
 }
@@ -637,6 +641,21 @@ int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace
 int rattn_prefill_chunk(const rattn_desc *desc, const rattn_args *args, void *workspace,
                         size_t workspace_bytes, void *stream) {
     return run_attention(desc, args, workspace, workspace_bytes, stream, RATTN_OP_PREFILL, RATTN_STAGE_ALL);
+}
+
+int rattn_decode_noalloc(const rattn_desc *desc, const rattn_args *args, void *stream) {
+    int st = check_desc(desc, RATTN_OP_DECODE);
+    if (st) return st;
+    st = check_args(desc, args);
+    if (st) return st;
+    Plan pl;
+    st = make_plan(desc, RATTN_OP_DECODE, &pl);
+    if (st) return st;
+    if (pl.total > rattn::kNoAllocScratchBytes) return RATTN_E_SCRATCH;
+    void *ws = nullptr;
+    st = hip_status(rattn::noalloc_scratch(&ws));
+    if (st) return st;
+    return run_attention(desc, args, ws, rattn::kNoAllocScratchBytes, stream, RATTN_OP_DECODE, RATTN_STAGE_ALL);
 }
 
 int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,

@@ -35,6 +35,8 @@
 // Loads never branch on the data: token indices beyond the split are clamped
 // to its last token (finite data) and those scores are masked to -inf, so
 // their weights are exactly zero.
+#include <mutex>
+
 #include "device.h"
 #include "internal.h"
 #include "stage.h"
@@ -1170,6 +1172,38 @@ static hipError_t launch_combine_t(const DecodeParams &dp, int D, hipStream_t st
     else
         hipLaunchKernelGGL((combine_kernel<T, 64>), grid, dim3(kCombineThreads), 0, st, dp);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------ static scratch --
+//
+// The split partials of rattn_decode_noalloc live here instead of in a caller
+// workspace.  Each GPU the library runs on holds its own copy of the array,
+// at its own address, until the process ends.  On the host the name `scratch`
+// is only a stand-in for the symbol, not a device address: host code uses the
+// address hipGetSymbolAddress returns for the current device, looked up once
+// per device and kept.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void **ptr) {
+    static std::atomic<void *> addr[64];
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void *p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> g(mu);
+        p = addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 hipError_t launch_decode(int bf16_in, const DecodeParams &dp, int D, int cpad, size_t lds, unsigned stages,

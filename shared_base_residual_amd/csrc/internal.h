@@ -165,6 +165,10 @@ struct DecodeParams {
     FastDiv fd_hq, fd_ql;  // query heads, query tokens (the merge's row index)
 };
 
+// Size of the static device buffer that rattn_decode_noalloc keeps its split
+// partials in (one per GPU, held until the process ends).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+
 // Dynamic LDS a split or prefill workgroup may use: all of gfx950's 160 KiB per
 // workgroup (neither kernel declares static LDS).
 constexpr int kLdsMax = 160 * 1024;
