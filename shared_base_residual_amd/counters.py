@@ -152,20 +152,145 @@ def summarize(config: int, fetch_dir: str, write_dir: str) -> None:
     print(json.dumps(e))
 
 
+# MI355X: 256 compute units of 4 SIMDs each
+SIMD_NUM = 1024
+
+
+def summarize_mfma(config: int, d: str) -> None:
+    """Matrix-unit utilisation of the kernel from one rocprofv3 pass with
+    --pmc MfmaUtil MfmaFlopsBF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE
+    (MfmaUtil = MFMA-busy SIMD cycles / (GPU-active cycles x SIMDs) x 100; the
+    bf16 MFMA flops are the counter's operation count x 512)."""
+    sys.path.insert(0, ROOT)
+    import synth
+    from shared_base_residual_amd.build import source_hash
+
+    case = synth.CONFIGS[config]
+    kern, wl = WORKLOADS[config]
+    paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    vals = {}
+    with open(paths[0]) as f:
+        for row in csv.DictReader(f):
+            if kern not in row.get("Kernel_Name", ""):
+                continue
+            vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {kern} dispatches in {paths[0]}")
+    avg = {k: sum(v) / len(v) for k, v in vals.items()}
+    n = len(next(iter(vals.values())))
+    util = avg.get("MfmaUtil")
+    flops = avg.get("MfmaFlopsBF16")
+    lines = [
+        f"# {kern} -- matrix-unit (MFMA) utilisation, {case.name}, MI355X", "",
+        "Commands (repository root, TMPDIR=/tmp):", "",
+        f"    rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE --output-format csv "
+        f"-d {d} -o run -- python3 -m shared_base_residual_amd.counters run --config {config}",
+        f"    python3 -m shared_base_residual_amd.counters summarize-mfma --config {config} --dir {d}", "",
+        f"Per dispatch ({n} dispatches averaged):", "",
+        "| counter | value |", "|---|---|",
+    ]
+    for k in sorted(avg):
+        lines.append(f"| {k} | {avg[k]:.6g} |")
+    lines.append("")
+    if util is not None:
+        lines.append(f"MfmaUtil (rocprofv3's derived metric: SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / "
+                     f"(GRBM_GUI_ACTIVE x {SIMD_NUM} SIMDs) x 100): **{util:.1f} %** of the SIMD cycles the matrix "
+                     f"units are busy.")
+    if flops is not None:
+        lines.append(f"MfmaFlopsBF16: {flops / 1e12:.3f} TFLOP executed per dispatch on bf16 MFMAs "
+                     f"(counted operations x 512).")
+    lines += ["", f"Library sources hash {source_hash()}.", ""]
+    out = os.path.join(ROOT, "profiles", f"{kern}.{wl}.mfma.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def summarize_trace(config: int, d: str, bench_json: str, cmd: str) -> None:
+    """Kernel durations of one rocprofv3 --kernel-trace --stats run of bench.py
+    for one workload: the library's kernels from kernel_stats.csv, the average
+    of the last launches of the roofline kernel (bench.py's back-to-back
+    window) from kernel_trace.csv, and the bench line of the same run."""
+    sys.path.insert(0, ROOT)
+    import synth
+    from shared_base_residual_amd.build import source_hash
+
+    case = synth.CONFIGS[config]
+    kern, wl = WORKLOADS[config]
+    with open(bench_json) as f:
+        line = [l for l in f.read().splitlines() if l.startswith("{")][-1]
+    rec = json.loads(line)
+    roof = rec["roofline"]
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        raise SystemExit(f"kernel_stats.csv / kernel_trace.csv missing under {d}")
+    rows = []
+    with open(stats[0]) as f:
+        for r in csv.DictReader(f):
+            rows.append(r)
+    durs = []
+    with open(trace[0]) as f:
+        for r in csv.DictReader(f):
+            if kern in r["Kernel_Name"]:
+                durs.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    durs.sort()
+    n_k = roof["launches_timed"]
+    last = [x for _, x in durs[-n_k:]]
+    lib_rows = [r for r in rows if "rattn" in r["Name"]]
+    lines = [
+        f"# {kern} -- {case.name}, MI355X", "",
+        "Command (repository root, TMPDIR=/tmp):", "",
+        f"    {cmd}", "",
+        "Kernels of the library (kernel_stats.csv; durations in microseconds):", "",
+        "| kernel | calls | avg | min | max | share of GPU time |", "|---|---|---|---|---|---|",
+    ]
+    for r in lib_rows:
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} % |")
+    lines += [
+        "", "The bench's other kernels (input draws and copies) run outside the timed region.", "",
+        f"The last {len(last)} {kern} launches in the trace (the back-to-back launches bench.py times for the "
+        f"roofline) average {sum(last) / max(1, len(last)) / 1e3:.2f} us; bench.py's HIP-event average over the "
+        f"same launches is {roof['avg_launch_us']} us (fraction {roof['frac']} of the {roof['peak']} "
+        f"{roof['unit']} peak).", "",
+        "Bench line of the same run:", "", "    " + line, "",
+        f"Library sources hash {source_hash()}.", "",
+    ]
+    out = os.path.join(ROOT, "profiles", f"{kern}.{wl}.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines[:20]))
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
-    sub = ap.add_subparsers(dest="cmd", required=True)
+    sub = ap.add_subparsers(dest="action", required=True)
     r = sub.add_parser("run")
     r.add_argument("--config", type=int, required=True)
     s = sub.add_parser("summarize")
     s.add_argument("--config", type=int, required=True)
     s.add_argument("--fetch", required=True)
     s.add_argument("--write", required=True)
+    m = sub.add_parser("summarize-mfma")
+    m.add_argument("--config", type=int, required=True)
+    m.add_argument("--dir", required=True)
+    t = sub.add_parser("summarize-trace")
+    t.add_argument("--config", type=int, required=True)
+    t.add_argument("--dir", required=True)
+    t.add_argument("--bench-json", required=True)
+    t.add_argument("--cmd", required=True)
     a = ap.parse_args()
-    if a.cmd == "run":
+    if a.action == "run":
         run(a.config)
-    else:
+    elif a.action == "summarize":
         summarize(a.config, a.fetch, a.write)
+    elif a.action == "summarize-mfma":
+        summarize_mfma(a.config, a.dir)
+    else:
+        summarize_trace(a.config, a.dir, a.bench_json, a.cmd)
 
 
 if __name__ == "__main__":
