@@ -354,6 +354,101 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None):
     return rec
 
 
+# The cache-write path, measured beside the attention workloads: the low-rank
+# cache rows of a 32768-token shared context for 4 agents with their own
+# down-projections (BaseShared "LR prefill" on an agent switch; ForkKV's base
+# hit with an adapter miss), Llama-3-8B-shaped (d_in = 4096, r = 16); and a
+# 4096-token append of base rows (H_kv = 8, d = 128, bf16) into a paged pool
+# whose partly filled last page is shared (one copy-on-write page).
+LR_PREFILL = dict(name="BaseShared LR prefill (low-rank cache write)", n_sets=4, d_in=4096, r=16, T=32768)
+APPEND = dict(name="paged base append with copy-on-write", HK=8, D=128, ps=16, cur_len=8200, T=4096)
+
+
+def measure_lr_prefill(K, W, dev, hip, stream, probe):
+    import numpy as np
+    import torch
+
+    import shared_base_residual_amd as R
+    import synth
+
+    c = LR_PREFILL
+    say(f"[bench] {c['name']}: drawing inputs")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    n_rep = 2  # X (268 MB) alternates between two replicas so each launch reads HBM
+    xs = [torch.randn((1, c["T"], c["d_in"]), generator=g, device=dev).to(torch.bfloat16) for _ in range(n_rep)]
+    ak = (torch.randn((c["n_sets"], c["r"], c["d_in"]), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+    av = (torch.randn((c["n_sets"], c["r"], c["d_in"]), generator=g, device=dev) * 0.05).to(torch.bfloat16)
+    lk = torch.empty((c["n_sets"], c["T"], c["r"]), device=dev, dtype=torch.bfloat16)
+    lv = torch.empty_like(lk)
+    fn = lambda i: R.lr_project(xs[i % n_rep], ak, av, lk, lv, stream=stream)
+    for i in range(W):
+        fn(i)
+    stable_ms(hip, fn, 8, ctypes.c_void_p(stream.cuda_stream))
+    ms = hip.time_ms(fn, K, ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    nbytes = xs[0].numel() * 2 + 2 * ak.numel() * 2 + 2 * lk.numel() * 2
+    achieved = nbytes / (ms / 1e3) / 1e9
+    rows = c["n_sets"] * c["T"]
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "lr_project_kernel",
+            "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2), "launches_timed": K}
+    if probe:
+        roof["achievable"] = probe["achievable"]
+        roof["frac_of_achievable"] = round(achieved / probe["achievable"], 4)
+    say(f"[bench] {c['name']}: {ms * 1e3:.2f} us, frac {roof['frac']}")
+    del xs, ak, av, lk, lv
+    return {"metric": "low-rank cache rows written per second (agent x token)", "value": round(rows / ms / 1e6, 4),
+            "unit": "G rows/s", "steps": K, "warmup": W, "ms_per_step": round(ms, 5), "dtype": "bf16",
+            "config": {"workload": c["name"], "n_sets": c["n_sets"], "d_in": c["d_in"], "rank": c["r"],
+                       "n_tokens": c["T"], "shared_x": True, "shared_a": False}, "roofline": roof}
+
+
+def measure_append(K, W, dev, hip, stream, probe):
+    import numpy as np
+    import torch
+
+    import shared_base_residual_amd as R
+
+    c = APPEND
+    HK, D, ps, L0, T = c["HK"], c["D"], c["ps"], c["cur_len"], c["T"]
+    n_phys = 2 * (-(-(L0 + T) // ps)) + 8
+    say(f"[bench] {c['name']}")
+    pool_k = torch.zeros((n_phys, HK, ps, D), device=dev, dtype=torch.bfloat16)
+    pool_v = torch.zeros_like(pool_k)
+    kn = torch.randn((HK, T, D), device=dev).to(torch.bfloat16)
+    vn = torch.randn((HK, T, D), device=dev).to(torch.bfloat16)
+    pp = R.PagePool(n_phys)
+    base = pp.alloc(-(-L0 // ps))
+    pp.retain(base)  # a second sequence shares every page
+    table = np.full(-(-(L0 + T) // ps), -1, np.int32)
+    table[:base.size] = base
+    cow = pp.plan_append(table, L0, T, ps)
+    tdev = torch.from_numpy(table).to(dev)
+    fn = lambda i: R.append_kv(pool_k, pool_v, tdev, L0, kn, vn, cow=cow, stream=stream)
+    for i in range(W):
+        fn(i)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    stable_ms(hip, fn, 8, sp)
+    ms = hip.time_ms(fn, K, sp)
+    torch.cuda.synchronize()
+    off = L0 % ps
+    nbytes = 2 * (2 * HK * T * D * 2) + 2 * (2 * HK * off * D * 2) + table.size * 4
+    achieved = nbytes / (ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "append_kv_kernel",
+            "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2), "launches_timed": K}
+    if probe:
+        roof["achievable"] = probe["achievable"]
+        roof["frac_of_achievable"] = round(achieved / probe["achievable"], 4)
+    say(f"[bench] {c['name']}: {ms * 1e3:.2f} us, frac {roof['frac']}")
+    del pool_k, pool_v, kn, vn
+    return {"metric": "base rows appended per second (token x KV head)", "value": round(HK * T / ms / 1e6, 4),
+            "unit": "G rows/s", "steps": K, "warmup": W, "ms_per_step": round(ms, 5), "dtype": "bf16",
+            "config": {"workload": c["name"], "n_kv_heads": HK, "head_dim": D, "page_size": ps,
+                       "cur_len": L0, "n_tokens": T, "copy_on_write_pages": int(cow[0] >= 0)}, "roofline": roof}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -364,6 +459,7 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="input sets rotated (0: auto)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-cache-write", action="store_true", help="skip the cache-write sub-records")
     ap.add_argument("--seed", type=int, default=None)
     args = ap.parse_args()
 
@@ -389,6 +485,9 @@ def main():
     if subs:
         res["sub_records"] = [measure(c, args.steps, args.warmup, dev, hip, stream, args.replicas, None, probe)
                               for c in subs]
+    if not args.no_cache_write:
+        res.setdefault("sub_records", []).extend([measure_lr_prefill(args.steps, args.warmup, dev, hip, stream, probe),
+                                                  measure_append(args.steps, args.warmup, dev, hip, stream, probe)])
     if probe:
         res["hbm_probe"] = probe
     if not args.no_cpu:

@@ -60,7 +60,8 @@ typedef enum rattn_status {
     RATTN_E_WORKSPACE = -4,   /* workspace NULL or smaller than rattn_workspace_bytes */
     RATTN_E_ALIGN = -5,       /* a pointer is not 16-byte aligned */
     RATTN_E_HIP = -6,         /* a HIP runtime call or kernel launch failed */
-    RATTN_E_SCRATCH = -7      /* rattn_decode_noalloc: the call needs more than its static buffer */
+    RATTN_E_SCRATCH = -7,     /* rattn_decode_noalloc: the call needs more than its static buffer */
+    RATTN_E_POOL = -8         /* page pool: not enough free pages (or host memory) */
 } rattn_status;
 
 typedef enum rattn_dtype {
@@ -206,6 +207,108 @@ int rattn_gather_base(const rattn_desc *desc, const void *pool, const int32_t *b
 #define RATTN_STAGE_ALL 3u
 int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,
                            size_t workspace_bytes, void *stream, unsigned stages);
+
+/* ------------------------------------------------------------------------
+ * The cache-write path: what fills the caches the attention calls read.
+ * ------------------------------------------------------------------------ */
+
+/* Shape of one low-rank projection call. */
+typedef struct rattn_lr_desc {
+    int32_t n_sets;    /* output sets: one low-rank cache pair per agent (BaseShared), or 1 (BaseLRShared) */
+    int32_t shared_x;  /* 1: one input X for every set ([1, T, d_in]); 0: one per set */
+    int32_t shared_a;  /* 1: one A for every set (Shared-A LoRA); 0: one per set */
+    int32_t d_in;      /* model width the down-projection reads: a multiple of 128 */
+    int32_t rank;      /* r: 8, 16, 32, 64 or 128 */
+    int64_t n_tokens;  /* T >= 0 new tokens */
+    int64_t pos0;      /* first cache row written (>= 0) */
+    int64_t cache_len; /* rows of each set's cache: pos0 + T <= cache_len */
+    int32_t dtype;     /* RATTN_BF16 (the only one supported) */
+} rattn_lr_desc;
+
+/*
+ * The low-rank cache rows of T new tokens: for every set n and token t,
+ *     lk[n][pos0 + t] = X_n[t] A_k,n      lv[n][pos0 + t] = X_n[t] A_v,n
+ * (r values each), with X_n = x[0] when shared_x and A_.,n the set's (or the
+ * shared) down-projection.  This is the LR cache of LRAgent ("Schemi di
+ * Condivisione": BaseShared keeps X_i A_i per agent and recomputes it over
+ * the whole context on an agent switch, the "LR prefill"; BaseLRShared
+ * shares A and so one cache) and the factored residual cache X A of the
+ * ForkKV Guide ("The Disaggregated Memory Layout"), which on a base hit with
+ * an adapter miss is all that is computed ("Two-Tier Lookup Mechanics",
+ * Case B).  The up-projections B are applied later, inside the attention.
+ *
+ * Layouts (device pointers, row-major, 16-byte aligned, bf16):
+ *   x     [shared_x ? 1 : n_sets, T, d_in]
+ *   ak_t  [shared_a ? 1 : n_sets, r, d_in]   A_k transposed (one row per rank
+ *   av_t  same as ak_t                        component, as a linear layer
+ *                                             d_in -> r stores its weight)
+ *   lk    [n_sets, cache_len, r]   rows pos0 .. pos0 + T - 1 written, the rest untouched
+ *   lv    same as lk
+ * Each output value is the fp32 sum of the d_in products rounded to bf16
+ * (round to nearest even).  shared_x = shared_a = 1 requires n_sets = 1.
+ * One kernel launch on `stream`; T = 0 launches nothing.  Errors as the
+ * attention calls (RATTN_E_UNSUPPORTED for a dtype other than bf16, d_in not a
+ * multiple of 128, or another rank).
+ */
+int rattn_lr_project(const rattn_lr_desc *desc, const void *x, const void *ak_t, const void *av_t, void *lk,
+                     void *lv, void *stream);
+
+/*
+ * Page allocator of a paged KV pool with copy-on-write (ForkKV Guide, "The
+ * Copy-on-Write Paradigm"; "Reference Counting and Eviction").  A host
+ * object: reference counts per physical page and a free list; it never
+ * touches device memory.  Sequences that share a prefix hold the same pages
+ * (retain once per sharing sequence, as a fork does); a page returns to the
+ * free list when its last holder releases it.  Every call validates before
+ * changing anything (a failed call changes nothing); calls on one pool may
+ * come from several threads (one lock per pool).  Pages are numbered
+ * 0 .. n_pages - 1 and index the pools of the attention calls.
+ */
+typedef struct rattn_pagepool rattn_pagepool;
+int rattn_pagepool_create(int64_t n_pages, rattn_pagepool **out);
+void rattn_pagepool_destroy(rattn_pagepool *pool);
+/* Free pages, or a negative rattn_status. */
+int64_t rattn_pagepool_free_pages(rattn_pagepool *pool);
+int rattn_pagepool_refcount(rattn_pagepool *pool, int32_t page, int32_t *count);
+/* n free pages, each with one reference, into pages[0 .. n-1] (RATTN_E_POOL if fewer are free). */
+int rattn_pagepool_alloc(rattn_pagepool *pool, int64_t n, int32_t *pages);
+/* One more reference to each listed page (each must be held); a page listed k times gains k. */
+int rattn_pagepool_retain(rattn_pagepool *pool, const int32_t *pages, int64_t n);
+/* One reference fewer per listing; pages reaching 0 are free again. */
+int rattn_pagepool_release(rattn_pagepool *pool, const int32_t *pages, int64_t n);
+/*
+ * Plans the append of n_new tokens to a sequence of cur_len tokens whose
+ * host block table is table[0 .. table_cap - 1]; updates the table:
+ *   - the partly filled last page (cur_len % page_size != 0) is written in
+ *     place when the sequence holds it alone; when it is shared, a free page
+ *     becomes its private copy: *cow_src / *cow_dst name the original and the
+ *     copy, the table points at the copy and the original loses this
+ *     sequence's reference (else both are -1);
+ *   - every further page the new tokens reach comes from the free list.
+ * The caller then copies the table to the device and runs rattn_append_kv
+ * with the same cur_len, n_new and cow pages.  RATTN_E_POOL (nothing changed)
+ * when the free pages do not suffice; RATTN_E_SHAPE when the table is too
+ * short or names a page the pool does not hold.
+ */
+int rattn_pagepool_plan_append(rattn_pagepool *pool, int32_t *table, int64_t table_cap, int64_t cur_len,
+                               int64_t n_new, int32_t page_size, int32_t *cow_src, int32_t *cow_dst);
+
+/*
+ * The data movement of a planned append, on the device: writes the T = n_new
+ * new rows of every KV head, k_new/v_new [H_kv, T, d] (device, same dtype as
+ * the pools), at logical positions cur_len .. cur_len + T - 1 of the sequence
+ * whose updated block table is `table` (device, int32, >= ceil((cur_len + T)
+ * / page_size) entries), into both pools [n_phys_pages, H_kv, page_size, d];
+ * and, when cow_src >= 0, first fills rows 0 .. (cur_len % page_size) - 1 of
+ * every head of page cow_dst from page cow_src (the private copy keeps the
+ * rows the original held).  Uses desc->n_kv_heads, head_dim, page_size,
+ * n_phys_pages and dtype.  One kernel launch; byte-exact.  The table's
+ * entries and the cow pages must lie in [0, n_phys_pages) (cow pages checked
+ * on the host, table entries not).  k_new/v_new must not overlap the pools.
+ */
+int rattn_append_kv(const rattn_desc *desc, void *pool_k, void *pool_v, const int32_t *table, int64_t cur_len,
+                    int64_t n_new, const void *k_new, const void *v_new, int32_t cow_src, int32_t cow_dst,
+                    void *stream);
 
 /* Work decomposition chosen for a call (host-only introspection; no HIP call).
  * The kernel that runs is determined by (dtype, head_dim, path, resid_cols,

@@ -27,11 +27,14 @@ LIB_PATH = os.path.join(HERE, "librattn.so")
 RATTN_F32, RATTN_BF16 = 0, 1
 RATTN_OP_DECODE, RATTN_OP_PREFILL = 0, 1
 STATUS = {0: "RATTN_OK", -1: "RATTN_E_NULL", -2: "RATTN_E_SHAPE", -3: "RATTN_E_UNSUPPORTED",
-          -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP", -7: "RATTN_E_SCRATCH"}
+          -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP", -7: "RATTN_E_SCRATCH",
+          -8: "RATTN_E_POOL"}
 NOALLOC_SCRATCH_BYTES = 32 << 20
 EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
            "rattn_decode_plan", "rattn_prefill_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error",
-           "rattn_attention_stages", "rattn_decode_noalloc")
+           "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
+           "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
+           "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv")
 STAGE_SPLIT, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
 
 
@@ -60,6 +63,12 @@ class Args(ctypes.Structure):
                  "lse")]
 
 
+class LrDesc(ctypes.Structure):
+    _fields_ = [("n_sets", ctypes.c_int32), ("shared_x", ctypes.c_int32), ("shared_a", ctypes.c_int32),
+                ("d_in", ctypes.c_int32), ("rank", ctypes.c_int32), ("n_tokens", ctypes.c_int64),
+                ("pos0", ctypes.c_int64), ("cache_len", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+
+
 class PlanInfo(ctypes.Structure):
     _fields_ = [("n_prefix_splits", ctypes.c_int32), ("prefix_split_len", ctypes.c_int64),
                 ("n_priv_splits", ctypes.c_int32), ("priv_split_len", ctypes.c_int64),
@@ -79,6 +88,13 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"librattn is not built ({LIB_PATH} missing): run "
                                "`python -m shared_base_residual_amd.build`")
+        # torch first: its HIP runtime is then the one librattn binds to (one
+        # runtime per process; loading librattn first would bind the system
+        # runtime, under which torch's own device calls then fail)
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         P, I = ctypes.c_void_p, ctypes.c_int
         L.rattn_workspace_bytes.argtypes = [ctypes.POINTER(Desc), I, ctypes.POINTER(ctypes.c_size_t)]
@@ -90,11 +106,31 @@ def lib():
         L.rattn_attention_stages.argtypes = [ctypes.POINTER(Desc), I, ctypes.POINTER(Args), P, ctypes.c_size_t, P,
                                              ctypes.c_uint]
         L.rattn_decode_noalloc.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P]
+        I64, I32P = ctypes.c_int64, ctypes.POINTER(ctypes.c_int32)
+        L.rattn_lr_project.argtypes = [ctypes.POINTER(LrDesc), P, P, P, P, P, P]
+        L.rattn_pagepool_create.argtypes = [I64, ctypes.POINTER(P)]
+        L.rattn_pagepool_destroy.argtypes = [P]
+        L.rattn_pagepool_destroy.restype = None
+        L.rattn_pagepool_free_pages.argtypes = [P]
+        L.rattn_pagepool_free_pages.restype = I64
+        L.rattn_pagepool_refcount.argtypes = [P, ctypes.c_int32, I32P]
+        L.rattn_pagepool_alloc.argtypes = [P, I64, I32P]
+        L.rattn_pagepool_retain.argtypes = [P, I32P, I64]
+        L.rattn_pagepool_release.argtypes = [P, I32P, I64]
+        L.rattn_pagepool_plan_append.argtypes = [P, I32P, I64, I64, I64, ctypes.c_int32, I32P, I32P]
+        L.rattn_append_kv.argtypes = [ctypes.POINTER(Desc), P, P, P, I64, I64, P, P, ctypes.c_int32,
+                                      ctypes.c_int32, P]
+        for f in ("rattn_lr_project", "rattn_pagepool_create", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
+                  "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append",
+                  "rattn_append_kv"):
+            getattr(L, f).restype = I
         L.rattn_status_str.argtypes = [I]
         L.rattn_status_str.restype = ctypes.c_char_p
         for f in ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "rattn_gather_base",
                   "rattn_decode_plan", "rattn_prefill_plan", "rattn_version", "rattn_last_hip_error",
-                  "rattn_attention_stages", "rattn_decode_noalloc"):
+                  "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
+           "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
+           "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -323,6 +359,134 @@ def decode_noalloc(inputs: dict, *, shared_lr=None, prefix_len=None, out, lse=No
     if st:
         raise RattnError(st, "rattn_decode_noalloc")
     return out
+
+
+def lr_project(x, ak_t, av_t, lk, lv, *, pos0: int = 0, stream=None):
+    """rattn_lr_project: rows pos0 .. pos0 + T - 1 of the low-rank caches,
+    lk[n][pos0 + t] = X_n[t] A_k,n and lv likewise (bf16 out of an fp32 sum).
+    x [1 or n_sets, T, d_in]; ak_t, av_t [1 or n_sets, r, d_in] (A transposed);
+    lk, lv [n_sets, cache_len, r].  Returns (lk, lv)."""
+    import torch
+
+    n_sets, cache_len, r = lk.shape
+    nx, T, d_in = x.shape
+    desc = LrDesc(n_sets, int(nx == 1 and n_sets > 1 or n_sets == 1), int(ak_t.shape[0] == 1 and n_sets > 1 or
+                                                                          n_sets == 1),
+                  d_in, r, T, pos0, cache_len, RATTN_BF16 if x.dtype == torch.bfloat16 else RATTN_F32)
+    want = {"x": (1 if desc.shared_x else n_sets, T, d_in), "ak_t": (1 if desc.shared_a else n_sets, r, d_in),
+            "av_t": (1 if desc.shared_a else n_sets, r, d_in), "lv": (n_sets, cache_len, r)}
+    for name, t in dict(x=x, ak_t=ak_t, av_t=av_t, lk=lk, lv=lv).items():
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype:
+            raise ValueError(f"{name} must be a contiguous GPU tensor of x's dtype")
+        if name in want and tuple(t.shape) != want[name]:
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {want[name]}")
+    st = lib().rattn_lr_project(ctypes.byref(desc), x.data_ptr(), ak_t.data_ptr(), av_t.data_ptr(), lk.data_ptr(),
+                                lv.data_ptr(), _stream(stream))
+    if st:
+        raise RattnError(st, "rattn_lr_project")
+    return lk, lv
+
+
+class PagePool:
+    """The library's host page allocator (rattn_pagepool_*): reference counts
+    and a free list over n_pages physical pages, with copy-on-write appends."""
+
+    def __init__(self, n_pages: int):
+        h = ctypes.c_void_p()
+        st = lib().rattn_pagepool_create(n_pages, ctypes.byref(h))
+        if st:
+            raise RattnError(st, "rattn_pagepool_create")
+        self._h = h
+        self.n_pages = n_pages
+
+    def __del__(self):
+        if getattr(self, "_h", None) and _lib is not None:
+            _lib.rattn_pagepool_destroy(self._h)
+            self._h = None
+
+    @staticmethod
+    def _i32(pages):
+        import numpy as np
+
+        a = np.ascontiguousarray(pages, dtype=np.int32)
+        return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+    def free_pages(self) -> int:
+        return int(lib().rattn_pagepool_free_pages(self._h))
+
+    def refcount(self, page: int) -> int:
+        c = ctypes.c_int32()
+        st = lib().rattn_pagepool_refcount(self._h, page, ctypes.byref(c))
+        if st:
+            raise RattnError(st, "rattn_pagepool_refcount")
+        return c.value
+
+    def refcounts(self):
+        import numpy as np
+
+        return np.array([self.refcount(p) for p in range(self.n_pages)], np.int64)
+
+    def alloc(self, n: int):
+        import numpy as np
+
+        out = np.zeros(max(n, 1), np.int32)
+        st = lib().rattn_pagepool_alloc(self._h, n, out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+        if st:
+            raise RattnError(st, "rattn_pagepool_alloc")
+        return out[:n]
+
+    def retain(self, pages):
+        a, p = self._i32(pages)
+        st = lib().rattn_pagepool_retain(self._h, p, a.size)
+        if st:
+            raise RattnError(st, "rattn_pagepool_retain")
+
+    def release(self, pages):
+        a, p = self._i32(pages)
+        st = lib().rattn_pagepool_release(self._h, p, a.size)
+        if st:
+            raise RattnError(st, "rattn_pagepool_release")
+
+    def plan_append(self, table, cur_len: int, n_new: int, page_size: int):
+        """Updates ``table`` (a contiguous int32 numpy array, the sequence's
+        block table with room for the new pages) in place; returns the
+        copy-on-write pair (cow_src, cow_dst), (-1, -1) without a copy."""
+        import numpy as np
+
+        if not (isinstance(table, np.ndarray) and table.dtype == np.int32 and table.flags["C_CONTIGUOUS"]):
+            raise TypeError("table must be a contiguous int32 numpy array")
+        src, dst = ctypes.c_int32(), ctypes.c_int32()
+        st = lib().rattn_pagepool_plan_append(self._h, table.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                              table.size, cur_len, n_new, page_size, ctypes.byref(src),
+                                              ctypes.byref(dst))
+        if st:
+            raise RattnError(st, "rattn_pagepool_plan_append")
+        return src.value, dst.value
+
+
+def append_kv(pool_k, pool_v, table, cur_len: int, k_new, v_new, *, cow=(-1, -1), stream=None):
+    """rattn_append_kv: writes k_new/v_new [H_kv, T, d] at logical positions
+    cur_len .. cur_len + T - 1 of the sequence whose (updated) device block
+    table is ``table``, and fills the copy-on-write page's kept rows."""
+    import torch
+
+    n_phys, HK, ps, D = pool_k.shape
+    T = k_new.shape[1]
+    dt = RATTN_BF16 if pool_k.dtype == torch.bfloat16 else RATTN_F32
+    desc = make_desc(n_agents=1, n_q_heads=HK, n_kv_heads=HK, head_dim=D, rank=0, q_len=1, prefix_len=0,
+                     page_size=ps, n_phys_pages=n_phys, dtype=dt)
+    for name, t in dict(pool_k=pool_k, pool_v=pool_v, k_new=k_new, v_new=v_new).items():
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != pool_k.dtype:
+            raise ValueError(f"{name} must be a contiguous GPU tensor of the pool's dtype")
+    if tuple(pool_v.shape) != tuple(pool_k.shape) or tuple(k_new.shape) != (HK, T, D) or \
+            tuple(v_new.shape) != (HK, T, D):
+        raise ValueError("pool / new-row shapes disagree")
+    if not (table.is_cuda and table.dtype == torch.int32 and table.numel() >= -(-(cur_len + T) // ps)):
+        raise ValueError("table must be a GPU int32 tensor covering the new length")
+    st = lib().rattn_append_kv(ctypes.byref(desc), pool_k.data_ptr(), pool_v.data_ptr(), table.data_ptr(), cur_len,
+                               T, k_new.data_ptr(), v_new.data_ptr(), int(cow[0]), int(cow[1]), _stream(stream))
+    if st:
+        raise RattnError(st, "rattn_append_kv")
 
 
 def gather_base(pool, block_table, prefix_len: int, *, out=None, stream=None):

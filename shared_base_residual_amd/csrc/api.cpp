@@ -16,6 +16,8 @@ hipError_t launch_gather(const void *pool, const int32_t *table, void *dst, int6
                          int row_bytes, hipStream_t st);
 hipError_t launch_prefill(const PrefillParams &pp, int D, int cpad, size_t lds, hipStream_t st);
 hipError_t noalloc_scratch(void **ptr);
+hipError_t launch_lr_project(const LrParams &p, hipStream_t st);
+hipError_t launch_append_kv(const AppendParams &p, hipStream_t st);
 }  // namespace rattn
 
 static_assert(rattn::kNoAllocScratchBytes == RATTN_NOALLOC_SCRATCH_BYTES, "static scratch size in the header");
@@ -571,6 +573,7 @@ const char *rattn_status_str(int s) {
         case RATTN_E_ALIGN: return "misaligned pointer";
         case RATTN_E_HIP: return "HIP runtime error";
         case RATTN_E_SCRATCH: return "call needs more than the static scratch buffer holds";
+        case RATTN_E_POOL: return "page pool: not enough free pages";
         default: return "unknown status";
     }
 }
@@ -656,6 +659,80 @@ int rattn_decode_noalloc(const rattn_desc *desc, const rattn_args *args, void *s
     st = hip_status(rattn::noalloc_scratch(&ws));
     if (st) return st;
     return run_attention(desc, args, ws, rattn::kNoAllocScratchBytes, stream, RATTN_OP_DECODE, RATTN_STAGE_ALL);
+}
+
+int rattn_lr_project(const rattn_lr_desc *d, const void *x, const void *ak_t, const void *av_t, void *lk, void *lv,
+                     void *stream) {
+    if (!d) return RATTN_E_NULL;
+    if (d->n_sets < 1 || d->d_in < 1 || d->rank < 1 || d->n_tokens < 0 || d->pos0 < 0 || d->cache_len < 0 ||
+        (d->shared_x != 0 && d->shared_x != 1) || (d->shared_a != 0 && d->shared_a != 1))
+        return RATTN_E_SHAPE;
+    if (d->pos0 + d->n_tokens > d->cache_len) return RATTN_E_SHAPE;
+    if (d->shared_x && d->shared_a && d->n_sets != 1) return RATTN_E_SHAPE;
+    if (d->dtype != RATTN_BF16) return RATTN_E_UNSUPPORTED;
+    const int r = d->rank;
+    if (!(r == 8 || r == 16 || r == 32 || r == 64 || r == 128) || d->d_in % 128) return RATTN_E_UNSUPPORTED;
+    // index arithmetic: columns and workgroup counts in 32 bits
+    if ((int64_t)d->n_sets * 2 * r > (1ll << 24) || d->n_tokens > (1ll << 40)) return RATTN_E_UNSUPPORTED;
+    if (d->n_tokens == 0) return RATTN_OK;
+    if (!x || !ak_t || !av_t || !lk || !lv) return RATTN_E_NULL;
+    const void *ptrs[] = {x, ak_t, av_t, lk, lv};
+    for (const void *p : ptrs)
+        if (!aligned(p, 16)) return RATTN_E_ALIGN;
+    rattn::LrParams p{};
+    p.x = x;
+    p.ak = ak_t;
+    p.av = av_t;
+    p.lk = lk;
+    p.lv = lv;
+    p.T = d->n_tokens;
+    p.pos0 = d->pos0;
+    p.cache_len = d->cache_len;
+    p.d_in = d->d_in;
+    p.r = r;
+    p.shared_a = d->shared_a;
+    p.n_xsets = d->shared_x ? 1 : d->n_sets;
+    p.cols_per_xset = d->shared_x ? d->n_sets * 2 * r : 2 * r;
+    return hip_status(rattn::launch_lr_project(p, static_cast<hipStream_t>(stream)));
+}
+
+int rattn_append_kv(const rattn_desc *d, void *pool_k, void *pool_v, const int32_t *table, int64_t cur_len,
+                    int64_t n_new, const void *k_new, const void *v_new, int32_t cow_src, int32_t cow_dst,
+                    void *stream) {
+    if (!d) return RATTN_E_NULL;
+    if (d->n_kv_heads < 1 || d->head_dim < 1 || d->page_size < 1 || d->n_phys_pages < 1 || cur_len < 0 ||
+        n_new < 0)
+        return RATTN_E_SHAPE;
+    if (d->dtype != RATTN_F32 && d->dtype != RATTN_BF16) return RATTN_E_UNSUPPORTED;
+    if (d->page_size % 16 || (d->head_dim * esize(d->dtype)) % 16) return RATTN_E_UNSUPPORTED;
+    if ((cow_src < 0) != (cow_dst < 0)) return RATTN_E_SHAPE;
+    if (cow_src >= 0 && (cow_src >= d->n_phys_pages || cow_dst >= d->n_phys_pages || cow_src == cow_dst))
+        return RATTN_E_SHAPE;
+    if (cow_src >= 0 && cur_len % d->page_size == 0) return RATTN_E_SHAPE;  // nothing to keep from the original
+    if (d->n_phys_pages > INT32_MAX || (cur_len + n_new) / d->page_size > INT32_MAX) return RATTN_E_UNSUPPORTED;
+    const int64_t rows = (int64_t)d->n_kv_heads * (n_new + d->page_size);
+    if (rows > (1ll << 40)) return RATTN_E_UNSUPPORTED;
+    if (n_new == 0 && cow_src < 0) return RATTN_OK;
+    if (!pool_k || !pool_v || (n_new > 0 && (!table || !k_new || !v_new))) return RATTN_E_NULL;
+    const void *ptrs[] = {pool_k, pool_v, k_new, v_new};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, 16)) return RATTN_E_ALIGN;
+    if (table && !aligned(table, 4)) return RATTN_E_ALIGN;
+    rattn::AppendParams p{};
+    p.pool_k = pool_k;
+    p.pool_v = pool_v;
+    p.table = table;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.cur_len = cur_len;
+    p.T = n_new;
+    p.HK = d->n_kv_heads;
+    p.ps = d->page_size;
+    p.row_vec = (int)(d->head_dim * esize(d->dtype) / 16);
+    p.off = cow_src >= 0 ? (int)(cur_len % d->page_size) : 0;
+    p.cow_src = cow_src;
+    p.cow_dst = cow_dst;
+    return hip_status(rattn::launch_append_kv(p, static_cast<hipStream_t>(stream)));
 }
 
 int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,

@@ -208,3 +208,32 @@ struct PrefillParams {
 };
 
 }  // namespace rattn
+
+namespace rattn {
+
+// Low-rank cache projection of T new tokens (rattn_lr_project).  Output
+// column c of the workgroup grid belongs to set n = c / 2r, to Lk when
+// (c / r) % 2 == 0 and to Lv otherwise, component j = c % r.
+struct LrParams {
+    const void *x;        // [n_xsets, T, d_in]
+    const void *ak, *av;  // A^T of keys and values: [shared_a ? 1 : n_sets, r, d_in]
+    void *lk, *lv;        // [n_sets, cache_len, r]
+    int64_t T, pos0, cache_len;
+    int d_in, r, shared_a;
+    int n_xsets;          // 1 (one X for every set) or n_sets
+    int cols_per_xset;    // output columns one X set feeds: 2r per set it feeds
+};
+
+// Paged append of T new rows per KV head (rattn_append_kv); 16-byte vectors.
+struct AppendParams {
+    void *pool_k, *pool_v;        // [n_phys, H_kv, page, d]
+    const int32_t *table;         // the sequence's block table, already updated
+    const void *k_new, *v_new;    // [H_kv, T, d]
+    int64_t cur_len, T;
+    int HK, ps, row_vec;          // row_vec: 16-byte vectors per row (d * element size / 16)
+    int off;                      // rows copied from cow_src to cow_dst (cur_len % page, 0 without a copy)
+    int cow_src, cow_dst;
+};
+
+}  // namespace rattn
+

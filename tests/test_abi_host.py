@@ -20,7 +20,7 @@ FAKE = 0x10000  # never dereferenced: validation fails before any device call
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(rattn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|int64_t|void|const char \*)\s*(rattn_\w+)\s*\(", text, re.M)))
 
 
 def test_exports_every_declared_symbol():
