@@ -18,6 +18,9 @@ Contents
                        projection L = X A that fills the low-rank caches, the
                        logical rows of a paged pool, and the copy-on-write
                        rules an append of new base rows must obey.
+  * ``quant``       -- base keys as int8 codes with one scale per tensor
+                       (the quantiser, the dequantised keys, and fp64 inputs
+                       for ``attend`` with the keys dequantised).
 
 Every function here is pinned by ``tests/test_oracle_pins.py`` against facts the
 pages and the mathematics fix (brute force, closed forms, invariants, library
