@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define RATTN_VERSION 1
+#define RATTN_VERSION 2
 
 typedef enum rattn_status {
     RATTN_OK = 0,
@@ -68,6 +68,14 @@ typedef enum rattn_dtype {
     RATTN_F32 = 0, /* IEEE binary32 */
     RATTN_BF16 = 1 /* bfloat16 */
 } rattn_dtype;
+
+/* Storage of the base keys (rattn_desc.k_format). */
+typedef enum rattn_key_format {
+    RATTN_KEYS_DTYPE = 0, /* keys in the call's dtype, like the values */
+    RATTN_KEYS_INT8 = 1   /* int8 codes with one scale per tensor (PolyKV, section 2B): byte u holds
+                             code u - 128 (excess-128), key = k_scale * (u - 128); see
+                             rattn_quantize_keys */
+} rattn_key_format;
 
 typedef enum rattn_op {
     RATTN_OP_DECODE = 0,
@@ -89,6 +97,10 @@ typedef struct rattn_desc {
     int64_t n_phys_pages; /* pages in the pool (paged only) */
     int32_t dtype;        /* rattn_dtype of q, caches and up-projections */
     float sm_scale;       /* softmax scale; <= 0 means 1/sqrt(head_dim) */
+    int32_t k_format;     /* rattn_key_format of k_base (0: dtype).  RATTN_KEYS_INT8: bf16 decode,
+                             head_dim 128, priv_len 0 (else RATTN_E_UNSUPPORTED); k_base then holds
+                             one byte per element in the same layout */
+    float k_scale;        /* RATTN_KEYS_INT8: the keys' scale (> 0); else ignored */
 } rattn_desc;
 
 /* Tensors of one call.  Shapes use the descriptor's names. */
@@ -207,6 +219,20 @@ int rattn_gather_base(const rattn_desc *desc, const void *pool, const int32_t *b
 #define RATTN_STAGE_ALL 3u
 int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,
                            size_t workspace_bytes, void *stream, unsigned stages);
+
+/*
+ * Base keys to int8 codes with one scale per tensor (PolyKV, section 2B: keys
+ * in int8 with per-tensor linear quantisation; the shared pool is written once
+ * and read by every agent).  Over the n elements at k (device, dtype
+ * RATTN_BF16 or RATTN_F32, any layout: pass exactly the keys the scale must
+ * cover): amax = max |k|, *scale = amax / 127 (an fp64 division rounded once to
+ * fp32; 1 when amax = 0), and codes[i] = round-half-to-even(k[i] / scale) in
+ * fp64, clamped to [-127, 127], stored as the byte code + 128.  scale is a
+ * device pointer (one float, written on the stream; copy it to the host for
+ * rattn_desc.k_scale); codes (n bytes, device) keep k's layout.  Four kernel
+ * launches on `stream`; deterministic.  Inputs must be finite.
+ */
+int rattn_quantize_keys(const void *k, int64_t n, int32_t dtype, void *codes, float *scale, void *stream);
 
 /* ------------------------------------------------------------------------
  * The cache-write path: what fills the caches the attention calls read.

@@ -25,6 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "librattn.so")
 
 RATTN_F32, RATTN_BF16 = 0, 1
+RATTN_KEYS_DTYPE, RATTN_KEYS_INT8 = 0, 1
 RATTN_OP_DECODE, RATTN_OP_PREFILL = 0, 1
 STATUS = {0: "RATTN_OK", -1: "RATTN_E_NULL", -2: "RATTN_E_SHAPE", -3: "RATTN_E_UNSUPPORTED",
           -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP", -7: "RATTN_E_SCRATCH",
@@ -34,7 +35,8 @@ EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "ratt
            "rattn_decode_plan", "rattn_prefill_plan", "rattn_status_str", "rattn_version", "rattn_last_hip_error",
            "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
            "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
-           "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv")
+           "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv",
+           "rattn_quantize_keys")
 STAGE_SPLIT, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
 
 
@@ -54,6 +56,7 @@ class Desc(ctypes.Structure):
         ("prefix_len", ctypes.c_int64), ("priv_len", ctypes.c_int64),
         ("page_size", ctypes.c_int32), ("shared_lr", ctypes.c_int32),
         ("n_phys_pages", ctypes.c_int64), ("dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+        ("k_format", ctypes.c_int32), ("k_scale", ctypes.c_float),
     ]
 
 
@@ -120,7 +123,8 @@ def lib():
         L.rattn_pagepool_plan_append.argtypes = [P, I32P, I64, I64, I64, ctypes.c_int32, I32P, I32P]
         L.rattn_append_kv.argtypes = [ctypes.POINTER(Desc), P, P, P, I64, I64, P, P, ctypes.c_int32,
                                       ctypes.c_int32, P]
-        for f in ("rattn_lr_project", "rattn_pagepool_create", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
+        L.rattn_quantize_keys.argtypes = [P, I64, ctypes.c_int32, P, P, P]
+        for f in ("rattn_quantize_keys", "rattn_lr_project", "rattn_pagepool_create", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
                   "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append",
                   "rattn_append_kv"):
             getattr(L, f).restype = I
@@ -130,16 +134,18 @@ def lib():
                   "rattn_decode_plan", "rattn_prefill_plan", "rattn_version", "rattn_last_hip_error",
                   "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
            "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
-           "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv"):
+           "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv",
+           "rattn_quantize_keys"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
 
 
 def make_desc(*, n_agents, n_q_heads, n_kv_heads, head_dim, rank, q_len, prefix_len, priv_len=0, page_size=0,
-              shared_lr=False, n_phys_pages=0, dtype=RATTN_BF16, sm_scale=0.0) -> Desc:
+              shared_lr=False, n_phys_pages=0, dtype=RATTN_BF16, sm_scale=0.0, k_format=RATTN_KEYS_DTYPE,
+              k_scale=0.0) -> Desc:
     return Desc(n_agents, n_q_heads, n_kv_heads, head_dim, rank, q_len, prefix_len, priv_len, page_size,
-                int(bool(shared_lr)), n_phys_pages, dtype, sm_scale)
+                int(bool(shared_lr)), n_phys_pages, dtype, sm_scale, k_format, k_scale)
 
 
 def workspace_bytes(desc: Desc, op: int = RATTN_OP_DECODE) -> int:
@@ -175,6 +181,8 @@ def kernel_of(desc: Desc, op: int = RATTN_OP_DECODE) -> tuple:
     masked, twelve-wave form) or ("prefill", dtype, d, residual columns)."""
     p = plan(desc, op)
     dt = "bf16" if desc.dtype == RATTN_BF16 else "f32"
+    if desc.k_format == RATTN_KEYS_INT8:
+        dt += "-k8"
     if p["path"] == 1:
         return ("prefill", dt, desc.head_dim, p["resid_cols"])
     return ("split", dt, desc.head_dim, p["resid_cols"], bool(p["masked"]), p["waves"] > 8)
@@ -192,8 +200,9 @@ def _stream(stream):
 
 
 def describe(q, k_base, lk=None, bk=None, *, block_table=None, k_priv=None, prefix_len=None, shared_lr=None,
-             sm_scale=0.0, op=RATTN_OP_DECODE) -> Desc:
-    """Descriptor read off the tensors' shapes."""
+             sm_scale=0.0, op=RATTN_OP_DECODE, k_scale=None) -> Desc:
+    """Descriptor read off the tensors' shapes.  A uint8 k_base holds int8 key
+    codes (excess-128, RATTN_KEYS_INT8) whose scale ``k_scale`` must be given."""
     import torch
 
     if q.dim() != 4:
@@ -225,9 +234,14 @@ def describe(q, k_base, lk=None, bk=None, *, block_table=None, k_priv=None, pref
         dt = RATTN_F32
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
+    kf, ks = RATTN_KEYS_DTYPE, 0.0
+    if k_base is not None and k_base.dtype == torch.uint8:
+        if k_scale is None:
+            raise ValueError("int8 keys (uint8 k_base) need k_scale")
+        kf, ks = RATTN_KEYS_INT8, float(k_scale)
     return make_desc(n_agents=N, n_q_heads=HQ, n_kv_heads=HK, head_dim=D, rank=r, q_len=QL,
                      prefix_len=prefix_len, priv_len=S, page_size=ps, shared_lr=shared_lr,
-                     n_phys_pages=n_phys, dtype=dt, sm_scale=sm_scale)
+                     n_phys_pages=n_phys, dtype=dt, sm_scale=sm_scale, k_format=kf, k_scale=ks)
 
 
 def _check_tensors(desc: Desc, tensors: dict):
@@ -255,6 +269,8 @@ def _check_tensors(desc: Desc, tensors: dict):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
         exp_dt = torch.float32 if name in ("out", "lse") else (torch.int32 if name == "block_table" else dt)
+        if name == "k_base" and desc.k_format == RATTN_KEYS_INT8:
+            exp_dt = torch.uint8
         if t.dtype != exp_dt:
             raise TypeError(f"{name}: dtype {t.dtype}, expected {exp_dt}")
         if name in want and tuple(t.shape) != want[name]:
@@ -290,12 +306,12 @@ def workspace_for(nbytes: int, device, stream=None):
 
 
 def _run(fn_name, op, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_priv, shared_lr, out, lse,
-         workspace, sm_scale, prefix_len, stream, desc, stages=None):
+         workspace, sm_scale, prefix_len, stream, desc, stages=None, k_scale=None):
     import torch
 
     if desc is None:
         desc = describe(q, k_base, lk, bk, block_table=block_table, k_priv=k_priv, prefix_len=prefix_len,
-                        shared_lr=shared_lr, sm_scale=sm_scale, op=op)
+                        shared_lr=shared_lr, sm_scale=sm_scale, op=op, k_scale=k_scale)
     if out is None:
         out = torch.empty(tuple(q.shape), device=q.device, dtype=torch.float32)
     tensors = dict(q=q, k_base=k_base, v_base=v_base, block_table=block_table, lk=lk, lv=lv, bk=bk, bv=bv,
@@ -359,6 +375,28 @@ def decode_noalloc(inputs: dict, *, shared_lr=None, prefix_len=None, out, lse=No
     if st:
         raise RattnError(st, "rattn_decode_noalloc")
     return out
+
+
+def quantize_keys(k, *, codes=None, scale=None, stream=None):
+    """rattn_quantize_keys: int8 codes (uint8, excess-128) of the device tensor k
+    (bf16 or fp32, every element covered by the one scale) and the scale as a
+    one-element device tensor.  Returns (codes, scale)."""
+    import torch
+
+    if not k.is_cuda or not k.is_contiguous():
+        raise ValueError("k must be a contiguous GPU tensor")
+    if codes is None:
+        codes = torch.empty(tuple(k.shape), device=k.device, dtype=torch.uint8)
+    if scale is None:
+        scale = torch.empty(1, device=k.device, dtype=torch.float32)
+    dt = RATTN_BF16 if k.dtype == torch.bfloat16 else RATTN_F32
+    if codes.numel() != k.numel() or codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous uint8 tensor of k's size")
+    st = lib().rattn_quantize_keys(k.data_ptr(), k.numel(), dt, codes.data_ptr(), scale.data_ptr(),
+                                   _stream(stream))
+    if st:
+        raise RattnError(st, "rattn_quantize_keys")
+    return codes, scale
 
 
 def lr_project(x, ak_t, av_t, lk, lv, *, pos0: int = 0, stream=None):
@@ -509,9 +547,10 @@ def gather_base(pool, block_table, prefix_len: int, *, out=None, stream=None):
 
 
 def attend(inputs: dict, *, mode: str = "decode", shared_lr=None, prefix_len=None, out=None, lse=None,
-           workspace=None, stream=None, desc=None, stages=None):
+           workspace=None, stream=None, desc=None, stages=None, k_scale=None):
     """Runs decode or prefill on a dict of device tensors named as in the layouts above.
-    ``stages`` (a mask of STAGE_*) runs only those launches through rattn_attention_stages."""
+    ``stages`` (a mask of STAGE_*) runs only those launches through rattn_attention_stages.
+    A uint8 ``k_base`` holds int8 key codes with scale ``k_scale``."""
     if mode == "decode":
         fn_name, op = "rattn_decode", RATTN_OP_DECODE
     else:
@@ -519,4 +558,4 @@ def attend(inputs: dict, *, mode: str = "decode", shared_lr=None, prefix_len=Non
     g = inputs.get
     return _run(fn_name, op, inputs["q"], g("k_base"), g("v_base"), g("lk"), g("lv"), g("bk"), g("bv"),
                 g("block_table"), g("k_priv"), g("v_priv"), shared_lr, out, lse, workspace, 0.0, prefix_len, stream,
-                desc, stages)
+                desc, stages, k_scale)

@@ -18,6 +18,7 @@ hipError_t launch_prefill(const PrefillParams &pp, int D, int cpad, size_t lds, 
 hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_lr_project(const LrParams &p, hipStream_t st);
 hipError_t launch_append_kv(const AppendParams &p, hipStream_t st);
+hipError_t launch_quantize(const void *k, int64_t n, int bf16_in, void *codes, float *scale, hipStream_t st);
 }  // namespace rattn
 
 static_assert(rattn::kNoAllocScratchBytes == RATTN_NOALLOC_SCRATCH_BYTES, "static scratch size in the header");
@@ -65,6 +66,14 @@ int check_desc(const rattn_desc *d, int op) {
     }
     if (op == RATTN_OP_PREFILL && d->q_len != d->priv_len) return RATTN_E_SHAPE;
     if (op != RATTN_OP_DECODE && op != RATTN_OP_PREFILL) return RATTN_E_SHAPE;
+    if (d->k_format != RATTN_KEYS_DTYPE && d->k_format != RATTN_KEYS_INT8) return RATTN_E_SHAPE;
+    if (d->k_format == RATTN_KEYS_INT8) {
+        if (!(d->k_scale > 0.f && d->k_scale <= 3.0e38f)) return RATTN_E_SHAPE;
+        // int8 base keys: bf16 decode over a shared prefix, d = 128, no private tokens
+        if (d->dtype != RATTN_BF16 || d->head_dim != 128 || d->priv_len != 0 || d->prefix_len < 1 ||
+            op != RATTN_OP_DECODE)
+            return RATTN_E_UNSUPPORTED;
+    }
     // Index arithmetic inside the kernels uses 32-bit row and item counts.
     const int64_t rows = (int64_t)d->n_agents * d->q_len * d->n_q_heads;
     if (rows > (1ll << 28) || d->prefix_len > (1ll << 30) || d->priv_len > (1ll << 30))
@@ -104,6 +113,12 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     p.lr_own = RATTN_LR_OWN;
     const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
     p.c = scale * 1.44269504088896340736f;
+    p.kq8 = d->k_format == RATTN_KEYS_INT8;
+    p.u_scale = 1.0f;
+    if (p.kq8) {  // scores in code units: the exponent's scale takes the key scale, U its inverse
+        p.c = (float)((double)scale * 1.44269504088896340736 * (double)d->k_scale);
+        p.u_scale = (float)(1.0 / (double)d->k_scale);
+    }
 
     // The decomposition: the masked mode first where it applies, else (or when
     // its ring does not fit) block-diagonal residual columns.
@@ -141,7 +156,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         if (!rattn::split_ok(d->dtype == RATTN_BF16, D, pl->cpad)) return RATTN_E_UNSUPPORTED;
 
         const int es = (int)esize(d->dtype);
-        const int kv_row = D * es;  // bytes of one key (or value) row
+        const int kv_row = D * es;                   // bytes of one value row (and key row, unquantised)
+        const int k_row = p.kq8 ? D : kv_row;         // bytes of one key row (int8: one per element)
         // Row groups of bpg blocks: the agents of a group, and the low-rank bytes per
         // token a stage holds for them (or for the shared cache).
         int ag_max = 1, nb_min = 4, nb_max = 1, lr_row = 0;
@@ -215,13 +231,14 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         auto max_fpw = [&](int T, int H, int lr_row_bytes, int np) {
             const int G = T / 16, nkv = 2 * H * G, npairs = nkv + (lr_row_bytes ? 2 * G : 0);
             const int n_kv = (16 * (kv_row / 16)) / 64, n_lr = (16 * (lr_row_bytes / 16) + 63) / 64;
+            const int n_k = (16 * (k_row / 16)) / 64;  // K pairs (the first H G) take n_k loads
             const bool own = p.lr_own && lr_row_bytes && np >= 2;  // as make_fill_plan
             int mx = 0;
             for (int w = 0; w < np; ++w) {
                 int f = 0;
                 const int b = own ? (w == np - 1 ? nkv : w) : w, e = own && w < np - 1 ? nkv : npairs;
                 const int st = own ? (w == np - 1 ? 1 : np - 1) : np;
-                for (int pi = b; pi < e; pi += st) f += pi < nkv ? n_kv : n_lr;
+                for (int pi = b; pi < e; pi += st) f += pi < H * G ? n_k : pi < nkv ? n_kv : n_lr;
                 if (f > mx) mx = f;
             }
             return mx;
@@ -232,7 +249,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             // are back-pressured at issue, so large tiles stream faster from more
             // waves.  More if the outstanding-load limit needs them, then fewer stages.
             const int G = T / 16;
-            const int tile_loads = 2 * H * G * ((16 * (kv_row / 16)) / 64) +
+            const int tile_loads = H * G * ((16 * (kv_row / 16)) / 64 + (16 * (k_row / 16)) / 64) +
                                    (lr_row_bytes ? 2 * G * ((16 * (lr_row_bytes / 16) + 63) / 64) : 0);
             const int np0 = tile_loads >= 40 && p.nw + 4 <= 12 ? 4 : (p.lr_own ? 3 : 2);
             for (int np = np0; np <= 4; np += 1) {
@@ -262,7 +279,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             auto pick = [&](int tg_max, int H, int lr_row_bytes, int need, int *T, int *nst, int *stage) {
                 for (int t = 128; t >= 16; t /= 2) {
                     if (t % (16 * tg_max) || t > 16 * nw) continue;  // the fill gives each 16-row group one wave
-                    const int sb = t * (2 * H * kv_row + 2 * lr_row_bytes);
+                    const int sb = t * (H * (k_row + kv_row) + 2 * lr_row_bytes);
                     const int n = (rattn::kLdsMax - table_bytes) / sb;
                     if (n >= 3 || (t == 16 * tg_max && n >= need)) {
                         *T = t;
@@ -337,7 +354,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
                 // Preference: a prefix tile of 32 or more tokens (the per-tile
                 // synchronisation is a large share of a tile's time), then the
                 // fewest bytes staged per context token, then more heads per item.
-                const int64_t bytes = (int64_t)p.n_rg * HK * 2 * kv_row + (int64_t)p.n_hg * p.n_rg * 2 * lr_row;
+                const int64_t bytes = (int64_t)p.n_rg * HK * (k_row + kv_row) + (int64_t)p.n_hg * p.n_rg * 2 * lr_row;
                 const int64_t cost = (L > 0 && p.T_pre < 32 ? (int64_t)1 << 40 : 0) + bytes * 16 + (8 - p.H);
                 if (best_cost < 0 || cost < best_cost) {
                     best_cost = cost;
@@ -733,6 +750,14 @@ int rattn_append_kv(const rattn_desc *d, void *pool_k, void *pool_v, const int32
     p.cow_src = cow_src;
     p.cow_dst = cow_dst;
     return hip_status(rattn::launch_append_kv(p, static_cast<hipStream_t>(stream)));
+}
+
+int rattn_quantize_keys(const void *k, int64_t n, int32_t dtype, void *codes, float *scale, void *stream) {
+    if (n < 1) return RATTN_E_SHAPE;
+    if (dtype != RATTN_F32 && dtype != RATTN_BF16) return RATTN_E_UNSUPPORTED;
+    if (!k || !codes || !scale) return RATTN_E_NULL;
+    if (!aligned(k, esize(dtype)) || !aligned(scale, 4)) return RATTN_E_ALIGN;
+    return hip_status(rattn::launch_quantize(k, n, dtype == RATTN_BF16, codes, scale, static_cast<hipStream_t>(stream)));
 }
 
 int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,

@@ -167,24 +167,40 @@ __device__ inline void step16(Acc<T, D, CPAD> &acc, const ReadOfs<T, D, CPAD> &r
 // the number of agents.
 // arow: the agent (0 .. na-1 within the tile) of this lane's row, -1 if none;
 // ast: LDS bytes from one agent's low-rank rows to the next.
-template <int D, int CPAD, bool MASKED>
+// KQ8: the keys are excess-128 int8 codes (kb: the K rows, vb: the V rows of
+// the step; without KQ8 both are kvb) met by the fp16 query rows qH; kinit
+// starts each row's score at minus 1152 times the sum of its fp16 query
+// (so the product gives q . code), and U arrives divided by the key scale.
+template <int D, int CPAD, bool MASKED, bool KQ8 = false>
 __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, D, CPAD> &ro, const uint32_t *vtr,
                                    const uint32_t *wtr, const char *kvb, const char *lrb, int t, bool masked,
                                    const Ops<bf16>::frag *qB, const Ops<bf16>::frag *uH, const Ops<bf16>::frag *uL,
                                    float cl2, bool resid, int t1, bool causal, int tq, int j4, int na, int arow,
-                                   int ast) {
+                                   int ast, const char *vb = nullptr, const f16x8 *qH = nullptr,
+                                   float kinit = 0.0f) {
     using O = Ops<bf16>;
     using frag = O::frag;
     using frag4 = O::frag4;
     constexpr int KS = D / 32, VPL = D / 16;
     constexpr int CS = CPAD / 32, CPL = CPAD / 16;
     constexpr int CSx = CS > 0 ? CS : 1;
+    if constexpr (!KQ8) vb = kvb;
 
     frag kf[KS], lf[CSx];
+    f16x8 kh[KQ8 ? KS : 1];
+    if constexpr (KQ8) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-        const Row<bf16, 8> kr = lds_get<bf16, 8>(kvb, ro.k[s]);
-        __builtin_memcpy(&kf[s], &kr, sizeof(frag));
+        for (int s = 0; s < KS; ++s) {
+            uint32_t w[2];
+            __builtin_memcpy(w, __builtin_assume_aligned(kvb + ro.k[s][0], 8), 8);
+            kh[s] = codes_to_f16(w[0], w[1]);
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            const Row<bf16, 8> kr = lds_get<bf16, 8>(kvb, ro.k[s]);
+            __builtin_memcpy(&kf[s], &kr, sizeof(frag));
+        }
     }
     if (CS > 0 && resid) {
 #pragma unroll
@@ -196,13 +212,20 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     // S^T = K Q^T + Lk U^T, raw, in two independent accumulator chains (even
     // and odd contraction steps, U hi and U lo) so that consecutive MFMAs do not
     // wait for each other's results; summed once at the end
-    f32x4 a = {0.f, 0.f, 0.f, 0.f}, a2 = {0.f, 0.f, 0.f, 0.f};
+    f32x4 a = {kinit, kinit, kinit, kinit}, a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-        if (s & 1)
-            a2 = O::mma(kf[s], qB[s], a2);
-        else
-            a = O::mma(kf[s], qB[s], a);
+        if constexpr (KQ8) {
+            if (s & 1)
+                a2 = mma_f16(kh[s], qH[s], a2);
+            else
+                a = mma_f16(kh[s], qH[s], a);
+        } else {
+            if (s & 1)
+                a2 = O::mma(kf[s], qB[s], a2);
+            else
+                a = O::mma(kf[s], qB[s], a);
+        }
     }
     if (CS > 0 && resid) {
         if constexpr (MASKED) {
@@ -238,7 +261,7 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     // value operands: issued now, consumed after the softmax
     bf16x4 va[VPL];
 #pragma unroll
-    for (int jj = 0; jj < VPL; ++jj) va[jj] = lds_tr4(kvb + vtr[jj]);
+    for (int jj = 0; jj < VPL; ++jj) va[jj] = lds_tr4(vb + vtr[jj]);
     bf16x4 wa[CPL > 0 ? CPL : 1];
     if constexpr (CPL > 0) {
         if (resid) {
@@ -328,16 +351,20 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
 // MASKED (bf16, per-agent caches of rank CPAD >= 32 with several agents per
 // 16-row block): U and W hold CPAD columns and the rank-r products run per agent
 // of the block (see step16_bf16).
-template <typename T, int D, int CPAD, bool MASKED, int MAXW>
+// KQ8 (bf16 only): base keys are excess-128 int8 codes with one scale; only
+// prefix items exist then (no private tokens).
+template <typename T, int D, int CPAD, bool MASKED, int MAXW, bool KQ8 = false>
 __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p) {
     using O = Ops<T>;
     using frag = typename O::frag;
+    static_assert(!KQ8 || sizeof(T) == 2, "int8 keys with bf16 queries and values only");
     constexpr int KS = D / 32;
     constexpr int VPL = D / 16;
     constexpr int CS = CPAD / 32;
     constexpr int CSx = CS > 0 ? CS : 1;
     constexpr int CPLx = CPAD > 0 ? CPAD / 16 : 1;
     constexpr int ES = (int)sizeof(T);
+    constexpr int KRE = KQ8 ? D / 2 : D;  // elements of T per staged K row (int8: two codes each)
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
     touch_params<DecodeParams>();
@@ -418,6 +445,8 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     g.stage_bytes = prefix ? p.stage_bytes_pre : p.stage_bytes_pv;
     g.cpr_kv = D * ES / 16;
     g.lg_kv = ilog2(g.cpr_kv);
+    g.cpr_k = KRE * ES / 16;
+    g.lg_k = ilog2(g.cpr_k);
     if (resid) {
         g.cpa_lr = p.r * ES / 16;
         g.lg_lr = ilog2(g.cpa_lr);
@@ -429,8 +458,8 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     }
     g.lr_grp = 16 * g.na_lr * g.cpa_lr;
     g.H = nh;
-    g.ofs_v = nh * g.T * g.cpr_kv;
-    g.ofs_lk = 2 * nh * g.T * g.cpr_kv;
+    g.ofs_v = nh * g.T * g.cpr_k;
+    g.ofs_lk = g.ofs_v + nh * g.T * g.cpr_kv;
     g.ofs_lv = g.ofs_lk + (resid ? (g.T >> 4) * g.lr_grp : 0);
     g.chunks = g.ofs_lv + (resid ? (g.T >> 4) * g.lr_grp : 0);
 
@@ -442,6 +471,8 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     src.lr_agent_stride = 0;
     src.head_stride = 0;
     src.page_stride = 0;
+    src.k_head_stride = 0;
+    src.k_page_stride = 0;
     src.fps = p.fd_ps;
     src.pg0 = 0;
     src.pages = s_pages;
@@ -450,14 +481,17 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         src.vb = static_cast<const T *>(p.vb);
         if (p.ps > 0) {
             src.page_stride = (int64_t)p.HK * p.ps * D;
-            src.kb += (int64_t)k0 * p.ps * D;
+            src.k_page_stride = (int64_t)p.HK * p.ps * KRE;
+            src.kb += (int64_t)k0 * p.ps * KRE;
             src.vb += (int64_t)k0 * p.ps * D;
             src.head_stride = (int64_t)p.ps * D;
+            src.k_head_stride = (int64_t)p.ps * KRE;
             src.pg0 = fdiv(t0, p.fd_ps);
         } else {
-            src.kb += (int64_t)k0 * p.L * D;
+            src.kb += (int64_t)k0 * p.L * KRE;
             src.vb += (int64_t)k0 * p.L * D;
             src.head_stride = p.L * D;
+            src.k_head_stride = p.L * KRE;
         }
         if (resid) {
             const int64_t a_lr = p.shared_lr ? 0 : a_lo;
@@ -470,6 +504,9 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         src.kb = static_cast<const T *>(p.kp) + seg;
         src.vb = static_cast<const T *>(p.vp) + seg;
     }
+    if constexpr (KQ8) {
+        if (!prefix) return;  // never planned: int8 keys come without private tokens
+    }
     if (src.page_stride && t1 > t0) {
         // the split's page-table entries, read once into LDS
         const int npg = fdiv(t1 - 1, p.fd_ps) - src.pg0 + 1;
@@ -480,14 +517,14 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     // The fill plan of this wave.
     const bool compute_wave = wave < p.nw;  // the others only load
     FillPlan fp;
-    make_fill_plan<T, D>(fp, g, src, resid, compute_wave ? p.np : wave - p.nw, lane, p.np, p.lr_own != 0);
+    make_fill_plan<T, D, KRE>(fp, g, src, resid, compute_wave ? p.np : wave - p.nw, lane, p.np, p.lr_own != 0);
     // keys and values that no other workgroup reads are streamed past the caches
     fp.kv_nt = prefix ? p.n_rg == 1 : p.n_prg == 1;
     const int n_tiles = (t1 - t0 + g.T - 1) >> ilog2(g.T);  // T is a power of two
     const int fpw = fp.fpw;
     auto fill = [&](int tile, int stage) {
         const int tt = t0 + tile * g.T;
-        fill_stage<T, D>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
+        fill_stage<T, D, KRE>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
     };
     // ---- the load waves start the ring (tiles 0 .. nst-2) at once, before the
     // compute waves set up their rows, load the queries and form U
@@ -538,7 +575,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
 
     // ---- lane offsets of this wave's LDS reads: its head's K and V regions
     // of the stage (chunks)
-    const int kreg = hw * g.T * g.cpr_kv, vreg = g.ofs_v + hw * g.T * g.cpr_kv;
+    const int kreg = hw * g.T * g.cpr_k, vreg = g.ofs_v + hw * g.T * g.cpr_kv;
     ReadOfs<T, D, CPAD> ro;
     {
         using RO = ReadOfs<T, D, CPAD>;
@@ -546,7 +583,8 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int c = 0; c < RO::FC; ++c)
-                ro.k[s][c] = elem_ofs(kreg, n16, (32 * s + 8 * j4) * ES + 16 * c, g.cpr_kv, g.lg_kv);
+                ro.k[s][c] = KQ8 ? elem_ofs(kreg, n16, 32 * s + 8 * j4, g.cpr_k, g.lg_k)  // 8 code bytes
+                                 : elem_ofs(kreg, n16, (32 * s + 8 * j4) * ES + 16 * c, g.cpr_k, g.lg_k);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -570,6 +608,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
                     resid ? lr_ofs(g, g.ofs_lv, colv >> p.lr_shift, 4 * j4 + i, (colv & (p.r - 1)) * ES + 16 * c) : 0u;
     }
     const int kv_rowb = D * ES, lr_rowb = 16 * g.na_lr * g.cpa_lr;  // a step at row0 starts row0 * these bytes in
+    const int k_rowb = KRE * ES;                                       // (K rows: k_rowb)
     // bf16 step: transposed value reads.  For d-tile jj, lane (4i + a, j4) points at
     // row 4*j4 + i, columns 16*jj + 4a (residual columns of the block; padding
     // columns read column 0 of the block, their W is dropped at the store).
@@ -591,7 +630,9 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     // results land in its own B-operand slots.
     frag uH[CSx], uL[CSx];
     constexpr bool kBf16 = sizeof(T) == 2;
-    const float uscale = kBf16 ? 1.0f : cl2;  // the bf16 step folds the scale into the exponent
+    // the bf16 step folds the scale into the exponent; with int8 keys the
+    // exponent's scale includes the key scale, so U is divided by it
+    const float uscale = KQ8 ? p.u_scale : kBf16 ? 1.0f : cl2;
 #pragma unroll
     for (int s = 0; s < CSx; ++s) {
         uH[s] = O::zero();
@@ -756,6 +797,24 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         }
     }
 
+    // int8 keys: the query rows as fp16 (exact for bf16 values of normal range)
+    // and each row's score offset, minus 1152 times the sum of those values
+    f16x8 qH[KQ8 ? KS : 1];
+    float kinit = 0.0f;
+    if constexpr (KQ8) {
+        if (compute_wave) wait_vmcnt(0);
+        float qs = 0.0f;
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const f16 h = (f16)(float)qB[s].v[i];
+                qH[s][i] = h;
+                qs += (float)h;
+            }
+        kinit = -1152.0f * row_sum4(qs);
+    }
+
     // Every register load (q, Bk) of a compute wave has landed, so the compiler
     // has nothing pending inside the ring loop and adds no waits of its own there.
     if (compute_wave) wait_vmcnt(0);
@@ -782,7 +841,15 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
             const bool masked = causal || tt + g.T > t1;
             for (int u = 0; u < spw; ++u) {
                 const int row0 = 16 * (tg * spw + u);
-                if constexpr (kBf16) {
+                if constexpr (KQ8) {
+                    // K rows (int8) and V rows have different pitches: two stage bases
+                    const int ko = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * k_rowb);
+                    const int vo = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * kv_rowb);
+                    const int lo = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * lr_rowb);
+                    step16_bf16<D, CPAD, MASKED, true>(acc, ro, vtr, wtr, smem + ko, smem + lo, tt + row0, masked,
+                                                       qB, uH, uL, cl2, resid, t1, causal, tq, j4, blk.na,
+                                                       vm ? arow_m : -1, 256 * g.cpa_lr, smem + vo, qH, kinit);
+                } else if constexpr (kBf16) {
                     // the step's stage offsets as opaque wave-uniform values: one add per
                     // operand read, rather than per-read offsets advanced every step
                     const int ko = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * kv_rowb);
@@ -1101,13 +1168,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 
 // ---------------------------------------------------------------- launchers --
 
-template <typename T, int D, int CP, bool M, int W>
+template <typename T, int D, int CP, bool M, int W, bool Q>
 struct SplitSlot {};
 
-template <typename T, int D, int CP, bool M, int W>
+template <typename T, int D, int CP, bool M, int W, bool Q = false>
 static hipError_t launch_split_w(const DecodeParams &dp, size_t lds, hipStream_t st) {
-    auto *fn = decode_split_kernel<T, D, CP, M, W>;
-    const hipError_t e = ensure_lds<SplitSlot<T, D, CP, M, W>>(reinterpret_cast<const void *>(fn), (int)lds);
+    auto *fn = decode_split_kernel<T, D, CP, M, W, Q>;
+    const hipError_t e = ensure_lds<SplitSlot<T, D, CP, M, W, Q>>(reinterpret_cast<const void *>(fn), (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3(8 * dp.per_xcd), dim3(64 * (dp.nw + dp.np)), lds, st, dp);
     return hipGetLastError();
@@ -1115,15 +1182,15 @@ static hipError_t launch_split_w(const DecodeParams &dp, size_t lds, hipStream_t
 
 // Only the instantiations that fit in registers (split_ok, split_wide_ok) exist;
 // the planner never asks for another.
-template <typename T, int D, int CP, bool M>
+template <typename T, int D, int CP, bool M, bool Q = false>
 static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t st) {
     constexpr bool kBf = sizeof(T) == 2;
-    if constexpr (!split_ok(kBf, D, CP)) {
+    if constexpr (!split_ok(kBf, D, CP) || (Q && (!kBf || D != 128))) {
         return hipErrorInvalidValue;
     } else {
-        if (dp.nw + dp.np <= 8) return launch_split_w<T, D, CP, M, 8>(dp, lds, st);
+        if (dp.nw + dp.np <= 8) return launch_split_w<T, D, CP, M, 8, Q>(dp, lds, st);
         if constexpr (split_wide_ok(kBf, D, CP))
-            return launch_split_w<T, D, CP, M, 12>(dp, lds, st);
+            return launch_split_w<T, D, CP, M, 12, Q>(dp, lds, st);
         else
             return hipErrorInvalidValue;
     }
@@ -1132,6 +1199,22 @@ static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t s
 template <typename T>
 static hipError_t launch_split_t(const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
+        if (dp.kq8) {  // int8 base keys: d = 128 only
+            if (D != 128) return hipErrorInvalidValue;
+            if (dp.masked) {
+                switch (cpad) {
+                    case 32: return launch_split<T, 128, 32, true, true>(dp, lds, st);
+                    case 64: return launch_split<T, 128, 64, true, true>(dp, lds, st);
+                    default: return launch_split<T, 128, 128, true, true>(dp, lds, st);
+                }
+            }
+            switch (cpad) {
+                case 0: return launch_split<T, 128, 0, false, true>(dp, lds, st);
+                case 32: return launch_split<T, 128, 32, false, true>(dp, lds, st);
+                case 64: return launch_split<T, 128, 64, false, true>(dp, lds, st);
+                default: return launch_split<T, 128, 128, false, true>(dp, lds, st);
+            }
+        }
         if (dp.masked) {  // per-agent caches of rank cpad >= 32, several agents per block
             if (D == 128) {
                 switch (cpad) {

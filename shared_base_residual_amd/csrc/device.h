@@ -138,6 +138,31 @@ struct Ops<float> {
 
 __device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---- int8 keys -------------------------------------------------------------
+//
+// Base keys stored as excess-128 int8 codes (byte u = code + 128) enter the
+// score product as fp16 values 1024 + u = 1152 + code, which are exact: a byte
+// permute builds {0x64, u_1, 0x64, u_0} for each pair of codes, and 0x64uu is
+// the fp16 number 1024 + uu.  The query rows meet them in an fp16 MFMA; the
+// constant 1152 * sum(q) per query row is taken off by starting the score
+// accumulator at minus that value.
+typedef _Float16 f16;
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline f16x8 codes_to_f16(uint32_t w0, uint32_t w1) {
+    constexpr uint32_t kHi = 0x64646464u;  // v_perm_b32 selectors 4..7 take bytes of the first operand
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(kHi, w0, 0x04010400u);  // {0x64, w0.b1, 0x64, w0.b0}
+    r[1] = __builtin_amdgcn_perm(kHi, w0, 0x04030402u);  // {0x64, w0.b3, 0x64, w0.b2}
+    r[2] = __builtin_amdgcn_perm(kHi, w1, 0x04010400u);
+    r[3] = __builtin_amdgcn_perm(kHi, w1, 0x04030402u);
+    return __builtin_bit_cast(f16x8, r);
+}
+
+__device__ inline f32x4 mma_f16(const f16x8 &a, const f16x8 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 // Four floats to bf16 (round to nearest even).
 __device__ inline bf16x4 to_bf16x4(float a, float b, float c, float d) {
     const bf16x2 x = __builtin_convertvector(f32x2{a, b}, bf16x2);
@@ -291,6 +316,15 @@ __device__ inline float row_max4(float x) {
     x = amax(__uint_as_float(a[0]), __uint_as_float(a[1]));
     const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return amax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum over the four lanes l, l^16, l^32, l^48 (one query row's lanes), with
+// the gfx950 lane swaps.
+__device__ inline float row_sum4(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Sum over the lanes l' of the wave with l' = l (mod g), g a power of two in

@@ -138,7 +138,9 @@ struct DecodeParams {
     int64_t L, S;     // < 2^30 (validated on the host)
     int N, QL, HQ, HK, g, r, lr_shift, rpa, apb, bpa, ps, shared_lr;
     int causal;       // private token j is visible to query token t only if j <= t
-    float c;          // softmax scale * log2(e)
+    float c;          // softmax scale * log2(e) (times the key scale with int8 keys)
+    int kq8;          // base keys are excess-128 int8 codes with one scale (no private tokens then)
+    float u_scale;    // int8 keys: 1 / key scale, applied to U so that the correction adds to code scores
     int n_blocks, n_rg, n_ps;
     int H, n_hg;      // KV heads per prefix item (sharing its low-rank tile), head groups
     int bpg;          // 16-row blocks per prefix row group (1, 2 or 4)

@@ -176,6 +176,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         g.stage_bytes = pre ? p.stage_bytes_pre : p.stage_bytes_ch;
         g.cpr_kv = D * ES / 16;
         g.lg_kv = ilog2(g.cpr_kv);
+        g.cpr_k = g.cpr_kv;
+        g.lg_k = g.lg_kv;
         if (res) {
             g.cpa_lr = p.r * ES / 16;
             g.lg_lr = ilog2(g.cpa_lr);
@@ -199,6 +201,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         src.lr_agent_stride = 0;
         src.head_stride = 0;
         src.page_stride = 0;
+        src.k_head_stride = 0;
+        src.k_page_stride = 0;
         src.fps = p.fd_ps;
         src.pg0 = 0;
         src.pages = s_pages;
@@ -216,6 +220,8 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                 src.kb += (int64_t)k * p.L * D;
                 src.vb += (int64_t)k * p.L * D;
             }
+            src.k_page_stride = src.page_stride;
+            src.k_head_stride = src.head_stride;
             if (res) {
                 const int64_t a_lr = p.shared_lr ? 0 : a;
                 src.lk = static_cast<const T *>(p.lk) + a_lr * p.L * p.r;

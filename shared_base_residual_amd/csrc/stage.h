@@ -18,11 +18,13 @@ namespace rattn {
 struct Geo {
     int T;                    // tokens per stage
     int nst;                  // stages in the ring
-    int cpr_kv, lg_kv;        // chunks per K (or V) row, its log2
+    int cpr_kv, lg_kv;        // chunks per V row (and K row with unquantised keys), its log2
+    int cpr_k, lg_k;          // chunks per K row (fewer with int8 keys), its log2
     int cpa_lr, lg_lr;        // chunks per low-rank row of one agent (r * sizeof(T) / 16), its log2
     int na_lr;                // agents in the low-rank regions
     int lr_grp;               // chunks of one 16-token group of a low-rank region (16 * na_lr * cpa_lr)
-    int H;                    // KV heads staged: K regions 0..H-1, then V regions, then Lk, Lv
+    int H;                    // KV heads staged: K regions 0..H-1 (T rows of cpr_k chunks each),
+                              // then V regions (T rows of cpr_kv), then Lk, Lv
     int ofs_v, ofs_lk, ofs_lv;  // region offsets (chunks): V of head 0, Lk, Lv
     int chunks;               // chunks per stage
     int stage_bytes;          // stride between stages
@@ -40,8 +42,10 @@ __device__ inline int small_div(int n, int d) {
 template <typename T>
 struct Src {
     const T *kb, *vb;         // contiguous: the first head's rows; paged: pool + that head's offset
-    int64_t head_stride;      // elements from one staged head to the next
-    int64_t page_stride;      // paged: elements per physical page (0: contiguous)
+    int64_t head_stride;      // V (and unquantised K): elements from one staged head to the next
+    int64_t page_stride;      // V (and unquantised K), paged: elements per physical page (0: contiguous)
+    int64_t k_head_stride;    // the same for K, in elements of T (int8 keys: two codes per element)
+    int64_t k_page_stride;
     FastDiv fps;              // page size (paged)
     int pg0;                  // first logical page of the split
     const int *pages;         // LDS copy of the split's page-table entries (paged)
@@ -51,14 +55,16 @@ struct Src {
     int tlast;                // last valid token of the item
 };
 
-template <typename T, int D>
-__device__ inline const T *kv_row(const Src<T> &s, const T *base, int tok) {
-    if (s.page_stride) {
+// Row `tok` of a K or V region source: RE elements of T per row, page_stride
+// elements per physical page (0: contiguous).
+template <typename T, int RE>
+__device__ inline const T *kv_row(const Src<T> &s, const T *base, int tok, int64_t page_stride) {
+    if (page_stride) {
         const int lp = fdiv(tok, s.fps);
         const int64_t pg = s.pages[lp - s.pg0];
-        return base + pg * s.page_stride + (int64_t)(tok - lp * s.fps.d) * D;
+        return base + pg * page_stride + (int64_t)(tok - lp * s.fps.d) * RE;
     }
-    return base + (int64_t)tok * D;
+    return base + (int64_t)tok * RE;
 }
 
 // ------------------------------------------------------------ stage fill --
@@ -80,32 +86,34 @@ struct FillPlan {
     int G, lgG;               // groups per tile (a power of two), its log2
     int npairs;               // (region, group) pairs per tile
     int pbeg, pend, pstep;    // the pairs this wave fills: pbeg, pbeg + pstep, ... < pend
-    int n_kv, n_lr;           // loads per group of a K/V region, of an Lk/Lv region
+    int n_kv, n_lr;           // loads per group of a V (and unquantised K) region, of an Lk/Lv region
+    int n_k;                  // loads per group of a K region
     int fpw;                  // loads this wave issues per stage
     uint32_t lr_stride;       // bytes between agents' low-rank caches
     bool kv_nt;               // K/V rows are read by this workgroup only: stream them
-    uint32_t kv_off[kMaxKvLoads];  // lane byte offset of K/V load i from the group's first row
+    uint32_t kv_off[kMaxKvLoads];  // lane byte offset of V (or K) load i from the group's first row
                                    // (only the first d * sizeof(T) / 64 are set and used)
+    uint32_t k_off[kMaxKvLoads];   // the same for K rows of KRE elements
 };
 
 // Lane byte offset of K/V load i of a group from the group's first row, and the
 // lane's row within the group.  Recomputed per load (a few integer operations)
 // rather than kept in registers.
-template <typename T, int D>
-__device__ inline uint32_t kv_lane_off(const Geo &g, int i, int lane, int *row_out) {
-    constexpr int ES = (int)sizeof(T);
+// cpr, lg: chunks per row of the region and its log2; rowb: bytes per row.
+__device__ inline uint32_t kv_lane_off(int cpr, int lg, int rowb, int i, int lane, int *row_out) {
     const int q = 64 * i + lane;
-    const int row = q >> g.lg_kv;
-    const int c = swz(row, q & (g.cpr_kv - 1), g.cpr_kv, g.lg_kv);
+    const int row = q >> lg;
+    const int c = swz(row, q & (cpr - 1), cpr, lg);
     *row_out = row;
-    return (uint32_t)(row * D * ES + 16 * c);
+    return (uint32_t)(row * rowb + 16 * c);
 }
 
 // wave: index among the nw filling waves (a wave with wave >= nw fills nothing).
 // lr_own: with a residual and nw >= 2, the last filling wave fills every
 // low-rank pair and the others share the K/V pairs, so that low-rank rows
 // (mostly L2 hits) do not queue behind HBM reads in one wave's load order.
-template <typename T, int D>
+// KRE: elements of T per K row (D, or D / 2 for int8 keys: two codes per element).
+template <typename T, int D, int KRE = D>
 __device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f, const Geo &g, const Src<T> &s,
                                                                      bool resid, int wave, int lane, int nw,
                                                                      bool lr_own = false) {
@@ -133,16 +141,24 @@ __device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f
         f.pstep = nw;
     }
     f.n_kv = (16 * g.cpr_kv) >> 6;
+    f.n_k = (16 * g.cpr_k) >> 6;
     f.n_lr = resid ? ((g.lr_grp + 63) >> 6) : 0;
     f.fpw = 0;
-    for (int pi = f.pbeg; pi < f.pend; pi += f.pstep) f.fpw += pi < nkv ? f.n_kv : f.n_lr;
+    const int nk_pairs = g.H * f.G;  // K pairs come first, then V
+    for (int pi = f.pbeg; pi < f.pend; pi += f.pstep) f.fpw += pi < nk_pairs ? f.n_k : pi < nkv ? f.n_kv : f.n_lr;
     f.lr_stride = (uint32_t)(s.lr_agent_stride * ES);
     f.kv_nt = false;
-    constexpr int NKV = D * ES / 64;  // loads per K/V group: 16 rows of d elements
+    constexpr int NKV = D * ES / 64;  // loads per V group: 16 rows of d elements
+    constexpr int NK = KRE * ES / 64;  // loads per K group
 #pragma unroll
     for (int i = 0; i < NKV; ++i) {
         int row;
-        f.kv_off[i] = kv_lane_off<T, D>(g, i, lane, &row);
+        f.kv_off[i] = kv_lane_off(g.cpr_kv, g.lg_kv, D * ES, i, lane, &row);
+    }
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        int row;
+        f.k_off[i] = kv_lane_off(g.cpr_k, g.lg_k, KRE * ES, i, lane, &row);
     }
 }
 
@@ -170,40 +186,54 @@ __device__ inline uint32_t lr_ofs(const Geo &g, int rbase, int a, int x, int cb)
 // clamp: rows past the item's last token read that token instead (the tail
 // tile); otherwise every row is valid and a uniform base per pair serves.
 // Always the same number of loads per wave (f.fpw), which the ring's waits count.
-template <typename T, int D>
+// One K or V group of 16 rows of RE elements: N direct loads at lane offsets off[].
+template <typename T, int RE>
+__device__ __attribute__((always_inline)) inline void fill_kv_group(const FillPlan &f, const Src<T> &s,
+                                                                    const T *base, int64_t page_stride,
+                                                                    const uint32_t *off, int lg, int tg0,
+                                                                    uint32_t dst, bool clamp, int lane) {
+    constexpr int ES = (int)sizeof(T);
+    constexpr int N = RE * ES / 64;
+    if (!clamp) {
+        const char *b = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, RE>(s, base, tg0, page_stride)));
+        if (f.kv_nt) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) dma16s_nt(b, off[i], dst + 1024 * i);
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; ++i) dma16s(b, off[i], dst + 1024 * i);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int row = (64 * i + lane) >> lg;
+            int tok = tg0 + row;
+            tok = tok < s.tlast ? tok : s.tlast;
+            const uint32_t rowoff = off[i] - (uint32_t)(row * RE * ES);  // chunk part
+            dma16(reinterpret_cast<const char *>(kv_row<T, RE>(s, base, tok, page_stride)) + rowoff, dst + 1024 * i);
+        }
+    }
+}
+
+template <typename T, int D, int KRE = D>
 __device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan &f, const Geo &g, const Src<T> &s,
                                                                  int t0, char *stage, bool clamp, int lane) {
     constexpr int ES = (int)sizeof(T);
     const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(stage));
-    const int nkv = 2 * g.H * f.G;  // K/V pairs come first
+    const int nkv = 2 * g.H * f.G;  // K pairs (regions 0 .. H-1), then V pairs, come first
     for (int pi = f.pbeg; pi < f.pend; pi += f.pstep) {
         const int gg = pi & (f.G - 1);
         const int tg0 = t0 + 16 * gg;  // the group's first token
         if (pi < nkv) {
-            // K (region < H) or V rows of head region % H
             const int region = pi >> f.lgG;
-            const bool isv = region >= g.H;
-            const T *base = (isv ? s.vb : s.kb) + (int64_t)(isv ? region - g.H : region) * s.head_stride;
-            const uint32_t dst = lds0 + 16 * ((region * g.T + 16 * gg) * g.cpr_kv);
-            constexpr int NKV = D * ES / 64;
-            if (!clamp) {
-                const char *b = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, base, tg0)));
-                if (f.kv_nt) {
-#pragma unroll
-                    for (int i = 0; i < NKV; ++i) dma16s_nt(b, f.kv_off[i], dst + 1024 * i);
-                } else {
-#pragma unroll
-                    for (int i = 0; i < NKV; ++i) dma16s(b, f.kv_off[i], dst + 1024 * i);
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < NKV; ++i) {
-                    const int row = (64 * i + lane) >> g.lg_kv;
-                    int tok = tg0 + row;
-                    tok = tok < s.tlast ? tok : s.tlast;
-                    const uint32_t rowoff = f.kv_off[i] - (uint32_t)(row * D * ES);  // chunk part
-                    dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, base, tok)) + rowoff, dst + 1024 * i);
-                }
+            if (region >= g.H) {  // V rows of head region - H
+                const T *base = s.vb + (int64_t)(region - g.H) * s.head_stride;
+                const uint32_t dst = lds0 + 16 * (g.ofs_v + ((region - g.H) * g.T + 16 * gg) * g.cpr_kv);
+                fill_kv_group<T, D>(f, s, base, s.page_stride, f.kv_off, g.lg_kv, tg0, dst, clamp, lane);
+            } else {  // K rows of head region
+                const T *base = s.kb + (int64_t)region * s.k_head_stride;
+                const uint32_t dst = lds0 + 16 * ((region * g.T + 16 * gg) * g.cpr_k);
+                fill_kv_group<T, KRE>(f, s, base, s.k_page_stride, f.k_off, g.lg_k, tg0, dst, clamp, lane);
             }
         } else {
             // Lk (first) or Lv rows of every agent of the workgroup
@@ -259,7 +289,7 @@ __device__ __attribute__((always_inline)) inline void make_group_fill(GroupFill 
 #pragma unroll
     for (int i = 0; i < NKV; ++i) {
         int row;
-        f.kv_off[i] = kv_lane_off<T, D>(g, i, lane, &row);
+        f.kv_off[i] = kv_lane_off(g.cpr_kv, g.lg_kv, D * ES, i, lane, &row);
     }
     f.lr_stride = (uint32_t)(s.lr_agent_stride * ES);
 }
@@ -275,8 +305,8 @@ __device__ __attribute__((always_inline)) inline void fill_group(const GroupFill
     const uint32_t ll0 = lds0 + 16 * (g.ofs_lk + f.g * g.lr_grp), lw0 = lds0 + 16 * (g.ofs_lv + f.g * g.lr_grp);
     if (!clamp) {
         if (f.rK || f.rV) {
-            const char *kb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tg0)));
-            const char *vb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tg0)));
+            const char *kb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tg0, s.page_stride)));
+            const char *vb = uniform_ptr(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tg0, s.page_stride)));
 #pragma unroll
             for (int i = 0; i < NKV; ++i)
                 if (f.rK) dma16s(kb, f.kv_off[i], lk0 + 1024 * i);
@@ -306,8 +336,10 @@ __device__ __attribute__((always_inline)) inline void fill_group(const GroupFill
             int tok = tg0 + row;
             tok = tok < s.tlast ? tok : s.tlast;
             const uint32_t rowoff = f.kv_off[i] - (uint32_t)(row * D * ES);  // chunk part
-            if (f.rK) dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tok)) + rowoff, lk0 + 1024 * i);
-            if (f.rV) dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tok)) + rowoff, lv0 + 1024 * i);
+            if (f.rK)
+                dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.kb, tok, s.page_stride)) + rowoff, lk0 + 1024 * i);
+            if (f.rV)
+                dma16(reinterpret_cast<const char *>(kv_row<T, D>(s, s.vb, tok, s.page_stride)) + rowoff, lv0 + 1024 * i);
         }
     }
     for (int i = 0; i < f.n_lr; ++i) {

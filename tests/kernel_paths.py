@@ -81,6 +81,26 @@ PATHS = [
 ]
 
 
+def _k8(N, HQ, HK, r, L, shared=False, name=""):
+    """Decode over int8 base keys (d = 128, no private tokens)."""
+    return C(N, HQ, HK, 128, r, L, dtype="bf16", shared_lr=shared, name=name)
+
+
+# split kernel over int8 base keys (d = 128): (residual columns, masked, twelve-wave form)
+PATHS_K8 = [
+    (("split", "bf16-k8", 128, 0, False, False), _k8(2, 4, 2, 0, 1000, name="int8 keys r0")),
+    (("split", "bf16-k8", 128, 0, False, True), _k8(2, 16, 1, 0, 1000, name="int8 keys r0 12 waves")),
+    (("split", "bf16-k8", 128, 32, False, False), _k8(1, 2, 2, 32, 1000, name="int8 keys r32 one agent")),
+    (("split", "bf16-k8", 128, 32, False, True), _k8(5, 4, 1, 8, 1000, name="int8 keys r8 12 waves")),
+    (("split", "bf16-k8", 128, 64, False, False), _k8(1, 2, 2, 64, 1000, name="int8 keys r64")),
+    (("split", "bf16-k8", 128, 128, False, False), _k8(1, 2, 2, 128, 1000, name="int8 keys r128")),
+    (("split", "bf16-k8", 128, 32, True, False), _k8(2, 2, 2, 32, 1000, name="int8 keys r32 masked")),
+    (("split", "bf16-k8", 128, 32, True, True), _k8(5, 4, 1, 32, 1000, name="int8 keys r32 masked 12 waves")),
+    (("split", "bf16-k8", 128, 64, True, False), _k8(2, 2, 2, 64, 1000, name="int8 keys r64 masked")),
+    (("split", "bf16-k8", 128, 128, True, False), _k8(2, 4, 4, 128, 1000, name="int8 keys r128 masked")),
+]
+
+
 def built_instantiations():
     """Every kernel instantiation librattn builds (the rules the launchers
     follow: which split widths fit in registers in the eight- and twelve-wave
@@ -100,4 +120,11 @@ def built_instantiations():
                         keys.add(("split", dt, d, cp, masked, True))
                 if dt == "bf16":
                     keys.add(("prefill", dt, d, cp))
+                    if d == 128:  # int8 keys: the d = 128 split kernels
+                        for masked in (False, True):
+                            if masked and cp == 0:
+                                continue
+                            keys.add(("split", "bf16-k8", d, cp, masked, False))
+                            if cp <= 32:
+                                keys.add(("split", "bf16-k8", d, cp, masked, True))
     return keys

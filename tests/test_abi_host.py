@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_strings():
-    assert R.lib().rattn_version() == 1
+    assert R.lib().rattn_version() == 2
     assert R.lib().rattn_status_str(0) == b"ok"
     assert R.lib().rattn_status_str(-4).startswith(b"workspace")
     assert R.lib().rattn_last_hip_error() == 0

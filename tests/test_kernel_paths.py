@@ -14,11 +14,12 @@ from tests import kernel_paths as KP
 pytestmark = pytest.mark.skipif(not os.path.exists(R.LIB_PATH), reason="librattn not built")
 
 
-def desc_of(c):
+def desc_of(c, k8=False):
     return R.make_desc(n_agents=c.n_agents, n_q_heads=c.n_q_heads, n_kv_heads=c.n_kv_heads, head_dim=c.head_dim,
                        rank=c.rank, q_len=c.q_len, prefix_len=c.prefix_len, priv_len=c.priv_len,
                        page_size=c.page_size, shared_lr=c.shared_lr, n_phys_pages=c.n_phys_pages,
-                       dtype=R.RATTN_BF16 if c.dtype == "bf16" else R.RATTN_F32)
+                       dtype=R.RATTN_BF16 if c.dtype == "bf16" else R.RATTN_F32,
+                       k_format=R.RATTN_KEYS_INT8 if k8 else R.RATTN_KEYS_DTYPE, k_scale=0.03 if k8 else 0.0)
 
 
 def op_of(c):
@@ -30,8 +31,13 @@ def test_workload_reaches_its_kernel(key, case):
     assert R.kernel_of(desc_of(case), op_of(case)) == key
 
 
+@pytest.mark.parametrize("key,case", KP.PATHS_K8, ids=[c.name for _, c in KP.PATHS_K8])
+def test_int8_key_workload_reaches_its_kernel(key, case):
+    assert R.kernel_of(desc_of(case, k8=True), R.RATTN_OP_DECODE) == key
+
+
 def test_every_built_kernel_is_listed():
-    listed = {k for k, _ in KP.PATHS}
+    listed = {k for k, _ in KP.PATHS} | {k for k, _ in KP.PATHS_K8}
     assert listed == KP.built_instantiations()
 
 
