@@ -113,10 +113,11 @@ def stable_ms(hip, fn, n, stream, tol=0.01, max_batches=40):
     return hist
 
 
-def algorithmic_bytes(c):
-    """Bytes every input is read once plus the fp32 output written once."""
+def algorithmic_bytes(c, k8=False):
+    """Bytes every input is read once plus the fp32 output written once (int8
+    base keys: one byte per key element)."""
     es = 2 if c.dtype == "bf16" else 4
-    base = 2 * c.n_kv_heads * c.prefix_len * c.head_dim * es
+    base = c.n_kv_heads * c.prefix_len * c.head_dim * ((1 if k8 else es) + es)
     resid = 2 * c.n_lr * c.prefix_len * c.rank * es
     bmat = 2 * c.n_agents * c.rank * c.n_kv_heads * c.head_dim * es
     q = c.n_agents * c.q_len * c.n_q_heads * c.head_dim * es
@@ -228,8 +229,10 @@ def hbm_probe(hip, stream, dev):
     return {"achievable": res[best], "unit": "GB/s", "reader": best, "buffer_bytes": nbytes, "all": res}
 
 
-def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None):
-    """Times one workload; returns its record (without cpu_baseline)."""
+def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k8=False):
+    """Times one workload; returns its record (without cpu_baseline).  k8: the
+    base keys are first quantised to int8 codes (rattn_quantize_keys, outside
+    the timed region) and every call reads the codes."""
     import torch
 
     import shared_base_residual_amd as R
@@ -237,7 +240,7 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None):
 
     case = synth.CONFIGS[config]
     seed = config if seed is None else seed
-    ab = algorithmic_bytes(case)
+    ab = algorithmic_bytes(case, k8)
     layers = case.layers
     op = R.RATTN_OP_PREFILL if case.mode == "prefill" else R.RATTN_OP_DECODE
     say(f"[bench] {case.name}: drawing inputs")
@@ -252,27 +255,39 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None):
         reps = replicas or max(1, min(8, -(-1024 * 2 ** 20 // ab["call"])))
         sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(reps - 1)]
         n_sets = reps
+    k_scale = None
+    if k8:
+        for st in sets:  # each set's keys become int8 codes with that set's scale
+            codes, sc = R.quantize_keys(st["k_base"])
+            st["k_base"] = codes
+            st["k_scale"] = float(sc.cpu().numpy()[0])
+        k_scale = sets[0]["k_scale"]
     desc = R.describe(sets[0]["q"], sets[0]["k_base"], sets[0]["lk"], sets[0]["bk"],
                       block_table=sets[0]["block_table"], k_priv=sets[0]["k_priv"], prefix_len=case.prefix_len,
-                      shared_lr=case.shared_lr)
+                      shared_lr=case.shared_lr, k_scale=k_scale)
     kernel = R.kernel_of(desc, op)
     wsb = R.workspace_bytes(desc, op)
     ws = torch.empty(max(wsb, 256), device=dev, dtype=torch.uint8)
     outs = [torch.empty(tuple(s["q"].shape), device=dev, dtype=torch.float32) for s in sets]
-    argv = []
+    argv, descs = [], []
     for s, o in zip(sets, outs):
         t = dict(s, out=o, lse=None)
+        t.pop("k_scale", None)
         R._check_tensors(desc, t)
         argv.append(R.Args(*[None if t[n] is None else t[n].data_ptr() for n, _ in R.Args._fields_]))
+        d_i = R.Desc.from_buffer_copy(desc)
+        if k8:
+            d_i.k_scale = s["k_scale"]  # one scale per set (per layer)
+        descs.append(d_i)
     sp = ctypes.c_void_p(stream.cuda_stream)
     lib = R.lib()
     wsp, wss = ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel())
-    dref = ctypes.byref(desc)
+    drefs = [ctypes.byref(d_i) for d_i in descs]
     arefs = [ctypes.byref(a) for a in argv]
     fn = lib.rattn_attention_stages
 
     def launch(i, stages):
-        st = fn(dref, op, arefs[i % n_sets], wsp, wss, sp, stages)
+        st = fn(drefs[i % n_sets], op, arefs[i % n_sets], wsp, wss, sp, stages)
         if st:
             raise R.RattnError(st, "rattn_attention_stages")
 
@@ -326,7 +341,7 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None):
     else:
         achieved = ab["split"] / (kern_avg / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_counters(f"decode_cfg{config}"),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_counters(f"decode_cfg{config}" + ("_k8" if k8 else "")),
                 "kernel": "decode_split_kernel", "bytes_per_launch": ab["split"],
                 "avg_launch_us": round(kern_avg * 1e3, 2), "launches_timed": n_k,
                 # the whole call (split + merge) over the timed steps
@@ -339,7 +354,8 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None):
         "metric": METRIC, "value": round(value, 4), "unit": "Gtok/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": case.dtype, "data": "synthetic (seeded N(0,1) caches and queries, N(0,0.05^2) up-projections)",
-        "config": {"workload": case.name, "n_agents": case.n_agents, "n_q_heads": case.n_q_heads,
+        "config": {"workload": case.name + (", int8 keys" if k8 else ""), "n_agents": case.n_agents,
+                   "n_q_heads": case.n_q_heads, "key_format": "int8 (per-tensor scale)" if k8 else case.dtype,
                    "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim, "prefix_len": case.prefix_len,
                    "priv_len": case.priv_len, "q_len": case.q_len, "rank": case.rank, "page_size": case.page_size,
                    "shared_lr": case.shared_lr, "layers": layers, "mode": case.mode, "input_sets_rotated": n_sets},
@@ -460,6 +476,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cache-write", action="store_true", help="skip the cache-write sub-records")
+    ap.add_argument("--no-int8", action="store_true", help="skip the int8-key sub-records")
     ap.add_argument("--seed", type=int, default=None)
     args = ap.parse_args()
 
@@ -485,6 +502,9 @@ def main():
     if subs:
         res["sub_records"] = [measure(c, args.steps, args.warmup, dev, hip, stream, args.replicas, None, probe)
                               for c in subs]
+    if not args.no_int8:
+        res.setdefault("sub_records", []).extend(
+            [measure(c, args.steps, args.warmup, dev, hip, stream, args.replicas, None, probe, k8=True) for c in (1, 4)])
     if not args.no_cache_write:
         res.setdefault("sub_records", []).extend([measure_lr_prefill(args.steps, args.warmup, dev, hip, stream, probe),
                                                   measure_append(args.steps, args.warmup, dev, hip, stream, probe)])

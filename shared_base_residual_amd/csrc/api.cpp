@@ -251,7 +251,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             const int G = T / 16;
             const int tile_loads = H * G * ((16 * (kv_row / 16)) / 64 + (16 * (k_row / 16)) / 64) +
                                    (lr_row_bytes ? 2 * G * ((16 * (lr_row_bytes / 16) + 63) / 64) : 0);
-            const int np0 = tile_loads >= 40 && p.nw + 4 <= 12 ? 4 : (p.lr_own ? 3 : 2);
+            // (int8 keys: four, whose tiles take fewer loads than the rule counts on)
+            const int np0 = (tile_loads >= 40 || p.kq8) && p.nw + 4 <= 12 ? 4 : (p.lr_own ? 3 : 2);
             for (int np = np0; np <= 4; np += 1) {
                 const int f = max_fpw(T, H, lr_row_bytes, np);
                 if (f * (*nst - 1) <= 63) {

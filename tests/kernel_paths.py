@@ -97,7 +97,7 @@ PATHS_K8 = [
     (("split", "bf16-k8", 128, 32, True, False), _k8(2, 2, 2, 32, 1000, name="int8 keys r32 masked")),
     (("split", "bf16-k8", 128, 32, True, True), _k8(5, 4, 1, 32, 1000, name="int8 keys r32 masked 12 waves")),
     (("split", "bf16-k8", 128, 64, True, False), _k8(2, 2, 2, 64, 1000, name="int8 keys r64 masked")),
-    (("split", "bf16-k8", 128, 128, True, False), _k8(2, 4, 4, 128, 1000, name="int8 keys r128 masked")),
+    (("split", "bf16-k8", 128, 128, True, False), _k8(3, 16, 2, 128, 1000, name="int8 keys r128 masked")),
 ]
 
 
