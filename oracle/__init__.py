@@ -18,6 +18,10 @@ Contents
                        projection L = X A that fills the low-rank caches, the
                        logical rows of a paged pool, and the copy-on-write
                        rules an append of new base rows must obey.
+  * ``recon``       -- attention with the residual keys rebuilt per token and
+                       rotated by position before the score (the pages' own
+                       in-register kernel design; needed once keys are rotated
+                       after the up-projection);
   * ``quant``       -- base keys as int8 codes with one scale per tensor
                        (the quantiser, the dequantised keys, and fp64 inputs
                        for ``attend`` with the keys dequantised).

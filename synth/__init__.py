@@ -215,6 +215,17 @@ def make_inputs_torch(case: Case, seed: int, layer: int, device, *, q_scale: flo
     return res
 
 
+def rope_table(length: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """A model's positional (rotary) table for tokens 0 .. length-1: entry
+    [j, f] holds (cos, sin) of the angle j * base^(-2f/d), f < d/2, as fp32.
+    An input of the rebuilt-key attention (like the model's weights); the
+    angles are formed in fp64 and the cosines and sines rounded once to fp32."""
+    f = np.arange(head_dim // 2, dtype=np.float64)
+    theta = base ** (-2.0 * f / head_dim)
+    ang = np.arange(length, dtype=np.float64)[:, None] * theta[None, :]
+    return np.ascontiguousarray(np.stack([np.cos(ang), np.sin(ang)], axis=-1).astype(np.float32))
+
+
 def torch_to_numpy(t):
     """torch tensor (any device) -> numpy in this module's storage convention."""
     import torch
