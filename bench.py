@@ -465,6 +465,53 @@ def measure_append(K, W, dev, hip, stream, probe):
                        "cur_len": L0, "n_tokens": T, "copy_on_write_pages": int(cow[0] >= 0)}, "roofline": roof}
 
 
+def measure_reconstruct(config, K, W, dev, hip, stream, probe, rope):
+    """The rebuilt-key decode (rattn_decode_reconstruct) on one layer of a
+    decode workload, with or without the positional rotation; timed per call
+    (its split kernel and the merge), beside the factored path's roofline."""
+    import torch
+
+    import shared_base_residual_amd as R
+    import synth
+
+    case = synth.CONFIGS[config].replace(layers=1)
+    ab = algorithmic_bytes(case)
+    say(f"[bench] rebuilt keys ({case.name}, rope={rope}): drawing inputs")
+    x = synth.make_inputs(case, config)
+    base = synth.to_torch(x, dev)
+    reps = max(1, min(8, -(-1024 * 2 ** 20 // ab["call"])))
+    sets = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(reps - 1)]
+    theta = torch.from_numpy(synth.rope_theta(case.head_dim)).to(dev) if rope else None
+    outs = [torch.empty(tuple(s["q"].shape), device=dev, dtype=torch.float32) for s in sets]
+    desc = R.describe(base["q"], base["k_base"], base["lk"], base["bk"])
+    ws = torch.empty(R.workspace_bytes(desc, R.RATTN_OP_RECONSTRUCT), device=dev, dtype=torch.uint8)
+    fn = lambda i: R.decode_reconstruct(sets[i % reps], rope_theta=theta, out=outs[i % reps], workspace=ws,
+                                        stream=stream)
+    for i in range(W):
+        fn(i)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    stable_ms(hip, fn, 8, sp)
+    ms = hip.time_ms(fn, K, sp)
+    torch.cuda.synchronize()
+    achieved = ab["call"] / (ms / 1e3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "kernel": "recon_split_kernel + combine_kernel (whole call)", "bytes_per_launch": ab["call"],
+            "avg_launch_us": round(ms * 1e3, 2), "launches_timed": K}
+    if probe:
+        roof["achievable"] = probe["achievable"]
+        roof["frac_of_achievable"] = round(achieved / probe["achievable"], 4)
+    say(f"[bench] rebuilt keys ({case.name}, rope={rope}): {ms * 1e3:.2f} us per call, frac {roof['frac']}")
+    del sets, outs, ws
+    return {"metric": METRIC, "value": round(pairs_per_call(case) / (ms / 1e3) / 1e9, 4), "unit": "Gtok/s",
+            "steps": K, "warmup": W, "ms_per_step": round(ms, 5), "dtype": "bf16",
+            "config": {"workload": f"{case.name}, one layer, residual keys rebuilt in registers" +
+                                   (", rotated by position" if rope else ""), "n_agents": case.n_agents,
+                       "n_q_heads": case.n_q_heads, "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim,
+                       "prefix_len": case.prefix_len, "rank": case.rank, "rope": rope},
+            "roofline": roof}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -477,6 +524,7 @@ def main():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cache-write", action="store_true", help="skip the cache-write sub-records")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8-key sub-records")
+    ap.add_argument("--no-reconstruct", action="store_true", help="skip the rebuilt-key sub-records")
     ap.add_argument("--seed", type=int, default=None)
     args = ap.parse_args()
 
@@ -505,6 +553,10 @@ def main():
     if not args.no_int8:
         res.setdefault("sub_records", []).extend(
             [measure(c, args.steps, args.warmup, dev, hip, stream, args.replicas, None, probe, k8=True) for c in (1, 4)])
+    if not args.no_reconstruct:
+        res.setdefault("sub_records", []).extend(
+            [measure_reconstruct(c, args.steps, args.warmup, dev, hip, stream, probe, rope)
+             for c in (1, 4) for rope in (False, True)])
     if not args.no_cache_write:
         res.setdefault("sub_records", []).extend([measure_lr_prefill(args.steps, args.warmup, dev, hip, stream, probe),
                                                   measure_append(args.steps, args.warmup, dev, hip, stream, probe)])

@@ -79,7 +79,8 @@ typedef enum rattn_key_format {
 
 typedef enum rattn_op {
     RATTN_OP_DECODE = 0,
-    RATTN_OP_PREFILL = 1
+    RATTN_OP_PREFILL = 1,
+    RATTN_OP_RECONSTRUCT = 2 /* rattn_decode_reconstruct (rattn_workspace_bytes only) */
 } rattn_op;
 
 /* Shape of one call (one layer). */
@@ -143,6 +144,28 @@ int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes);
  */
 int rattn_decode(const rattn_desc *desc, const rattn_args *args, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/*
+ * Decode with the residual keys rebuilt per token in registers right before
+ * the score product -- the ForkKV Guide's own kernel design ("Fused
+ * ResidualAttention", section 2 On-the-Fly Register Fusion) -- and rotated by
+ * position when rope_theta is given.  Without a rotation it computes what
+ * rattn_decode computes (a variant to compare against the factored path);
+ * with one it computes attention over
+ *     K_a[j] = K_base[j] + rot_j(Lk_a[j] Bk_a^(k)),   V_a as in rattn_decode,
+ * where rot_j rotates each pair (f, f + d/2) of a d-vector by the angle
+ * j * rope_theta[f] (rotate-half rotary position embedding; K_base is taken as
+ * already rotated, values are not rotated).  That is the case the factored
+ * score cannot serve: (q Bk^T) Lk_j^T assumes the residual key unrotated.
+ * rope_theta: NULL, or a device pointer to d/2 fp32 frequencies (radians per
+ * position).  Positions are the logical prefix token indices 0 .. L-1.
+ * Limits (else RATTN_E_UNSUPPORTED): bf16, head_dim 128, rank 16 or 32, a
+ * contiguous base cache, priv_len 0, q_len * (H_q / H_kv) <= 16, unquantised
+ * keys.  Workspace: rattn_workspace_bytes(desc, RATTN_OP_RECONSTRUCT), as in
+ * rattn_decode.  Two launches (split kernel, then the decode merge).
+ */
+int rattn_decode_reconstruct(const rattn_desc *desc, const rattn_args *args, const float *rope_theta,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * rattn_decode for callers that cannot allocate device memory (code under HIP

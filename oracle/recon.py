@@ -16,8 +16,9 @@ rotate-half form: for d-vector x and frequency index f < d/2,
     rot_j(x)[f]       = x[f] cos_j[f] - x[f + d/2] sin_j[f]
     rot_j(x)[f + d/2] = x[f + d/2] cos_j[f] + x[f] sin_j[f]
 with the cosines and sines of token j's angles given as a table
-rope[j, f] = (cos, sin), fp32 (the positional table of the model, an input
-like its weights).  K_base is taken as already rotated (the base model wrote
+rope[j, f] = (cos, sin) (the positional table of the model, an input like its
+weights; ``table_from_theta`` forms it in fp64 from frequencies theta[f], the
+angle of token j being j * theta[f]).  K_base is taken as already rotated (the base model wrote
 it so); values are not rotated, so the value residual keeps its factored form.
 
 The definition, written out for agent a, KV head k, logical token j < L:
@@ -39,6 +40,13 @@ def _f64(a):
     if a.dtype == np.uint16:  # bf16 bit patterns
         return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     return a.astype(np.float64)
+
+
+def table_from_theta(theta: np.ndarray, length: int) -> np.ndarray:
+    """The (cos, sin) table [length, d/2, 2] that frequencies theta (radians
+    per position, the values as given) define: angle j * theta[f], in fp64."""
+    ang = np.arange(length, dtype=np.float64)[:, None] * np.asarray(theta, dtype=np.float64)[None, :]
+    return np.stack([np.cos(ang), np.sin(ang)], axis=-1)
 
 
 def rotate(x: np.ndarray, rope) -> np.ndarray:

@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(HERE, "librattn.so")
 
 RATTN_F32, RATTN_BF16 = 0, 1
 RATTN_KEYS_DTYPE, RATTN_KEYS_INT8 = 0, 1
-RATTN_OP_DECODE, RATTN_OP_PREFILL = 0, 1
+RATTN_OP_DECODE, RATTN_OP_PREFILL, RATTN_OP_RECONSTRUCT = 0, 1, 2
 STATUS = {0: "RATTN_OK", -1: "RATTN_E_NULL", -2: "RATTN_E_SHAPE", -3: "RATTN_E_UNSUPPORTED",
           -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP", -7: "RATTN_E_SCRATCH",
           -8: "RATTN_E_POOL"}
@@ -36,7 +36,7 @@ EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "ratt
            "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
            "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
            "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv",
-           "rattn_quantize_keys")
+           "rattn_quantize_keys", "rattn_decode_reconstruct")
 STAGE_SPLIT, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
 
 
@@ -124,7 +124,8 @@ def lib():
         L.rattn_append_kv.argtypes = [ctypes.POINTER(Desc), P, P, P, I64, I64, P, P, ctypes.c_int32,
                                       ctypes.c_int32, P]
         L.rattn_quantize_keys.argtypes = [P, I64, ctypes.c_int32, P, P, P]
-        for f in ("rattn_quantize_keys", "rattn_lr_project", "rattn_pagepool_create", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
+        L.rattn_decode_reconstruct.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P, P, ctypes.c_size_t, P]
+        for f in ("rattn_decode_reconstruct", "rattn_quantize_keys", "rattn_lr_project", "rattn_pagepool_create", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
                   "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append",
                   "rattn_append_kv"):
             getattr(L, f).restype = I
@@ -135,7 +136,7 @@ def lib():
                   "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
            "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
            "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv",
-           "rattn_quantize_keys"):
+           "rattn_quantize_keys", "rattn_decode_reconstruct"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -374,6 +375,40 @@ def decode_noalloc(inputs: dict, *, shared_lr=None, prefix_len=None, out, lse=No
     st = lib().rattn_decode_noalloc(ctypes.byref(desc), ctypes.byref(args), _stream(stream))
     if st:
         raise RattnError(st, "rattn_decode_noalloc")
+    return out
+
+
+def decode_reconstruct(inputs: dict, *, rope_theta=None, shared_lr=None, out=None, lse=None, workspace=None,
+                       stream=None):
+    """rattn_decode_reconstruct: decode with the residual keys rebuilt per token
+    in registers, rotated by position when ``rope_theta`` (a [d/2] fp32 GPU
+    tensor of frequencies) is given.  Returns out."""
+    import torch
+
+    g = inputs.get
+    q = inputs["q"]
+    desc = describe(q, g("k_base"), g("lk"), g("bk"), shared_lr=shared_lr)
+    if out is None:
+        out = torch.empty(tuple(q.shape), device=q.device, dtype=torch.float32)
+    tensors = dict(q=q, k_base=g("k_base"), v_base=g("v_base"), block_table=None, lk=g("lk"), lv=g("lv"),
+                   bk=g("bk"), bv=g("bv"), k_priv=None, v_priv=None, out=out, lse=lse)
+    _check_tensors(desc, tensors)
+    if rope_theta is not None:
+        if not (rope_theta.is_cuda and rope_theta.dtype == torch.float32 and
+                rope_theta.numel() == desc.head_dim // 2 and rope_theta.is_contiguous()):
+            raise ValueError("rope_theta must be a contiguous fp32 GPU tensor of head_dim / 2 values")
+    nbytes = workspace_bytes(desc, RATTN_OP_RECONSTRUCT)
+    if workspace is None:
+        workspace = workspace_for(nbytes, q.device, stream)
+    args = Args(*[_ptr(tensors[n]) for n in
+                  ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out",
+                   "lse")])
+    st = lib().rattn_decode_reconstruct(ctypes.byref(desc), ctypes.byref(args), _ptr(rope_theta),
+                                        ctypes.c_void_p(workspace.data_ptr()),
+                                        ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                        _stream(stream))
+    if st:
+        raise RattnError(st, "rattn_decode_reconstruct")
     return out
 
 

@@ -19,6 +19,7 @@ hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_lr_project(const LrParams &p, hipStream_t st);
 hipError_t launch_append_kv(const AppendParams &p, hipStream_t st);
 hipError_t launch_quantize(const void *k, int64_t n, int bf16_in, void *codes, float *scale, hipStream_t st);
+hipError_t launch_recon(const ReconParams &p, hipStream_t st);
 }  // namespace rattn
 
 static_assert(rattn::kNoAllocScratchBytes == RATTN_NOALLOC_SCRATCH_BYTES, "static scratch size in the header");
@@ -65,7 +66,15 @@ int check_desc(const rattn_desc *d, int op) {
         if (d->prefix_len > 0 && d->n_phys_pages < 1) return RATTN_E_SHAPE;
     }
     if (op == RATTN_OP_PREFILL && d->q_len != d->priv_len) return RATTN_E_SHAPE;
-    if (op != RATTN_OP_DECODE && op != RATTN_OP_PREFILL) return RATTN_E_SHAPE;
+    if (op != RATTN_OP_DECODE && op != RATTN_OP_PREFILL && op != RATTN_OP_RECONSTRUCT) return RATTN_E_SHAPE;
+    if (op == RATTN_OP_RECONSTRUCT) {
+        // rebuilt residual keys: bf16, d = 128, rank 16 or 32, a contiguous base
+        // cache, no private tokens, at most 16 query rows per agent and KV head
+        if (d->dtype != RATTN_BF16 || d->head_dim != 128 || (d->rank != 16 && d->rank != 32) ||
+            d->page_size != 0 || d->priv_len != 0 || d->prefix_len < 1 ||
+            (int64_t)d->q_len * (d->n_q_heads / d->n_kv_heads) > 16 || d->k_format != RATTN_KEYS_DTYPE)
+            return RATTN_E_UNSUPPORTED;
+    }
     if (d->k_format != RATTN_KEYS_DTYPE && d->k_format != RATTN_KEYS_INT8) return RATTN_E_SHAPE;
     if (d->k_format == RATTN_KEYS_INT8) {
         if (!(d->k_scale > 0.f && d->k_scale <= 3.0e38f)) return RATTN_E_SHAPE;
@@ -474,6 +483,82 @@ int make_prefill_plan(const rattn_desc *d, PrefillPlan *pl) {
     return RATTN_OK;
 }
 
+// ---- decode with rebuilt residual keys (rattn_decode_reconstruct): its split
+// kernel writes the decode workspace layout, whose merge launch finishes it.
+struct ReconPlan {
+    rattn::ReconParams rp;
+    rattn::DecodeParams dp;  // for the merge
+    size_t off_ml, off_o, off_w, total;
+};
+
+int make_recon_plan(const rattn_desc *d, ReconPlan *pl) {
+    rattn::ReconParams &p = pl->rp;
+    p = rattn::ReconParams{};
+    const int N = d->n_agents, HK = d->n_kv_heads, g = d->n_q_heads / d->n_kv_heads, r = d->rank;
+    const int D = d->head_dim;
+    const int64_t L = d->prefix_len;
+    p.L = L;
+    p.N = N;
+    p.QL = d->q_len;
+    p.HQ = d->n_q_heads;
+    p.HK = HK;
+    p.g = g;
+    p.rpa = d->q_len * g;
+    p.r = r;
+    p.shared_lr = d->shared_lr;
+    const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
+    p.c = scale * 1.44269504088896340736f;
+    p.n_ag = (int)cdiv(N, rattn::kReconWaves);
+    const int64_t base = (int64_t)HK * p.n_ag;
+    int64_t n = cdiv(kTargetItems, base);
+    const int64_t nmax = cdiv(L, rattn::kReconT);
+    if (n > nmax) n = nmax;
+    if (n < 1) n = 1;
+    p.tok_split = (int)roundup(cdiv(L, n), rattn::kReconT);
+    p.n_splits = (int)cdiv(L, p.tok_split);
+    p.n_slots = p.n_splits;
+    if (p.n_slots > rattn::kMaxSlots) return RATTN_E_UNSUPPORTED;
+    const int64_t items = (int64_t)p.n_splits * base;
+    if (items > (1ll << 30)) return RATTN_E_UNSUPPORTED;
+    p.n_items = (int)items;
+    p.per_xcd = (int)cdiv(items, 8);
+    const int na_lr = d->shared_lr ? 1 : (N < rattn::kReconWaves ? N : rattn::kReconWaves);
+    if ((int64_t)na_lr * L * r * 2 >= (1ll << 31)) return RATTN_E_UNSUPPORTED;  // 32-bit fill offsets
+    p.stage_bytes = rattn::kReconT * (2 * D * 2 + 2 * na_lr * r * 2);
+    const int nst = rattn::kLdsMax / p.stage_bytes;
+    p.nst = nst < 4 ? nst : 4;
+    if (p.nst < 2) return RATTN_E_UNSUPPORTED;
+
+    // the merge: every field combine_kernel reads
+    rattn::DecodeParams &q = pl->dp;
+    q = rattn::DecodeParams{};
+    q.L = L;
+    q.N = N;
+    q.QL = d->q_len;
+    q.HQ = d->n_q_heads;
+    q.HK = HK;
+    q.g = g;
+    q.r = r;
+    q.rpa = p.rpa;
+    q.n_ps = p.n_splits;
+    q.n_slots = p.n_slots;
+    q.fd_hq = rattn::make_fastdiv(q.HQ);
+    q.fd_ql = rattn::make_fastdiv(q.QL);
+    q.fd_g = rattn::make_fastdiv(g);
+    const int64_t rows_kv = (int64_t)HK * N * p.rpa;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += (bytes + 255) & ~(size_t)255;
+        return o;
+    };
+    pl->off_ml = take((size_t)rows_kv * p.n_slots * 2 * sizeof(float));
+    pl->off_o = take((size_t)rows_kv * p.n_slots * D * sizeof(float));
+    pl->off_w = take((size_t)rows_kv * p.n_slots * r * sizeof(float));
+    pl->total = off;
+    return RATTN_OK;
+}
+
 int check_args(const rattn_desc *d, const rattn_args *a) {
     if (!a) return RATTN_E_NULL;
     const bool paged = d->page_size > 0;
@@ -605,6 +690,13 @@ int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes) {
         st = make_prefill_plan(desc, &pp);
         if (st) return st;
         *bytes = 0;  // the prefill kernel needs no workspace
+        return RATTN_OK;
+    }
+    if (op == RATTN_OP_RECONSTRUCT) {
+        ReconPlan rp;
+        st = make_recon_plan(desc, &rp);
+        if (st) return st;
+        *bytes = rp.total;
         return RATTN_OK;
     }
     Plan pl;
@@ -759,6 +851,44 @@ int rattn_quantize_keys(const void *k, int64_t n, int32_t dtype, void *codes, fl
     if (!k || !codes || !scale) return RATTN_E_NULL;
     if (!aligned(k, esize(dtype)) || !aligned(scale, 4)) return RATTN_E_ALIGN;
     return hip_status(rattn::launch_quantize(k, n, dtype == RATTN_BF16, codes, scale, static_cast<hipStream_t>(stream)));
+}
+
+int rattn_decode_reconstruct(const rattn_desc *desc, const rattn_args *args, const float *rope_theta,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    int st = check_desc(desc, RATTN_OP_RECONSTRUCT);
+    if (st) return st;
+    st = check_args(desc, args);
+    if (st) return st;
+    ReconPlan pl;
+    st = make_recon_plan(desc, &pl);
+    if (st) return st;
+    if (!workspace) return RATTN_E_WORKSPACE;
+    if (workspace_bytes < pl.total) return RATTN_E_WORKSPACE;
+    if (!aligned(workspace, 256)) return RATTN_E_ALIGN;
+    if (rope_theta && !aligned(rope_theta, 4)) return RATTN_E_ALIGN;
+    char *w = static_cast<char *>(workspace);
+    rattn::ReconParams &p = pl.rp;
+    p.q = args->q;
+    p.kb = args->k_base;
+    p.vb = args->v_base;
+    p.lk = args->lk;
+    p.lv = args->lv;
+    p.bk = args->bk;
+    p.theta = rope_theta;
+    p.p_ml = reinterpret_cast<float *>(w + pl.off_ml);
+    p.p_o = reinterpret_cast<float *>(w + pl.off_o);
+    p.p_w = reinterpret_cast<float *>(w + pl.off_w);
+    rattn::DecodeParams &q = pl.dp;
+    q.p_ml = p.p_ml;
+    q.p_o = p.p_o;
+    q.p_w = p.p_w;
+    q.bv = args->bv;
+    q.out = args->out;
+    q.lse = args->lse;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = hip_status(rattn::launch_recon(p, s));
+    if (st) return st;
+    return hip_status(rattn::launch_decode(1, q, desc->head_dim, 0, 0, RATTN_STAGE_COMBINE, s));
 }
 
 int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *args, void *workspace,

@@ -239,3 +239,26 @@ struct AppendParams {
 
 }  // namespace rattn
 
+namespace rattn {
+
+// Decode with the residual keys rebuilt per token in registers (and rotated by
+// position when a frequency vector is given): one workgroup per (split, KV
+// head, group of up to four agents), one wave per agent.
+constexpr int kReconWaves = 4;
+constexpr int kReconT = 64;  // tokens per LDS stage
+
+struct ReconParams {
+    const void *q, *kb, *vb, *lk, *lv, *bk;
+    const float *theta;  // [d / 2] rotation frequencies (radians per position), or null
+    float *p_ml, *p_o, *p_w;  // the decode workspace layout (max/sum, P V_base, P Lv)
+    int64_t L;
+    int N, QL, HQ, HK, g, rpa, r, shared_lr;
+    float c;             // softmax scale * log2(e)
+    int n_ag;            // agent groups (of up to kReconWaves agents)
+    int n_splits, tok_split, n_slots;
+    int n_items, per_xcd;
+    int nst, stage_bytes;
+};
+
+}  // namespace rattn
+

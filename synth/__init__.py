@@ -215,6 +215,13 @@ def make_inputs_torch(case: Case, seed: int, layer: int, device, *, q_scale: flo
     return res
 
 
+def rope_theta(head_dim: int, base: float = 10000.0) -> np.ndarray:
+    """Rotation frequencies of a rotary positional table, base^(-2f/d) for
+    f < d/2, as fp32 (radians per position)."""
+    f = np.arange(head_dim // 2, dtype=np.float64)
+    return (base ** (-2.0 * f / head_dim)).astype(np.float32)
+
+
 def rope_table(length: int, head_dim: int, base: float = 10000.0) -> np.ndarray:
     """A model's positional (rotary) table for tokens 0 .. length-1: entry
     [j, f] holds (cos, sin) of the angle j * base^(-2f/d), f < d/2, as fp32.

@@ -52,3 +52,14 @@ def test_hand_worked_token():
                      3.0 + (0.5 * 0.6 + 1 * 0.8), 4.0 + (2.0 * 0.0 + -2 * 1.0)])
     got = recon.rebuilt_keys(case, x, 0, rope)[0, 0]
     assert np.allclose(got, want, rtol=0, atol=1e-7)
+
+
+def test_table_from_theta_matches_the_fp32_table():
+    """The fp64 table of the fp32 frequencies equals synth's fp32 positional
+    table (angles from fp64 frequencies) up to the frequencies' rounding
+    (angle error <= j * 2^-24 theta) and the table's own, and angle 0 gives (1, 0)."""
+    theta = synth.rope_theta(64)
+    t64 = recon.table_from_theta(theta, 300)
+    t32 = synth.rope_table(300, 64)
+    assert np.abs(t64 - t32).max() <= 300 * 2.0 ** -24 + 2.0 ** -23
+    assert np.array_equal(t64[0, :, 0], np.ones(32)) and np.array_equal(t64[0, :, 1], np.zeros(32))
