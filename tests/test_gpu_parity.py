@@ -197,6 +197,9 @@ EDGE = [
     synth.Case(2, 8, 2, 128, 64, 300, priv_len=30, q_len=30, mode="prefill", name="prefill r=64"),
     # more than 64 splits per row: the merge's weight pass across waves
     synth.Case(2, 4, 1, 128, 16, 40000, name="more than 64 splits"),
+    synth.Case(4, 32, 8, 128, 16, 500, priv_len=3000, name="private tokens outnumber the prefix"),
+    synth.Case(12, 8, 2, 128, 64, 1000, priv_len=700, page_size=16, n_phys_pages=120,
+               name="masked paged, long private suffixes"),
     # one row per agent (g = 1, r = 32): the masked ring does not fit, so blocks of
     # two agents with block-diagonal residual columns
     synth.Case(16, 4, 4, 128, 32, 600, priv_len=5, name="g=1 r=32, two agents per block"),
