@@ -491,7 +491,7 @@ struct ReconPlan {
     size_t off_ml, off_o, off_w, total;
 };
 
-int make_recon_plan(const rattn_desc *d, ReconPlan *pl) {
+int make_recon_plan(const rattn_desc *d, bool rope, ReconPlan *pl) {
     rattn::ReconParams &p = pl->rp;
     p = rattn::ReconParams{};
     const int N = d->n_agents, HK = d->n_kv_heads, g = d->n_q_heads / d->n_kv_heads, r = d->rank;
@@ -508,26 +508,39 @@ int make_recon_plan(const rattn_desc *d, ReconPlan *pl) {
     p.shared_lr = d->shared_lr;
     const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
     p.c = scale * 1.44269504088896340736f;
-    p.n_ag = (int)cdiv(N, rattn::kReconWaves);
+    // agents in balanced groups of at most one per wave; each agent's rows take
+    // waves / agents waves, at most one per 16-token step of a stage
+    const int waves = rattn::recon_waves(rope);
+    const int n_groups = (int)cdiv(N, waves);
+    p.apg = (int)cdiv(N, n_groups);
+    p.n_ag = (int)cdiv(N, p.apg);
+    const int na_lr = d->shared_lr ? 1 : p.apg;
+    if ((int64_t)na_lr * L * r * 2 >= (1ll << 31)) return RATTN_E_UNSUPPORTED;  // 32-bit fill offsets
+    auto stage_of = [&](int t) { return t * (2 * D * 2 + 2 * na_lr * r * 2); };
+    const int room = rattn::kLdsMax;
+    p.T = rattn::kReconTMax;
+    if (room / stage_of(p.T) < 3) p.T /= 2;
+    p.stage_bytes = stage_of(p.T);
+    const int nst = room / p.stage_bytes;
+    p.nst = nst < 4 ? nst : 4;
+    if (p.nst < 2) return RATTN_E_UNSUPPORTED;
+    p.tg = waves / p.apg;
+    if (p.tg > p.T / 16) p.tg = p.T / 16;
+    if (p.tg == 3) p.tg = 2;  // a power of two, dividing the steps of a stage
     const int64_t base = (int64_t)HK * p.n_ag;
     int64_t n = cdiv(kTargetItems, base);
-    const int64_t nmax = cdiv(L, rattn::kReconT);
+    const int64_t nmax = cdiv(L, p.T);
     if (n > nmax) n = nmax;
+    if (n > rattn::kMaxSlots / p.tg) n = rattn::kMaxSlots / p.tg;
     if (n < 1) n = 1;
-    p.tok_split = (int)roundup(cdiv(L, n), rattn::kReconT);
+    p.tok_split = (int)roundup(cdiv(L, n), p.T);
     p.n_splits = (int)cdiv(L, p.tok_split);
-    p.n_slots = p.n_splits;
+    p.n_slots = p.n_splits * p.tg;
     if (p.n_slots > rattn::kMaxSlots) return RATTN_E_UNSUPPORTED;
     const int64_t items = (int64_t)p.n_splits * base;
     if (items > (1ll << 30)) return RATTN_E_UNSUPPORTED;
     p.n_items = (int)items;
     p.per_xcd = (int)cdiv(items, 8);
-    const int na_lr = d->shared_lr ? 1 : (N < rattn::kReconWaves ? N : rattn::kReconWaves);
-    if ((int64_t)na_lr * L * r * 2 >= (1ll << 31)) return RATTN_E_UNSUPPORTED;  // 32-bit fill offsets
-    p.stage_bytes = rattn::kReconT * (2 * D * 2 + 2 * na_lr * r * 2);
-    const int nst = rattn::kLdsMax / p.stage_bytes;
-    p.nst = nst < 4 ? nst : 4;
-    if (p.nst < 2) return RATTN_E_UNSUPPORTED;
 
     // the merge: every field combine_kernel reads
     rattn::DecodeParams &q = pl->dp;
@@ -540,7 +553,7 @@ int make_recon_plan(const rattn_desc *d, ReconPlan *pl) {
     q.g = g;
     q.r = r;
     q.rpa = p.rpa;
-    q.n_ps = p.n_splits;
+    q.n_ps = p.n_slots;  // every slot carries W
     q.n_slots = p.n_slots;
     q.fd_hq = rattn::make_fastdiv(q.HQ);
     q.fd_ql = rattn::make_fastdiv(q.QL);
@@ -693,10 +706,13 @@ int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes) {
         return RATTN_OK;
     }
     if (op == RATTN_OP_RECONSTRUCT) {
-        ReconPlan rp;
-        st = make_recon_plan(desc, &rp);
+        // enough for the call with or without a rotation (their plans differ)
+        ReconPlan rp, rp2;
+        st = make_recon_plan(desc, false, &rp);
         if (st) return st;
-        *bytes = rp.total;
+        st = make_recon_plan(desc, true, &rp2);
+        if (st) return st;
+        *bytes = rp.total > rp2.total ? rp.total : rp2.total;
         return RATTN_OK;
     }
     Plan pl;
@@ -860,7 +876,7 @@ int rattn_decode_reconstruct(const rattn_desc *desc, const rattn_args *args, con
     st = check_args(desc, args);
     if (st) return st;
     ReconPlan pl;
-    st = make_recon_plan(desc, &pl);
+    st = make_recon_plan(desc, rope_theta != nullptr, &pl);
     if (st) return st;
     if (!workspace) return RATTN_E_WORKSPACE;
     if (workspace_bytes < pl.total) return RATTN_E_WORKSPACE;

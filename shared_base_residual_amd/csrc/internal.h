@@ -243,9 +243,12 @@ namespace rattn {
 
 // Decode with the residual keys rebuilt per token in registers (and rotated by
 // position when a frequency vector is given): one workgroup per (split, KV
-// head, group of up to four agents), one wave per agent.
-constexpr int kReconWaves = 4;
-constexpr int kReconT = 64;  // tokens per LDS stage
+// head, group of agents), of eight waves (four with the rotation, whose state
+// takes the registers of a second wave per SIMD).  Each agent of the group
+// takes tg = waves / agents waves (at most the steps of a stage), which share
+// out the 16-token steps of every stage and write separate partials.
+constexpr int recon_waves(bool rope) { return rope ? 4 : 8; }
+constexpr int kReconTMax = 64;  // tokens per LDS stage (64, or 32 when three such stages do not fit)
 
 struct ReconParams {
     const void *q, *kb, *vb, *lk, *lv, *bk;
@@ -254,7 +257,10 @@ struct ReconParams {
     int64_t L;
     int N, QL, HQ, HK, g, rpa, r, shared_lr;
     float c;             // softmax scale * log2(e)
-    int n_ag;            // agent groups (of up to kReconWaves agents)
+    int n_ag;            // agent groups
+    int apg;             // agents per group (<= kReconMaxAgents)
+    int tg;              // waves (token groups) per agent; partial slot = split * tg + token group
+    int T;               // tokens per LDS stage (a multiple of 16 tg)
     int n_splits, tok_split, n_slots;
     int n_items, per_xcd;
     int nst, stage_bytes;

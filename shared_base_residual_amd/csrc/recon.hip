@@ -27,10 +27,14 @@
 // t + 4 of the same lane.
 //
 // Each workgroup stages the split's base keys and values and the low-rank rows
-// of its agents through an LDS ring (direct loads, every wave filling its own
-// 16-row group of each region), so the base tile is read from HBM once for up
-// to four agents.  Partials go to the decode workspace layout and the decode
-// merge kernel finishes the call.
+// of its agents through an LDS ring (direct loads, every wave filling 16-row
+// groups of some regions), so the base tile is read from HBM once for up to
+// eight agents.  An agent's rows take tg waves (token groups), which share out
+// the stage's 16-token steps (wave tg_i takes steps tg_i, tg_i + tg, ...) and
+// each keep their own softmax state, written as partial slot split * tg + tg_i:
+// two waves per SIMD hide the long dependent chain of a step (rank product,
+// conversion, score, softmax, value products).  Partials go to the decode
+// workspace layout and the decode merge kernel finishes the call.
 #include "device.h"
 #include "internal.h"
 #include "stage.h"
@@ -48,10 +52,10 @@ __device__ inline float rev_of(double pos, float theta) {
 }
 
 template <int R, bool ROPE>
-__global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconParams p) {
+__global__ __launch_bounds__(64 * recon_waves(ROPE)) void recon_split_kernel(ReconParams p) {
     constexpr int D = 128, KS = D / 32, VPL = D / 16, ES = 2;
     constexpr int CPL = R / 16;  // residual column tiles of W
-    constexpr int T = kReconT;
+    const int T = p.T;
     using O = Ops<bf16>;
     using frag = O::frag;
     using frag4 = O::frag4;
@@ -69,13 +73,14 @@ __global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconPara
     if (li >= p.n_items) return;
     const int ag = li % p.n_ag, rest = li / p.n_ag;
     const int k = rest % p.HK, sp = rest / p.HK;
-    const int a0 = ag * kReconWaves;
-    const int na = p.N - a0 < kReconWaves ? p.N - a0 : kReconWaves;
+    const int a0 = ag * p.apg;
+    const int na = p.N - a0 < p.apg ? p.N - a0 : p.apg;
     const int t0 = sp * p.tok_split;
     int t1 = t0 + p.tok_split < p.L ? t0 + p.tok_split : (int)p.L;
     if (t1 < t0) t1 = t0;
-    const int a = a0 + wave;  // this wave's agent
-    const bool active = wave < na;
+    const int wa = small_div(wave, p.tg), tgi = wave - wa * p.tg;  // this wave's agent (in the group), token group
+    const int a = a0 + wa;
+    const bool active = wa < na;
 
     // ---- stage geometry: one head's K and V rows, the agents' Lk and Lv rows
     Geo g;
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconPara
     src.tlast = t1 > t0 ? t1 - 1 : t0;
 
     GroupFill fp;
-    make_group_fill<bf16, D>(fp, g, src, true, wave, lane, kReconWaves);
+    make_group_fill<bf16, D>(fp, g, src, true, wave, lane, recon_waves(ROPE));  // a multiple of T / 16
     const int n_tiles = (t1 - t0 + T - 1) / T;
     const int fpw = fp.fpw;
     auto fill = [&](int tile, int stage) {
@@ -157,8 +162,9 @@ __global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconPara
 #pragma unroll
             for (int i = 0; i < BS; ++i) bkt[t][i] = bk[(int64_t)(BS * j4 + i) * ldb + 16 * t];
     }
-    // rotation state: cos / sin of token (t0 + 16 step + n16) for f = 16 t + 4 j4 + i
-    // (t < 4), advanced by 16 tokens per step with the angle-addition rule
+    // rotation state: cos / sin of this wave's next token (t0 + 16 tgi + n16 first)
+    // for f = 16 t + 4 j4 + i (t < 4), advanced by the 16 tg tokens between the
+    // wave's steps with the angle-addition rule
     float cs[4][4], sn[4][4], c16[4][4], s16[4][4];
     if constexpr (ROPE) {
 #pragma unroll
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconPara
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float th = p.theta[16 * t + 4 * j4 + i];
-                const float r0 = rev_of((double)(t0 + n16), th), r16 = rev_of(16.0, th);
+                const float r0 = rev_of((double)(t0 + 16 * tgi + n16), th), r16 = rev_of(16.0 * p.tg, th);
                 cs[t][i] = cos_rev(r0);
                 sn[t][i] = sin_rev(r0);
                 c16[t][i] = cos_rev(r16);
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconPara
 #pragma unroll
     for (int jj = 0; jj < VPL; ++jj)
         vtr[jj] = elem_ofs(g.ofs_v, 4 * j4 + (n16 >> 2), ES * (16 * jj + 4 * (n16 & 3)), g.cpr_kv, g.lg_kv);
-    const int la = p.shared_lr ? 0 : wave;  // this agent among the staged low-rank rows
+    const int la = p.shared_lr ? 0 : wa;  // this agent among the staged low-rank rows
     const uint32_t lko = lr_ofs(g, 0, la, n16, ES * BS * j4);  // rank slots of token n16
     uint32_t wtr[CPL];
 #pragma unroll
@@ -210,7 +216,7 @@ __global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconPara
         const char *st = smem + (size_t)(it % g.nst) * g.stage_bytes;
         const int tt = t0 + it * T;
 #pragma unroll 1
-        for (int u = 0; u < T / 16; ++u) {
+        for (int u = tgi; u < (T >> 4); u += p.tg) {
             const char *kvb = st + 16 * u * D * ES;
             const char *lkb = st + 16 * (g.ofs_lk + u * g.lr_grp);
             const char *lvb = st + 16 * (g.ofs_lv + u * g.lr_grp);
@@ -242,8 +248,9 @@ __global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconPara
                         sn[t][i] = s * c16[t][i] + c * s16[t][i];
                     }
             }
-            // S^T = K_base Q^T + dK Q^T (dK as bf16 hi + lo), two chains
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+            // S^T = K_base Q^T + dK Q^T (dK as bf16 hi + lo), three independent
+            // accumulator chains (base, hi, lo) so that no MFMA waits on the previous one
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 frag kf, dh, dl;
@@ -260,9 +267,9 @@ __global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconPara
                 }
                 acc = O::mma(kf, qB[s], acc);
                 acc2 = O::mma(dh, qB[s], acc2);
-                acc = O::mma(dl, qB[s], acc);
+                acc3 = O::mma(dl, qB[s], acc3);
             }
-            acc += acc2;
+            acc += acc2 + acc3;
             if (tok + 16 > t1) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -313,7 +320,7 @@ __global__ __launch_bounds__(64 * kReconWaves) void recon_split_kernel(ReconPara
 
     // ---- partials of this agent's rows (split sp)
     if (vm) {
-        const int64_t rec = ((int64_t)k * p.N * rpa + (int64_t)a * rpa + ria) * p.n_slots + sp;
+        const int64_t rec = ((int64_t)k * p.N * rpa + (int64_t)a * rpa + ria) * p.n_slots + sp * p.tg + tgi;
         float *po = p.p_o + rec * D + 4 * j4;
 #pragma unroll
         for (int jj = 0; jj < VPL; ++jj) *reinterpret_cast<f32x4 *>(po + 16 * jj) = o[jj];
@@ -332,7 +339,7 @@ static hipError_t launch_recon_one(const ReconParams &p, hipStream_t st) {
     const size_t lds = (size_t)p.nst * p.stage_bytes;
     const hipError_t e = ensure_lds<ReconSlot<R, ROPE>>(reinterpret_cast<const void *>(fn), (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(8 * p.per_xcd), dim3(64 * kReconWaves), lds, st, p);
+    hipLaunchKernelGGL(fn, dim3(8 * p.per_xcd), dim3(64 * recon_waves(ROPE)), lds, st, p);
     return hipGetLastError();
 }
 

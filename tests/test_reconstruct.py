@@ -62,6 +62,8 @@ CASES = [
     synth.Case(6, 16, 2, 128, 16, 777, shared_lr=True, name="shared low-rank"),
     synth.Case(3, 8, 2, 128, 16, 1000, q_len=3, name="multi-token decode"),
     synth.Case(1, 4, 1, 128, 32, 65, name="single agent, two tiles"),
+    synth.Case(2, 8, 2, 128, 16, 1500, name="two agents, four token groups each"),
+    synth.Case(12, 8, 2, 128, 16, 2000, name="twelve agents, two groups of six"),
 ]
 
 
