@@ -17,9 +17,12 @@
 //
 // MFMA form: out^T = A^T X^T over 16 columns x 16 tokens per tile
 // (v_mfma_f32_16x16x32_bf16): the A operand is 16 rows of A^T (one per output
-// column, k contiguous) read from LDS, the B operand 16 token rows of X read
-// straight from global memory (16 bytes per lane), so each lane ends with four
-// consecutive columns of one token, stored as one 8-byte bf16 write.
+// column, k contiguous), the B operand 16 token rows of X, both read from LDS,
+// so each lane ends with four consecutive columns of one token, stored as one
+// 8-byte bf16 write.  Both operands stream through a four-stage LDS ring of
+// 64-wide slices of the contraction (direct loads, three slices in flight):
+// with 128 tokens per workgroup the A^T rows are as many bytes as the X rows,
+// and the loop is bound by how many loads are in flight, not by the products.
 #include "device.h"
 #include "internal.h"
 
@@ -29,11 +32,16 @@ constexpr int kLrWaves = 4;           // waves per workgroup
 constexpr int kLrTokWave = 32;        // tokens per wave (two 16-token MFMA blocks)
 constexpr int kLrTok = kLrWaves * kLrTokWave;  // tokens per workgroup
 constexpr int kLrCols = 128;          // output columns per workgroup (8 tiles of 16)
-constexpr int kLrKc = 128;            // d_in per LDS chunk (256 bytes per A^T row)
+constexpr int kLrKc = 64;             // d_in per stage (128 bytes per row: 8 chunks of 16)
+constexpr int kLrStages = 4;
+constexpr int kLrRegion = 128 * kLrKc * 2;     // bytes of one region (A^T rows or X rows) of a stage
+constexpr int kLrStage = 2 * kLrRegion;        // A^T region, then X region
 
-// LDS: two chunks of kLrCols A^T rows of kLrKc bf16 (16 chunks of 16 bytes per
-// row, chunk q of row c stored at chunk q ^ (c & 15), so that 16 lanes reading
-// one logical chunk of 16 rows touch distinct banks).
+// Row x of a region holds chunk q (16 bytes) at physical chunk q ^ ((x >> 1) & 7):
+// the 16 rows an MFMA operand read touches (row pairs share a 256-byte bank
+// line) land on distinct banks.
+__device__ inline int lr_phys(int row, int q) { return q ^ ((row >> 1) & 7); }
+
 __global__ __launch_bounds__(64 * kLrWaves) void lr_project_kernel(LrParams p) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int lane = threadIdx.x & 63;
@@ -58,43 +66,34 @@ __global__ __launch_bounds__(64 * kLrWaves) void lr_project_kernel(LrParams p) {
         return static_cast<const bf16 *>(kv ? p.av : p.ak) + ((int64_t)na * p.r + j) * p.d_in;
     };
 
-    // ---- this wave's share of each A^T chunk fill: kLrCols rows x 16 chunks =
-    // 2048 chunks, 32 direct loads of 64 chunks; wave w issues loads w, w + 4, ...
-    // Load i covers rows 4i .. 4i + 3; lane l writes LDS chunk 64 i + l (row
-    // 4i + l / 16, physical chunk l % 16) from logical chunk (l % 16) ^ (row & 15).
-    constexpr int kLoads = kLrCols * 16 / 64;
-    constexpr int kLoadsPerWave = kLoads / kLrWaves;
-    uint32_t a_goff[kLoadsPerWave];  // byte offset within the chunk's k range
-    const bf16 *a_src[kLoadsPerWave];
+    // ---- this wave's loads of a stage: each region is 128 rows x 8 chunks =
+    // 16 direct loads of 64 chunks; wave w issues loads w, w + 4, w + 8, w + 12
+    // of both.  Load i covers rows 8i .. 8i + 7; lane l writes physical chunk
+    // l % 8 of row 8i + l / 8, read from that row's logical chunk.
+    constexpr int kPer = 16 / kLrWaves;  // loads per region per wave
+    const bf16 *a_src[kPer], *x_src[kPer];
 #pragma unroll
-    for (int u = 0; u < kLoadsPerWave; ++u) {
+    for (int u = 0; u < kPer; ++u) {
         const int i = wave + kLrWaves * u;
-        const int row = 4 * i + (lane >> 4);
-        const int phys = lane & 15, logical = phys ^ (row & 15);
-        const int c = c0 + (row < ncol ? row : ncol - 1);  // rows past the block repeat a valid one
-        a_src[u] = a_row(c);
-        a_goff[u] = (uint32_t)(16 * logical);
+        const int row = 8 * i + (lane >> 3);
+        const int logical = lr_phys(row, lane & 7);  // the swizzle is its own inverse
+        a_src[u] = a_row(c0 + (row < ncol ? row : ncol - 1)) + 8 * logical;  // rows past the block repeat a valid one
+        int64_t t = tb * kLrTok + row;
+        t = t < p.T ? t : p.T - 1;  // tokens past the end repeat the last one
+        x_src[u] = x + t * p.d_in + 8 * logical;
     }
     const uint32_t lds0 = lds_addr(smem);
-    auto fill = [&](int chunk, int buf) {
+    auto fill = [&](int chunk, int stage) {
         const int64_t kofs = (int64_t)chunk * kLrKc;
+        const uint32_t sb = lds0 + (uint32_t)(stage * kLrStage);
 #pragma unroll
-        for (int u = 0; u < kLoadsPerWave; ++u) {
+        for (int u = 0; u < kPer; ++u) {
             const int i = wave + kLrWaves * u;
-            const char *g = reinterpret_cast<const char *>(a_src[u] + kofs) + a_goff[u];
-            dma16(g, lds0 + (uint32_t)(buf * kLrCols * 256 + 1024 * i));
+            dma16(a_src[u] + kofs, sb + (uint32_t)(1024 * i));
+            dma16(x_src[u] + kofs, sb + (uint32_t)(kLrRegion + 1024 * i));
         }
     };
-
-    // ---- this wave's token rows (B operand), clamped to the last token
-    const int64_t tw = tb * kLrTok + wave * kLrTokWave;
-    const bf16 *xr[2];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        int64_t t = tw + 16 * b + n16;
-        t = t < p.T ? t : p.T - 1;
-        xr[b] = x + t * p.d_in + 8 * j4;
-    }
+    constexpr int kFpw = 2 * kPer;  // loads per wave per stage
 
     f32x4 acc[2][8];
 #pragma unroll
@@ -103,52 +102,37 @@ __global__ __launch_bounds__(64 * kLrWaves) void lr_project_kernel(LrParams p) {
         for (int jj = 0; jj < 8; ++jj) acc[b][jj] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     const int nchunks = p.d_in / kLrKc;
-    // X operands of a chunk: 4 contraction steps of 32 x 2 token blocks
-    Ops<bf16>::frag xf[2][4], xn[2][4];
-    auto load_x = [&](Ops<bf16>::frag (&dst)[2][4], int chunk) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) dst[b][s] = Ops<bf16>::load8(xr[b] + chunk * kLrKc + 32 * s);
-    };
-    fill(0, 0);
-    load_x(xf, 0);
+    for (int i = 0; i < kLrStages - 1 && i < nchunks; ++i) fill(i, i);
     for (int ch = 0; ch < nchunks; ++ch) {
-        const int buf = ch & 1;
-        // the next chunk's A^T rows and X rows are requested before this chunk's products
-        if (ch + 1 < nchunks) {
-            fill(ch + 1, buf ^ 1);
-            load_x(xn, ch + 1);
-            wait_vmcnt(kLoadsPerWave + 8);  // this chunk's fill (and X) landed; the next one's in flight
-        } else {
-            wait_vmcnt(0);
-        }
-        __syncthreads();  // every wave's share of this chunk's A^T rows is in LDS
-        const char *st = smem + buf * kLrCols * 256;
+        const int later = (nchunks - 1 - ch) < (kLrStages - 2) ? (nchunks - 1 - ch) : (kLrStages - 2);
+        wait_vmcnt(later * kFpw);  // this wave's loads of slice ch have landed
+        ring_barrier();            // ... everyone's, and everyone is done with slice ch - 1
+        if (ch + kLrStages - 1 < nchunks) fill(ch + kLrStages - 1, (ch + kLrStages - 1) % kLrStages);
+        const char *st = smem + (size_t)(ch % kLrStages) * kLrStage;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < kLrKc / 32; ++s) {
+            Ops<bf16>::frag xf[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const int row = kLrTokWave * wave + 16 * b + n16;
+                xf[b] = Ops<bf16>::load8(
+                    reinterpret_cast<const bf16 *>(st + kLrRegion + row * 128 + 16 * lr_phys(row, 4 * s + j4)));
+            }
 #pragma unroll
             for (int jj = 0; jj < 8; ++jj) {
                 if (jj < nct) {
                     const int row = 16 * jj + n16;
-                    const int phys = (4 * s + j4) ^ (row & 15);
-                    Ops<bf16>::frag af = Ops<bf16>::load8(
-                        reinterpret_cast<const bf16 *>(st + row * 256 + 16 * phys));
+                    const Ops<bf16>::frag af =
+                        Ops<bf16>::load8(reinterpret_cast<const bf16 *>(st + row * 128 + 16 * lr_phys(row, 4 * s + j4)));
 #pragma unroll
-                    for (int b = 0; b < 2; ++b) acc[b][jj] = Ops<bf16>::mma(af, xf[b][s], acc[b][jj]);
+                    for (int b = 0; b < 2; ++b) acc[b][jj] = Ops<bf16>::mma(af, xf[b], acc[b][jj]);
                 }
             }
-        }
-        __syncthreads();  // everyone is done with this buffer before it is refilled
-        if (ch + 1 < nchunks) {
-#pragma unroll
-            for (int b = 0; b < 2; ++b)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) xf[b][s] = xn[b][s];
         }
     }
 
     // ---- store: lane (n16, j4) holds columns c0 + 16 jj + 4 j4 + i of token tw + 16 b + n16
+    const int64_t tw = tb * kLrTok + wave * kLrTokWave;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         const int64_t t = tw + 16 * b + n16;
@@ -171,7 +155,7 @@ hipError_t launch_lr_project(const LrParams &p, hipStream_t st) {
     if (p.T == 0) return hipSuccess;
     const int64_t tblocks = (p.T + kLrTok - 1) / kLrTok;
     const int blocks_per_x = (p.cols_per_xset + kLrCols - 1) / kLrCols;
-    const size_t lds = 2 * kLrCols * 256;
+    const size_t lds = (size_t)kLrStages * kLrStage;
     struct Slot {};
     const hipError_t e = ensure_lds<Slot>(reinterpret_cast<const void *>(lr_project_kernel), (int)lds);
     if (e != hipSuccess) return e;
