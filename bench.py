@@ -238,7 +238,7 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k
     import shared_base_residual_amd as R
     import synth
 
-    case = synth.CONFIGS[config]
+    case = synth.WORKLOADS[config]
     seed = config if seed is None else seed
     ab = algorithmic_bytes(case, k8)
     layers = case.layers
@@ -474,7 +474,7 @@ def measure_reconstruct(config, K, W, dev, hip, stream, probe, rope):
     import shared_base_residual_amd as R
     import synth
 
-    case = synth.CONFIGS[config].replace(layers=1)
+    case = synth.WORKLOADS[config].replace(layers=1)
     ab = algorithmic_bytes(case)
     say(f"[bench] rebuilt keys ({case.name}, rope={rope}): drawing inputs")
     x = synth.make_inputs(case, config)
@@ -517,7 +517,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=4, help="headline workload (synth.CONFIGS index)")
+    ap.add_argument("--config", type=int, default=4, help="headline workload (synth.WORKLOADS index)")
     ap.add_argument("--sub", default="1,2,3", help="workloads measured as sub-records ('' for none)")
     ap.add_argument("--replicas", type=int, default=0, help="input sets rotated (0: auto)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -566,7 +566,7 @@ def main():
         import synth
 
         say("[bench] cpu baseline")
-        res["cpu_baseline"] = cpu_baseline(synth.CONFIGS[args.config],
+        res["cpu_baseline"] = cpu_baseline(synth.WORKLOADS[args.config],
                                            args.config if args.seed is None else args.seed)
     print(json.dumps(res), flush=True)
 

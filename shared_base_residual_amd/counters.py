@@ -54,7 +54,7 @@ def run(config: int) -> None:
     import shared_base_residual_amd as R
     import synth
 
-    case = synth.CONFIGS[config]
+    case = synth.WORKLOADS[config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     # calibration: one plain copy of known size
@@ -106,7 +106,7 @@ def summarize(config: int, fetch_dir: str, write_dir: str) -> None:
     import synth
     from shared_base_residual_amd.build import source_hash
 
-    case = synth.CONFIGS[config]
+    case = synth.WORKLOADS[config]
     kern, wl = WORKLOADS[config]
     cf, kf = _per_dispatch(fetch_dir, "FETCH_SIZE")
     cw, kw = _per_dispatch(write_dir, "WRITE_SIZE")
@@ -165,7 +165,7 @@ def summarize_mfma(config: int, d: str) -> None:
     import synth
     from shared_base_residual_amd.build import source_hash
 
-    case = synth.CONFIGS[config]
+    case = synth.WORKLOADS[config]
     kern, wl = WORKLOADS[config]
     paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
     if not paths:
@@ -217,7 +217,7 @@ def summarize_trace(config: int, d: str, bench_json: str, cmd: str) -> None:
     import synth
     from shared_base_residual_amd.build import source_hash
 
-    case = synth.CONFIGS[config]
+    case = synth.WORKLOADS[config]
     kern, wl = WORKLOADS[config]
     with open(bench_json) as f:
         line = [l for l in f.read().splitlines() if l.startswith("{")][-1]

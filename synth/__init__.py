@@ -75,7 +75,7 @@ class Case:
 
 
 # The five workloads (one entry per call shape).
-CONFIGS = {
+WORKLOADS = {
     0: Case(2, 4, 2, 64, 8, 256, dtype="f32", name="tiny decode"),
     1: Case(4, 32, 8, 128, 16, 32768, name="Llama-3-8B-shaped decode"),
     2: Case(16, 32, 8, 128, 64, 8192, priv_len=512, page_size=16, n_phys_pages=1024,

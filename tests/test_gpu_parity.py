@@ -83,7 +83,7 @@ def compare(case, x, *, with_b0=False, what="", row_mask=None):
 
 @pytest.mark.parametrize("variant", ["base", "stress"])
 def test_tiny_decode_fp32(variant):
-    c = synth.CONFIGS[0]
+    c = synth.WORKLOADS[0]
     kw = synth.STRESS if variant == "stress" else {}
     seed = 0 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0)
     compare(c, synth.make_inputs(c, seed, **kw), with_b0=True, what=f"tiny decode fp32 {variant}")
@@ -91,7 +91,7 @@ def test_tiny_decode_fp32(variant):
 
 @pytest.mark.parametrize("variant", ["base", "stress"])
 def test_llama8b_decode(variant):
-    c = synth.CONFIGS[1]
+    c = synth.WORKLOADS[1]
     kw = synth.STRESS if variant == "stress" else {}
     seed = 1 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0)
     compare(c, synth.make_inputs(c, seed, **kw), with_b0=(variant == "base"), what=f"8B decode {variant}")
@@ -99,7 +99,7 @@ def test_llama8b_decode(variant):
 
 @pytest.mark.parametrize("variant", ["base", "stress"])
 def test_paged_cow_decode(variant):
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS[2]
     kw = synth.STRESS if variant == "stress" else {}
     seed = 2 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0)
     x = synth.make_inputs(c, seed, **kw)
@@ -112,7 +112,7 @@ def test_paged_cow_decode(variant):
 def test_shared_lr_chunked_prefill_all_rows(variant):
     """The full BaseLRShared prefill (32 agents x 256-token chunks, L = 16384):
     every one of the 262,144 query rows against the oracle."""
-    c = synth.CONFIGS[3]
+    c = synth.WORKLOADS[3]
     kw = synth.STRESS if variant == "stress" else {}
     seed = 3 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0)
     x = synth.make_inputs(c, seed, **kw)
@@ -128,7 +128,7 @@ def test_full_depth_decode_all_rows_of_eight_layers():
     eight layers (first and last among them) is checked against the oracle,
     per layer and aggregated over the eight layers' elements, lse included."""
     R = rattn()
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     say(f"[gpu] 70B full-depth decode: generating {c.layers} layers on the device")
     layers = [synth.make_inputs_torch(c, 4, l, DEV) for l in range(c.layers)]
     outs = [torch.empty(layers[0]["q"].shape, device=DEV, dtype=torch.float32) for _ in range(c.layers)]
@@ -215,7 +215,7 @@ def test_edge_cases(case):
 
 
 def test_run_twice_bitwise():
-    c = synth.CONFIGS[1].replace(prefix_len=8192)
+    c = synth.WORKLOADS[1].replace(prefix_len=8192)
     x = synth.make_inputs(c, 5)
     a, la = run_gpu(c, x)
     b, lb = run_gpu(c, x)
@@ -226,7 +226,7 @@ def test_run_twice_bitwise():
 
 def test_gather_base_bit_exact():
     R = rattn()
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS[2]
     x = synth.make_inputs(c, 2)
     say("[gpu] gather_base on the paged workload")
     t = synth.to_torch(x, DEV)
@@ -248,7 +248,7 @@ def test_gather_base_bit_exact():
 def test_shuffled_table_bitwise_equals_identity():
     """Output depends only on logical token order: a shuffled pool with its table and
     the identity pool give bit-identical results; unused NaN pages change nothing."""
-    c = synth.CONFIGS[2].replace(prefix_len=2048, n_phys_pages=300, priv_len=100)
+    c = synth.WORKLOADS[2].replace(prefix_len=2048, n_phys_pages=300, priv_len=100)
     x = synth.make_inputs(c, 9)
     say("[gpu] shuffled vs identity page table")
     a, la = run_gpu(c, x)

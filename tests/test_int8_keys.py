@@ -124,7 +124,7 @@ def compare_k8(case, x, what, with_b0=False):
 @pytest.mark.parametrize("variant", ["base", "stress"])
 def test_int8_keys_llama8b_decode(variant):
     """The 8B-shaped decode (4 agents, 32768-token prefix, r = 16) over int8 keys."""
-    c = synth.CONFIGS[1]
+    c = synth.WORKLOADS[1]
     kw = synth.STRESS if variant == "stress" else {}
     x = synth.make_inputs(c, 1 + (synth.STRESS_SEED_OFFSET if variant == "stress" else 0), **kw)
     compare_k8(c, x, f"8B-shaped decode {variant}", with_b0=(variant == "base"))
@@ -133,7 +133,7 @@ def test_int8_keys_llama8b_decode(variant):
 @pytest.mark.gpu
 def test_int8_keys_70b_layer():
     """One layer of the 70B-shaped decode (8 agents, g = 8, 65536-token prefix)."""
-    c = synth.CONFIGS[4].replace(layers=1)
+    c = synth.WORKLOADS[4].replace(layers=1)
     x = synth.make_inputs(c, 4)
     compare_k8(c, x, "70B-shaped layer", with_b0=True)
 

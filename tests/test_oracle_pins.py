@@ -105,7 +105,8 @@ def test_b_zero_is_plain_attention(paged):
 
 def test_single_agent_is_standard_attention():
     """N = 1: the call is one adapter's attention over K_1 = K_base + Lk Bk, V_1 likewise
-    (the benchmark spec's decomposition), computed here by the library routine."""
+    (the decomposition of an adapted cache into base plus low-rank residual), computed here by the
+    library routine."""
     case = synth.Case(1, 4, 2, 8, 3, 33, priv_len=5, dtype="f32")
     x = synth.make_inputs(case, 4, b_sigma=0.3)
     o, _ = oracle.attend(case, x)

@@ -92,7 +92,7 @@ def test_reconstruct_without_rotation_matches_decode():
     """Same inputs, no rotation: the rebuilt-key kernel and rattn_decode agree
     within the bars (they differ only in rounding order)."""
     torch = pytest.importorskip("torch")
-    c = synth.CONFIGS[1]
+    c = synth.WORKLOADS[1]
     x = synth.make_inputs(c, 1, **synth.STRESS)
     got, _ = run(c, x)
     t = synth.to_torch(x, DEV)
