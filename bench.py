@@ -182,7 +182,39 @@ def cpu_baseline(case, seed, budget_s=12.0):
     return {"value": round(pairs_per_call(case) * frac / t / 1e9, 6), "unit": "Gtok/s", "cores": threads,
             "kind": "oracle", "cpu": cpu_model(),
             "sample": f"{what} ({case.name}, one layer), {len(times)} runs, median {t:.3f} s, fp64, "
-                      f"{threads} threads"}
+                      f"{threads} threads",
+            "one_thread": [one_thread_baseline(c, c) for c in (0, 1, 2)]}
+
+
+def one_thread_baseline(config, seed, budget_s=3.0):
+    """The oracle on one host thread for a small workload: the whole call of the
+    tiny decode, else the query rows of agent 0 and KV head 0 (one materialised
+    cache, its g rows), the rate scaled by the fraction of rows computed."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    case = synth.WORKLOADS[config]
+    x = synth.make_inputs(case, seed)
+    mask, frac, what = None, 1.0, "whole call"
+    if config != 0:
+        g = case.n_q_heads // case.n_kv_heads
+        mask = np.zeros((case.n_agents, case.q_len, case.n_q_heads), bool)
+        mask[0, :, :g] = True
+        frac = float(mask.sum()) / mask.size
+        what = "agent 0's rows of KV head 0"
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.attend(case, x, n_threads=1, row_mask=mask)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s or len(times) >= 9:
+            break
+    t = statistics.median(times)
+    return {"workload": case.name, "value": round(pairs_per_call(case) * frac / t / 1e9, 7), "unit": "Gtok/s",
+            "cores": 1, "sample": f"{what}, {len(times)} runs, median {t:.4f} s, fp64, 1 thread"}
 
 
 def traffic_from_counters(kernel_key):
@@ -376,8 +408,6 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k
 # hit with an adapter miss), Llama-3-8B-shaped (d_in = 4096, r = 16); and a
 # 4096-token append of base rows (H_kv = 8, d = 128, bf16) into a paged pool
 # whose partly filled last page is shared (one copy-on-write page).
-LR_PREFILL = dict(name="BaseShared LR prefill (low-rank cache write)", n_sets=4, d_in=4096, r=16, T=32768)
-APPEND = dict(name="paged base append with copy-on-write", HK=8, D=128, ps=16, cur_len=8200, T=4096)
 
 
 def measure_lr_prefill(K, W, dev, hip, stream, probe):
@@ -387,7 +417,7 @@ def measure_lr_prefill(K, W, dev, hip, stream, probe):
     import shared_base_residual_amd as R
     import synth
 
-    c = LR_PREFILL
+    c = synth.LR_PREFILL
     say(f"[bench] {c['name']}: drawing inputs")
     g = torch.Generator(device=dev)
     g.manual_seed(7)
@@ -407,7 +437,8 @@ def measure_lr_prefill(K, W, dev, hip, stream, probe):
     achieved = nbytes / (ms / 1e3) / 1e9
     rows = c["n_sets"] * c["T"]
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "lr_project_kernel",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_counters("lr_prefill"),
+            "kernel": "lr_project_kernel",
             "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2), "launches_timed": K}
     if probe:
         roof["achievable"] = probe["achievable"]
@@ -425,8 +456,9 @@ def measure_append(K, W, dev, hip, stream, probe):
     import torch
 
     import shared_base_residual_amd as R
+    import synth
 
-    c = APPEND
+    c = synth.APPEND
     HK, D, ps, L0, T = c["HK"], c["D"], c["ps"], c["cur_len"], c["T"]
     n_phys = 2 * (-(-(L0 + T) // ps)) + 8
     say(f"[bench] {c['name']}")
@@ -452,7 +484,8 @@ def measure_append(K, W, dev, hip, stream, probe):
     nbytes = 2 * (2 * HK * T * D * 2) + 2 * (2 * HK * off * D * 2) + table.size * 4
     achieved = nbytes / (ms / 1e3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "append_kv_kernel",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_counters("append"),
+            "kernel": "append_kv_kernel",
             "bytes_per_launch": nbytes, "avg_launch_us": round(ms * 1e3, 2), "launches_timed": K}
     if probe:
         roof["achievable"] = probe["achievable"]
@@ -495,7 +528,8 @@ def measure_reconstruct(config, K, W, dev, hip, stream, probe, rope):
     torch.cuda.synchronize()
     achieved = ab["call"] / (ms / 1e3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_counters(f"recon_cfg{config}" + ("_rope" if rope else "")),
             "kernel": "recon_split_kernel + combine_kernel (whole call)", "bytes_per_launch": ab["call"],
             "avg_launch_us": round(ms * 1e3, 2), "launches_timed": K}
     if probe:

@@ -86,6 +86,13 @@ WORKLOADS = {
 }
 
 
+# Cache-write workloads (shapes only): the low-rank projection of a shared
+# context for four agents (one X, per-agent A), and the append of new base rows
+# into a paged pool whose last page is shared (so the first write copies it).
+LR_PREFILL = dict(name="BaseShared LR prefill (low-rank cache write)", n_sets=4, d_in=4096, r=16, T=32768)
+APPEND = dict(name="paged base append with copy-on-write", HK=8, D=128, ps=16, cur_len=8200, T=4096)
+
+
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp64/fp32 -> bf16 bit patterns (uint16) via fp32, round to nearest even."""
     x32 = np.ascontiguousarray(x, dtype=np.float32)
