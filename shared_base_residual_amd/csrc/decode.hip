@@ -828,13 +828,21 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     acc.l = 0.0f;
     acc.ls = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- the ring: wait for tile i, refill the stage freed by tile i-1, compute tile i
+    // ---- the ring.  Load waves: wait for their loads of tile i, meet the others
+    // at the ring barrier (everyone is done with tile i-1), refill that stage.
+    // Compute waves: meet at the barrier (tile i has landed), compute it.  Each
+    // role runs a loop of its own with the same barriers, so neither carries the
+    // other's state through its loop.
     const int spw = g.T / (16 * TG);  // 16-token steps per wave per tile
-    for (int i = 0; i < n_tiles; ++i) {
-        const int later = (n_tiles - 1 - i) < (g.nst - 2) ? (n_tiles - 1 - i) : (g.nst - 2);
-        wait_vmcnt(later * fpw);  // this wave's loads of tile i have landed
-        ring_barrier();           // ... everyone's, and everyone is done with tile i-1
-        if (fp.fpw && i + g.nst - 1 < n_tiles) fill(i + g.nst - 1, (i + g.nst - 1) % g.nst);
+    if (!compute_wave) {
+        for (int i = 0; i < n_tiles; ++i) {
+            const int later = (n_tiles - 1 - i) < (g.nst - 2) ? (n_tiles - 1 - i) : (g.nst - 2);
+            wait_vmcnt(later * fpw);  // this wave's loads of tile i have landed
+            ring_barrier();
+            if (fpw && i + g.nst - 1 < n_tiles) fill(i + g.nst - 1, (i + g.nst - 1) % g.nst);
+        }
+    } else for (int i = 0; i < n_tiles; ++i) {
+        ring_barrier();
         if (wave_on) {
             const char *st = smem + (size_t)(i % g.nst) * g.stage_bytes;
             const int tt = t0 + i * g.T;
