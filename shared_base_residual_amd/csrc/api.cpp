@@ -510,7 +510,7 @@ int make_recon_plan(const rattn_desc *d, bool rope, ReconPlan *pl) {
     p.c = scale * 1.44269504088896340736f;
     // agents in balanced groups of at most one per wave; each agent's rows take
     // waves / agents waves, at most one per 16-token step of a stage
-    const int waves = rattn::recon_waves(rope);
+    const int waves = rattn::recon_waves(rope, r);
     const int n_groups = (int)cdiv(N, waves);
     p.apg = (int)cdiv(N, n_groups);
     p.n_ag = (int)cdiv(N, p.apg);

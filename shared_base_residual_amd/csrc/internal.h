@@ -243,11 +243,11 @@ namespace rattn {
 
 // Decode with the residual keys rebuilt per token in registers (and rotated by
 // position when a frequency vector is given): one workgroup per (split, KV
-// head, group of agents), of eight waves (four with the rotation, whose state
-// takes the registers of a second wave per SIMD).  Each agent of the group
+// head, group of agents), of eight waves (four with the rotation at ranks
+// above 16, whose state takes the registers of a second wave per SIMD).  Each agent of the group
 // takes tg = waves / agents waves (at most the steps of a stage), which share
 // out the 16-token steps of every stage and write separate partials.
-constexpr int recon_waves(bool rope) { return rope ? 4 : 8; }
+constexpr int recon_waves(bool rope, int r) { return rope && r > 16 ? 4 : 8; }
 constexpr int kReconTMax = 64;  // tokens per LDS stage (64, or 32 when three such stages do not fit)
 
 struct ReconParams {

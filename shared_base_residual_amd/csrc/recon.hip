@@ -33,7 +33,8 @@
 // the stage's 16-token steps (wave tg_i takes steps tg_i, tg_i + tg, ...) and
 // each keep their own softmax state, written as partial slot split * tg + tg_i:
 // two waves per SIMD hide the long dependent chain of a step (rank product,
-// conversion, score, softmax, value products).  Partials go to the decode
+// conversion, score, softmax, value products); with the rotation at rank 32
+// its state leaves room for one wave per SIMD (four waves).  Partials go to the decode
 // workspace layout and the decode merge kernel finishes the call.
 #include "device.h"
 #include "internal.h"
@@ -52,7 +53,7 @@ __device__ inline float rev_of(double pos, float theta) {
 }
 
 template <int R, bool ROPE>
-__global__ __launch_bounds__(64 * recon_waves(ROPE)) void recon_split_kernel(ReconParams p) {
+__global__ __launch_bounds__(64 * recon_waves(ROPE, R)) void recon_split_kernel(ReconParams p) {
     constexpr int D = 128, KS = D / 32, VPL = D / 16, ES = 2;
     constexpr int CPL = R / 16;  // residual column tiles of W
     const int T = p.T;
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(64 * recon_waves(ROPE)) void recon_split_kernel(Rec
     src.tlast = t1 > t0 ? t1 - 1 : t0;
 
     GroupFill fp;
-    make_group_fill<bf16, D>(fp, g, src, true, wave, lane, recon_waves(ROPE));  // a multiple of T / 16
+    make_group_fill<bf16, D>(fp, g, src, true, wave, lane, recon_waves(ROPE, R));  // a multiple of T / 16
     const int n_tiles = (t1 - t0 + T - 1) / T;
     const int fpw = fp.fpw;
     auto fill = [&](int tile, int stage) {
@@ -248,9 +249,8 @@ __global__ __launch_bounds__(64 * recon_waves(ROPE)) void recon_split_kernel(Rec
                         sn[t][i] = s * c16[t][i] + c * s16[t][i];
                     }
             }
-            // S^T = K_base Q^T + dK Q^T (dK as bf16 hi + lo), three independent
-            // accumulator chains (base, hi, lo) so that no MFMA waits on the previous one
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
+            // S^T = K_base Q^T + dK Q^T (dK as bf16 hi + lo), two accumulator chains
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 frag kf, dh, dl;
@@ -267,9 +267,9 @@ __global__ __launch_bounds__(64 * recon_waves(ROPE)) void recon_split_kernel(Rec
                 }
                 acc = O::mma(kf, qB[s], acc);
                 acc2 = O::mma(dh, qB[s], acc2);
-                acc3 = O::mma(dl, qB[s], acc3);
+                acc = O::mma(dl, qB[s], acc);
             }
-            acc += acc2 + acc3;
+            acc += acc2;
             if (tok + 16 > t1) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -339,7 +339,7 @@ static hipError_t launch_recon_one(const ReconParams &p, hipStream_t st) {
     const size_t lds = (size_t)p.nst * p.stage_bytes;
     const hipError_t e = ensure_lds<ReconSlot<R, ROPE>>(reinterpret_cast<const void *>(fn), (int)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, dim3(8 * p.per_xcd), dim3(64 * recon_waves(ROPE)), lds, st, p);
+    hipLaunchKernelGGL(fn, dim3(8 * p.per_xcd), dim3(64 * recon_waves(ROPE, R)), lds, st, p);
     return hipGetLastError();
 }
 
