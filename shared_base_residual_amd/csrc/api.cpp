@@ -403,9 +403,11 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         off += (bytes + 255) & ~(size_t)255;
         return o;
     };
+    // partial O and W: fp16 (divided by the row's weight sum) on the bf16 path, fp32 otherwise
+    const size_t pes = d->dtype == RATTN_BF16 ? 2 : sizeof(float);
     pl->off_ml = take((size_t)rows_kv * p.n_slots * 2 * sizeof(float));
-    pl->off_o = take((size_t)rows_kv * p.n_slots * D * sizeof(float));
-    pl->off_w = take(resid ? (size_t)rows_kv * p.n_slots * r * sizeof(float) : 0);
+    pl->off_o = take((size_t)rows_kv * p.n_slots * D * pes);
+    pl->off_w = take(resid ? (size_t)rows_kv * p.n_slots * r * pes : 0);
     pl->total = off;
     return RATTN_OK;
 }
@@ -566,8 +568,8 @@ int make_recon_plan(const rattn_desc *d, bool rope, ReconPlan *pl) {
         return o;
     };
     pl->off_ml = take((size_t)rows_kv * p.n_slots * 2 * sizeof(float));
-    pl->off_o = take((size_t)rows_kv * p.n_slots * D * sizeof(float));
-    pl->off_w = take((size_t)rows_kv * p.n_slots * r * sizeof(float));
+    pl->off_o = take((size_t)rows_kv * p.n_slots * D * 2);  // fp16, divided by l
+    pl->off_w = take((size_t)rows_kv * p.n_slots * r * 2);
     pl->total = off;
     return RATTN_OK;
 }
@@ -646,8 +648,8 @@ int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_
     p.out = a->out;
     p.lse = a->lse;
     p.p_ml = reinterpret_cast<float *>(w + pl.off_ml);
-    p.p_o = reinterpret_cast<float *>(w + pl.off_o);
-    p.p_w = reinterpret_cast<float *>(w + pl.off_w);
+    p.p_o = w + pl.off_o;
+    p.p_w = w + pl.off_w;
     if (!(d->rank > 0 && d->prefix_len > 0)) p.r = 0;  // no residual without a prefix
     return hip_status(rattn::launch_decode(d->dtype == RATTN_BF16, p, d->head_dim, pl.cpad, pl.lds, stages,
                                            static_cast<hipStream_t>(stream)));
@@ -892,8 +894,8 @@ int rattn_decode_reconstruct(const rattn_desc *desc, const rattn_args *args, con
     p.bk = args->bk;
     p.theta = rope_theta;
     p.p_ml = reinterpret_cast<float *>(w + pl.off_ml);
-    p.p_o = reinterpret_cast<float *>(w + pl.off_o);
-    p.p_w = reinterpret_cast<float *>(w + pl.off_w);
+    p.p_o = w + pl.off_o;
+    p.p_w = w + pl.off_w;
     rattn::DecodeParams &q = pl.dp;
     q.p_ml = p.p_ml;
     q.p_o = p.p_o;

@@ -934,11 +934,15 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
 
     // ---- write this split's partial state of every valid row
     if (kBf16 && tg == 0 && vm) {
-        // natural order: tile jj, element i of this lane is d (or c) = 16*jj + 4*j4 + i
+        // natural order: tile jj, element i of this lane is d (or c) = 16*jj + 4*j4 + i;
+        // O and W divided by the row's weight sum, as fp16 (a row without a visible
+        // token, l = 0, stores zeros and gets weight 0 in the merge)
         const int64_t rec = ((int64_t)k * p.N * p.rpa + grow) * p.n_slots + slot;
-        float *po = p.p_o + rec * D + 4 * j4;
+        const float inv_l = l_run > 0.0f ? 1.0f / l_run : 0.0f;
+        f16 *po = static_cast<f16 *>(p.p_o) + rec * D + 4 * j4;
+        f16 *pw = static_cast<f16 *>(p.p_w) + rec * p.r;
 #pragma unroll
-        for (int jj = 0; jj < VPL; ++jj) *reinterpret_cast<f32x4 *>(po + 16 * jj) = acc.o[jj];
+        for (int jj = 0; jj < VPL; ++jj) *reinterpret_cast<f16x4 *>(po + 16 * jj) = to_f16x4(acc.o[jj] * inv_l);
         if (resid) {
             const int arel = agent_m - blk.a0;
             if constexpr (MASKED) {
@@ -950,7 +954,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int c = 16 * jj + 4 * j4 + i;
-                        if (c < cvalid) p.p_w[rec * p.r + (c & (p.r - 1))] = acc.w[jj][i];
+                        if (c < cvalid) pw[c & (p.r - 1)] = (f16)(acc.w[jj][i] * inv_l);
                     }
             } else {
                 // the lane's four columns c0 .. c0 + 3 of tile jj belong to one agent (r >= 8)
@@ -958,7 +962,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
                 for (int jj = 0; jj < CPLx; ++jj) {
                     const int c0 = 16 * jj + 4 * j4;
                     if (c0 < cvalid && (p.shared_lr || (c0 >> p.lr_shift) == arel))
-                        *reinterpret_cast<f32x4 *>(p.p_w + rec * p.r + (c0 & (p.r - 1))) = acc.w[jj];
+                        *reinterpret_cast<f16x4 *>(pw + (c0 & (p.r - 1))) = to_f16x4(acc.w[jj] * inv_l);
                 }
             }
         }
@@ -971,7 +975,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int jj = 0; jj < VPL; ++jj) ov[VPL * i + jj] = acc.o[jj][i];
-        float *po = p.p_o + rec * D + 4 * VPL * j4;
+        float *po = static_cast<float *>(p.p_o) + rec * D + 4 * VPL * j4;
 #pragma unroll
         for (int c = 0; c < VPL; ++c)
             *reinterpret_cast<f32x4 *>(po + 4 * c) = f32x4{ov[4 * c], ov[4 * c + 1], ov[4 * c + 2], ov[4 * c + 3]};
@@ -983,7 +987,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
                 for (int jj = 0; jj < CPLx; ++jj) {
                     const int c = CPLx * (4 * j4 + i) + jj;
                     if (c < cvalid && (p.shared_lr || (c >> p.lr_shift) == arel))
-                        p.p_w[rec * p.r + (c & (p.r - 1))] = acc.w[jj][i];
+                        static_cast<float *>(p.p_w)[rec * p.r + (c & (p.r - 1))] = acc.w[jj][i];
                 }
         }
         if (j4 == 0) *reinterpret_cast<float2 *>(p.p_ml + rec * 2) = float2{m_run, l_run};
@@ -1028,22 +1032,33 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     // this thread's slot statistics (one slot per thread: n_slots <= kMaxSlots = NT),
     // loaded first: the weight pass waits for it alone
     const float2 ml = tid < ns ? *reinterpret_cast<const float2 *>(p.p_ml + (rec0 + tid) * 2) : float2{-3.0e38f, 0.0f};
-    // first batch of O (float4 q = slot * D/4 + column group), W and Bv, issued now
-    const f32x4 *po = reinterpret_cast<const f32x4 *>(p.p_o + rec0 * D);
+    // Partial O and W, read four elements at a time (q = slot * D/4 + column group):
+    // fp16 divided by the slot's weight sum on the bf16 path (so slot s enters with
+    // weight w_s l_s), fp32 unnormalised otherwise (weight w_s).
+    constexpr bool kHalf = sizeof(T) == 2;
+    constexpr int PE = kHalf ? 2 : 4;
+    auto load4 = [](const char *b, int q) -> f32x4 {
+        if constexpr (kHalf)
+            return __builtin_convertvector(*reinterpret_cast<const f16x4 *>(b + 8 * (int64_t)q), f32x4);
+        else
+            return *reinterpret_cast<const f32x4 *>(b + 16 * (int64_t)q);
+    };
+    // first batch of O, W and Bv, issued now
+    const char *po = static_cast<const char *>(p.p_o) + rec0 * D * PE;
     const int nq = ns * D4;
     f32x4 ob[B];
 #pragma unroll
     for (int u = 0; u < B; ++u) {
         const int q = tid + u * NT;
-        ob[u] = q < nq ? po[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+        ob[u] = q < nq ? load4(po, q) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const f32x4 *pw = reinterpret_cast<const f32x4 *>(p.p_w + rec0 * (wres ? r : 0));
+    const char *pw = static_cast<const char *>(p.p_w) + rec0 * (wres ? r : 0) * PE;
     const int nqw = wres ? nps * R4 : 0;
     f32x4 wb[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int q = tid + u * NT;
-        wb[u] = q < nqw ? pw[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+        wb[u] = q < nqw ? load4(pw, q) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // Bv rows: thread t takes columns 8 (t % CPR) .. + 7 of rows j = t / CPR + RPR u
     // (CPR = D / 8 threads per row, RPR = NT / CPR rows per round), every row of
@@ -1069,7 +1084,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
         M = lane_max64(m1.x);
         const float w1 = lane < ns ? fexp2(m1.x - M) : 0.0f;
         Lsum = lane_group_sum(w1 * m1.y, 1);
-        s_w[wv * 64 + lane] = w1;
+        s_w[wv * 64 + lane] = kHalf ? w1 * m1.y : w1;
         __builtin_amdgcn_wave_barrier();
         sw = s_w + wv * 64;
     } else {
@@ -1080,7 +1095,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 #pragma unroll
         for (int i = 1; i < NWV; ++i) M = fmaxf(M, s_red[i]);
         const float w = tid < ns ? fexp2(ml.x - M) : 0.0f;
-        s_w[tid] = w;
+        s_w[tid] = kHalf ? w * ml.y : w;
         const float lloc = lane_group_sum(w * ml.y, 1);
         if (lane == 0) s_red[NWV + wv] = lloc;
         __syncthreads();
@@ -1101,7 +1116,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 #pragma unroll
         for (int u = 0; u < B; ++u) {
             const int q = q0 + tid + u * NT;
-            ob[u] = q < nq ? po[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+            ob[u] = q < nq ? load4(po, q) : f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int u = 0; u < B; ++u) {
@@ -1118,7 +1133,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
         const int q = tid + u * NT;
         if (q < nqw) wacc += sw[q / R4] * wb[u];
     }
-    for (int q = tid + 2 * NT; q < nqw; q += NT) wacc += sw[q / R4] * pw[q];
+    for (int q = tid + 2 * NT; q < nqw; q += NT) wacc += sw[q / R4] * load4(pw, q);
     if (wres) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) wacc[e] = lane_group_sum(wacc[e], R4);

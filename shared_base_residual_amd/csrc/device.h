@@ -148,6 +148,10 @@ __device__ inline float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // accumulator at minus that value.
 typedef _Float16 f16;
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Four floats to fp16 (round to nearest even).
+__device__ inline f16x4 to_f16x4(f32x4 x) { return __builtin_convertvector(x, f16x4); }
 
 __device__ inline f16x8 codes_to_f16(uint32_t w0, uint32_t w1) {
     constexpr uint32_t kHi = 0x64646464u;  // v_perm_b32 selectors 4..7 take bytes of the first operand

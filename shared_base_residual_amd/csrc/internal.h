@@ -132,9 +132,10 @@ struct DecodeParams {
     const int32_t *table;
     const void *lk, *lv, *bk, *bv, *kp, *vp;
     float *out, *lse;
-    float *p_ml;      // [H_kv, N*rpa, n_slots, 2]  running max (log2 units), sum of weights
-    float *p_o;       // [H_kv, N*rpa, n_slots, d]  unnormalised P V_base (+ private P V)
-    float *p_w;       // [H_kv, N*rpa, n_slots, r]  unnormalised P Lv
+    float *p_ml;      // [H_kv, N*rpa, n_slots, 2]  running max (log2 units), sum of weights l
+    void *p_o;        // [H_kv, N*rpa, n_slots, d]  P V_base (+ private P V): fp32 unnormalised (fp32
+                      // path); fp16 divided by l (bf16 path: half the bytes, every value within |V|)
+    void *p_w;        // [H_kv, N*rpa, n_slots, r]  P Lv, in the same form as p_o
     int64_t L, S;     // < 2^30 (validated on the host)
     int N, QL, HQ, HK, g, r, lr_shift, rpa, apb, bpa, ps, shared_lr;
     int causal;       // private token j is visible to query token t only if j <= t
@@ -253,7 +254,8 @@ constexpr int kReconTMax = 64;  // tokens per LDS stage (64, or 32 when three su
 struct ReconParams {
     const void *q, *kb, *vb, *lk, *lv, *bk;
     const float *theta;  // [d / 2] rotation frequencies (radians per position), or null
-    float *p_ml, *p_o, *p_w;  // the decode workspace layout (max/sum, P V_base, P Lv)
+    float *p_ml;         // the bf16 decode workspace layout: max/sum, P V_base / l and P Lv / l as fp16
+    void *p_o, *p_w;
     int64_t L;
     int N, QL, HQ, HK, g, rpa, r, shared_lr;
     float c;             // softmax scale * log2(e)

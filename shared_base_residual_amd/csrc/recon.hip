@@ -318,14 +318,17 @@ __global__ __launch_bounds__(64 * recon_waves(ROPE, R)) void recon_split_kernel(
         }
     }
 
-    // ---- partials of this agent's rows (split sp)
+    // ---- partials of this agent's rows (split sp, token group tgi): O and W divided
+    // by the weight sum, as fp16 (zeros when no token was visible)
     if (vm) {
         const int64_t rec = ((int64_t)k * p.N * rpa + (int64_t)a * rpa + ria) * p.n_slots + sp * p.tg + tgi;
-        float *po = p.p_o + rec * D + 4 * j4;
+        const float inv_l = ls[0] > 0.0f ? 1.0f / ls[0] : 0.0f;
+        f16 *po = static_cast<f16 *>(p.p_o) + rec * D + 4 * j4;
 #pragma unroll
-        for (int jj = 0; jj < VPL; ++jj) *reinterpret_cast<f32x4 *>(po + 16 * jj) = o[jj];
+        for (int jj = 0; jj < VPL; ++jj) *reinterpret_cast<f16x4 *>(po + 16 * jj) = to_f16x4(o[jj] * inv_l);
+        f16 *pw = static_cast<f16 *>(p.p_w) + rec * R + 4 * j4;
 #pragma unroll
-        for (int jj = 0; jj < CPL; ++jj) *reinterpret_cast<f32x4 *>(p.p_w + rec * R + 16 * jj + 4 * j4) = w[jj];
+        for (int jj = 0; jj < CPL; ++jj) *reinterpret_cast<f16x4 *>(pw + 16 * jj) = to_f16x4(w[jj] * inv_l);
         if (j4 == 0) *reinterpret_cast<float2 *>(p.p_ml + rec * 2) = float2{m, ls[0]};
     }
 }
