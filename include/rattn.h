@@ -135,7 +135,10 @@ int rattn_workspace_bytes(const rattn_desc *desc, int op, size_t *bytes);
  *
  * Limits (RATTN_E_UNSUPPORTED beyond them): the low-rank caches of the agents
  * that share one 16-row MFMA block group (up to 4 blocks) must span less than
- * 2 GiB (N_group * L * r * element size < 2^31).
+ * 2 GiB (N_group * L * r * element size < 2^31).  Range (not checked): with
+ * bf16 inputs each split's P V and P Lv are kept in the workspace divided by
+ * the split's weight sum, as fp16, so entries of V_base, the private V and Lv
+ * must lie within fp16's range (|x| <= 65504).
  *
  * Workspace: at least rattn_workspace_bytes(desc, RATTN_OP_DECODE) bytes of
  * device memory, 256-byte aligned.  Its contents on entry do not matter and are
