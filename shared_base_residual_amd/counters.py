@@ -33,6 +33,9 @@ library sources the counters were taken on; bench.py reports it as
 roofline.traffic only while the sources are unchanged) and a short text
 summary beside it.
 
+LDS and matrix-unit occupancy: one pass with the eight SQ counters of
+SQ_COUNTERS, then ``summarize-sq --workload W --dir D``.
+
 Kernel trace: one ``rocprofv3 --kernel-trace --stats`` run of bench.py, then
 ``summarize-trace --workload W`` per record, which finds the record's timed
 launches in the trace (records are measured one after another, so each
@@ -325,6 +328,62 @@ def summarize_mfma(key: str, d: str) -> None:
     print("\n".join(lines))
 
 
+SQ_COUNTERS = ("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_ACTIVE_INST_LDS", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS",
+               "SQ_BUSY_CU_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU")
+
+
+def summarize_sq(key: str, d: str) -> None:
+    """LDS and matrix-unit occupancy of the workload's first kernel from one
+    rocprofv3 pass with --pmc SQ_COUNTERS (eight SQ counters, the most one pass
+    collects).  The counters are summed over the chip: SQ_BUSY_CU_CYCLES over the
+    256 compute units, SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs, the LDS
+    counters over the compute units."""
+    sys.path.insert(0, ROOT)
+    from shared_base_residual_amd.build import source_hash
+
+    spec = SPECS[key]
+    kern, wl = spec["files"]
+    paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not paths:
+        raise SystemExit(f"no counter_collection.csv under {d}")
+    per = {}
+    with open(paths[0]) as f:
+        for row in csv.DictReader(f):
+            if spec["kernels"][0] not in row.get("Kernel_Name", ""):
+                continue
+            dd = per.setdefault(row["Dispatch_Id"], {})
+            dd[row["Counter_Name"]] = dd.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {spec['kernels'][0]} dispatches in {paths[0]}")
+    ds = [per[k] for k in sorted(per, key=int)]
+    avg = {c: sum(x.get(c, 0.0) for x in ds) / len(ds) for c in ds[0]}
+    cu = avg["SQ_BUSY_CU_CYCLES"]
+    lines = [
+        f"# {spec['kernels'][0]} -- LDS and matrix-unit occupancy, workload {key}, MI355X", "",
+        "Commands (repository root, TMPDIR=/tmp):", "",
+        f"    rocprofv3 --pmc {' '.join(SQ_COUNTERS)} --output-format csv -d {d} -o run -- "
+        f"python3 -m shared_base_residual_amd.counters run --workload {key}",
+        f"    python3 -m shared_base_residual_amd.counters summarize-sq --workload {key} --dir {d}", "",
+        f"Per dispatch ({len(ds)} dispatches averaged; sums over the chip):", "",
+        "| counter | value |", "|---|---|",
+    ]
+    for k in sorted(avg):
+        lines.append(f"| {k} | {avg[k]:.6g} |")
+    lines += [
+        "",
+        f"- matrix units busy: SQ_VALU_MFMA_BUSY_CYCLES / (4 x SQ_BUSY_CU_CYCLES) = "
+        f"**{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (4 * cu) * 100:.1f} %** of the SIMD cycles;",
+        f"- LDS active (indexed reads and writes) {avg['SQ_LDS_IDX_ACTIVE'] / cu * 100:.1f} % of the CU cycles, "
+        f"of which bank-conflict stalls {avg['SQ_LDS_BANK_CONFLICT'] / max(avg['SQ_LDS_IDX_ACTIVE'], 1) * 100:.1f} %;",
+        f"- SQ_BUSY_CU_CYCLES / 256 = {cu / 256:.4g} cycles per compute unit per dispatch.",
+        "", f"Library sources hash {source_hash()}.", "",
+    ]
+    out = os.path.join(ROOT, "profiles", f"{kern}.{wl}.sq.txt")
+    with open(out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def _stretches(launches):
     """Split (start, duration) launches, sorted by start, where they are more
     than GAP_NS apart."""
@@ -438,6 +497,9 @@ def main() -> None:
     m = sub.add_parser("summarize-mfma")
     m.add_argument("--workload", required=True, choices=sorted(SPECS))
     m.add_argument("--dir", required=True)
+    q = sub.add_parser("summarize-sq")
+    q.add_argument("--workload", required=True, choices=sorted(SPECS))
+    q.add_argument("--dir", required=True)
     t = sub.add_parser("summarize-trace")
     t.add_argument("--workload", required=True, choices=sorted(SPECS))
     t.add_argument("--dir", required=True)
@@ -450,6 +512,8 @@ def main() -> None:
         summarize(a.workload, a.fetch, a.write)
     elif a.action == "summarize-mfma":
         summarize_mfma(a.workload, a.dir)
+    elif a.action == "summarize-sq":
+        summarize_sq(a.workload, a.dir)
     else:
         summarize_trace(a.workload, a.dir, a.bench_json, a.cmd)
 
