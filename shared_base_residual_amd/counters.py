@@ -13,14 +13,14 @@ Workloads (``--workload``) are the bench.py records:
     append                                     the paged append with copy-on-write
 
 Traffic: two counter passes, each a rocprofv3 run of its own (repository root,
-TMPDIR=/tmp), then the summary:
+TMPDIR=/tmp, OUT any output folder), then the summary:
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/ctr_fetch_W -o run -- \\
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/ctr_fetch_W -o run -- \\
         python3 -m shared_base_residual_amd.counters run --workload W
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/ctr_write_W -o run -- \\
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT/ctr_write_W -o run -- \\
         python3 -m shared_base_residual_amd.counters run --workload W
     python3 -m shared_base_residual_amd.counters summarize --workload W \\
-        --fetch gpurun_out/ctr_fetch_W --write gpurun_out/ctr_write_W
+        --fetch OUT/ctr_fetch_W --write OUT/ctr_write_W
 
 ``run`` copies a 256 MiB device buffer once (a plain device-to-device copy:
 256 MiB read and 256 MiB written), then makes a few calls of the workload over

@@ -53,7 +53,7 @@ TINY = [
 
 @pytest.mark.parametrize("case", TINY, ids=lambda c: c.name)
 def test_brute_force_tiny(case):
-    """North-star pin: brute force on tiny shapes (40-digit decimal, independent code)."""
+    """Pin: brute force on tiny shapes (40-digit decimal, independent code)."""
     x = synth.make_inputs(case, 7, b_sigma=0.7, q_scale=2.0)
     ob, lb = brute.to_float(*brute.attend(case, x))
     oc, lc = oracle.attend(case, x)
