@@ -24,10 +24,15 @@ Contents
                        after the up-projection);
   * ``quant``       -- base keys as int8 codes with one scale per tensor
                        (the quantiser, the dequantised keys, and fp64 inputs
-                       for ``attend`` with the keys dequantised).
+                       for ``attend`` with the keys dequantised);
+  * ``values3``     -- base values as 3-bit codes after a Walsh-Hadamard
+                       rotation (the 8-level Lloyd-Max quantiser of N(0, 1)
+                       from its optimality conditions, the transform, the
+                       codes and scales, the decoded values, and fp64 inputs
+                       for ``attend`` with int8 keys and decoded values).
 
-Every function here is pinned by ``tests/test_oracle_pins.py`` against facts the
-pages and the mathematics fix (brute force, closed forms, invariants, library
+Every function here is pinned (``tests/test_oracle_pins.py`` and the
+``tests/test_*_oracle.py`` files) against facts the pages and the mathematics fix (brute force, closed forms, invariants, library
 attention for the special cases that reduce to it).
 """
 from __future__ import annotations
