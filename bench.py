@@ -9,7 +9,9 @@ resident in HBM, drawn on the device).  One step = the 80 layers' rattn_decode
 calls (split kernel, then merge) back to back on one stream.  The other
 workloads (8B-shaped decode, paged copy-on-write decode, BaseLRShared chunked
 prefill) follow as sub-records in the same JSON line, each with its own
-roofline.  For the single-layer workloads several replicas of the inputs are
+roofline, and so do the 8B- and 70B-shaped decodes over int8 keys and over
+int8 keys with 3-bit values (the caches encoded outside the timed region), the
+rebuilt-key decodes and the cache-write path.  For the single-layer workloads several replicas of the inputs are
 rotated so that each step reads from HBM, not from the 256 MB Infinity Cache
 left warm by the previous step.
 
@@ -113,11 +115,13 @@ def stable_ms(hip, fn, n, stream, tol=0.01, max_batches=40):
     return hist
 
 
-def algorithmic_bytes(c, k8=False):
+def algorithmic_bytes(c, k8=False, v3=False):
     """Bytes every input is read once plus the fp32 output written once (int8
-    base keys: one byte per key element)."""
+    base keys: one byte per key element; 3-bit values: 3 d / 8 bytes of codes
+    and a 4-byte scale per value vector)."""
     es = 2 if c.dtype == "bf16" else 4
-    base = c.n_kv_heads * c.prefix_len * c.head_dim * ((1 if k8 else es) + es)
+    v_vec = 3 * c.head_dim // 8 + 4 if v3 else c.head_dim * es
+    base = c.n_kv_heads * c.prefix_len * (c.head_dim * (1 if k8 else es) + v_vec)
     resid = 2 * c.n_lr * c.prefix_len * c.rank * es
     bmat = 2 * c.n_agents * c.rank * c.n_kv_heads * c.head_dim * es
     q = c.n_agents * c.q_len * c.n_q_heads * c.head_dim * es
@@ -261,10 +265,11 @@ def hbm_probe(hip, stream, dev):
     return {"achievable": res[best], "unit": "GB/s", "reader": best, "buffer_bytes": nbytes, "all": res}
 
 
-def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k8=False):
+def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k8=False, v3=False):
     """Times one workload; returns its record (without cpu_baseline).  k8: the
     base keys are first quantised to int8 codes (rattn_quantize_keys, outside
-    the timed region) and every call reads the codes."""
+    the timed region) and every call reads the codes; v3 (with k8): the base
+    values too, to 3-bit codes and scales (rattn_quantize_values)."""
     import torch
 
     import shared_base_residual_amd as R
@@ -272,7 +277,7 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k
 
     case = synth.WORKLOADS[config]
     seed = config if seed is None else seed
-    ab = algorithmic_bytes(case, k8)
+    ab = algorithmic_bytes(case, k8, v3)
     layers = case.layers
     op = R.RATTN_OP_PREFILL if case.mode == "prefill" else R.RATTN_OP_DECODE
     say(f"[bench] {case.name}: drawing inputs")
@@ -294,9 +299,12 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k
             st["k_base"] = codes
             st["k_scale"] = float(sc.cpu().numpy()[0])
         k_scale = sets[0]["k_scale"]
+    if v3:
+        for st in sets:  # each set's values become 3-bit codes and scales
+            st["v_base"], st["v_scale"] = R.quantize_values(st["v_base"])
     desc = R.describe(sets[0]["q"], sets[0]["k_base"], sets[0]["lk"], sets[0]["bk"],
                       block_table=sets[0]["block_table"], k_priv=sets[0]["k_priv"], prefix_len=case.prefix_len,
-                      shared_lr=case.shared_lr, k_scale=k_scale)
+                      shared_lr=case.shared_lr, k_scale=k_scale, v_base=sets[0]["v_base"])
     kernel = R.kernel_of(desc, op)
     wsb = R.workspace_bytes(desc, op)
     ws = torch.empty(max(wsb, 256), device=dev, dtype=torch.uint8)
@@ -306,7 +314,7 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k
         t = dict(s, out=o, lse=None)
         t.pop("k_scale", None)
         R._check_tensors(desc, t)
-        argv.append(R.Args(*[None if t[n] is None else t[n].data_ptr() for n, _ in R.Args._fields_]))
+        argv.append(R.Args(*[None if t.get(n) is None else t[n].data_ptr() for n, _ in R.Args._fields_]))
         d_i = R.Desc.from_buffer_copy(desc)
         if k8:
             d_i.k_scale = s["k_scale"]  # one scale per set (per layer)
@@ -373,7 +381,8 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k
     else:
         achieved = ab["split"] / (kern_avg / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_counters(f"decode_cfg{config}" + ("_k8" if k8 else "")),
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic_from_counters(f"decode_cfg{config}" + ("_k8" if k8 else "") + ("v3" if v3 else "")),
                 "kernel": "decode_split_kernel", "bytes_per_launch": ab["split"],
                 "avg_launch_us": round(kern_avg * 1e3, 2), "launches_timed": n_k,
                 # the whole call (split + merge) over the timed steps
@@ -386,8 +395,10 @@ def measure(config, K, W, dev, hip, stream, replicas=0, seed=None, probe=None, k
         "metric": METRIC, "value": round(value, 4), "unit": "Gtok/s", "n_gpus": 1, "steps": K, "warmup": W,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": case.dtype, "data": "synthetic (seeded N(0,1) caches and queries, N(0,0.05^2) up-projections)",
-        "config": {"workload": case.name + (", int8 keys" if k8 else ""), "n_agents": case.n_agents,
-                   "n_q_heads": case.n_q_heads, "key_format": "int8 (per-tensor scale)" if k8 else case.dtype,
+        "config": {"workload": case.name + (", int8 keys" if k8 else "") + (", 3-bit values" if v3 else ""),
+                   "n_agents": case.n_agents, "n_q_heads": case.n_q_heads,
+                   "key_format": "int8 (per-tensor scale)" if k8 else case.dtype,
+                   "value_format": "3-bit Walsh-Hadamard-rotated codes (per-vector scale)" if v3 else case.dtype,
                    "n_kv_heads": case.n_kv_heads, "head_dim": case.head_dim, "prefix_len": case.prefix_len,
                    "priv_len": case.priv_len, "q_len": case.q_len, "rank": case.rank, "page_size": case.page_size,
                    "shared_lr": case.shared_lr, "layers": layers, "mode": case.mode, "input_sets_rotated": n_sets},
@@ -558,6 +569,7 @@ def main():
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-cache-write", action="store_true", help="skip the cache-write sub-records")
     ap.add_argument("--no-int8", action="store_true", help="skip the int8-key sub-records")
+    ap.add_argument("--no-values3", action="store_true", help="skip the int8-key + 3-bit-value sub-records")
     ap.add_argument("--no-reconstruct", action="store_true", help="skip the rebuilt-key sub-records")
     ap.add_argument("--seed", type=int, default=None)
     args = ap.parse_args()
@@ -587,6 +599,10 @@ def main():
     if not args.no_int8:
         res.setdefault("sub_records", []).extend(
             [measure(c, args.steps, args.warmup, dev, hip, stream, args.replicas, None, probe, k8=True) for c in (1, 4)])
+    if not args.no_values3:
+        res.setdefault("sub_records", []).extend(
+            [measure(c, args.steps, args.warmup, dev, hip, stream, args.replicas, None, probe, k8=True, v3=True)
+             for c in (1, 4)])
     if not args.no_reconstruct:
         res.setdefault("sub_records", []).extend(
             [measure_reconstruct(c, args.steps, args.warmup, dev, hip, stream, probe, rope)

@@ -77,6 +77,15 @@ typedef enum rattn_key_format {
                              rattn_quantize_keys */
 } rattn_key_format;
 
+/* Storage of the base values (rattn_desc.v_format). */
+typedef enum rattn_value_format {
+    RATTN_VALUES_DTYPE = 0, /* values in the call's dtype */
+    RATTN_VALUES_FWHT3 = 1  /* 3-bit codes after a Walsh-Hadamard rotation (PolyKV, section 2B,
+                               TurboQuant MSE); see rattn_quantize_values for the format.  Requires
+                               RATTN_KEYS_INT8 (the pages' asymmetric pairing), a contiguous base
+                               cache and the same limits as int8 keys */
+} rattn_value_format;
+
 typedef enum rattn_op {
     RATTN_OP_DECODE = 0,
     RATTN_OP_PREFILL = 1,
@@ -102,6 +111,8 @@ typedef struct rattn_desc {
                              head_dim 128, priv_len 0 (else RATTN_E_UNSUPPORTED); k_base then holds
                              one byte per element in the same layout */
     float k_scale;        /* RATTN_KEYS_INT8: the keys' scale (> 0); else ignored */
+    int32_t v_format;     /* rattn_value_format of v_base (0: dtype).  RATTN_VALUES_FWHT3: v_base holds
+                             [H_kv, L, 3 d / 8] bytes of codes and rattn_args.v_scale the scales */
 } rattn_desc;
 
 /* Tensors of one call.  Shapes use the descriptor's names. */
@@ -118,6 +129,7 @@ typedef struct rattn_args {
     const void *v_priv;        /* [N, H_kv, S, d] */
     float *out;                /* [N, q_len, H_q, d] fp32 */
     float *lse;                /* [N, q_len, H_q] fp32 natural-log sum of exp of the scores, or NULL */
+    const float *v_scale;      /* RATTN_VALUES_FWHT3: [H_kv, L] fp32 scale of each value vector; else NULL */
 } rattn_args;
 
 /* Bytes of device workspace that rattn_decode (op = RATTN_OP_DECODE) or
@@ -259,6 +271,36 @@ int rattn_attention_stages(const rattn_desc *desc, int op, const rattn_args *arg
  * launches on `stream`; deterministic.  Inputs must be finite.
  */
 int rattn_quantize_keys(const void *k, int64_t n, int32_t dtype, void *codes, float *scale, void *stream);
+
+/*
+ * Base values to 3-bit codes after a Walsh-Hadamard rotation (PolyKV, section
+ * 2B, TurboQuant MSE: each value vector is rotated by a fast Walsh-Hadamard
+ * transform so that its coordinates approach a standard normal, each
+ * coordinate is mapped to one of eight Lloyd-Max centroids for N(0, 1), and
+ * decoding looks the centroids up and undoes the rotation).  For each of the n
+ * vectors v of head_dim d (64 or 128) elements at v (device, dtype RATTN_BF16
+ * or RATTN_F32, vectors back to back, e.g. a [H_kv, L, d] value cache):
+ *   z = H_d v, with H_d the Sylvester-ordered Hadamard matrix (entries +-1);
+ *   u_j = z_j / ||v|| (0 for a zero vector), so the u_j have mean square 1;
+ *   code_j = the number of inner boundaries b_1 < ... < b_7 of the 8-level
+ *     minimum-MSE quantiser of N(0, 1) with u_j >= b_k (the quantiser is the
+ *     fixed point of its two conditions: every centroid the N(0, 1) mean of its
+ *     cell, every boundary the midpoint of its centroids; the library derives
+ *     it on the host);
+ *   codes (3 d / 8 bytes per vector, device): three bit planes of d / 8 bytes,
+ *     plane p holding bit p of code_j at bit j % 8 of byte j / 8;
+ *   scale[i] = ||v|| / d rounded once to fp32 (device, one float per vector).
+ * z, ||v||, u and the comparisons are computed in fp64 (z and ||v||^2 exactly
+ * for bf16 inputs).  The decoded vector is scale * H_d c, c_j the centroid of
+ * code_j.  One kernel launch on `stream`; deterministic.  Inputs must be finite.
+ * codes must be 16-byte aligned, v aligned to its element and scale to 4 bytes.
+ */
+int rattn_quantize_values(const void *v, int64_t n, int32_t head_dim, int32_t dtype, void *codes, float *scale,
+                          void *stream);
+
+/* The 8-level Lloyd-Max quantiser of N(0, 1) the library uses (host-only, no
+ * HIP call): centroids[8] ascending and boundaries[7] ascending, in fp64. */
+int rattn_values_codebook(double *centroids, double *boundaries);
 
 /* ------------------------------------------------------------------------
  * The cache-write path: what fills the caches the attention calls read.

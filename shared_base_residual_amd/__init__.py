@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(HERE, "librattn.so")
 
 RATTN_F32, RATTN_BF16 = 0, 1
 RATTN_KEYS_DTYPE, RATTN_KEYS_INT8 = 0, 1
+RATTN_VALUES_DTYPE, RATTN_VALUES_FWHT3 = 0, 1
 RATTN_OP_DECODE, RATTN_OP_PREFILL, RATTN_OP_RECONSTRUCT = 0, 1, 2
 STATUS = {0: "RATTN_OK", -1: "RATTN_E_NULL", -2: "RATTN_E_SHAPE", -3: "RATTN_E_UNSUPPORTED",
           -4: "RATTN_E_WORKSPACE", -5: "RATTN_E_ALIGN", -6: "RATTN_E_HIP", -7: "RATTN_E_SCRATCH",
@@ -36,7 +37,7 @@ EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "ratt
            "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
            "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
            "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv",
-           "rattn_quantize_keys", "rattn_decode_reconstruct")
+           "rattn_quantize_keys", "rattn_decode_reconstruct", "rattn_quantize_values", "rattn_values_codebook")
 STAGE_SPLIT, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
 
 
@@ -56,14 +57,16 @@ class Desc(ctypes.Structure):
         ("prefix_len", ctypes.c_int64), ("priv_len", ctypes.c_int64),
         ("page_size", ctypes.c_int32), ("shared_lr", ctypes.c_int32),
         ("n_phys_pages", ctypes.c_int64), ("dtype", ctypes.c_int32), ("sm_scale", ctypes.c_float),
-        ("k_format", ctypes.c_int32), ("k_scale", ctypes.c_float),
+        ("k_format", ctypes.c_int32), ("k_scale", ctypes.c_float), ("v_format", ctypes.c_int32),
     ]
 
 
+ARG_NAMES = ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out", "lse",
+             "v_scale")
+
+
 class Args(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in
-                ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out",
-                 "lse")]
+    _fields_ = [(n, ctypes.c_void_p) for n in ARG_NAMES]
 
 
 class LrDesc(ctypes.Structure):
@@ -125,6 +128,8 @@ def lib():
                                       ctypes.c_int32, P]
         L.rattn_quantize_keys.argtypes = [P, I64, ctypes.c_int32, P, P, P]
         L.rattn_decode_reconstruct.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P, P, ctypes.c_size_t, P]
+        L.rattn_quantize_values.argtypes = [P, I64, ctypes.c_int32, ctypes.c_int32, P, P, P]
+        L.rattn_values_codebook.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
         for f in ("rattn_decode_reconstruct", "rattn_quantize_keys", "rattn_lr_project", "rattn_pagepool_create", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
                   "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append",
                   "rattn_append_kv"):
@@ -136,7 +141,7 @@ def lib():
                   "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
            "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
            "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv",
-           "rattn_quantize_keys", "rattn_decode_reconstruct"):
+           "rattn_quantize_keys", "rattn_decode_reconstruct", "rattn_quantize_values", "rattn_values_codebook"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -144,9 +149,9 @@ def lib():
 
 def make_desc(*, n_agents, n_q_heads, n_kv_heads, head_dim, rank, q_len, prefix_len, priv_len=0, page_size=0,
               shared_lr=False, n_phys_pages=0, dtype=RATTN_BF16, sm_scale=0.0, k_format=RATTN_KEYS_DTYPE,
-              k_scale=0.0) -> Desc:
+              k_scale=0.0, v_format=RATTN_VALUES_DTYPE) -> Desc:
     return Desc(n_agents, n_q_heads, n_kv_heads, head_dim, rank, q_len, prefix_len, priv_len, page_size,
-                int(bool(shared_lr)), n_phys_pages, dtype, sm_scale, k_format, k_scale)
+                int(bool(shared_lr)), n_phys_pages, dtype, sm_scale, k_format, k_scale, v_format)
 
 
 def workspace_bytes(desc: Desc, op: int = RATTN_OP_DECODE) -> int:
@@ -184,6 +189,8 @@ def kernel_of(desc: Desc, op: int = RATTN_OP_DECODE) -> tuple:
     dt = "bf16" if desc.dtype == RATTN_BF16 else "f32"
     if desc.k_format == RATTN_KEYS_INT8:
         dt += "-k8"
+    if desc.v_format == RATTN_VALUES_FWHT3:
+        dt += "v3"
     if p["path"] == 1:
         return ("prefill", dt, desc.head_dim, p["resid_cols"])
     return ("split", dt, desc.head_dim, p["resid_cols"], bool(p["masked"]), p["waves"] > 8)
@@ -201,9 +208,10 @@ def _stream(stream):
 
 
 def describe(q, k_base, lk=None, bk=None, *, block_table=None, k_priv=None, prefix_len=None, shared_lr=None,
-             sm_scale=0.0, op=RATTN_OP_DECODE, k_scale=None) -> Desc:
+             sm_scale=0.0, op=RATTN_OP_DECODE, k_scale=None, v_base=None) -> Desc:
     """Descriptor read off the tensors' shapes.  A uint8 k_base holds int8 key
-    codes (excess-128, RATTN_KEYS_INT8) whose scale ``k_scale`` must be given."""
+    codes (excess-128, RATTN_KEYS_INT8) whose scale ``k_scale`` must be given;
+    a uint8 v_base holds 3-bit value codes (RATTN_VALUES_FWHT3)."""
     import torch
 
     if q.dim() != 4:
@@ -240,9 +248,10 @@ def describe(q, k_base, lk=None, bk=None, *, block_table=None, k_priv=None, pref
         if k_scale is None:
             raise ValueError("int8 keys (uint8 k_base) need k_scale")
         kf, ks = RATTN_KEYS_INT8, float(k_scale)
+    vf = RATTN_VALUES_FWHT3 if v_base is not None and v_base.dtype == torch.uint8 else RATTN_VALUES_DTYPE
     return make_desc(n_agents=N, n_q_heads=HQ, n_kv_heads=HK, head_dim=D, rank=r, q_len=QL,
                      prefix_len=prefix_len, priv_len=S, page_size=ps, shared_lr=shared_lr,
-                     n_phys_pages=n_phys, dtype=dt, sm_scale=sm_scale, k_format=kf, k_scale=ks)
+                     n_phys_pages=n_phys, dtype=dt, sm_scale=sm_scale, k_format=kf, k_scale=ks, v_format=vf)
 
 
 def _check_tensors(desc: Desc, tensors: dict):
@@ -262,6 +271,9 @@ def _check_tensors(desc: Desc, tensors: dict):
         want["block_table"] = ((L + desc.page_size - 1) // desc.page_size,)
     else:
         want["k_base"] = want["v_base"] = (HK, L, D)
+    if desc.v_format == RATTN_VALUES_FWHT3:
+        want["v_base"] = (HK, L, 3 * D // 8)
+        want["v_scale"] = (HK, L)
     for name, t in tensors.items():
         if t is None:
             continue
@@ -272,6 +284,10 @@ def _check_tensors(desc: Desc, tensors: dict):
         exp_dt = torch.float32 if name in ("out", "lse") else (torch.int32 if name == "block_table" else dt)
         if name == "k_base" and desc.k_format == RATTN_KEYS_INT8:
             exp_dt = torch.uint8
+        if name == "v_base" and desc.v_format == RATTN_VALUES_FWHT3:
+            exp_dt = torch.uint8
+        if name == "v_scale":
+            exp_dt = torch.float32
         if t.dtype != exp_dt:
             raise TypeError(f"{name}: dtype {t.dtype}, expected {exp_dt}")
         if name in want and tuple(t.shape) != want[name]:
@@ -307,16 +323,16 @@ def workspace_for(nbytes: int, device, stream=None):
 
 
 def _run(fn_name, op, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_priv, shared_lr, out, lse,
-         workspace, sm_scale, prefix_len, stream, desc, stages=None, k_scale=None):
+         workspace, sm_scale, prefix_len, stream, desc, stages=None, k_scale=None, v_scale=None):
     import torch
 
     if desc is None:
         desc = describe(q, k_base, lk, bk, block_table=block_table, k_priv=k_priv, prefix_len=prefix_len,
-                        shared_lr=shared_lr, sm_scale=sm_scale, op=op, k_scale=k_scale)
+                        shared_lr=shared_lr, sm_scale=sm_scale, op=op, k_scale=k_scale, v_base=v_base)
     if out is None:
         out = torch.empty(tuple(q.shape), device=q.device, dtype=torch.float32)
     tensors = dict(q=q, k_base=k_base, v_base=v_base, block_table=block_table, lk=lk, lv=lv, bk=bk, bv=bv,
-                   k_priv=k_priv, v_priv=v_priv, out=out, lse=lse)
+                   k_priv=k_priv, v_priv=v_priv, out=out, lse=lse, v_scale=v_scale)
     _check_tensors(desc, tensors)
     nbytes = workspace_bytes(desc, op)
     if workspace is None:
@@ -324,9 +340,7 @@ def _run(fn_name, op, q, k_base, v_base, lk, lv, bk, bv, block_table, k_priv, v_
     elif workspace.numel() * workspace.element_size() < nbytes:
         raise RattnError(-4, f"{fn_name}: workspace has {workspace.numel() * workspace.element_size()} bytes, "
                              f"needs {nbytes}")
-    args = Args(*[_ptr(tensors[n]) for n in
-                  ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out",
-                   "lse")])
+    args = Args(*[_ptr(tensors.get(n)) for n in ARG_NAMES])
     wsp = ctypes.c_void_p(workspace.data_ptr())
     wsb = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     if stages is None:
@@ -365,13 +379,12 @@ def decode_noalloc(inputs: dict, *, shared_lr=None, prefix_len=None, out, lse=No
     g = inputs.get
     if desc is None:
         desc = describe(inputs["q"], g("k_base"), g("lk"), g("bk"), block_table=g("block_table"),
-                        k_priv=g("k_priv"), prefix_len=prefix_len, shared_lr=shared_lr)
+                        k_priv=g("k_priv"), prefix_len=prefix_len, shared_lr=shared_lr, v_base=g("v_base"))
     tensors = dict(q=inputs["q"], k_base=g("k_base"), v_base=g("v_base"), block_table=g("block_table"), lk=g("lk"),
-                   lv=g("lv"), bk=g("bk"), bv=g("bv"), k_priv=g("k_priv"), v_priv=g("v_priv"), out=out, lse=lse)
+                   lv=g("lv"), bk=g("bk"), bv=g("bv"), k_priv=g("k_priv"), v_priv=g("v_priv"), out=out, lse=lse,
+                   v_scale=g("v_scale"))
     _check_tensors(desc, tensors)
-    args = Args(*[_ptr(tensors[n]) for n in
-                  ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out",
-                   "lse")])
+    args = Args(*[_ptr(tensors.get(n)) for n in ARG_NAMES])
     st = lib().rattn_decode_noalloc(ctypes.byref(desc), ctypes.byref(args), _stream(stream))
     if st:
         raise RattnError(st, "rattn_decode_noalloc")
@@ -400,9 +413,7 @@ def decode_reconstruct(inputs: dict, *, rope_theta=None, shared_lr=None, out=Non
     nbytes = workspace_bytes(desc, RATTN_OP_RECONSTRUCT)
     if workspace is None:
         workspace = workspace_for(nbytes, q.device, stream)
-    args = Args(*[_ptr(tensors[n]) for n in
-                  ("q", "k_base", "v_base", "block_table", "lk", "lv", "bk", "bv", "k_priv", "v_priv", "out",
-                   "lse")])
+    args = Args(*[_ptr(tensors.get(n)) for n in ARG_NAMES])
     st = lib().rattn_decode_reconstruct(ctypes.byref(desc), ctypes.byref(args), _ptr(rope_theta),
                                         ctypes.c_void_p(workspace.data_ptr()),
                                         ctypes.c_size_t(workspace.numel() * workspace.element_size()),
@@ -432,6 +443,41 @@ def quantize_keys(k, *, codes=None, scale=None, stream=None):
     if st:
         raise RattnError(st, "rattn_quantize_keys")
     return codes, scale
+
+
+def quantize_values(v, *, codes=None, scale=None, stream=None):
+    """rattn_quantize_values: 3-bit codes (uint8, three bit planes of d / 8
+    bytes per vector) and fp32 scales of the value vectors in the device tensor
+    v [..., d] (bf16 or fp32).  Returns (codes [..., 3 d / 8], scale [...])."""
+    import torch
+
+    if not v.is_cuda or not v.is_contiguous():
+        raise ValueError("v must be a contiguous GPU tensor")
+    d = v.shape[-1]
+    n = v.numel() // d
+    if codes is None:
+        codes = torch.empty(tuple(v.shape[:-1]) + (3 * d // 8,), device=v.device, dtype=torch.uint8)
+    if scale is None:
+        scale = torch.empty(tuple(v.shape[:-1]), device=v.device, dtype=torch.float32)
+    if codes.numel() != n * (3 * d // 8) or codes.dtype != torch.uint8 or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous uint8 tensor of 3 d / 8 bytes per vector")
+    if scale.numel() != n or scale.dtype != torch.float32 or not scale.is_contiguous():
+        raise ValueError("scale must be a contiguous fp32 tensor of one value per vector")
+    dt = RATTN_BF16 if v.dtype == torch.bfloat16 else RATTN_F32
+    st = lib().rattn_quantize_values(v.data_ptr(), n, d, dt, codes.data_ptr(), scale.data_ptr(), _stream(stream))
+    if st:
+        raise RattnError(st, "rattn_quantize_values")
+    return codes, scale
+
+
+def values_codebook():
+    """The library's 8-level quantiser of N(0, 1): (centroids[8], boundaries[7])."""
+    c = (ctypes.c_double * 8)()
+    b = (ctypes.c_double * 7)()
+    st = lib().rattn_values_codebook(c, b)
+    if st:
+        raise RattnError(st, "rattn_values_codebook")
+    return list(c), list(b)
 
 
 def lr_project(x, ak_t, av_t, lk, lv, *, pos0: int = 0, stream=None):
@@ -585,7 +631,8 @@ def attend(inputs: dict, *, mode: str = "decode", shared_lr=None, prefix_len=Non
            workspace=None, stream=None, desc=None, stages=None, k_scale=None):
     """Runs decode or prefill on a dict of device tensors named as in the layouts above.
     ``stages`` (a mask of STAGE_*) runs only those launches through rattn_attention_stages.
-    A uint8 ``k_base`` holds int8 key codes with scale ``k_scale``."""
+    A uint8 ``k_base`` holds int8 key codes with scale ``k_scale``; a uint8
+    ``v_base`` holds 3-bit value codes with their scales in ``inputs["v_scale"]``."""
     if mode == "decode":
         fn_name, op = "rattn_decode", RATTN_OP_DECODE
     else:
@@ -593,4 +640,4 @@ def attend(inputs: dict, *, mode: str = "decode", shared_lr=None, prefix_len=Non
     g = inputs.get
     return _run(fn_name, op, inputs["q"], g("k_base"), g("v_base"), g("lk"), g("lv"), g("bk"), g("bv"),
                 g("block_table"), g("k_priv"), g("v_priv"), shared_lr, out, lse, workspace, 0.0, prefix_len, stream,
-                desc, stages, k_scale)
+                desc, stages, k_scale, g("v_scale"))

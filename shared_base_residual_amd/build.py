@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librattn.so")
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "gather.hip", "cache_write.hip", "pagepool.cpp", "quant.hip", "recon.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "gather.hip", "cache_write.hip", "pagepool.cpp", "quant.hip", "recon.hip",
+           "values3.hip"]
 # the benchmark's HBM read-bandwidth probe: a library of its own, not librattn
 PROBE_LIB = os.path.join(HERE, "libhbm_probe.so")
 PROBE_SOURCES = ["hbm_probe.hip"]

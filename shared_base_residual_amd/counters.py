@@ -8,6 +8,7 @@ Workloads (``--workload``) are the bench.py records:
     decode_cfg1, decode_cfg2, decode_cfg4      the split kernel of a decode call
     prefill_cfg3                               the prefill kernel
     decode_cfg1_k8, decode_cfg4_k8             the split kernel over int8 base keys
+    decode_cfg1_k8v3, decode_cfg4_k8v3         ... over int8 keys and 3-bit values
     recon_cfg1[_rope], recon_cfg4[_rope]       the rebuilt-key decode (split + merge)
     lr_prefill                                 the low-rank projection
     append                                     the paged append with copy-on-write
@@ -64,10 +65,11 @@ def _synth():
     return synth
 
 
-def _dec(cfg, name, k8=False):
+def _dec(cfg, name, k8=False, v3=False):
     def match(rec):
-        return rec.get("config", {}).get("workload") == _synth().WORKLOADS[cfg].name + (", int8 keys" if k8 else "")
-    return dict(kind="decode", config=cfg, k8=k8, kernels=["decode_split_kernel"],
+        return rec.get("config", {}).get("workload") == (_synth().WORKLOADS[cfg].name + (", int8 keys" if k8 else "") +
+                                                         (", 3-bit values" if v3 else ""))
+    return dict(kind="decode", config=cfg, k8=k8, v3=v3, kernels=["decode_split_kernel"],
                 files=("decode_split_kernel", name), match=match)
 
 
@@ -89,6 +91,8 @@ SPECS = {
                          match=lambda rec: rec.get("roofline", {}).get("kernel") == "prefill_kernel"),
     "decode_cfg1_k8": _dec(1, "llama8b_decode_int8_keys", k8=True),
     "decode_cfg4_k8": _dec(4, "70b_layer_int8_keys", k8=True),
+    "decode_cfg1_k8v3": _dec(1, "llama8b_decode_int8_keys_3bit_values", k8=True, v3=True),
+    "decode_cfg4_k8v3": _dec(4, "70b_layer_int8_keys_3bit_values", k8=True, v3=True),
     "recon_cfg1": _rec(1, "llama8b_decode_rebuilt_keys", False),
     "recon_cfg1_rope": _rec(1, "llama8b_decode_rebuilt_keys_rotated", True),
     "recon_cfg4": _rec(4, "70b_layer_rebuilt_keys", False),
@@ -139,6 +143,9 @@ def run(key: str) -> None:
                 codes, sc = R.quantize_keys(st["k_base"])
                 st["k_base"] = codes
                 scales[i] = float(sc.cpu().numpy()[0])
+        if spec.get("v3"):
+            for st in sets:
+                st["v_base"], st["v_scale"] = R.quantize_values(st["v_base"])
         stages = None if case.mode == "prefill" else R.STAGE_SPLIT
         torch.cuda.synchronize()
         for i in range(CALLS):

@@ -20,6 +20,8 @@ hipError_t launch_lr_project(const LrParams &p, hipStream_t st);
 hipError_t launch_append_kv(const AppendParams &p, hipStream_t st);
 hipError_t launch_quantize(const void *k, int64_t n, int bf16_in, void *codes, float *scale, hipStream_t st);
 hipError_t launch_recon(const ReconParams &p, hipStream_t st);
+hipError_t launch_values3_encode(const void *v, int64_t n, int D, int bf16_in, const double *boundaries, void *codes,
+                                 float *scale, hipStream_t st);
 }  // namespace rattn
 
 static_assert(rattn::kNoAllocScratchBytes == RATTN_NOALLOC_SCRATCH_BYTES, "static scratch size in the header");
@@ -40,6 +42,47 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t roundup(int64_t a, int64_t b) { return cdiv(a, b) * b; }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The 8-level minimum-MSE (Lloyd-Max) quantiser of N(0, 1) behind the 3-bit
+// values (PolyKV, section 2B): the fixed point of Lloyd's two conditions, each
+// centroid the N(0, 1) mean of its cell, (pdf(a) - pdf(b)) / (cdf(b) - cdf(a))
+// over [a, b), and each inner boundary the midpoint of its two centroids.
+// Iterated on the non-negative half from 0.5, 1.5, 2.5, 3.5 and mirrored, so
+// the middle boundary is exactly 0.
+struct ValuesCodebook {
+    double c[8], b[7];
+};
+
+const ValuesCodebook &values_codebook() {
+    static const ValuesCodebook cb = [] {
+        const double inv_sqrt2pi = 0.39894228040143267794, inv_sqrt2 = 0.70710678118654752440;
+        auto pdf = [&](double x) { return isinf(x) ? 0.0 : inv_sqrt2pi * exp(-0.5 * x * x); };
+        auto cdf = [&](double x) { return isinf(x) ? 1.0 : 0.5 * (1.0 + erf(x * inv_sqrt2)); };
+        double c[4] = {0.5, 1.5, 2.5, 3.5};
+        for (int it = 0; it < 10000; ++it) {
+            const double e[5] = {0.0, 0.5 * (c[0] + c[1]), 0.5 * (c[1] + c[2]), 0.5 * (c[2] + c[3]), INFINITY};
+            double n[4], dmax = 0.0;
+            for (int i = 0; i < 4; ++i) {
+                n[i] = (pdf(e[i]) - pdf(e[i + 1])) / (cdf(e[i + 1]) - cdf(e[i]));
+                dmax = fmax(dmax, fabs(n[i] - c[i]));
+            }
+            for (int i = 0; i < 4; ++i) c[i] = n[i];
+            if (dmax <= 1e-16) break;
+        }
+        ValuesCodebook k;
+        for (int i = 0; i < 4; ++i) {
+            k.c[4 + i] = c[i];
+            k.c[3 - i] = -c[i];
+        }
+        k.b[3] = 0.0;
+        for (int i = 0; i < 3; ++i) {
+            k.b[4 + i] = 0.5 * (c[i] + c[i + 1]);
+            k.b[2 - i] = -k.b[4 + i];
+        }
+        return k;
+    }();
+    return cb;
+}
 
 int pow2ceil(int x) {
     int v = 1;
@@ -72,7 +115,8 @@ int check_desc(const rattn_desc *d, int op) {
         // cache, no private tokens, at most 16 query rows per agent and KV head
         if (d->dtype != RATTN_BF16 || d->head_dim != 128 || (d->rank != 16 && d->rank != 32) ||
             d->page_size != 0 || d->priv_len != 0 || d->prefix_len < 1 ||
-            (int64_t)d->q_len * (d->n_q_heads / d->n_kv_heads) > 16 || d->k_format != RATTN_KEYS_DTYPE)
+            (int64_t)d->q_len * (d->n_q_heads / d->n_kv_heads) > 16 || d->k_format != RATTN_KEYS_DTYPE ||
+            d->v_format != RATTN_VALUES_DTYPE)
             return RATTN_E_UNSUPPORTED;
     }
     if (d->k_format != RATTN_KEYS_DTYPE && d->k_format != RATTN_KEYS_INT8) return RATTN_E_SHAPE;
@@ -81,6 +125,12 @@ int check_desc(const rattn_desc *d, int op) {
         // int8 base keys: bf16 decode over a shared prefix, d = 128, no private tokens
         if (d->dtype != RATTN_BF16 || d->head_dim != 128 || d->priv_len != 0 || d->prefix_len < 1 ||
             op != RATTN_OP_DECODE)
+            return RATTN_E_UNSUPPORTED;
+    }
+    if (d->v_format != RATTN_VALUES_DTYPE && d->v_format != RATTN_VALUES_FWHT3) return RATTN_E_SHAPE;
+    if (d->v_format == RATTN_VALUES_FWHT3) {
+        // 3-bit values: with int8 keys (so bf16 decode, d = 128, no private tokens), contiguous cache
+        if (d->k_format != RATTN_KEYS_INT8 || d->page_size != 0 || op != RATTN_OP_DECODE)
             return RATTN_E_UNSUPPORTED;
     }
     // Index arithmetic inside the kernels uses 32-bit row and item counts.
@@ -123,6 +173,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
     const float scale = d->sm_scale > 0.f ? d->sm_scale : 1.0f / sqrtf((float)D);
     p.c = scale * 1.44269504088896340736f;
     p.kq8 = d->k_format == RATTN_KEYS_INT8;
+    p.vq3 = d->v_format == RATTN_VALUES_FWHT3;
+    for (int k = 0; k < 8; ++k) p.vq_c[k] = p.vq3 ? (float)values_codebook().c[k] : 0.0f;
     p.u_scale = 1.0f;
     if (p.kq8) {  // scores in code units: the exponent's scale takes the key scale, U its inverse
         p.c = (float)((double)scale * 1.44269504088896340736 * (double)d->k_scale);
@@ -167,6 +219,12 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
         const int es = (int)esize(d->dtype);
         const int kv_row = D * es;                   // bytes of one value row (and key row, unquantised)
         const int k_row = p.kq8 ? D : kv_row;         // bytes of one key row (int8: one per element)
+        // 3-bit values: a stage holds, per 16-token group and head, 1 KiB for the
+        // codes and scales (two loads) instead of value rows, which are decoded into
+        // two buffers of H T rows after the ring; HBM holds 3 d / 8 + 4 bytes per
+        // value vector
+        const int vq_row = p.vq3 ? 64 : 0;
+        const int v_hbm = p.vq3 ? 3 * D / 8 + 4 : kv_row;
         // Row groups of bpg blocks: the agents of a group, and the low-rank bytes per
         // token a stage holds for them (or for the shared cache).
         int ag_max = 1, nb_min = 4, nb_max = 1, lr_row = 0;
@@ -247,7 +305,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
                 int f = 0;
                 const int b = own ? (w == np - 1 ? nkv : w) : w, e = own && w < np - 1 ? nkv : npairs;
                 const int st = own ? (w == np - 1 ? 1 : np - 1) : np;
-                for (int pi = b; pi < e; pi += st) f += pi < H * G ? n_k : pi < nkv ? n_kv : n_lr;
+                for (int pi = b; pi < e; pi += st) f += pi < H * G ? n_k : pi < nkv ? (p.vq3 ? 2 : n_kv) : n_lr;
                 if (f > mx) mx = f;
             }
             return mx;
@@ -258,7 +316,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             // are back-pressured at issue, so large tiles stream faster from more
             // waves.  More if the outstanding-load limit needs them, then fewer stages.
             const int G = T / 16;
-            const int tile_loads = H * G * ((16 * (kv_row / 16)) / 64 + (16 * (k_row / 16)) / 64) +
+            const int tile_loads = H * G * ((p.vq3 ? 2 : (16 * (kv_row / 16)) / 64) + (16 * (k_row / 16)) / 64) +
                                    (lr_row_bytes ? 2 * G * ((16 * (lr_row_bytes / 16) + 63) / 64) : 0);
             // (int8 keys: four, whose tiles take fewer loads than the rule counts on)
             const int np0 = (tile_loads >= 40 || p.kq8) && p.nw + 4 <= 12 ? 4 : (p.lr_own ? 3 : 2);
@@ -289,11 +347,13 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             auto pick = [&](int tg_max, int H, int lr_row_bytes, int need, int *T, int *nst, int *stage) {
                 for (int t = 128; t >= 16; t /= 2) {
                     if (t % (16 * tg_max) || t > 16 * nw) continue;  // the fill gives each 16-row group one wave
-                    const int sb = t * (H * (k_row + kv_row) + 2 * lr_row_bytes);
-                    const int n = (rattn::kLdsMax - table_bytes) / sb;
+                    const int sb = t * (H * (k_row + (p.vq3 ? vq_row : kv_row)) + 2 * lr_row_bytes);
+                    const int vbuf = p.vq3 ? 2 * H * t * kv_row : 0;  // the decoded value buffers
+                    const int n = (rattn::kLdsMax - table_bytes - vbuf) / sb;
                     if (n >= 3 || (t == 16 * tg_max && n >= need)) {
                         *T = t;
-                        *nst = n < 4 ? n : 4;
+                        const int cap = p.vq3 ? 6 : 4;  // (small 3-bit stages: more of them in flight)
+                        *nst = n < cap ? n : cap;
                         *stage = sb;
                         return true;
                     }
@@ -307,6 +367,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
                 if (!pick(tg_max, p.H, lr_row, min_nst, &p.T_pre, &p.nst_pre, &p.stage_bytes_pre)) return false;
                 if (!fit_vmcnt(p.T_pre, p.H, lr_row, &p.nst_pre)) return false;
                 lds_ring = p.nst_pre * p.stage_bytes_pre;
+                p.vbuf_off = lds_ring;
+                if (p.vq3) lds_ring += 2 * p.H * p.T_pre * kv_row;
             }
             if (S > 0) {
                 int tg_max = 1;
@@ -364,7 +426,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
                 // Preference: a prefix tile of 32 or more tokens (the per-tile
                 // synchronisation is a large share of a tile's time), then the
                 // fewest bytes staged per context token, then more heads per item.
-                const int64_t bytes = (int64_t)p.n_rg * HK * (k_row + kv_row) + (int64_t)p.n_hg * p.n_rg * 2 * lr_row;
+                const int64_t bytes = (int64_t)p.n_rg * HK * (k_row + v_hbm) + (int64_t)p.n_hg * p.n_rg * 2 * lr_row;
                 const int64_t cost = (L > 0 && p.T_pre < 32 ? (int64_t)1 << 40 : 0) + bytes * 16 + (8 - p.H);
                 if (best_cost < 0 || cost < best_cost) {
                     best_cost = cost;
@@ -590,6 +652,12 @@ int check_args(const rattn_desc *d, const rattn_args *a) {
         if (p && !aligned(p, 16)) return RATTN_E_ALIGN;
     if (a->lse && !aligned(a->lse, 4)) return RATTN_E_ALIGN;
     if (a->block_table && !aligned(a->block_table, 4)) return RATTN_E_ALIGN;
+    if (d->v_format == RATTN_VALUES_FWHT3) {
+        if (pre && !a->v_scale) return RATTN_E_NULL;
+        if (a->v_scale && !aligned(a->v_scale, 16)) return RATTN_E_ALIGN;
+    } else if (a->v_scale) {
+        return RATTN_E_NULL;
+    }
     return RATTN_OK;
 }
 
@@ -647,6 +715,7 @@ int run_attention(const rattn_desc *d, const rattn_args *a, void *ws, size_t ws_
     p.vp = a->v_priv;
     p.out = a->out;
     p.lse = a->lse;
+    p.vs = a->v_scale;
     p.p_ml = reinterpret_cast<float *>(w + pl.off_ml);
     p.p_o = w + pl.off_o;
     p.p_w = w + pl.off_w;
@@ -869,6 +938,25 @@ int rattn_quantize_keys(const void *k, int64_t n, int32_t dtype, void *codes, fl
     if (!k || !codes || !scale) return RATTN_E_NULL;
     if (!aligned(k, esize(dtype)) || !aligned(scale, 4)) return RATTN_E_ALIGN;
     return hip_status(rattn::launch_quantize(k, n, dtype == RATTN_BF16, codes, scale, static_cast<hipStream_t>(stream)));
+}
+
+int rattn_quantize_values(const void *v, int64_t n, int32_t head_dim, int32_t dtype, void *codes, float *scale,
+                          void *stream) {
+    if (n < 1) return RATTN_E_SHAPE;
+    if (head_dim != 64 && head_dim != 128) return RATTN_E_UNSUPPORTED;
+    if (dtype != RATTN_F32 && dtype != RATTN_BF16) return RATTN_E_UNSUPPORTED;
+    if (!v || !codes || !scale) return RATTN_E_NULL;
+    if (!aligned(v, esize(dtype)) || !aligned(codes, 8) || !aligned(scale, 4)) return RATTN_E_ALIGN;
+    return hip_status(rattn::launch_values3_encode(v, n, head_dim, dtype == RATTN_BF16, values_codebook().b, codes,
+                                                   scale, static_cast<hipStream_t>(stream)));
+}
+
+int rattn_values_codebook(double *centroids, double *boundaries) {
+    if (!centroids || !boundaries) return RATTN_E_NULL;
+    const ValuesCodebook &cb = values_codebook();
+    for (int k = 0; k < 8; ++k) centroids[k] = cb.c[k];
+    for (int k = 0; k < 7; ++k) boundaries[k] = cb.b[k];
+    return RATTN_OK;
 }
 
 int rattn_decode_reconstruct(const rattn_desc *desc, const rattn_args *args, const float *rope_theta,

@@ -344,6 +344,57 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     }
 }
 
+// 3-bit values (PolyKV, section 2B): the groups of value codes this wave
+// filled into `stage` (the V pairs of its fill plan) become bf16 value rows in
+// `vrows` (laid out like a stage's value region), scale times centroid in the
+// rotated coordinates; the compute waves then read them like any value rows,
+// and the merge undoes the rotation.  Lane (x, c4) = (lane / 4, lane % 4) decodes token x of the group,
+// coordinates 32 c4 .. 32 c4 + 31: bit j of the three 32-bit plane words is
+// coordinate 32 c4 + j.  Codes become byte selectors (v_perm_b32) into the
+// low and high bytes of the token's eight scaled centroids.
+__device__ inline uint32_t spread4(uint32_t x) {  // bit i of x (i < 4) to bit 0 of byte i
+    return (x * 0x00204081u) & 0x01010101u;
+}
+
+__device__ inline void decode_values3(const FillPlan &f, const Geo &g, const char *stage, char *vrows, int lane,
+                                      const float *cent) {
+    const int nk_pairs = g.H * f.G, nkv = 2 * g.H * f.G;
+    const int x = lane >> 2, c4 = lane & 3;
+    for (int pi = f.pbeg; pi < f.pend; pi += f.pstep) {
+        if (pi < nk_pairs || pi >= nkv) continue;
+        const int h = (pi >> f.lgG) - g.H, gg = pi & (f.G - 1);
+        const char *vq = stage + 16 * (g.ofs_vq + (h * f.G + gg) * 64);
+        const uint32_t w0 = *reinterpret_cast<const uint32_t *>(vq + 48 * x + 4 * c4);
+        const uint32_t w1 = *reinterpret_cast<const uint32_t *>(vq + 48 * x + 16 + 4 * c4);
+        const uint32_t w2 = *reinterpret_cast<const uint32_t *>(vq + 48 * x + 32 + 4 * c4);
+        const float sg = *reinterpret_cast<const float *>(vq + 768 + 4 * x);
+        // the token's scaled centroids as bf16: low bytes (entries 0..3, 4..7) and high bytes
+        uint32_t tl[2] = {0u, 0u}, th[2] = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t b = __builtin_bit_cast(uint16_t, (bf16)(sg * cent[k]));
+            tl[k >> 2] |= (b & 0xFFu) << (8 * (k & 3));
+            th[k >> 2] |= (b >> 8) << (8 * (k & 3));
+        }
+        char *row = vrows + 16 * ((h * g.T + 16 * gg + x) * g.cpr_kv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // chunk 4 c4 + q: coordinates 32 c4 + 8 q .. + 7
+            const uint32_t b0 = (w0 >> (8 * q)) & 0xFFu, b1 = (w1 >> (8 * q)) & 0xFFu, b2 = (w2 >> (8 * q)) & 0xFFu;
+            const uint32_t sa = spread4(b0 & 15u) | (spread4(b1 & 15u) << 1) | (spread4(b2 & 15u) << 2);
+            const uint32_t sb = spread4(b0 >> 4) | (spread4(b1 >> 4) << 1) | (spread4(b2 >> 4) << 2);
+            const uint32_t la = __builtin_amdgcn_perm(tl[1], tl[0], sa), ha = __builtin_amdgcn_perm(th[1], th[0], sa);
+            const uint32_t lb = __builtin_amdgcn_perm(tl[1], tl[0], sb), hb = __builtin_amdgcn_perm(th[1], th[0], sb);
+            u32x4 out;
+            out[0] = __builtin_amdgcn_perm(ha, la, 0x05010400u);  // coordinate pairs (0, 1), (2, 3), ...
+            out[1] = __builtin_amdgcn_perm(ha, la, 0x07030602u);
+            out[2] = __builtin_amdgcn_perm(hb, lb, 0x05010400u);
+            out[3] = __builtin_amdgcn_perm(hb, lb, 0x07030602u);
+            const int pc = swz(x, 4 * c4 + q, g.cpr_kv, g.lg_kv);
+            *reinterpret_cast<u32x4 *>(row + 16 * pc) = out;
+        }
+    }
+}
+
 // ------------------------------------------------------------ split kernel --
 
 // MAXW: most waves a workgroup of this instantiation runs (compute + load
@@ -353,11 +404,12 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
 // of the block (see step16_bf16).
 // KQ8 (bf16 only): base keys are excess-128 int8 codes with one scale; only
 // prefix items exist then (no private tokens).
-template <typename T, int D, int CPAD, bool MASKED, int MAXW, bool KQ8 = false>
+template <typename T, int D, int CPAD, bool MASKED, int MAXW, bool KQ8 = false, bool VQ3 = false>
 __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p) {
     using O = Ops<T>;
     using frag = typename O::frag;
     static_assert(!KQ8 || sizeof(T) == 2, "int8 keys with bf16 queries and values only");
+    static_assert(!VQ3 || KQ8, "3-bit values come with int8 keys");
     constexpr int KS = D / 32;
     constexpr int VPL = D / 16;
     constexpr int CS = CPAD / 32;
@@ -459,9 +511,14 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     g.lr_grp = 16 * g.na_lr * g.cpa_lr;
     g.H = nh;
     g.ofs_v = nh * g.T * g.cpr_k;
-    g.ofs_lk = g.ofs_v + nh * g.T * g.cpr_kv;
+    // 3-bit values: a stage holds no value rows (they are decoded into a double
+    // buffer after the ring, vbuf_off), but their codes and scales at its end
+    g.ofs_lk = g.ofs_v + (VQ3 ? 0 : nh * g.T * g.cpr_kv);
     g.ofs_lv = g.ofs_lk + (resid ? (g.T >> 4) * g.lr_grp : 0);
     g.chunks = g.ofs_lv + (resid ? (g.T >> 4) * g.lr_grp : 0);
+    g.ofs_vq = g.chunks;
+    if constexpr (VQ3) g.chunks += nh * (g.T >> 4) * 64;
+    const int vbuf_bytes = VQ3 ? nh * g.T * g.cpr_kv * 16 : 0;  // one decoded buffer
 
     int *s_pages = reinterpret_cast<int *>(smem + p.table_lds_off);
     Src<T> src;
@@ -476,6 +533,14 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     src.fps = p.fd_ps;
     src.pg0 = 0;
     src.pages = s_pages;
+    src.vq = nullptr;
+    src.vs = nullptr;
+    src.vq_hs = 0;
+    if constexpr (VQ3) {  // prefix items of a contiguous base cache only (the planner's limits)
+        src.vq = static_cast<const uint8_t *>(p.vb) + (int64_t)k0 * p.L * 48;
+        src.vs = p.vs + (int64_t)k0 * p.L;
+        src.vq_hs = p.L;
+    }
     if (prefix) {
         src.kb = static_cast<const T *>(p.kb);
         src.vb = static_cast<const T *>(p.vb);
@@ -517,7 +582,7 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     // The fill plan of this wave.
     const bool compute_wave = wave < p.nw;  // the others only load
     FillPlan fp;
-    make_fill_plan<T, D, KRE>(fp, g, src, resid, compute_wave ? p.np : wave - p.nw, lane, p.np, p.lr_own != 0);
+    make_fill_plan<T, D, KRE>(fp, g, src, resid, compute_wave ? p.np : wave - p.nw, lane, p.np, p.lr_own != 0, VQ3);
     // keys and values that no other workgroup reads are streamed past the caches
     fp.kv_nt = prefix ? p.n_rg == 1 : p.n_prg == 1;
     const int n_tiles = (t1 - t0 + g.T - 1) >> ilog2(g.T);  // T is a power of two
@@ -838,6 +903,12 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
         for (int i = 0; i < n_tiles; ++i) {
             const int later = (n_tiles - 1 - i) < (g.nst - 2) ? (n_tiles - 1 - i) : (g.nst - 2);
             wait_vmcnt(later * fpw);  // this wave's loads of tile i have landed
+            // 3-bit values: decode the groups this wave loaded into buffer i % 2 (the
+            // compute waves finished tile i - 2, its last user, before the barrier
+            // this wave passed in the previous iteration)
+            if constexpr (VQ3)
+                decode_values3(fp, g, smem + (size_t)(i % g.nst) * g.stage_bytes,
+                               smem + p.vbuf_off + (i & 1) * vbuf_bytes, lane, p.vq_c);
             ring_barrier();
             if (fpw && i + g.nst - 1 < n_tiles) fill(i + g.nst - 1, (i + g.nst - 1) % g.nst);
         }
@@ -852,7 +923,11 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
                 if constexpr (KQ8) {
                     // K rows (int8) and V rows have different pitches: two stage bases
                     const int ko = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * k_rowb);
-                    const int vo = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * kv_rowb);
+                    // (3-bit values: the decoded buffer i % 2, laid out like a stage's value
+                    // region, whose offset the read offsets include)
+                    const int vo = __builtin_amdgcn_readfirstlane(
+                        VQ3 ? p.vbuf_off + (i & 1) * vbuf_bytes - 16 * g.ofs_v + row0 * kv_rowb
+                            : (int)(st - smem) + row0 * kv_rowb);
                     const int lo = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * lr_rowb);
                     step16_bf16<D, CPAD, MASKED, true>(acc, ro, vtr, wtr, smem + ko, smem + lo, tt + row0, masked,
                                                        qB, uH, uL, cl2, resid, t1, causal, tq, j4, blk.na,
@@ -1018,6 +1093,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     __shared__ f32x4 s_wp[NWV * 32];  // per-wave W column-group sums
     __shared__ float s_wt[128];       // merged W (r <= 128)
     __shared__ float s_wbv[NWV * D];  // per-wave (W Bv) column sums
+    __shared__ float s_fw[D];         // 3-bit values: the merged O before the inverse rotation
     touch_params<DecodeParams>();
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int R = blockIdx.x;  // (agent, query token, query head), < 2^31
@@ -1176,11 +1252,31 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
     __syncthreads();
 
     // o[d] for d = tid (< D)
+    float o = 0.0f;
     if (tid < D) {
         const int c4 = tid >> 2, e = tid & 3;
-        float o = 0.0f;
 #pragma unroll
         for (int i = 0; i < NWV; ++i) o += s_o[i * D4 + c4][e];
+    }
+    if (p.vq3) {
+        // 3-bit values were decoded in the rotated coordinates: o <- H_d o (Sylvester
+        // order, entries +-1), the stride-64 butterfly through LDS, strides 32 .. 1
+        // between lanes (pair j, j ^ h: the lower index takes a + b, the upper a - b)
+        if (tid < D) s_fw[tid] = o;
+        __syncthreads();
+        if (tid < D) {
+            if constexpr (D == 128) {
+                const float lo = s_fw[tid & 63], hi = s_fw[(tid & 63) | 64];
+                o = tid < 64 ? lo + hi : lo - hi;
+            }
+#pragma unroll
+            for (int hh = 32; hh >= 1; hh >>= 1) {
+                const float u = __shfl_xor(o, hh);
+                o = (lane & hh) ? u - o : o + u;
+            }
+        }
+    }
+    if (tid < D) {
         if (wres)
 #pragma unroll
             for (int i = 0; i < NWV; ++i) o += s_wbv[i * D + tid];
@@ -1191,13 +1287,13 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(DecodeParams p
 
 // ---------------------------------------------------------------- launchers --
 
-template <typename T, int D, int CP, bool M, int W, bool Q>
+template <typename T, int D, int CP, bool M, int W, bool Q, bool V>
 struct SplitSlot {};
 
-template <typename T, int D, int CP, bool M, int W, bool Q = false>
+template <typename T, int D, int CP, bool M, int W, bool Q = false, bool V = false>
 static hipError_t launch_split_w(const DecodeParams &dp, size_t lds, hipStream_t st) {
-    auto *fn = decode_split_kernel<T, D, CP, M, W, Q>;
-    const hipError_t e = ensure_lds<SplitSlot<T, D, CP, M, W, Q>>(reinterpret_cast<const void *>(fn), (int)lds);
+    auto *fn = decode_split_kernel<T, D, CP, M, W, Q, V>;
+    const hipError_t e = ensure_lds<SplitSlot<T, D, CP, M, W, Q, V>>(reinterpret_cast<const void *>(fn), (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, dim3(8 * dp.per_xcd), dim3(64 * (dp.nw + dp.np)), lds, st, dp);
     return hipGetLastError();
@@ -1205,15 +1301,15 @@ static hipError_t launch_split_w(const DecodeParams &dp, size_t lds, hipStream_t
 
 // Only the instantiations that fit in registers (split_ok, split_wide_ok) exist;
 // the planner never asks for another.
-template <typename T, int D, int CP, bool M, bool Q = false>
+template <typename T, int D, int CP, bool M, bool Q = false, bool V = false>
 static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t st) {
     constexpr bool kBf = sizeof(T) == 2;
     if constexpr (!split_ok(kBf, D, CP) || (Q && (!kBf || D != 128))) {
         return hipErrorInvalidValue;
     } else {
-        if (dp.nw + dp.np <= 8) return launch_split_w<T, D, CP, M, 8, Q>(dp, lds, st);
+        if (dp.nw + dp.np <= 8) return launch_split_w<T, D, CP, M, 8, Q, V>(dp, lds, st);
         if constexpr (split_wide_ok(kBf, D, CP))
-            return launch_split_w<T, D, CP, M, 12, Q>(dp, lds, st);
+            return launch_split_w<T, D, CP, M, 12, Q, V>(dp, lds, st);
         else
             return hipErrorInvalidValue;
     }
@@ -1222,6 +1318,22 @@ static hipError_t launch_split(const DecodeParams &dp, size_t lds, hipStream_t s
 template <typename T>
 static hipError_t launch_split_t(const DecodeParams &dp, int D, int cpad, size_t lds, hipStream_t st) {
     if constexpr (sizeof(T) == 2) {
+        if (dp.kq8 && dp.vq3) {  // int8 keys and 3-bit values: d = 128 only
+            if (D != 128) return hipErrorInvalidValue;
+            if (dp.masked) {
+                switch (cpad) {
+                    case 32: return launch_split<T, 128, 32, true, true, true>(dp, lds, st);
+                    case 64: return launch_split<T, 128, 64, true, true, true>(dp, lds, st);
+                    default: return launch_split<T, 128, 128, true, true, true>(dp, lds, st);
+                }
+            }
+            switch (cpad) {
+                case 0: return launch_split<T, 128, 0, false, true, true>(dp, lds, st);
+                case 32: return launch_split<T, 128, 32, false, true, true>(dp, lds, st);
+                case 64: return launch_split<T, 128, 64, false, true, true>(dp, lds, st);
+                default: return launch_split<T, 128, 128, false, true, true>(dp, lds, st);
+            }
+        }
         if (dp.kq8) {  // int8 base keys: d = 128 only
             if (D != 128) return hipErrorInvalidValue;
             if (dp.masked) {

@@ -229,6 +229,12 @@ __device__ inline void dma16s(const void *sbase, uint32_t voff, uint32_t lds_bas
                  : "memory");
 }
 
+// One direct load of 4 bytes per lane: gsrc (per lane) to LDS byte lds_base + 4*lane.
+__device__ inline void dma4(const void *gsrc, uint32_t lds_base) {
+    lds_base = __builtin_amdgcn_readfirstlane(lds_base);
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(gsrc), "{m0}"(lds_base) : "memory");
+}
+
 // Streaming variants (nontemporal bit): for data read exactly once, such as
 // the base and private key/value rows.  On gfx950 the direct loads sustain
 // about 7.3 TB/s with the bit against 5.9 TB/s without it (a one-workgroup-

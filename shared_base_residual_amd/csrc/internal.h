@@ -166,6 +166,15 @@ struct DecodeParams {
     // the same divisors for one multiply each (see FastDiv)
     FastDiv fd_hg, fd_rg, fd_hk, fd_pv, fd_prg, fd_rpa, fd_bpa, fd_g, fd_ps;
     FastDiv fd_hq, fd_ql;  // query heads, query tokens (the merge's row index)
+    // Base values as 3-bit codes after a Walsh-Hadamard rotation (with int8 keys):
+    // vb then holds [H_kv, L, 3 d / 8] bytes of codes and vs the [H_kv, L] scales.
+    // The split kernel stages the codes and scales and its load waves decode them
+    // to bf16 (scale times centroid) in the stage's value region, so the partial
+    // O is in the rotated coordinates; the merge applies H_d once per row.
+    const float *vs;
+    int vq3;
+    int vbuf_off;   // LDS byte offset of the two decoded value buffers (after the ring)
+    float vq_c[8];  // centroids, ascending
 };
 
 // Size of the static device buffer that rattn_decode_noalloc keeps its split

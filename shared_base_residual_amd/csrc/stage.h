@@ -26,6 +26,7 @@ struct Geo {
     int H;                    // KV heads staged: K regions 0..H-1 (T rows of cpr_k chunks each),
                               // then V regions (T rows of cpr_kv), then Lk, Lv
     int ofs_v, ofs_lk, ofs_lv;  // region offsets (chunks): V of head 0, Lk, Lv
+    int ofs_vq;               // 3-bit values: codes and scales, 64 chunks per (head, 16-token group)
     int chunks;               // chunks per stage
     int stage_bytes;          // stride between stages
 };
@@ -53,6 +54,9 @@ struct Src {
     int64_t lr_agent_stride;  // elements between agents' low-rank caches
     int r;                    // rank
     int tlast;                // last valid token of the item
+    const uint8_t *vq;        // 3-bit values: the codes of the first staged head (48 bytes per token)
+    const float *vs;          // and its scales (one per token)
+    int64_t vq_hs;            // tokens per head (the stride of both, in vectors)
 };
 
 // Row `tok` of a K or V region source: RE elements of T per row, page_stride
@@ -91,6 +95,7 @@ struct FillPlan {
     int fpw;                  // loads this wave issues per stage
     uint32_t lr_stride;       // bytes between agents' low-rank caches
     bool kv_nt;               // K/V rows are read by this workgroup only: stream them
+    bool vq3;                 // V pairs stage 3-bit codes and scales (two loads each)
     uint32_t kv_off[kMaxKvLoads];  // lane byte offset of V (or K) load i from the group's first row
                                    // (only the first d * sizeof(T) / 64 are set and used)
     uint32_t k_off[kMaxKvLoads];   // the same for K rows of KRE elements
@@ -116,7 +121,7 @@ __device__ inline uint32_t kv_lane_off(int cpr, int lg, int rowb, int i, int lan
 template <typename T, int D, int KRE = D>
 __device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f, const Geo &g, const Src<T> &s,
                                                                      bool resid, int wave, int lane, int nw,
-                                                                     bool lr_own = false) {
+                                                                     bool lr_own = false, bool vq3 = false) {
     constexpr int ES = (int)sizeof(T);
     f.G = g.T >> 4;
     f.lgG = ilog2(f.G);
@@ -144,8 +149,10 @@ __device__ __attribute__((always_inline)) inline void make_fill_plan(FillPlan &f
     f.n_k = (16 * g.cpr_k) >> 6;
     f.n_lr = resid ? ((g.lr_grp + 63) >> 6) : 0;
     f.fpw = 0;
+    f.vq3 = vq3;
     const int nk_pairs = g.H * f.G;  // K pairs come first, then V
-    for (int pi = f.pbeg; pi < f.pend; pi += f.pstep) f.fpw += pi < nk_pairs ? f.n_k : pi < nkv ? f.n_kv : f.n_lr;
+    const int n_v = vq3 ? 2 : f.n_kv;
+    for (int pi = f.pbeg; pi < f.pend; pi += f.pstep) f.fpw += pi < nk_pairs ? f.n_k : pi < nkv ? n_v : f.n_lr;
     f.lr_stride = (uint32_t)(s.lr_agent_stride * ES);
     f.kv_nt = false;
     constexpr int NKV = D * ES / 64;  // loads per V group: 16 rows of d elements
@@ -215,6 +222,27 @@ __device__ __attribute__((always_inline)) inline void fill_kv_group(const FillPl
     }
 }
 
+// One 16-token group of 3-bit values of one head: lanes 0..47 load the 768
+// bytes of codes (16 bytes each, token tg0 + lane / 3), lanes 0..15 the 16
+// scales (4 bytes each) into bytes 768..831 of the group's 1 KiB region.
+// Tokens past the item's last read that token instead.  Two direct loads.
+template <typename T>
+__device__ __attribute__((always_inline)) inline void fill_vq_group(const Src<T> &s, int head, int tg0,
+                                                                    uint32_t dst, int lane) {
+    const uint8_t *codes = s.vq + (int64_t)head * s.vq_hs * 48;
+    const float *scales = s.vs + (int64_t)head * s.vq_hs;
+    if (lane < 48) {
+        int tok = tg0 + lane / 3;
+        tok = tok < s.tlast ? tok : s.tlast;
+        dma16(codes + (int64_t)tok * 48 + 16 * (lane % 3), dst);
+    }
+    if (lane < 16) {
+        int tok = tg0 + lane;
+        tok = tok < s.tlast ? tok : s.tlast;
+        dma4(scales + tok, dst + 768);
+    }
+}
+
 template <typename T, int D, int KRE = D>
 __device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan &f, const Geo &g, const Src<T> &s,
                                                                  int t0, char *stage, bool clamp, int lane) {
@@ -226,7 +254,10 @@ __device__ __attribute__((always_inline)) inline void fill_stage(const FillPlan 
         const int tg0 = t0 + 16 * gg;  // the group's first token
         if (pi < nkv) {
             const int region = pi >> f.lgG;
-            if (region >= g.H) {  // V rows of head region - H
+            if (region >= g.H && f.vq3) {  // 3-bit codes and scales of head region - H
+                fill_vq_group<T>(s, region - g.H, tg0, lds0 + 16 * (g.ofs_vq + ((region - g.H) * f.G + gg) * 64),
+                                 lane);
+            } else if (region >= g.H) {  // V rows of head region - H
                 const T *base = s.vb + (int64_t)(region - g.H) * s.head_stride;
                 const uint32_t dst = lds0 + 16 * (g.ofs_v + ((region - g.H) * g.T + 16 * gg) * g.cpr_kv);
                 fill_kv_group<T, D>(f, s, base, s.page_stride, f.kv_off, g.lg_kv, tg0, dst, clamp, lane);

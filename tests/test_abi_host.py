@@ -152,7 +152,7 @@ def args(**kw):
     a = dict(q=FAKE, k_base=FAKE, v_base=FAKE, block_table=None, lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE,
              k_priv=None, v_priv=None, out=FAKE, lse=None)
     a.update(kw)
-    return R.Args(*[a[n] for n, _ in R.Args._fields_])
+    return R.Args(*[a.get(n) for n, _ in R.Args._fields_])
 
 
 def call(desc, a, ws_ptr=FAKE, ws_bytes=1 << 40, fn="rattn_decode"):
