@@ -329,7 +329,7 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
             }
             const int f = max_fpw(T, H, lr_row_bytes, 4);
             p.np = 4;
-            while (*nst > 2 && f * (*nst - 1) > 63) --*nst;
+            while (*nst > (p.vq3 ? 3 : 2) && f * (*nst - 1) > 63) --*nst;
             return f * (*nst - 1) <= 63;
         };
 
@@ -350,7 +350,8 @@ int make_plan(const rattn_desc *d, int op, Plan *pl) {
                     const int sb = t * (H * (k_row + (p.vq3 ? vq_row : kv_row)) + 2 * lr_row_bytes);
                     const int vbuf = p.vq3 ? 2 * H * t * kv_row : 0;  // the decoded value buffers
                     const int n = (rattn::kLdsMax - table_bytes - vbuf) / sb;
-                    if (n >= 3 || (t == 16 * tg_max && n >= need)) {
+                    // (3-bit values keep nst - 2 tiles in flight: at least three stages)
+                    if (n >= 3 || (!p.vq3 && t == 16 * tg_max && n >= need)) {
                         *T = t;
                         const int cap = p.vq3 ? 6 : 4;  // (small 3-bit stages: more of them in flight)
                         *nst = n < cap ? n : cap;

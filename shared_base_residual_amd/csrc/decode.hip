@@ -344,54 +344,62 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     }
 }
 
-// 3-bit values (PolyKV, section 2B): the groups of value codes this wave
-// filled into `stage` (the V pairs of its fill plan) become bf16 value rows in
-// `vrows` (laid out like a stage's value region), scale times centroid in the
-// rotated coordinates; the compute waves then read them like any value rows,
-// and the merge undoes the rotation.  Lane (x, c4) = (lane / 4, lane % 4) decodes token x of the group,
-// coordinates 32 c4 .. 32 c4 + 31: bit j of the three 32-bit plane words is
-// coordinate 32 c4 + j.  Codes become byte selectors (v_perm_b32) into the
-// low and high bytes of the token's eight scaled centroids.
+// 3-bit values (PolyKV, section 2B): the value codes of a stage become bf16
+// value rows in `vrows` (laid out like a stage's value region), scale times
+// centroid in the rotated coordinates; the compute waves then read them like
+// any value rows, and the merge undoes the rotation.  Work units: chunk m of
+// value group q (q = head * G + 16-token group, m = 0..3), one 16-byte chunk of
+// 8 coordinates per lane; lane (x, c4) = (lane / 4, lane % 4) takes token x of
+// the group, coordinates 32 c4 + 8 m .. + 7 (bits 8 m .. 8 m + 7 of the three
+// 32-bit plane words of coordinates 32 c4 ..).  Codes become byte selectors
+// (v_perm_b32) into the low and high bytes of the token's eight scaled centroids.
 __device__ inline uint32_t spread4(uint32_t x) {  // bit i of x (i < 4) to bit 0 of byte i
     return (x * 0x00204081u) & 0x01010101u;
 }
 
-__device__ inline void decode_values3(const FillPlan &f, const Geo &g, const char *stage, char *vrows, int lane,
+// Units u0 .. u1 - 1 (u = 4 q + m) of the stage at `stage`.
+__device__ inline void decode_values3(const Geo &g, int G, int u0, int u1, const char *stage, char *vrows, int lane,
                                       const float *cent) {
-    const int nk_pairs = g.H * f.G, nkv = 2 * g.H * f.G;
     const int x = lane >> 2, c4 = lane & 3;
-    for (int pi = f.pbeg; pi < f.pend; pi += f.pstep) {
-        if (pi < nk_pairs || pi >= nkv) continue;
-        const int h = (pi >> f.lgG) - g.H, gg = pi & (f.G - 1);
-        const char *vq = stage + 16 * (g.ofs_vq + (h * f.G + gg) * 64);
-        const uint32_t w0 = *reinterpret_cast<const uint32_t *>(vq + 48 * x + 4 * c4);
-        const uint32_t w1 = *reinterpret_cast<const uint32_t *>(vq + 48 * x + 16 + 4 * c4);
-        const uint32_t w2 = *reinterpret_cast<const uint32_t *>(vq + 48 * x + 32 + 4 * c4);
-        const float sg = *reinterpret_cast<const float *>(vq + 768 + 4 * x);
-        // the token's scaled centroids as bf16: low bytes (entries 0..3, 4..7) and high bytes
-        uint32_t tl[2] = {0u, 0u}, th[2] = {0u, 0u};
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const uint32_t b = __builtin_bit_cast(uint16_t, (bf16)(sg * cent[k]));
-            tl[k >> 2] |= (b & 0xFFu) << (8 * (k & 3));
-            th[k >> 2] |= (b >> 8) << (8 * (k & 3));
+    uint32_t w0 = 0, w1 = 0, w2 = 0, tl0 = 0, tl1 = 0, th0 = 0, th1 = 0;
+    char *row = vrows;
+    for (int u = u0; u < u1; ++u) {
+        const int q = u >> 2, m = u & 3;
+        if (m == 0 || u == u0) {  // a new group: its plane words, scale and centroid table
+            const char *vq = stage + 16 * (g.ofs_vq + q * 64);
+            w0 = *reinterpret_cast<const uint32_t *>(vq + 48 * x + 4 * c4);
+            w1 = *reinterpret_cast<const uint32_t *>(vq + 48 * x + 16 + 4 * c4);
+            w2 = *reinterpret_cast<const uint32_t *>(vq + 48 * x + 32 + 4 * c4);
+            const float sg = *reinterpret_cast<const float *>(vq + 768 + 4 * x);
+            // The token's scaled centroids as bf16, entries 0..7.  The codebook is
+            // symmetric (c_k = -c_{7-k}), so entries 4..7 are two packed conversions
+            // and entries 0..3 the same values reversed with the sign bit flipped.
+            const uint32_t e45 =
+                __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{sg * cent[4], sg * cent[5]}, bf16x2));
+            const uint32_t e67 =
+                __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{sg * cent[6], sg * cent[7]}, bf16x2));
+            const uint32_t e01 = __builtin_amdgcn_perm(e67, e67, 0x01000302u) ^ 0x80008000u;  // (-e7, -e6)
+            const uint32_t e23 = __builtin_amdgcn_perm(e45, e45, 0x01000302u) ^ 0x80008000u;  // (-e5, -e4)
+            // low and high bytes of entries 0..3 and 4..7: the byte tables of v_perm_b32
+            tl0 = __builtin_amdgcn_perm(e23, e01, 0x06040200u);
+            tl1 = __builtin_amdgcn_perm(e67, e45, 0x06040200u);
+            th0 = __builtin_amdgcn_perm(e23, e01, 0x07050301u);
+            th1 = __builtin_amdgcn_perm(e67, e45, 0x07050301u);
+            const int h = q / G, gg = q - h * G;
+            row = vrows + 16 * ((h * g.T + 16 * gg + x) * g.cpr_kv);
         }
-        char *row = vrows + 16 * ((h * g.T + 16 * gg + x) * g.cpr_kv);
+        u32x4 out;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {  // chunk 4 c4 + q: coordinates 32 c4 + 8 q .. + 7
-            const uint32_t b0 = (w0 >> (8 * q)) & 0xFFu, b1 = (w1 >> (8 * q)) & 0xFFu, b2 = (w2 >> (8 * q)) & 0xFFu;
-            const uint32_t sa = spread4(b0 & 15u) | (spread4(b1 & 15u) << 1) | (spread4(b2 & 15u) << 2);
-            const uint32_t sb = spread4(b0 >> 4) | (spread4(b1 >> 4) << 1) | (spread4(b2 >> 4) << 2);
-            const uint32_t la = __builtin_amdgcn_perm(tl[1], tl[0], sa), ha = __builtin_amdgcn_perm(th[1], th[0], sa);
-            const uint32_t lb = __builtin_amdgcn_perm(tl[1], tl[0], sb), hb = __builtin_amdgcn_perm(th[1], th[0], sb);
-            u32x4 out;
-            out[0] = __builtin_amdgcn_perm(ha, la, 0x05010400u);  // coordinate pairs (0, 1), (2, 3), ...
-            out[1] = __builtin_amdgcn_perm(ha, la, 0x07030602u);
-            out[2] = __builtin_amdgcn_perm(hb, lb, 0x05010400u);
-            out[3] = __builtin_amdgcn_perm(hb, lb, 0x07030602u);
-            const int pc = swz(x, 4 * c4 + q, g.cpr_kv, g.lg_kv);
-            *reinterpret_cast<u32x4 *>(row + 16 * pc) = out;
+        for (int hq = 0; hq < 2; ++hq) {  // coordinates 8 m + 4 hq .. + 3 of the lane's 32
+            const int b = 8 * m + 4 * hq;
+            const uint32_t sel = spread4(__builtin_amdgcn_ubfe(w0, b, 4)) |
+                                 (spread4(__builtin_amdgcn_ubfe(w1, b, 4)) << 1) |
+                                 (spread4(__builtin_amdgcn_ubfe(w2, b, 4)) << 2);  // byte i: code of b + i
+            const uint32_t lo = __builtin_amdgcn_perm(tl1, tl0, sel), hi = __builtin_amdgcn_perm(th1, th0, sel);
+            out[2 * hq] = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // coordinate pairs (0, 1), (2, 3)
+            out[2 * hq + 1] = __builtin_amdgcn_perm(hi, lo, 0x07030602u);
         }
+        *reinterpret_cast<u32x4 *>(row + 16 * swz(x, 4 * c4 + m, g.cpr_kv, g.lg_kv)) = out;
     }
 }
 
@@ -899,51 +907,86 @@ __global__ __launch_bounds__(64 * MAXW) void decode_split_kernel(DecodeParams p)
     // role runs a loop of its own with the same barriers, so neither carries the
     // other's state through its loop.
     const int spw = g.T / (16 * TG);  // 16-token steps per wave per tile
-    if (!compute_wave) {
-        for (int i = 0; i < n_tiles; ++i) {
-            const int later = (n_tiles - 1 - i) < (g.nst - 2) ? (n_tiles - 1 - i) : (g.nst - 2);
-            wait_vmcnt(later * fpw);  // this wave's loads of tile i have landed
-            // 3-bit values: decode the groups this wave loaded into buffer i % 2 (the
-            // compute waves finished tile i - 2, its last user, before the barrier
-            // this wave passed in the previous iteration)
-            if constexpr (VQ3)
-                decode_values3(fp, g, smem + (size_t)(i % g.nst) * g.stage_bytes,
-                               smem + p.vbuf_off + (i & 1) * vbuf_bytes, lane, p.vq_c);
-            ring_barrier();
-            if (fpw && i + g.nst - 1 < n_tiles) fill(i + g.nst - 1, (i + g.nst - 1) % g.nst);
+    // 3-bit values: each compute wave decodes its share of the value groups of a
+    // tile into buffer (tile % 2): tile 0 after a first barrier, tile i + 1 after
+    // computing tile i (that buffer's last reader, tile i - 1, finished before
+    // barrier i).  The load waves only load: their loop is bound by the issue of
+    // the direct loads, so decoding there lengthens every tile.
+    auto decode_share = [&](int j) {
+        if constexpr (VQ3) {
+            const int G = g.T >> 4, U = 4 * nh * G;
+            decode_values3(g, G, wave * U / p.nw, (wave + 1) * U / p.nw, smem + (size_t)(j % g.nst) * g.stage_bytes,
+                           smem + p.vbuf_off + (j & 1) * vbuf_bytes, lane, p.vq_c);
         }
-    } else for (int i = 0; i < n_tiles; ++i) {
-        ring_barrier();
-        if (wave_on) {
-            const char *st = smem + (size_t)(i % g.nst) * g.stage_bytes;
-            const int tt = t0 + i * g.T;
-            const bool masked = causal || tt + g.T > t1;
-            for (int u = 0; u < spw; ++u) {
-                const int row0 = 16 * (tg * spw + u);
-                if constexpr (KQ8) {
-                    // K rows (int8) and V rows have different pitches: two stage bases
-                    const int ko = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * k_rowb);
-                    // (3-bit values: the decoded buffer i % 2, laid out like a stage's value
-                    // region, whose offset the read offsets include)
-                    const int vo = __builtin_amdgcn_readfirstlane(
-                        VQ3 ? p.vbuf_off + (i & 1) * vbuf_bytes - 16 * g.ofs_v + row0 * kv_rowb
-                            : (int)(st - smem) + row0 * kv_rowb);
-                    const int lo = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * lr_rowb);
-                    step16_bf16<D, CPAD, MASKED, true>(acc, ro, vtr, wtr, smem + ko, smem + lo, tt + row0, masked,
-                                                       qB, uH, uL, cl2, resid, t1, causal, tq, j4, blk.na,
-                                                       vm ? arow_m : -1, 256 * g.cpa_lr, smem + vo, qH, kinit);
-                } else if constexpr (kBf16) {
-                    // the step's stage offsets as opaque wave-uniform values: one add per
-                    // operand read, rather than per-read offsets advanced every step
-                    const int ko = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * kv_rowb);
-                    const int lo = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * lr_rowb);
-                    step16_bf16<D, CPAD, MASKED>(acc, ro, vtr, wtr, smem + ko, smem + lo,
-                                                 tt + row0, masked, qB, uH, uL, cl2, resid, t1, causal, tq, j4,
-                                                 blk.na, vm ? arow_m : -1, 256 * g.cpa_lr);
+    };
+    if (!compute_wave) {
+        if constexpr (VQ3) {
+            // tile i + 1 is decoded after barrier i, so it must have landed by then:
+            // this wave waits one tile ahead, and the ring keeps nst - 2 tiles in flight
+            int issued = n_tiles < g.nst - 1 ? n_tiles : g.nst - 1;  // tiles 0 .. issued - 1
+            auto wait_landed = [&](int j) {  // this wave's loads of tiles 0 .. j have landed
+                const int after = issued - 1 - j;
+                wait_vmcnt(after > 0 ? after * fpw : 0);
+            };
+            wait_landed(n_tiles > 1 ? 1 : 0);
+            ring_barrier();  // tiles 0 and 1 have landed
+            for (int i = 0; i < n_tiles; ++i) {
+                ring_barrier();
+                if (i + g.nst - 1 < n_tiles) {
+                    if (fpw) fill(i + g.nst - 1, (i + g.nst - 1) % g.nst);
+                    ++issued;
                 }
-                else
-                    step16<T, D, CPAD>(acc, ro, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked, qB, uH,
-                                       uL, cl2, resid, t1, causal, tq, j4);
+                if (i + 2 < n_tiles) wait_landed(i + 2);
+            }
+        } else {
+            for (int i = 0; i < n_tiles; ++i) {
+                const int later = (n_tiles - 1 - i) < (g.nst - 2) ? (n_tiles - 1 - i) : (g.nst - 2);
+                wait_vmcnt(later * fpw);  // this wave's loads of tile i have landed
+                ring_barrier();
+                if (fpw && i + g.nst - 1 < n_tiles) fill(i + g.nst - 1, (i + g.nst - 1) % g.nst);
+            }
+        }
+    } else {
+        if constexpr (VQ3) {
+            ring_barrier();  // tiles 0 and 1 have landed
+            if (n_tiles > 0) decode_share(0);
+        }
+        for (int i = 0; i < n_tiles; ++i) {
+            ring_barrier();
+            if (wave_on) {
+                const char *st = smem + (size_t)(i % g.nst) * g.stage_bytes;
+                const int tt = t0 + i * g.T;
+                const bool masked = causal || tt + g.T > t1;
+                for (int u = 0; u < spw; ++u) {
+                    const int row0 = 16 * (tg * spw + u);
+                    if constexpr (KQ8) {
+                        // K rows (int8) and V rows have different pitches: two stage bases
+                        const int ko = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * k_rowb);
+                        // (3-bit values: the decoded buffer i % 2, laid out like a stage's value
+                        // region, whose offset the read offsets include)
+                        const int vo = __builtin_amdgcn_readfirstlane(
+                            VQ3 ? p.vbuf_off + (i & 1) * vbuf_bytes - 16 * g.ofs_v + row0 * kv_rowb
+                                : (int)(st - smem) + row0 * kv_rowb);
+                        const int lo = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * lr_rowb);
+                        step16_bf16<D, CPAD, MASKED, true>(acc, ro, vtr, wtr, smem + ko, smem + lo, tt + row0, masked,
+                                                           qB, uH, uL, cl2, resid, t1, causal, tq, j4, blk.na,
+                                                           vm ? arow_m : -1, 256 * g.cpa_lr, smem + vo, qH, kinit);
+                    } else if constexpr (kBf16) {
+                        // the step's stage offsets as opaque wave-uniform values: one add per
+                        // operand read, rather than per-read offsets advanced every step
+                        const int ko = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * kv_rowb);
+                        const int lo = __builtin_amdgcn_readfirstlane((int)(st - smem) + row0 * lr_rowb);
+                        step16_bf16<D, CPAD, MASKED>(acc, ro, vtr, wtr, smem + ko, smem + lo,
+                                                     tt + row0, masked, qB, uH, uL, cl2, resid, t1, causal, tq, j4,
+                                                     blk.na, vm ? arow_m : -1, 256 * g.cpa_lr);
+                    }
+                    else
+                        step16<T, D, CPAD>(acc, ro, st + row0 * kv_rowb, st + row0 * lr_rowb, tt + row0, masked, qB, uH,
+                                           uL, cl2, resid, t1, causal, tq, j4);
+                }
+            }
+            if constexpr (VQ3) {
+                if (i + 1 < n_tiles) decode_share(i + 1);
             }
         }
     }
