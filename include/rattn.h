@@ -293,7 +293,8 @@ int rattn_quantize_keys(const void *k, int64_t n, int32_t dtype, void *codes, fl
  * z, ||v||, u and the comparisons are computed in fp64 (z and ||v||^2 exactly
  * for bf16 inputs).  The decoded vector is scale * H_d c, c_j the centroid of
  * code_j.  One kernel launch on `stream`; deterministic.  Inputs must be finite.
- * codes must be 16-byte aligned, v aligned to its element and scale to 4 bytes.
+ * codes must be 8-byte aligned (rattn_decode reads them from a 16-byte aligned
+ * v_base), v aligned to its element and scale to 4 bytes.
  */
 int rattn_quantize_values(const void *v, int64_t n, int32_t head_dim, int32_t dtype, void *codes, float *scale,
                           void *stream);
