@@ -4,23 +4,27 @@
 // (ForkKV Guide, "Fused ResidualAttention"; LRAgent, "Flash-LoRA-Attention"):
 //   score  s = scale * (q . K_base[j] + (q Bk_a^T) . Lk_a[j])
 //   output o = sum_j p_j V_base[j] + (sum_j p_j Lv_a[j]) Bv_a
-// One launch.  Each workgroup (four or eight waves) takes one (KV head, row
-// group, context split):
-//   * U = scale*log2(e) * q Bk_a^T for its query rows, with MFMA;
-//   * the split's tokens are streamed in tiles of T tokens through a ring of
-//     LDS stages filled by direct global->LDS loads (no registers in between,
-//     several tiles in flight).  A stage holds the tile's base keys and values
-//     and the low-rank rows (Lk, Lv) of every agent the workgroup serves, each
-//     read from HBM once and shared by all the waves;
-//   * each wave owns one 16-row MFMA row block (query rows of one or more
-//     agents) and a share of each tile's tokens: one MFMA contraction scores the
-//     base keys against all agents' rows, a second adds the rank-r correction
-//     over the agents' Lk rows; online softmax in the log2 domain; P V_base and
-//     P Lv accumulate in registers.  Private tokens (decode suffix, causal
-//     prefill chunk) are extra work items with per-agent keys and no residual;
+// Two launches.  The split kernel: each workgroup takes one (group of KV heads,
+// row group, context split) and runs compute waves and load waves:
+//   * the load waves stream the split's tokens in tiles of T tokens through a
+//     ring of LDS stages with direct global->LDS loads (several tiles in
+//     flight) and wait for them; a stage holds the tile's base keys and values
+//     of the item's heads and the low-rank rows (Lk, Lv) of every agent the
+//     workgroup serves, each read from HBM once and shared by all compute waves;
+//   * each compute wave forms U = q Bk_a^T for its rows with MFMA, then owns one
+//     16-row MFMA row block (query rows of one or more agents) of one head and a
+//     share of each tile's tokens: one MFMA contraction scores the base keys
+//     against all agents' rows, a second adds the rank-r correction over the
+//     agents' Lk rows; online softmax in the log2 domain; P V_base and P Lv
+//     accumulate in registers.  Private tokens (decode suffix, causal prefill
+//     chunk) are extra work items with per-agent keys and no residual;
 //   * the partial state (max, sum, O, W) of every row goes to the workspace.
-// A second, small kernel merges the splits of each query row (one wavefront per
-// row, a log-sum-exp merge with wavefront reductions) and applies Bv once per
+// Variants: int8 base keys (PolyKV, section 2B; codes scored on fp16 MFMAs
+// against fp16 query rows) and, with them, 3-bit Walsh-Hadamard-rotated values
+// (the compute waves decode each tile's codes into a double buffer of bf16 rows,
+// and the merge undoes the rotation).
+// The merge kernel: one workgroup per query row combines the splits with a
+// log-sum-exp merge (lane reductions, one LDS pass) and applies Bv once per
 // row: o = (sum w O + (sum w W) Bv_a^(k)) / sum w l (LRAgent: B is applied once
 // per query block, not per token).
 //
@@ -29,8 +33,8 @@
 // scores arrive with one query row per lane column and the softmax statistics
 // of a row live in the lanes that own it.  The value product is O^T = V^T P^T
 // over 16-token steps (v_mfma_f32_16x16x16_bf16), so P feeds the B operand
-// straight from the score registers and each lane reads one contiguous
-// segment of a value row.
+// straight from the score registers, and V^T comes from gfx950's transposing
+// LDS read.
 //
 // Loads never branch on the data: token indices beyond the split are clamped
 // to its last token (finite data) and those scores are masked to -inf, so
