@@ -241,6 +241,20 @@ int rattn_gather_base(const rattn_desc *desc, const void *pool, const int32_t *b
                       void *stream);
 
 /*
+ * Debug check of a block table before it is used: writes to *bad_count (a
+ * device int32) the number of the ceil(prefix_len / page_size) entries of
+ * block_table that lie outside [0, n_phys_pages) -- the entries whose use by
+ * rattn_decode, rattn_prefill_chunk or rattn_gather_base is undefined
+ * behaviour (the table holds the ForkKV Guide's bCache block pointers as
+ * physical page indices, "Two-Tier Lookup Mechanics").  Reads only the table.
+ * One launch on `stream`; copy the count to the host after it.  Uses
+ * desc->prefix_len, page_size (a positive multiple of 16, else
+ * RATTN_E_UNSUPPORTED) and n_phys_pages; prefix_len = 0 writes 0.  block_table
+ * 4-byte and bad_count 4-byte aligned device pointers.
+ */
+int rattn_check_block_table(const rattn_desc *desc, const int32_t *block_table, int32_t *bad_count, void *stream);
+
+/*
  * Runs selected launches of rattn_decode (op = RATTN_OP_DECODE) or
  * rattn_prefill_chunk (op = RATTN_OP_PREFILL), in their fixed order:
  *   RATTN_STAGE_SPLIT    per-split partial attention into the workspace;

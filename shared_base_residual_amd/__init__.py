@@ -37,7 +37,7 @@ EXPORTS = ("rattn_workspace_bytes", "rattn_decode", "rattn_prefill_chunk", "ratt
            "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
            "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
            "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv",
-           "rattn_quantize_keys", "rattn_decode_reconstruct", "rattn_quantize_values", "rattn_values_codebook")
+           "rattn_quantize_keys", "rattn_decode_reconstruct", "rattn_quantize_values", "rattn_values_codebook", "rattn_check_block_table")
 STAGE_SPLIT, STAGE_COMBINE, STAGE_ALL = 1, 2, 3
 
 
@@ -130,6 +130,7 @@ def lib():
         L.rattn_decode_reconstruct.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(Args), P, P, ctypes.c_size_t, P]
         L.rattn_quantize_values.argtypes = [P, I64, ctypes.c_int32, ctypes.c_int32, P, P, P]
         L.rattn_values_codebook.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+        L.rattn_check_block_table.argtypes = [ctypes.POINTER(Desc), P, P, P]
         for f in ("rattn_decode_reconstruct", "rattn_quantize_keys", "rattn_lr_project", "rattn_pagepool_create", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
                   "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append",
                   "rattn_append_kv"):
@@ -141,7 +142,7 @@ def lib():
                   "rattn_attention_stages", "rattn_decode_noalloc", "rattn_lr_project", "rattn_pagepool_create",
            "rattn_pagepool_destroy", "rattn_pagepool_free_pages", "rattn_pagepool_refcount", "rattn_pagepool_alloc",
            "rattn_pagepool_retain", "rattn_pagepool_release", "rattn_pagepool_plan_append", "rattn_append_kv",
-           "rattn_quantize_keys", "rattn_decode_reconstruct", "rattn_quantize_values", "rattn_values_codebook"):
+           "rattn_quantize_keys", "rattn_decode_reconstruct", "rattn_quantize_values", "rattn_values_codebook", "rattn_check_block_table"):
             getattr(L, f).restype = I
         _lib = L
     return _lib
@@ -468,6 +469,25 @@ def quantize_values(v, *, codes=None, scale=None, stream=None):
     if st:
         raise RattnError(st, "rattn_quantize_values")
     return codes, scale
+
+
+def check_block_table(block_table, prefix_len: int, page_size: int, n_phys_pages: int, *, stream=None) -> int:
+    """rattn_check_block_table: the number of the ceil(prefix_len / page_size)
+    entries of the int32 device tensor ``block_table`` outside
+    [0, n_phys_pages).  Synchronises the stream to read the count."""
+    import torch
+
+    desc = make_desc(n_agents=1, n_q_heads=1, n_kv_heads=1, head_dim=128, rank=0, q_len=1, prefix_len=prefix_len,
+                     page_size=page_size, n_phys_pages=n_phys_pages)
+    n = -(-prefix_len // page_size) if page_size > 0 else 0
+    if block_table.dtype != torch.int32 or block_table.numel() < n or not block_table.is_contiguous():
+        raise ValueError("block_table: a contiguous int32 tensor of at least ceil(prefix_len / page_size) entries")
+    bad = torch.empty(1, device=block_table.device, dtype=torch.int32)
+    st = lib().rattn_check_block_table(ctypes.byref(desc), ctypes.c_void_p(block_table.data_ptr()),
+                                       ctypes.c_void_p(bad.data_ptr()), _stream(stream))
+    if st:
+        raise RattnError(st, "rattn_check_block_table")
+    return int(bad.cpu().item())
 
 
 def values_codebook():

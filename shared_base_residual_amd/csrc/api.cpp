@@ -20,6 +20,7 @@ hipError_t launch_lr_project(const LrParams &p, hipStream_t st);
 hipError_t launch_append_kv(const AppendParams &p, hipStream_t st);
 hipError_t launch_quantize(const void *k, int64_t n, int bf16_in, void *codes, float *scale, hipStream_t st);
 hipError_t launch_recon(const ReconParams &p, hipStream_t st);
+hipError_t launch_check_table(const int32_t *table, int64_t n, int64_t n_phys, int32_t *bad, hipStream_t st);
 hipError_t launch_values3_encode(const void *v, int64_t n, int D, int bf16_in, const double *boundaries, void *codes,
                                  float *scale, hipStream_t st);
 }  // namespace rattn
@@ -1018,6 +1019,18 @@ int rattn_gather_base(const rattn_desc *d, const void *pool, const int32_t *bloc
     if (!aligned(pool, 16) || !aligned(dst, 16) || !aligned(block_table, 4)) return RATTN_E_ALIGN;
     return hip_status(rattn::launch_gather(pool, block_table, dst, d->prefix_len, d->n_kv_heads, d->page_size,
                                            (int)(d->head_dim * esize(d->dtype)), static_cast<hipStream_t>(stream)));
+}
+
+int rattn_check_block_table(const rattn_desc *d, const int32_t *block_table, int32_t *bad_count, void *stream) {
+    if (!d || !bad_count) return RATTN_E_NULL;
+    if (d->prefix_len < 0 || d->page_size < 0 || d->n_phys_pages < 0) return RATTN_E_SHAPE;
+    if (d->page_size == 0 || d->page_size % 16) return RATTN_E_UNSUPPORTED;
+    if (!aligned(bad_count, 4)) return RATTN_E_ALIGN;
+    const int64_t n = cdiv(d->prefix_len, d->page_size);
+    if (n > 0 && !block_table) return RATTN_E_NULL;
+    if (block_table && !aligned(block_table, 4)) return RATTN_E_ALIGN;
+    return hip_status(rattn::launch_check_table(block_table, n, d->n_phys_pages, bad_count,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -39,4 +39,30 @@ hipError_t launch_gather(const void *pool, const int32_t *table, void *dst, int6
     return hipGetLastError();
 }
 
+// The debug check of a table: one workgroup counts the entries outside
+// [0, n_phys) (a grid-stride walk, then a workgroup sum through LDS) and
+// writes the count.  The table alone is read; no entry is followed.
+__global__ __launch_bounds__(1024) void check_table_kernel(const int32_t *__restrict__ table, int64_t n,
+                                                           int64_t n_phys, int32_t *bad) {
+    __shared__ int s_cnt[16];
+    int c = 0;
+    for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int64_t e = table[i];
+        c += (e < 0 || e >= n_phys) ? 1 : 0;
+    }
+    for (int h = 32; h >= 1; h >>= 1) c += __shfl_xor(c, h);
+    if ((threadIdx.x & 63) == 0) s_cnt[threadIdx.x >> 6] = c;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int t = 0;
+        for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += s_cnt[w];
+        bad[0] = t;
+    }
+}
+
+hipError_t launch_check_table(const int32_t *table, int64_t n, int64_t n_phys, int32_t *bad, hipStream_t st) {
+    hipLaunchKernelGGL(check_table_kernel, dim3(1), dim3(1024), 0, st, table, n, n_phys, bad);
+    return hipGetLastError();
+}
+
 }  // namespace rattn

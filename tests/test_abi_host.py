@@ -213,6 +213,21 @@ def test_gather_validation():
                                None, None, None) == OK
 
 
+def test_check_block_table_validation():
+    """rattn_check_block_table: every check before any HIP call."""
+    L = R.lib()
+    f = L.rattn_check_block_table
+    d = cfg1_desc(page_size=16, n_phys_pages=8, prefix_len=100)
+    assert f(ctypes.byref(d), FAKE, None, None) == E_NULL
+    assert f(None, FAKE, FAKE, None) == E_NULL
+    assert f(ctypes.byref(d), None, FAKE, None) == E_NULL
+    assert f(ctypes.byref(d), FAKE + 2, FAKE, None) == E_ALIGN
+    assert f(ctypes.byref(d), FAKE, FAKE + 1, None) == E_ALIGN
+    assert f(ctypes.byref(cfg1_desc(page_size=0)), FAKE, FAKE, None) == E_UNSUP
+    assert f(ctypes.byref(cfg1_desc(page_size=24, n_phys_pages=8)), FAKE, FAKE, None) == E_UNSUP
+    assert f(ctypes.byref(cfg1_desc(page_size=16, n_phys_pages=-1)), FAKE, FAKE, None) == E_SHAPE
+
+
 def test_stage_mask_validation():
     """rattn_attention_stages accepts only a non-empty subset of split | combine,
     and only the two ops; all checked before any HIP call."""

@@ -245,6 +245,36 @@ def test_gather_base_bit_exact():
                           oracle.gather_base(c2, x2["v_base"], x2["block_table"]).view(np.uint32))
 
 
+def test_check_block_table():
+    """The debug check counts exactly the entries outside [0, n_phys_pages)
+    among the first ceil(prefix_len / page_size); entries past those are not
+    read."""
+    R = rattn()
+    c = synth.WORKLOADS[2]
+    x = synth.make_inputs(c, 2)
+    say("[gpu] block-table check")
+    tab = x["block_table"].astype(np.int32)
+    n = c.n_table
+    t = torch.from_numpy(tab.copy()).to(DEV)
+    assert R.check_block_table(t, c.prefix_len, c.page_size, c.n_phys_pages) == 0
+    bad = tab.copy()
+    pos = [0, 7, n // 2, n - 1]
+    bad[pos] = [-1, c.n_phys_pages, 2 ** 31 - 1, -(2 ** 31)]
+    big = np.concatenate([bad, np.full(100, -5, np.int32)])  # a tail past the prefix's pages
+    tb = torch.from_numpy(big).to(DEV)
+    assert R.check_block_table(tb, c.prefix_len, c.page_size, c.n_phys_pages) == 4
+    assert R.check_block_table(tb, c.prefix_len - c.page_size, c.page_size, c.n_phys_pages) == 3
+    assert R.check_block_table(tb, 0, c.page_size, c.n_phys_pages) == 0
+    assert R.check_block_table(tb, c.prefix_len, c.page_size, 2 ** 31 - 1) == 3
+    # the count over a long table (many passes of the workgroup's stride)
+    rng = np.random.default_rng(5)
+    long = rng.integers(-3, 1003, 300001).astype(np.int32)
+    tl = torch.from_numpy(long).to(DEV)
+    exp = int(((long < 0) | (long >= 1000)).sum())
+    assert R.check_block_table(tl, 300001 * 16, 16, 1000) == exp
+    assert R.check_block_table(tl, 300001 * 16 - 15, 16, 1000) == exp
+
+
 def test_shuffled_table_bitwise_equals_identity():
     """Output depends only on logical token order: a shuffled pool with its table and
     the identity pool give bit-identical results; unused NaN pages change nothing."""
