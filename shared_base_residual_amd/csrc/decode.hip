@@ -321,19 +321,31 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
     if constexpr (CPL > 0) {
         if (resid) {
             if constexpr (MASKED) {
-                frag4 pz;
-                pz.v = bf16x4{};
-                for (int ag = 0; ag < na; ++ag) {
-                    const frag4 pa = arow == ag ? pB : pz;
+                // Two agents per product: the contraction runs over (agent,
+                // token) pairs, slots 0-3 of a lane agent ag's four tokens and
+                // slots 4-7 agent ag + 1's same four tokens, each agent's weights
+                // kept only in its own rows' lanes.  One 16x16x32 product takes
+                // the passes of one 16x16x16 product on this chip.
+                // An odd last agent pairs with itself, its second half weighted 0
+                // (arow never equals na).
+                const bf16x4 z4 = bf16x4{};
+                for (int ag = 0; ag < na; ag += 2) {
+                    const int agb = ag + 1 < na ? ag + 1 : ag;
                     if (ag > 0) {
 #pragma unroll
                         for (int jj = 0; jj < CPL; ++jj) wa[jj] = lds_tr4(lrb + ag * ast + wtr[jj]);
                     }
+                    bf16x4 wb[CPL];
+#pragma unroll
+                    for (int jj = 0; jj < CPL; ++jj) wb[jj] = lds_tr4(lrb + agb * ast + wtr[jj]);
+                    frag pp;
+                    pp.v = __builtin_shufflevector(arow == ag ? pB.v : z4, arow == ag + 1 ? pB.v : z4, 0, 1, 2, 3,
+                                                   4, 5, 6, 7);
 #pragma unroll
                     for (int jj = 0; jj < CPL; ++jj) {
-                        frag4 wA;
-                        wA.v = wa[jj];
-                        acc.w[jj] = O::mma16(wA, pa, acc.w[jj]);
+                        frag wA;
+                        wA.v = __builtin_shufflevector(wa[jj], wb[jj], 0, 1, 2, 3, 4, 5, 6, 7);
+                        acc.w[jj] = O::mma(wA, pp, acc.w[jj]);
                     }
                 }
             } else {
