@@ -103,12 +103,14 @@ __device__ inline void step16(Acc<T, D, CPAD> &acc, const ReadOfs<T, D, CPAD> &r
     // The O and W accumulators are rescaled only on the steps where some row's
     // reference max grows (a branch uniform over the wave); on the others
     // alpha is exactly 1.
-    float mx = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool grow = mx > acc.m + kRescaleSlack;
+    // The cross-lane maximum is formed only on the steps where some lane's own
+    // maximum passes the slack (a row's does iff one of its lanes' does).
+    const float lmx = fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]));
     float alpha = 1.0f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
+    if (__builtin_amdgcn_ballot_w64(lmx > acc.m + kRescaleSlack)) {
+        float mx = fmaxf(lmx, __shfl_xor(lmx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const bool grow = mx > acc.m + kRescaleSlack;
         const float m_new = grow ? mx : acc.m;
         alpha = fexp2(acc.m - m_new);
         acc.m = m_new;
@@ -281,14 +283,16 @@ __device__ inline void step16_bf16(Acc<bf16, D, CPAD> &acc, const ReadOfs<bf16, 
         }
     }
 
-    // online softmax (log2 domain, running max in scaled units)
-    float mx = amax3(a[0], a[1], amax(a[2], a[3]));  // scores are finite or -inf
-    mx = row_max4(mx) * cl2;  // -inf stays -inf
-    const bool grow = mx > acc.m + kRescaleSlack;
-    float alpha = 1.0f;
-    if (__builtin_amdgcn_ballot_w64(grow)) {
+    // online softmax (log2 domain, running max in scaled units).  A row's
+    // maximum passes the slack iff one of its four lanes' maxima does (the
+    // scale is positive and rounding keeps the order), so the cross-lane
+    // maximum is formed only on the steps where some lane's passes.
+    const float lmx = amax3(a[0], a[1], amax(a[2], a[3]));  // scores are finite or -inf
+    if (__builtin_amdgcn_ballot_w64(lmx * cl2 > acc.m + kRescaleSlack)) {
+        const float mx = row_max4(lmx) * cl2;  // -inf stays -inf
+        const bool grow = mx > acc.m + kRescaleSlack;
         const float m_new = grow ? mx : acc.m;
-        alpha = fexp2(acc.m - m_new);
+        const float alpha = fexp2(acc.m - m_new);
         acc.m = m_new;
 #pragma unroll
         for (int i = 0; i < VPL; ++i) acc.o[i] *= alpha;

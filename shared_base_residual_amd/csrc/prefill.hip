@@ -360,36 +360,42 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
                 }
 
                 // online softmax per block (log2 domain); P as the B operand over 32 keys:
-                // slots 0..3 = keys 4*j4+i of the first half, 4..7 = the second half
-                frag pB[NCB];
-                float alpha[NCB];
-                bool any_grow = false;
+                // slots 0..3 = keys 4*j4+i of the first half, 4..7 = the second half.
+                // A row's maximum passes the slack iff one of its four lanes' maxima
+                // does (the scale is positive and rounding keeps the order), so the
+                // cross-lane maxima are formed only on the steps where some lane's
+                // passes.  (Scores are finite or -inf, never NaN.)
+                float lmx[NCB];
+                bool lane_grow = false;
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) {
-                    // (scores are finite or -inf, never NaN)
-                    float mx = amax3(amax3(sc[cb][0][0], sc[cb][0][1], sc[cb][0][2]),
-                                     amax3(sc[cb][0][3], sc[cb][1][0], sc[cb][1][1]), amax(sc[cb][1][2], sc[cb][1][3]));
-                    mx = row_max4(mx) * cl2;  // scaled (log2 units); -inf stays -inf
-                    const bool grow = mx > m[cb] + kRescaleSlack;
-                    const float m_new = grow ? mx : m[cb];
-                    alpha[cb] = fexp2(m[cb] - m_new);
-                    m[cb] = m_new;
-                    any_grow = any_grow || grow;
-                    float e[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) e[i] = fexp2(__builtin_fmaf(sc[cb][i >> 2][i & 3], cl2, -m_new));
-                    pB[cb].v = __builtin_shufflevector(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]),
-                                                       0, 1, 2, 3, 4, 5, 6, 7);
+                    lmx[cb] = amax3(amax3(sc[cb][0][0], sc[cb][0][1], sc[cb][0][2]),
+                                    amax3(sc[cb][0][3], sc[cb][1][0], sc[cb][1][1]), amax(sc[cb][1][2], sc[cb][1][3]));
+                    lane_grow = lane_grow || lmx[cb] * cl2 > m[cb] + kRescaleSlack;
                 }
-                if (__builtin_amdgcn_ballot_w64(any_grow)) {
+                if (__builtin_amdgcn_ballot_w64(lane_grow)) {
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) {
+                        const float mx = row_max4(lmx[cb]) * cl2;  // scaled (log2 units); -inf stays -inf
+                        const bool grow = mx > m[cb] + kRescaleSlack;
+                        const float m_new = grow ? mx : m[cb];
+                        const float alpha = fexp2(m[cb] - m_new);
+                        m[cb] = m_new;
 #pragma unroll
-                        for (int i = 0; i < VPL; ++i) o[cb][i] *= alpha[cb];
+                        for (int i = 0; i < VPL; ++i) o[cb][i] *= alpha;
 #pragma unroll
-                        for (int i = 0; i < CPLx; ++i) w[cb][i] *= alpha[cb];
-                        l[cb] *= alpha[cb];
+                        for (int i = 0; i < CPLx; ++i) w[cb][i] *= alpha;
+                        l[cb] *= alpha;
                     }
+                }
+                frag pB[NCB];
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) {
+                    float e[8];
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) e[i] = fexp2(__builtin_fmaf(sc[cb][i >> 2][i & 3], cl2, -m[cb]));
+                    pB[cb].v = __builtin_shufflevector(to_bf16x4(e[0], e[1], e[2], e[3]), to_bf16x4(e[4], e[5], e[6], e[7]),
+                                                       0, 1, 2, 3, 4, 5, 6, 7);
                 }
                 // row sums on the matrix unit: a ones operand against P^T adds each
                 // row's weights exactly as the P V product takes them (bf16)

@@ -282,10 +282,11 @@ __global__ __launch_bounds__(64 * recon_waves(ROPE, R)) void recon_split_kernel(
             bf16x4 wa[CPL];
 #pragma unroll
             for (int jj = 0; jj < CPL; ++jj) wa[jj] = lds_tr4(lvb + wtr[jj]);
-            float mx = amax3(acc[0], acc[1], amax(acc[2], acc[3]));
-            mx = row_max4(mx) * cl2;
-            const bool grow = mx > m + kRescaleSlack;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
+            // the cross-lane maximum only where some lane's own passes the slack
+            const float lmx = amax3(acc[0], acc[1], amax(acc[2], acc[3]));
+            if (__builtin_amdgcn_ballot_w64(lmx * cl2 > m + kRescaleSlack)) {
+                const float mx = row_max4(lmx) * cl2;
+                const bool grow = mx > m + kRescaleSlack;
                 const float m_new = grow ? mx : m;
                 const float alpha = fexp2(m - m_new);
                 m = m_new;
