@@ -283,9 +283,39 @@ __global__ __launch_bounds__(512) void prefill_kernel(PrefillParams p) {
         const int lr_rowb = 16 * g.cpa_lr;
         const int n_tiles = (t1 - t0 + g.T - 1) / g.T;
         const int fpw = fp.fpw;
+        // contiguous caches with one 16-token group per wave: every wave fills
+        // all regions of its group, straight from per-wave source rows
+        const bool own = p.ps == 0 && (g.T >> 4) == NW;
         auto fill = [&](int tile, int stage) {
             const int tt = t0 + tile * g.T;
-            fill_group<T, D>(fp, g, src, tt, smem + (size_t)stage * g.stage_bytes, tt + g.T - 1 > src.tlast, lane);
+            char *sp = smem + (size_t)stage * g.stage_bytes;
+            if (own && tt + g.T - 1 <= src.tlast) {
+                constexpr int NKV = D * ES / 64;
+                const int tg0 = tt + 16 * wave;
+                const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(sp));
+                const char *kb = uniform_ptr(reinterpret_cast<const char *>(src.kb + (int64_t)tg0 * D));
+                const char *vb = uniform_ptr(reinterpret_cast<const char *>(src.vb + (int64_t)tg0 * D));
+                const uint32_t lk0 = lds0 + 16 * (16 * wave * g.cpr_kv), lv0 = lds0 + 16 * (g.ofs_v + 16 * wave * g.cpr_kv);
+#pragma unroll
+                for (int i = 0; i < NKV; ++i) dma16s(kb, fp.kv_off[i], lk0 + 1024 * i);
+#pragma unroll
+                for (int i = 0; i < NKV; ++i) dma16s(vb, fp.kv_off[i], lv0 + 1024 * i);
+                if (res) {
+                    const char *lk = uniform_ptr(reinterpret_cast<const char *>(src.lk + (int64_t)tg0 * src.r));
+                    const char *lv = uniform_ptr(reinterpret_cast<const char *>(src.lv + (int64_t)tg0 * src.r));
+                    const uint32_t ll0 = lds0 + 16 * (g.ofs_lk + wave * g.lr_grp), lw0 = lds0 + 16 * (g.ofs_lv + wave * g.lr_grp);
+                    for (int i = 0; i < fp.n_lr; ++i) {
+                        if (64 * i + lane < g.lr_grp) {
+                            int row;
+                            const uint32_t off = lr_lane_off(fp.lr_stride, g, i, lane, &row);
+                            dma16s(lk, off, ll0 + 1024 * i);
+                            dma16s(lv, off, lw0 + 1024 * i);
+                        }
+                    }
+                }
+                return;
+            }
+            fill_group<T, D>(fp, g, src, tt, sp, tt + g.T - 1 > src.tlast, lane);
         };
         for (int i = 0; i < g.nst - 1 && i < n_tiles; ++i) fill(i, i);
 
