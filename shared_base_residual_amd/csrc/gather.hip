@@ -3,7 +3,8 @@
 // Logical base token j of KV head k lives in slot j % page of physical page
 // table[j / page] (the page table plays the part of the bCache block pointers
 // of the ForkKV Guide's DualRadixTree lookup).  Pure data movement: 16-byte
-// vector copies, byte-exact.
+// vector copies, byte-exact.  Also the optional debug check of a table: a
+// count of its entries outside the pool, reading nothing but the table.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
